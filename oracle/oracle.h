@@ -1,0 +1,115 @@
+/*
+ * oracle.h -- CPU reference for C = A_sparse * B_dense.
+ *
+ * TEST INFRASTRUCTURE.  This library exists to check the HIP path; only the
+ * test suite, the smoke check and the benchmark's CPU-baseline leg may load
+ * it.  It shares no code, header, table or helper with the HIP library, and
+ * the HIP library never calls it.
+ *
+ * Everything here is a plain loop, in the order the definition states:
+ *   - floating point is widened exactly to double and summed in double, over
+ *     the stored entries of a row in ascending column order;
+ *   - int8 products are formed in int32 and summed in int64.
+ * OpenMP splits work over output rows only, so no element's summation order
+ * depends on the thread count.
+ *
+ * Sources (cited by page title and the part of the page):
+ *   [AS]  "AsyncSparse: Accelerating Sparse Matrix-Matrix Multiplication on
+ *         Asynchronous GPU Architectures" -- abstract; Figure 2 caption
+ *         (BCSR vs WCSR formats); summary paragraph "What carries the
+ *         argument" (row-window splitting across thread blocks).
+ *   [MC]  "Efficient Quantized Sparse Matrix Operations on Tensor Cores" --
+ *         abstract (SpMM on low-precision integers).
+ *   [TW]  "Accelerating Sparse DNNs Based on Tiled GEMM" -- abstract (the 2:4
+ *         pattern of the sparse tensor core; tile-wise sparsity).
+ *   [DP]  "Daily Papers" search page for sparse FP4 GEMM -- the entry on
+ *         block-sparse SpMM for Transformer inference on CPUs (SpMM as sparse
+ *         matrix times dense matrix) and the entry on N:M sparse training
+ *         (N of every M consecutive elements nonzero).
+ */
+#ifndef SDM_ORACLE_H
+#define SDM_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- exact conversions ------------------------------------------------- */
+double orc_bf16_to_double(uint16_t h);
+
+/* ---- BCSR packing [AS abstract, Fig. 2] -------------------------------- */
+/* Count the bm x bk blocks of the dense row-major bf16 matrix that hold at
+ * least one nonzero (bits & 0x7FFF != 0: +0 and -0 are zero, NaN is not).
+ * Returns the count, or -1 when m % bm or k % bk is nonzero or lda < k. */
+int64_t orc_bcsr_count(int64_t m, int64_t k, int32_t bm, int32_t bk,
+                       const uint16_t *a, int64_t lda);
+/* Fill row_ptr[m/bm + 1], col_idx[nnzb], vals[nnzb * bm * bk] (each block
+ * row-major), block rows ascending, block columns ascending. */
+void orc_bcsr_fill(int64_t m, int64_t k, int32_t bm, int32_t bk,
+                   const uint16_t *a, int64_t lda,
+                   int32_t *row_ptr, int32_t *col_idx, uint16_t *vals);
+/* Dense double image of a BCSR matrix (for brute-force checks). */
+void orc_bcsr_densify(int64_t m, int64_t k, int32_t bm, int32_t bk,
+                      const int32_t *row_ptr, const int32_t *col_idx,
+                      const uint16_t *vals, double *out);
+
+/* ---- CSR validation and row windows [AS abstract, Fig. 2] --------------- */
+/* 0 if canonical; otherwise a positive code:
+ *   1 row_ptr[0] != 0     2 row_ptr decreasing     3 row_ptr[m] != nnz
+ *   4 column out of [0,k) 5 columns not strictly ascending in a row */
+int orc_csr_check(int64_t m, int64_t k, int64_t nnz,
+                  const int64_t *row_ptr, const int32_t *col_idx);
+/* Number of chunks when windows of W rows are cut into pieces of at most T
+ * stored entries: each window contributes max(1, ceil(nnz_w / T)). */
+int64_t orc_wcsr_num_chunks(int64_t m, const int64_t *row_ptr, int32_t W, int64_t T);
+/* chunk_window[C] and chunk_begin[C + 1] (last entry = nnz). */
+void orc_wcsr_chunks(int64_t m, const int64_t *row_ptr, int32_t W, int64_t T,
+                     int32_t *chunk_window, int64_t *chunk_begin);
+void orc_csr_densify(int64_t m, int64_t k, const int64_t *row_ptr,
+                     const int32_t *col_idx, const float *vals, double *out);
+
+/* ---- 2:4 packing [TW abstract; DP N:M entry] ---------------------------- */
+/* For every group of 4 consecutive elements along k keep the two of largest
+ * |a| (as int, so -128 -> 128), ties to the lower index, stored in ascending
+ * index order: vals[i*(k/2) + 2g + {0,1}], and the two 2-bit positions as the
+ * nibble (i0 | i1 << 2) of meta[i*(k/8) + g/2], low nibble for even g.
+ * Returns 0, or -1 when k % 8 != 0 or lda < k. */
+int orc_pack24(int64_t m, int64_t k, const int8_t *a, int64_t lda,
+               int8_t *vals, uint8_t *meta);
+void orc_densify24(int64_t m, int64_t k, const int8_t *vals, const uint8_t *meta,
+                   int8_t *out);
+
+/* ---- reference products [AS abstract; MC abstract; DP SpMM entry] ------- */
+/* out[r][j - j0] = sum over stored (rows[r], c) in ascending c of
+ * A[rows[r]][c] * B[c][j], for j in [j0, j1).  out is row-major with
+ * (j1 - j0) columns. */
+void orc_csr_spmm_rows(const int64_t *row_ptr, const int32_t *col_idx, const float *vals,
+                       const float *B, int64_t ldb,
+                       int64_t nrows, const int64_t *rows, int64_t j0, int64_t j1,
+                       double *out);
+void orc_bcsr_spmm_rows(int32_t bm, int32_t bk, const int32_t *row_ptr,
+                        const int32_t *col_idx, const uint16_t *vals,
+                        const uint16_t *B, int64_t ldb,
+                        int64_t nrows, const int64_t *rows, int64_t j0, int64_t j1,
+                        double *out);
+/* int8 2:4: returns the number of sums with |sum| >= 2^31 (0 when exact). */
+int64_t orc_sp24_spmm_rows(int64_t k, const int8_t *vals, const uint8_t *meta,
+                           const int8_t *B, int64_t ldb,
+                           int64_t nrows, const int64_t *rows, int64_t j0, int64_t j1,
+                           int32_t *out);
+
+/* ---- brute force (dense, naive triple loops) ---------------------------- */
+void orc_gemm_f64(int64_t m, int64_t k, int64_t n, const double *A, const double *B,
+                  double *C);
+void orc_gemm_i8(int64_t m, int64_t k, int64_t n, const int8_t *A, const int8_t *B,
+                 int64_t *C);
+
+/* Number of OpenMP threads the reference loops use. */
+int orc_num_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

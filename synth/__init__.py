@@ -1,0 +1,253 @@
+"""Seeded synthetic inputs for sparse x dense multiplication (C = A_sparse * B_dense).
+
+This module only *draws* inputs: sparsity patterns, values and dense operands.
+It holds none of the multiplication's arithmetic and none of the packing rules,
+so both the CPU oracle and the HIP path can be fed from it without sharing any
+of the method.
+
+Random streams come from numpy's Philox bit generator (the counter-based
+Philox4x64-10 of Salmon et al., "Parallel random numbers: as easy as 1, 2, 3",
+SC'11).  Every stream is keyed by (seed, stream id), so each operand of a
+workload is reproducible on its own.
+
+Workloads follow the shapes the AsyncSparse page (abstract) benchmarks on --
+block-structured sparsity at 90% for a 7B-model MLP weight with 64K tokens, and
+irregular matrices from a public sparse-matrix collection -- and the 2:4 int8
+case of the tile-wise / Magicube pages.  The public matrix collection and the
+model weights are not available; the power-law CSR and the uniform block masks
+stand in for them.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict
+
+import numpy as np
+
+# stream ids: one independent Philox key per random quantity of a workload
+S_PATTERN, S_AVAL, S_BVAL, S_ROWLEN, S_COLS, S_BAND = 0, 1, 2, 3, 4, 5
+
+
+def rng(seed: int, stream: int) -> np.random.Generator:
+    """Philox generator for (seed, stream)."""
+    return np.random.Generator(np.random.Philox(key=(int(seed) << 16) | int(stream)))
+
+
+# ---------------------------------------------------------------------------
+# value formatting (input preparation only)
+# ---------------------------------------------------------------------------
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16, round-to-nearest-even, returned as uint16 bits.
+
+    Inputs are finite (nothing here draws NaN or Inf)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(h: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bits to float32."""
+    return (np.asarray(h, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def normal_f32(g: np.random.Generator, shape, sigma: float = 1.0) -> np.ndarray:
+    x = g.standard_normal(size=shape, dtype=np.float32)
+    if sigma != 1.0:
+        x *= np.float32(sigma)
+    return x
+
+
+def uniform_pm1_f32(g: np.random.Generator, shape) -> np.ndarray:
+    """U[-1, 1) in float32."""
+    x = g.random(size=shape, dtype=np.float32)
+    return x * np.float32(2.0) - np.float32(1.0)
+
+
+def int8_uniform(g: np.random.Generator, shape) -> np.ndarray:
+    """Integers uniform on {-127 ... 127}."""
+    return g.integers(-127, 128, size=shape, dtype=np.int8)
+
+
+# ---------------------------------------------------------------------------
+# sparse patterns
+# ---------------------------------------------------------------------------
+def csr_uniform(m: int, k: int, density: float, seed: int):
+    """CSR with exactly round(density*m*k) nonzeros at uniform random positions
+    (chosen without replacement), values U[-1,1) float32.
+
+    Returns (row_ptr int64[m+1], col_idx int32[nnz], vals float32[nnz])."""
+    total = m * k
+    nnz = int(round(density * total))
+    pos = np.sort(rng(seed, S_PATTERN).choice(total, size=nnz, replace=False))
+    rows = pos // k
+    cols = (pos % k).astype(np.int32)
+    vals = uniform_pm1_f32(rng(seed, S_AVAL), nnz)
+    row_ptr = np.zeros(m + 1, dtype=np.int64)
+    np.cumsum(np.bincount(rows, minlength=m), out=row_ptr[1:])
+    return row_ptr, cols, vals
+
+
+def zipf_lengths(m: int, exponent: float, cap: int, seed: int) -> np.ndarray:
+    """Row lengths L with P(L = j) proportional to j^-exponent on {1..cap}."""
+    j = np.arange(1, cap + 1, dtype=np.float64)
+    p = j ** (-exponent)
+    cdf = np.cumsum(p)
+    cdf /= cdf[-1]
+    u = rng(seed, S_ROWLEN).random(m)
+    return (np.searchsorted(cdf, u, side="right") + 1).astype(np.int64)
+
+
+def csr_powerlaw(m: int, k: int, exponent: float, cap: int, band_frac: float,
+                 band_half: int, seed: int):
+    """Irregular CSR: power-law row lengths, a fraction of the columns drawn
+    within +/-band_half of the diagonal and the rest uniform on [0, k).
+
+    Per draw: with probability band_frac the column is uniform on
+    [max(0, i-band_half), min(k-1, i+band_half)], else uniform on [0, k).
+    Duplicate (row, col) draws are collapsed keeping the first drawn value,
+    so a row can end up shorter than its drawn length.  Values U[-1,1).
+    """
+    lens = np.minimum(zipf_lengths(m, exponent, cap, seed), k)
+    total = int(lens.sum())
+    rows = np.repeat(np.arange(m, dtype=np.int64), lens)
+    banded = rng(seed, S_BAND).random(total) < band_frac
+    lo = np.maximum(rows - band_half, 0)
+    width = np.where(banded, np.minimum(rows + band_half, k - 1) - lo + 1, k)
+    lo[~banded] = 0
+    del banded
+    u = rng(seed, S_COLS).random(total)
+    u *= width
+    cols = lo + u.astype(np.int64)
+    del lo, width, u
+    np.minimum(cols, k - 1, out=cols)
+    vals = uniform_pm1_f32(rng(seed, S_AVAL), total)
+    # rows are already grouped; order each row by (col, draw order) and keep
+    # the first draw of every (row, col)
+    cols += rows * np.int64(k)
+    order = np.argsort(cols, kind="stable")
+    key = cols[order]
+    del cols
+    keep = np.empty(total, dtype=bool)
+    keep[0] = True
+    np.not_equal(key[1:], key[:-1], out=keep[1:])
+    order = order[keep]
+    key = key[keep]
+    col_idx = (key % np.int64(k)).astype(np.int32)
+    vals = vals[order]
+    row_ptr = np.zeros(m + 1, dtype=np.int64)
+    np.cumsum(np.bincount(key // np.int64(k), minlength=m), out=row_ptr[1:])
+    return row_ptr, col_idx, vals
+
+
+def block_sparse_dense_bf16(m: int, k: int, bm: int, bk: int, nblocks: int,
+                            sigma: float, seed: int):
+    """Dense row-major bf16 matrix (uint16 bits) that is zero except on exactly
+    `nblocks` bm x bk blocks chosen uniformly without replacement; values in
+    those blocks N(0, sigma) rounded to bf16.  Returns (a, block_ids)."""
+    mb, kb = m // bm, k // bk
+    ids = np.sort(rng(seed, S_PATTERN).choice(mb * kb, size=nblocks, replace=False))
+    a = np.zeros((m, k), dtype=np.uint16)
+    vals = f32_to_bf16_bits(normal_f32(rng(seed, S_AVAL), (nblocks, bm, bk), sigma))
+    for t, b in enumerate(ids):
+        r, c = divmod(int(b), kb)
+        a[r * bm:(r + 1) * bm, c * bk:(c + 1) * bk] = vals[t]
+    return a, ids
+
+
+def dense_bf16_normal(rows: int, cols: int, seed: int, stream: int = S_BVAL,
+                      sigma: float = 1.0, chunk_rows: int = 256) -> np.ndarray:
+    """Dense row-major bf16 (uint16 bits) N(0, sigma), drawn in row slabs to
+    bound the float32 temporary."""
+    out = np.empty((rows, cols), dtype=np.uint16)
+    g = rng(seed, stream)
+    for r0 in range(0, rows, chunk_rows):
+        r1 = min(rows, r0 + chunk_rows)
+        out[r0:r1] = f32_to_bf16_bits(normal_f32(g, (r1 - r0, cols), sigma))
+    return out
+
+
+def dense_f32_normal(rows: int, cols: int, seed: int, stream: int = S_BVAL) -> np.ndarray:
+    return normal_f32(rng(seed, stream), (rows, cols))
+
+
+# ---------------------------------------------------------------------------
+# workload catalogue
+# ---------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    fmt: str            # "wcsr" | "bcsr" | "sp24"
+    m: int
+    k: int
+    n: int
+    seed: int
+    density: float = 0.0          # wcsr uniform
+    powerlaw: bool = False        # wcsr power-law
+    zipf: float = 1.8
+    cap: int = 20000
+    band_frac: float = 0.3
+    band_half: int = 512
+    block: int = 64               # bcsr
+    nblocks: int = 0
+    sigma: float = 0.02
+
+    @property
+    def describe(self) -> str:
+        return f"{self.name} ({self.fmt}, m={self.m}, k={self.k}, n={self.n})"
+
+
+def _bcsr(name, m, k, n, zero_frac, seed, block=64):
+    total = (m // block) * (k // block)
+    return Workload(name, "bcsr", m, k, n, seed, block=block,
+                    nblocks=int(round((1.0 - zero_frac) * total)))
+
+
+# The five benchmark shapes (seed 20260000 + index) ...
+WORKLOADS: Dict[str, Workload] = {
+    "csr_tiny_256": Workload("csr_tiny_256", "wcsr", 256, 256, 64, 20260001, density=0.05),
+    "bcsr_4096_b64_90": _bcsr("bcsr_4096_b64_90", 4096, 4096, 4096, 0.90, 20260002),
+    "csr_powerlaw_1m": Workload("csr_powerlaw_1m", "wcsr", 1_000_000, 1_000_000, 128, 20260003,
+                                powerlaw=True),
+    "sp24_i8_8192": Workload("sp24_i8_8192", "sp24", 8192, 8192, 2048, 20260004),
+    "bcsr_prefill_18944x3584": _bcsr("bcsr_prefill_18944x3584", 18944, 3584, 65536, 0.90, 20260005),
+}
+
+# ... and smaller cases of the same construction for element-wise parity
+# (several tiles plus a ragged tail in every dimension the kernels tile).
+SMALL: Dict[str, Workload] = {
+    "csr_uniform_small": Workload("csr_uniform_small", "wcsr", 1000, 777, 200, 31, density=0.03),
+    "csr_powerlaw_small": Workload("csr_powerlaw_small", "wcsr", 20000, 20000, 128, 32,
+                                   powerlaw=True, cap=3000, band_half=64),
+    "bcsr_small": _bcsr("bcsr_small", 640, 512, 1000, 0.7, 33),
+    "sp24_small": Workload("sp24_small", "sp24", 320, 512, 400, 34),
+    "bcsr_prefill_slice": _bcsr("bcsr_prefill_slice", 18944, 3584, 4096 + 64 * 3, 0.90, 20260005),
+}
+
+
+def make_a(w: Workload) -> dict:
+    """Draw the sparse operand.  wcsr -> CSR arrays; bcsr -> dense bf16 bits;
+    sp24 -> dense int8 (not yet pruned: pruning is the packer's job)."""
+    if w.fmt == "wcsr":
+        if w.powerlaw:
+            rp, ci, v = csr_powerlaw(w.m, w.k, w.zipf, w.cap, w.band_frac, w.band_half, w.seed)
+        else:
+            rp, ci, v = csr_uniform(w.m, w.k, w.density, w.seed)
+        return {"row_ptr": rp, "col_idx": ci, "vals": v}
+    if w.fmt == "bcsr":
+        a, ids = block_sparse_dense_bf16(w.m, w.k, w.block, w.block, w.nblocks, w.sigma, w.seed)
+        return {"dense": a, "block_ids": ids}
+    if w.fmt == "sp24":
+        return {"dense": int8_uniform(rng(w.seed, S_AVAL), (w.m, w.k))}
+    raise ValueError(w.fmt)
+
+
+def make_b(w: Workload, n: int | None = None) -> np.ndarray:
+    """Draw the dense operand B [k x n] row-major."""
+    n = w.n if n is None else n
+    if w.fmt == "wcsr":
+        return dense_f32_normal(w.k, n, w.seed)
+    if w.fmt == "bcsr":
+        return dense_bf16_normal(w.k, n, w.seed)
+    if w.fmt == "sp24":
+        return int8_uniform(rng(w.seed, S_BVAL), (w.k, n))
+    raise ValueError(w.fmt)

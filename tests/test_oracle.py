@@ -1,0 +1,303 @@
+"""Pins for the CPU oracle: hand-worked fixtures, brute force, closed forms and
+invariants.  None of these re-types the oracle's own loops: each compares it
+with something the definitions fix independently (a hand computation, numpy's
+dense matmul on the densified matrix, an identity or permutation product, a
+numpy re-derivation of the 2:4 selection rule).
+
+Sources: AsyncSparse abstract and Figure 2 caption (BCSR, WCSR, row-window
+splitting); Magicube abstract (int8 SpMM); tiled-GEMM abstract (2:4 pattern);
+search-results page entries on N:M sparsity and on SpMM.
+"""
+import numpy as np
+import pytest
+
+import synth
+from conftest import read_golden
+
+# ---------------------------------------------------------------------------
+# hand-worked fixtures
+# ---------------------------------------------------------------------------
+
+
+def test_golden_pack24(orc):
+    g = read_golden("pack24_hand.txt")
+    a = np.array(g["a"], dtype=np.int8)
+    vals, meta = orc.pack24(a)
+    np.testing.assert_array_equal(vals, np.array(g["vals"], dtype=np.int8))
+    np.testing.assert_array_equal(meta, np.array(g["meta"], dtype=np.uint8))
+    k = a.shape[1]
+    B = np.zeros((k, 2), dtype=np.int8)
+    B[:, 0] = np.arange(1, k + 1)
+    B[:, 1] = np.where(np.arange(k) % 2 == 0, 2, -2)
+    c = orc.sp24_spmm(vals, meta, B)
+    np.testing.assert_array_equal(c, np.array(g["c"], dtype=np.int32))
+
+
+def test_golden_csr(orc):
+    g = read_golden("csr_hand.txt")
+    rp = np.array(g["row_ptr"][0], dtype=np.int64)
+    ci = np.array(g["col_idx"][0], dtype=np.int32)
+    v = np.array(g["vals"][0], dtype=np.float32)
+    B = np.array(g["b"], dtype=np.float32)
+    m = g["m"][0][0]
+    assert orc.csr_check(m, g["k"][0][0], rp, ci) == 0
+    c = orc.csr_spmm(rp, ci, v, B)
+    np.testing.assert_array_equal(c, np.array(g["c"], dtype=np.float64))
+    for W, T in ((2, 1), (2, 2), (1, 8)):
+        cw, cb = orc.wcsr_chunks(m, rp, W, T)
+        np.testing.assert_array_equal(cw, g[f"chunks W={W} T={T} window"][0])
+        np.testing.assert_array_equal(cb, g[f"chunks W={W} T={T} begin"][0])
+
+
+def test_golden_bcsr(orc):
+    g = read_golden("bcsr_hand.txt")
+    a = np.array(g["a"], dtype=np.uint16)
+    bm, bk = g["block"][0]
+    rp, ci, v = orc.pack_bcsr(a, bm, bk)
+    np.testing.assert_array_equal(rp, g["row_ptr"][0])
+    np.testing.assert_array_equal(ci, g["col_idx"][0])
+    np.testing.assert_array_equal(v.reshape(len(ci), -1), np.array(g["vals"], dtype=np.uint16))
+    B = synth.f32_to_bf16_bits(np.array(g["b"], dtype=np.float32))
+    c = orc.bcsr_spmm(bm, bk, rp, ci, v, B)
+    np.testing.assert_array_equal(c, np.array(g["c"], dtype=np.float64))
+
+
+def test_bf16_widening(orc):
+    # bit patterns whose values are fixed by the IEEE binary32 layout
+    assert orc.bf16_to_double(0x3F80) == 1.0
+    assert orc.bf16_to_double(0xC000) == -2.0
+    assert orc.bf16_to_double(0x3F00) == 0.5
+    assert orc.bf16_to_double(0x0001) == 2.0 ** -133   # smallest subnormal
+    assert orc.bf16_to_double(0x7F7F) == (2 - 2 ** -7) * 2.0 ** 127
+
+
+# ---------------------------------------------------------------------------
+# brute force on tiny random inputs: oracle vs numpy dense matmul of the
+# densified matrix (a library routine that shares nothing with the oracle)
+# ---------------------------------------------------------------------------
+
+
+def _np_dense_from_csr(m, k, rp, ci, v):
+    d = np.zeros((m, k), dtype=np.float64)
+    rows = np.repeat(np.arange(m), np.diff(rp))
+    d[rows, ci] = v
+    return d
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_csr_bruteforce(orc, seed):
+    r = np.random.default_rng(seed)
+    m, k, n = (int(x) for x in r.integers(1, 97, size=3))
+    rp, ci, v = synth.csr_uniform(m, k, float(r.uniform(0.0, 0.4)), 1000 + seed)
+    B = r.standard_normal((k, n)).astype(np.float32)
+    got = orc.csr_spmm(rp, ci, v, B)
+    dense = _np_dense_from_csr(m, k, rp, ci, v)
+    np.testing.assert_array_equal(orc.csr_densify(m, k, rp, ci, v), dense)
+    ref = dense @ B.astype(np.float64)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+    # the oracle's own naive dense GEMM agrees exactly: same k order, and the
+    # zero products it adds do not change a double sum
+    np.testing.assert_array_equal(got + 0.0, orc.gemm_f64(dense, B.astype(np.float64)) + 0.0)
+    # a row subset and a column slab are slices of the full product
+    rows = np.sort(r.choice(m, size=max(1, m // 3), replace=False)).astype(np.int64)
+    j0, j1 = sorted(int(x) for x in r.integers(0, n + 1, size=2))
+    np.testing.assert_array_equal(orc.csr_spmm(rp, ci, v, B, rows=rows, j0=j0, j1=j1),
+                                  got[rows][:, j0:j1])
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_bcsr_bruteforce(orc, seed):
+    r = np.random.default_rng(100 + seed)
+    bm, bk = (int(x) for x in r.choice([1, 2, 4, 8, 16], size=2))
+    mb, kb = (int(x) for x in r.integers(1, 7, size=2))
+    m, k, n = mb * bm, kb * bk, int(r.integers(1, 70))
+    nblocks = int(r.integers(0, mb * kb + 1))
+    a, ids = synth.block_sparse_dense_bf16(m, k, bm, bk, nblocks, 0.5, 2000 + seed)
+    rp, ci, v = orc.pack_bcsr(a, bm, bk)
+    # block mask = the drawn blocks (N(0,0.5) never rounds a whole block to 0)
+    assert len(ci) == nblocks
+    assert sorted(int(x) for x in (np.repeat(np.arange(mb), np.diff(rp)) * kb + ci)) == \
+        sorted(int(x) for x in ids)
+    dense = synth.bf16_bits_to_f32(a).astype(np.float64)
+    np.testing.assert_array_equal(orc.bcsr_densify(m, k, bm, bk, rp, ci, v), dense)
+    Bb = synth.f32_to_bf16_bits(r.standard_normal((k, n)).astype(np.float32))
+    got = orc.bcsr_spmm(bm, bk, rp, ci, v, Bb)
+    ref = dense @ synth.bf16_bits_to_f32(Bb).astype(np.float64)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def _np_prune24(a):
+    """2:4 selection re-derived with numpy: stable argsort of -|a| per group."""
+    m, k = a.shape
+    g = a.reshape(m, k // 4, 4).astype(np.int64)
+    order = np.argsort(-np.abs(g), axis=2, kind="stable")[:, :, :2]
+    keep = np.zeros_like(g, dtype=bool)
+    np.put_along_axis(keep, order, True, axis=2)
+    return np.where(keep, g, 0).reshape(m, k).astype(np.int8)
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_sp24_bruteforce(orc, seed):
+    r = np.random.default_rng(300 + seed)
+    m, n = int(r.integers(1, 97)), int(r.integers(1, 97))
+    k = 8 * int(r.integers(1, 13))
+    # small alphabets force ties; full range covers -128
+    lo, hi = [(-2, 3), (-128, 128), (-127, 128)][seed % 3]
+    a = r.integers(lo, hi, size=(m, k)).astype(np.int8)
+    vals, meta = orc.pack24(a)
+    pruned = orc.densify24(vals, meta)
+    np.testing.assert_array_equal(pruned, _np_prune24(a))
+    # the pruned matrix is 2:4 and idempotent under packing
+    assert ((pruned.reshape(m, k // 4, 4) != 0).sum(axis=2) <= 2).all()
+    v2, m2 = orc.pack24(pruned)
+    np.testing.assert_array_equal(v2, vals)
+    np.testing.assert_array_equal(m2, meta)
+    # every stored pair is in ascending position order
+    nib = np.stack([meta & 0xF, meta >> 4], axis=2).reshape(m, k // 4)
+    assert ((nib & 3) < (nib >> 2)).all()
+    B = r.integers(-128, 128, size=(k, n)).astype(np.int8)
+    got = orc.sp24_spmm(vals, meta, B)
+    ref = pruned.astype(np.int64) @ B.astype(np.int64)
+    np.testing.assert_array_equal(got, ref)
+    np.testing.assert_array_equal(orc.gemm_i8(pruned, B), ref)
+
+
+# ---------------------------------------------------------------------------
+# closed forms
+# ---------------------------------------------------------------------------
+
+
+def test_identity_and_permutation_csr(orc):
+    n, m = 37, 50
+    r = np.random.default_rng(7)
+    B = r.standard_normal((m, n)).astype(np.float32)
+    rp = np.arange(m + 1, dtype=np.int64)
+    ci = np.arange(m, dtype=np.int32)
+    np.testing.assert_array_equal(orc.csr_spmm(rp, ci, np.ones(m, np.float32), B), B)
+    perm = r.permutation(m).astype(np.int32)
+    # row i of P holds a one at column perm[i] -> (P B)[i] = B[perm[i]]
+    np.testing.assert_array_equal(orc.csr_spmm(rp, perm, np.ones(m, np.float32), B), B[perm])
+    for e in (-3, 0, 5):
+        got = orc.csr_spmm(rp, ci, np.full(m, 2.0 ** e, np.float32), B)
+        np.testing.assert_array_equal(got, B.astype(np.float64) * 2.0 ** e)
+
+
+def test_identity_and_permutation_bcsr(orc):
+    bm = 4
+    m = 6 * bm
+    r = np.random.default_rng(8)
+    B = synth.f32_to_bf16_bits(r.standard_normal((m, 29)).astype(np.float32))
+    Bf = synth.bf16_bits_to_f32(B).astype(np.float64)
+    eye = synth.f32_to_bf16_bits(np.eye(m, dtype=np.float32))
+    rp, ci, v = orc.pack_bcsr(eye, bm, bm)
+    assert len(ci) == m // bm                      # only diagonal blocks stored
+    np.testing.assert_array_equal(orc.bcsr_spmm(bm, bm, rp, ci, v, B), Bf)
+    perm = r.permutation(m)
+    P = np.zeros((m, m), dtype=np.float32)
+    P[np.arange(m), perm] = 1.0
+    rp, ci, v = orc.pack_bcsr(synth.f32_to_bf16_bits(P), bm, bm)
+    np.testing.assert_array_equal(orc.bcsr_spmm(bm, bm, rp, ci, v, B), Bf[perm])
+    # single nonzero a at (i, k): row i = a * B[k], all other rows zero
+    S = np.zeros((m, m), dtype=np.float32)
+    S[5, 17] = -0.375
+    rp, ci, v = orc.pack_bcsr(synth.f32_to_bf16_bits(S), bm, bm)
+    got = orc.bcsr_spmm(bm, bm, rp, ci, v, B)
+    exp = np.zeros_like(got)
+    exp[5] = -0.375 * Bf[17]
+    np.testing.assert_array_equal(got, exp)
+
+
+def test_identity_and_linearity_sp24(orc):
+    m = 64
+    eye = np.eye(m, dtype=np.int8)
+    vals, meta = orc.pack24(eye)
+    np.testing.assert_array_equal(orc.densify24(vals, meta), eye)   # I is 2:4 already
+    r = np.random.default_rng(9)
+    B1 = r.integers(-64, 64, size=(m, 33)).astype(np.int8)
+    B2 = r.integers(-63, 64, size=(m, 33)).astype(np.int8)
+    np.testing.assert_array_equal(orc.sp24_spmm(vals, meta, B1), B1.astype(np.int32))
+    a = r.integers(-127, 128, size=(40, m)).astype(np.int8)
+    v, mt = orc.pack24(a)
+    lhs = orc.sp24_spmm(v, mt, (B1.astype(np.int16) + B2).astype(np.int8))
+    rhs = orc.sp24_spmm(v, mt, B1).astype(np.int64) + orc.sp24_spmm(v, mt, B2)
+    np.testing.assert_array_equal(lhs, rhs)
+
+
+def test_sp24_extreme_sum_is_exact(orc):
+    # |C| = (k/2) * 128 * 128 with every kept value -128 and B = -128:
+    # k = 8192 gives 4096 * 16384 = 2^26, well inside int32
+    k = 8192
+    a = np.full((2, k), -128, dtype=np.int8)
+    v, mt = orc.pack24(a)
+    B = np.full((k, 3), -128, dtype=np.int8)
+    np.testing.assert_array_equal(orc.sp24_spmm(v, mt, B), np.full((2, 3), (k // 2) * 16384))
+
+
+# ---------------------------------------------------------------------------
+# invariants of the packers
+# ---------------------------------------------------------------------------
+
+
+def test_bcsr_zero_matrix(orc):
+    a = np.zeros((128, 192), dtype=np.uint16)
+    a[5, 7] = 0x8000    # -0.0 is zero
+    rp, ci, v = orc.pack_bcsr(a, 64, 64)
+    assert len(ci) == 0 and (rp == 0).all()
+    B = synth.f32_to_bf16_bits(np.ones((192, 10), np.float32))
+    assert (orc.bcsr_spmm(64, 64, rp, ci, v, B) == 0).all()
+
+
+def test_bcsr_nan_block_kept(orc):
+    a = np.zeros((64, 128), dtype=np.uint16)
+    a[3, 70] = 0x7FC0   # NaN counts as nonzero
+    rp, ci, v = orc.pack_bcsr(a, 64, 64)
+    assert list(ci) == [1] and list(rp) == [0, 1]
+
+
+def test_bcsr_rejects_ragged(orc):
+    with pytest.raises(ValueError):
+        orc.pack_bcsr(np.zeros((65, 64), dtype=np.uint16), 64, 64)
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_wcsr_chunk_invariants(orc, seed):
+    r = np.random.default_rng(500 + seed)
+    m = int(r.integers(1, 400))
+    lens = r.integers(0, 3, size=m) * r.integers(0, 60, size=m)
+    rp = np.zeros(m + 1, dtype=np.int64)
+    np.cumsum(lens, out=rp[1:])
+    W, T = int(r.integers(1, 40)), int(r.integers(1, 200))
+    cw, cb = orc.wcsr_chunks(m, rp, W, T)
+    nnz = int(rp[-1])
+    assert cb[0] == 0 and cb[-1] == nnz and (np.diff(cb) >= 0).all()
+    assert (np.diff(cw) >= 0).all() and cw[-1] == (m - 1) // W
+    expected = 0
+    for w in range((m + W - 1) // W):
+        s, e = int(rp[w * W]), int(rp[min(m, (w + 1) * W)])
+        mine = np.nonzero(cw == w)[0]
+        assert len(mine) >= 1
+        expected += max(1, -(-(e - s) // T))
+        assert cb[mine[0]] == s and cb[mine[-1] + 1] == e           # covers the window
+        assert (np.diff(cb[mine[0]:mine[-1] + 2]) <= T).all()        # at most T each
+        if e - s <= T:
+            assert len(mine) == 1
+    assert len(cw) == expected
+
+
+def test_csr_check_codes(orc):
+    rp = np.array([0, 2, 2, 4], dtype=np.int64)
+    ci = np.array([1, 3, 0, 2], dtype=np.int32)
+    assert orc.csr_check(3, 4, rp, ci) == 0
+    assert orc.csr_check(3, 4, np.array([1, 2, 2, 4]), ci) == 1
+    assert orc.csr_check(3, 4, np.array([0, 3, 2, 4]), ci) == 2
+    assert orc.csr_check(3, 4, np.array([0, 2, 2, 3]), ci) == 3
+    assert orc.csr_check(3, 4, rp, np.array([1, 4, 0, 2])) == 4
+    assert orc.csr_check(3, 4, rp, np.array([3, 1, 0, 2])) == 5
+    assert orc.csr_check(3, 4, rp, np.array([1, 1, 0, 2])) == 5
+
+
+def test_rel_frobenius(orc):
+    assert orc.rel_frobenius([3.0, 4.0], [3.0, 4.0]) == 0.0
+    assert orc.rel_frobenius([3.0, 4.0 + 5e-3], [3.0, 4.0]) == pytest.approx(1e-3)
+    assert orc.rel_frobenius([0.0], [0.0]) == 0.0
+    assert orc.rel_frobenius([1.0], [0.0]) == float("inf")

@@ -1,0 +1,247 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse x dense multiply C = A_sparse * B_dense on one MI355X.
+
+A step is one spmm_execute (every kernel the plan launches) over one dense B
+that is already resident in HBM; packing and planning are one-time costs,
+reported separately.  The default workload is the 4096 x 4096 BCSR bf16
+matrix with 90% of its 64 x 64 blocks zero and B of 4096 columns; the other
+workloads of the catalogue run with --workload.
+
+Prints one JSON line:
+  value      effective GFLOP/s = 2 * nnz * n / (time per step)
+  roofline   the dominant kernel against its bound (MFMA peak of its dtype,
+             or HBM bandwidth for the irregular CSR), from HIP events over
+             the timed region on the stream the kernels run on
+  cpu_baseline  the CPU oracle timed on a bounded sample of rows of the same
+             workload (a reported baseline, not a target)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "SpMM effective GFLOP/s (2*nnz*N) and % of HBM/MFMA roofline on 1 MI355X"
+HEADLINE = "bcsr_4096_b64_90"
+
+# MI355X published peaks
+PEAK_HBM_GBS = 8000.0
+PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "i8": 5000.0}
+
+
+def log(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--window-rows", type=int, default=None)
+    ap.add_argument("--max-chunk-nnz", type=int, default=None)
+    return ap.parse_args()
+
+
+def setup(w, S, args):
+    """Draw inputs, pack and plan.  Returns a dict describing the workload."""
+    import synth
+    t0 = time.perf_counter()
+    a = synth.make_a(w)
+    B = synth.make_b(w)
+    t_gen = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    if w.fmt == "bcsr":
+        M = S.spmm_pack_bcsr(a["dense"], w.block, w.block)
+        types = (S.BF16, S.BF16)
+    elif w.fmt == "wcsr":
+        W = args.window_rows or S.DEFAULT_WINDOW_ROWS
+        T = args.max_chunk_nnz or S.DEFAULT_MAX_CHUNK_NNZ
+        M = S.spmm_pack_wcsr(w.m, w.k, a["row_ptr"], a["col_idx"], a["vals"], W, T)
+        types = (S.F32, S.F32)
+    else:
+        M = S.spmm_pack_24(a["dense"])
+        types = (S.I8, S.I32)
+    t_pack = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    P = S.spmm_plan(M, w.n, *types)
+    t_plan = time.perf_counter() - t0
+    info = S.spmm_matrix_info(M)
+    return {"a": a, "B": B, "M": M, "P": P, "info": info, "t_gen": t_gen, "t_pack": t_pack,
+            "t_plan": t_plan}
+
+
+def algorithmic(w, d):
+    """(flops, bytes, dtype) of one step.  bytes = compulsory HBM traffic:
+    the packed operand once, every B row the sparse operand touches once, and
+    C written once."""
+    info = d["info"]
+    n = w.n
+    flops = 2.0 * info["nnz"] * n
+    if w.fmt == "bcsr":
+        nnzb = info["nnzb"]
+        mb = w.m // w.block
+        import sparse_dense_matrix_amd as S
+        cols = np.unique(S.spmm_matrix_array(d["M"], S.ARRAY_COL_IDX))
+        a_bytes = nnzb * w.block * w.block * 2 + 4 * (mb + 1) + 4 * nnzb
+        b_bytes = len(cols) * w.block * n * 2
+        c_bytes = w.m * n * 2
+        return flops, a_bytes + b_bytes + c_bytes, "bf16"
+    if w.fmt == "wcsr":
+        nnz = info["nnz"]
+        touched = len(np.unique(d["a"]["col_idx"]))
+        a_bytes = 8 * (w.m + 1) + 8 * nnz
+        return flops, a_bytes + touched * n * 4 + w.m * n * 4, "f32"
+    a_bytes = w.m * w.k // 2 + w.m * w.k // 8
+    return flops, a_bytes + w.k * n + w.m * n * 4, "i8"
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU: the multiply shards by columns "
+                                   "of B with no communication, but only the one-GPU path is "
+                                   "built and measured; run with --gpus 1"}), flush=True)
+        sys.exit(2)
+    import torch
+    import synth
+    import sparse_dense_matrix_amd as S
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        sys.exit(1)
+    cat = dict(synth.WORKLOADS)
+    cat.update(synth.SMALL)
+    if args.workload not in cat:
+        log(f"unknown workload {args.workload}; choose from {sorted(cat)}")
+        sys.exit(2)
+    w = cat[args.workload]
+    log(f"workload {w.describe}")
+    d = setup(w, S, args)
+    log(f"generated in {d['t_gen']:.1f}s, packed in {d['t_pack']:.2f}s, planned in {d['t_plan']:.2f}s")
+
+    # device operands
+    B = d["B"]
+    Bh = torch.from_numpy(B.view(np.int16) if B.dtype == np.uint16 else B)
+    Bt = Bh.cuda()
+    cdt = {"bcsr": torch.int16, "wcsr": torch.float32, "sp24": torch.int32}[w.fmt]
+    Ct = torch.empty((w.m, w.n), dtype=cdt, device="cuda")
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        S.spmm_execute(d["P"], Bt, Ct, stream=stream)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        S.spmm_execute(d["P"], Bt, Ct, stream=stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / args.steps
+    log(f"{args.steps} steps: {ms_total:.3f} ms on the stream, {wall * 1e3:.3f} ms wall")
+
+    flops, nbytes, dtype = algorithmic(w, d)
+    gflops = flops / (ms_step * 1e-3) / 1e9
+    if w.fmt == "wcsr":
+        achieved = nbytes / (ms_step * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+    else:
+        achieved = flops / (ms_step * 1e-3) / 1e12
+        peak = PEAK_MFMA_TFLOPS[dtype]
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None}
+    pinfo = S.spmm_plan_info(d["P"])
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, d, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(gflops, 1),
+        "unit": "GFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded; shapes and sparsity of the pages' workloads)",
+        "config": {"workload": w.name, "format": w.fmt, "m": w.m, "k": w.k, "n": w.n,
+                   "nnz": d["info"]["nnz"], "nnzb": d["info"]["nnzb"],
+                   "num_chunks": d["info"]["num_chunks"],
+                   "split_rows": pinfo["num_split_rows"], "grid": pinfo["grid"],
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "hbm_compulsory": {"bytes": int(nbytes),
+                           "GB_s": round(nbytes / (ms_step * 1e-3) / 1e9, 1),
+                           "frac": round(nbytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "one_time_s": {"generate": round(d["t_gen"], 3), "pack": round(d["t_pack"], 3),
+                       "plan": round(d["t_plan"], 3)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(w, d, target_s):
+    """Time the oracle on a growing sample of rows until it takes about
+    target_s; report effective GFLOP/s over the sampled rows."""
+    import oracle
+    a, B = d["a"], d["B"]
+    r = np.random.default_rng(0)
+    if w.fmt == "bcsr":
+        rp, ci, v = oracle.pack_bcsr(a["dense"], w.block, w.block)
+        row_nnz = np.repeat(np.diff(rp).astype(np.int64) * w.block, w.block)
+
+        def run(rows):
+            oracle.bcsr_spmm(w.block, w.block, rp, ci, v, B, rows=rows)
+    elif w.fmt == "wcsr":
+        row_nnz = np.diff(a["row_ptr"])
+
+        def run(rows):
+            oracle.csr_spmm(a["row_ptr"], a["col_idx"], a["vals"], B, rows=rows)
+    else:
+        vals, meta = oracle.pack24(a["dense"])
+        row_nnz = np.full(w.m, w.k // 2, dtype=np.int64)
+
+        def run(rows):
+            oracle.sp24_spmm(vals, meta, B, rows=rows)
+    perm = r.permutation(w.m).astype(np.int64)
+    count, spent, rows = 8, 0.0, None
+    while True:
+        rows = np.sort(perm[:count])
+        t0 = time.perf_counter()
+        run(rows)
+        spent = time.perf_counter() - t0
+        if spent >= target_s or count >= w.m:
+            break
+        grow = max(2.0, min(8.0, 0.9 * target_s / max(spent, 1e-3)))
+        count = min(w.m, int(count * grow))
+    flops = 2.0 * float(row_nnz[rows].sum()) * w.n
+    log(f"cpu oracle: {len(rows)} rows in {spent:.2f}s on {oracle.num_threads()} threads")
+    return {"value": round(flops / spent / 1e9, 3), "unit": "GFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{len(rows)} of {w.m} rows (uniform without replacement, seed 0), "
+                      f"all {w.n} columns; fp64 accumulation"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,190 @@
+/*
+ * spmm.h -- C ABI of the MI355X (gfx950) sparse x dense multiplication library.
+ *
+ * The library computes C = A * B, A sparse, B and C dense, for three sparse
+ * encodings:
+ *
+ *   BCSR  block compressed sparse row, bf16 A and B, fp32 accumulation,
+ *         bf16 C.  Block-structured sparsity: "AsyncSparse: Accelerating
+ *         Sparse Matrix-Matrix Multiplication on Asynchronous GPU
+ *         Architectures", abstract and Figure 2 caption.
+ *   WCSR  CSR processed in windows of consecutive rows whose stored entries
+ *         are cut into bounded chunks, so one long window is spread over many
+ *         workgroups; fp32 A, B, C.  Irregular sparsity: same page, abstract
+ *         and the summary's "What carries the argument" paragraph
+ *         (row-window splitting across thread blocks for load balance).
+ *   2:4   int8 A pruned so that every group of 4 consecutive elements along k
+ *         holds at most 2 nonzeros, stored compressed with 2-bit positions;
+ *         int8 B, exact int32 C.  "Accelerating Sparse DNNs Based on Tiled
+ *         GEMM", abstract (2:4 pattern); "Efficient Quantized Sparse Matrix
+ *         Operations on Tensor Cores", abstract (SpMM on low-precision
+ *         integers); the N:M entry of the "Daily Papers" search page.
+ *
+ * Usage: pack A once on the host (spmm_pack_*), build a device plan for a
+ * given number of columns n (spmm_plan), then multiply any number of dense B
+ * by it (spmm_execute) on the caller's HIP stream.
+ *
+ * Conventions for every call:
+ *   - Each call returns a status.  On failure any out-parameter is set to
+ *     NULL, nothing leaks, and spmm_last_error() returns a message (per
+ *     thread).  No exception or abort crosses the ABI.
+ *   - Dense matrices are row-major with a leading dimension (elements between
+ *     consecutive rows).
+ *   - Integers in the ABI are signed 64-bit unless stated; row and column
+ *     counts must fit in int32.
+ */
+#ifndef SPMM_H
+#define SPMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* HIP stream handle, as in hip_runtime_api.h (NULL = the legacy default stream). */
+typedef struct ihipStream_t *hipStream_t;
+
+typedef enum {
+  SPMM_OK = 0,
+  SPMM_ERR_INVALID_ARG = 1,   /* bad pointer, size, layout or non-canonical input   */
+  SPMM_ERR_UNSUPPORTED = 2,   /* valid request outside what the kernels implement   */
+  SPMM_ERR_OUT_OF_MEMORY = 3, /* host or device allocation failed                   */
+  SPMM_ERR_HIP = 4,           /* a HIP runtime call failed; message holds its text  */
+  SPMM_ERR_INTERNAL = 5
+} spmm_status_t;
+
+typedef enum { SPMM_F32 = 0, SPMM_BF16 = 1, SPMM_I8 = 2, SPMM_I32 = 3 } spmm_dtype_t;
+
+typedef enum { SPMM_FORMAT_BCSR = 0, SPMM_FORMAT_WCSR = 1, SPMM_FORMAT_24 = 2 } spmm_format_t;
+
+/* Packed sparse operand: immutable host arrays in the canonical layout below,
+ * reference counted (a plan holds a reference). */
+typedef struct spmm_matrix_s *spmm_matrix_t;
+/* Device copy of a packed operand plus kernel choice and workspace, for one n. */
+typedef struct spmm_plan_s *spmm_plan_t;
+
+typedef struct {
+  int32_t format;        /* spmm_format_t                                      */
+  int32_t dtype;         /* element type of A                                  */
+  int64_t m, k;          /* logical shape of A                                 */
+  int64_t nnz;           /* stored entries: nnzb*bm*bk, CSR nnz, or m*k/2      */
+  int64_t nnzb;          /* BCSR: stored blocks; otherwise 0                   */
+  int32_t block_m, block_k;        /* BCSR block shape; otherwise 0            */
+  int32_t window_rows;             /* WCSR: rows per window W; otherwise 0     */
+  int64_t max_chunk_nnz;           /* WCSR: chunk bound T; otherwise 0         */
+  int64_t num_windows, num_chunks; /* WCSR; otherwise 0                        */
+} spmm_matrix_info_t;
+
+/* Canonical arrays, read with spmm_matrix_array(which):
+ *  BCSR (nnzb blocks, mb = m / block_m block rows)
+ *    SPMM_ARRAY_ROW_PTR   int32[mb + 1]   blocks of block row r: [row_ptr[r], row_ptr[r+1])
+ *    SPMM_ARRAY_COL_IDX   int32[nnzb]     block column, ascending within a block row
+ *    SPMM_ARRAY_VALS      bf16 bits, uint16[nnzb * bm * bk], each block row-major
+ *  WCSR
+ *    SPMM_ARRAY_ROW_PTR   int64[m + 1]
+ *    SPMM_ARRAY_COL_IDX   int32[nnz]      strictly ascending within a row
+ *    SPMM_ARRAY_VALS      float[nnz]
+ *    SPMM_ARRAY_CHUNK_WINDOW  int32[num_chunks]    window of each chunk
+ *    SPMM_ARRAY_CHUNK_BEGIN   int64[num_chunks+1]  first stored entry; last = nnz
+ *  2:4
+ *    SPMM_ARRAY_VALS      int8[m * k/2]   the two kept values of group g of row i at
+ *                                         [i*k/2 + 2g], [i*k/2 + 2g + 1], ascending position
+ *    SPMM_ARRAY_META      uint8[m * k/8]  nibble (i0 | i1 << 2) of group g in byte
+ *                                         i*k/8 + g/2, low nibble for even g            */
+typedef enum {
+  SPMM_ARRAY_ROW_PTR = 0,
+  SPMM_ARRAY_COL_IDX = 1,
+  SPMM_ARRAY_VALS = 2,
+  SPMM_ARRAY_META = 3,
+  SPMM_ARRAY_CHUNK_WINDOW = 4,
+  SPMM_ARRAY_CHUNK_BEGIN = 5
+} spmm_array_t;
+
+/* ---- packing (host only; inputs are borrowed for the call and copied) ---- */
+
+/* BCSR from a dense row-major bf16 matrix a_host [m x k] (uint16 bit patterns,
+ * leading dimension lda >= k).  A block_m x block_k block is stored when any
+ * element is numerically nonzero (+0 and -0 are zero, NaN is not); block rows
+ * ascending, block columns ascending, values row-major within the block.
+ * Requires dtype == SPMM_BF16 (else UNSUPPORTED), m % block_m == 0 and
+ * k % block_k == 0 (else INVALID_ARG).  The kernels take 64 x 64 blocks. */
+spmm_status_t spmm_pack_bcsr(int64_t m, int64_t k, int32_t block_m, int32_t block_k,
+                             spmm_dtype_t dtype, const void *a_host, int64_t lda,
+                             spmm_matrix_t *out);
+
+/* WCSR from a canonical CSR on the host: row_ptr int64[m+1] with row_ptr[0] = 0,
+ * non-decreasing; col_idx int32[nnz] strictly ascending within each row and in
+ * [0, k); vals float[nnz] (explicit zeros are kept).  Anything else is
+ * INVALID_ARG, never silently fixed.  Rows are grouped into windows of
+ * window_rows rows; a window holding at most max_chunk_nnz entries is one
+ * chunk (even when empty), a longer one is cut into ceil(nnz_w / T) chunks of
+ * T consecutive entries (the last one shorter).  dtype must be SPMM_F32. */
+spmm_status_t spmm_pack_wcsr(int64_t m, int64_t k, spmm_dtype_t dtype,
+                             const int64_t *row_ptr, const int32_t *col_idx,
+                             const void *vals, int32_t window_rows,
+                             int64_t max_chunk_nnz, spmm_matrix_t *out);
+
+/* 2:4 from a dense row-major int8 matrix a_host [m x k] (lda >= k): in every
+ * group of 4 consecutive elements of a row keep the two of largest |a| (as
+ * integers: |-128| = 128), ties to the lower position, and store them with
+ * their 2-bit positions as described above.  Packing an already 2:4 matrix is
+ * lossless.  Requires k % 8 == 0. */
+spmm_status_t spmm_pack_24(int64_t m, int64_t k, const int8_t *a_host, int64_t lda,
+                           spmm_matrix_t *out);
+
+spmm_status_t spmm_matrix_info(spmm_matrix_t a, spmm_matrix_info_t *info);
+/* Read-only view of a canonical array, valid while the matrix lives.
+ * *count receives the number of elements.  INVALID_ARG if the format has no
+ * such array. */
+spmm_status_t spmm_matrix_array(spmm_matrix_t a, int32_t which, const void **data,
+                                int64_t *count);
+/* Drop the caller's reference (plans keep their own); NULL is ignored. */
+void spmm_matrix_destroy(spmm_matrix_t a);
+
+/* ---- plan (host -> device, synchronous) ---- */
+
+/* Copy the packed operand to device `device`, choose the kernel and tiles
+ * for n columns, and allocate the workspace.  Supported (b_dtype, c_dtype):
+ *   BCSR (64 x 64 blocks): (BF16, BF16), n % 8 == 0
+ *   WCSR:                  (F32, F32), any n >= 1
+ *   2:4:                   (I8, I32), n % 16 == 0
+ * anything else is UNSUPPORTED.  n = 0 is allowed (execute does nothing). */
+spmm_status_t spmm_plan(spmm_matrix_t a, int64_t n, spmm_dtype_t b_dtype,
+                        spmm_dtype_t c_dtype, int32_t device, spmm_plan_t *out);
+
+typedef struct {
+  int32_t format;
+  int32_t device;
+  int64_t m, k, n;
+  int64_t device_bytes;     /* packed operand + tables on the device          */
+  int64_t workspace_bytes;  /* WCSR partial rows of split windows             */
+  int64_t num_split_rows;   /* WCSR rows whose entries span several chunks    */
+  int64_t num_slots;        /* WCSR partial rows                              */
+  int32_t tile_m, tile_n;   /* output tile of one workgroup                   */
+  int64_t grid;             /* workgroups of the main kernel                  */
+} spmm_plan_info_t;
+spmm_status_t spmm_plan_info(spmm_plan_t p, spmm_plan_info_t *info);
+void spmm_plan_destroy(spmm_plan_t p);
+
+/* ---- execute (asynchronous on the caller's stream) ---- */
+
+/* C = A * B on `stream`; every element of C[m x n] is overwritten (rows of A
+ * without entries give zeros).  b_dev [k x n] and c_dev [m x n] are device
+ * pointers on the plan's device, 16-byte aligned, with ldb >= n, ldc >= n and
+ * ldb * elem, ldc * elem multiples of 16 bytes.  Allocates nothing and does
+ * not synchronise; launch errors are returned, faults surface at the caller's
+ * next synchronisation.  A plan's workspace allows one execute in flight at a
+ * time: concurrent streams need separate plans.  B and C must not overlap. */
+spmm_status_t spmm_execute(spmm_plan_t p, const void *b_dev, int64_t ldb, void *c_dev,
+                           int64_t ldc, hipStream_t stream);
+
+/* ---- errors ---- */
+const char *spmm_status_str(spmm_status_t s);
+/* Message of the last failing call on this thread ("" if none). */
+const char *spmm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPMM_H */

@@ -1,0 +1,490 @@
+// api.cpp -- the C ABI of spmm.h: argument checks, object lifetimes, device
+// upload and per-format launch dispatch.
+#include <algorithm>
+#include <cstdarg>
+#include <cstring>
+#include <new>
+
+#include "internal.h"
+
+namespace sdm {
+
+static thread_local std::string g_last_error;
+
+spmm_status_t fail(spmm_status_t s, const std::string &msg) {
+  g_last_error = msg;
+  return s;
+}
+
+spmm_status_t hip_fail(hipError_t e, const char *what) {
+  g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+  return e == hipErrorOutOfMemory ? SPMM_ERR_OUT_OF_MEMORY : SPMM_ERR_HIP;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+void retain(Matrix *a) { a->refs.fetch_add(1, std::memory_order_relaxed); }
+
+void release(Matrix *a) {
+  if (a && a->refs.fetch_sub(1, std::memory_order_acq_rel) == 1)
+    delete static_cast<spmm_matrix_s *>(a);
+}
+
+namespace {
+
+template <class F>
+spmm_status_t guarded(F &&f) {
+  try {
+    return f();
+  } catch (const std::bad_alloc &) {
+    return fail(SPMM_ERR_OUT_OF_MEMORY, "host allocation failed");
+  } catch (const std::exception &e) {
+    return fail(SPMM_ERR_INTERNAL, e.what());
+  } catch (...) {
+    return fail(SPMM_ERR_INTERNAL, "unknown exception");
+  }
+}
+
+// Restores the caller's current device on scope exit.
+struct DeviceScope {
+  int prev = -1;
+  hipError_t err = hipSuccess;
+  explicit DeviceScope(int dev) {
+    err = hipGetDevice(&prev);
+    if (err == hipSuccess && prev != dev) err = hipSetDevice(dev);
+  }
+  ~DeviceScope() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+void free_plan(spmm_plan_s *p) {
+  if (!p) return;
+  if (!p->allocations.empty()) {
+    DeviceScope ds(p->device);
+    for (void *ptr : p->allocations) (void)hipFree(ptr);
+  }
+  release(p->a);
+  delete p;
+}
+
+// hipMalloc + copy; the pointer is owned by the plan.
+spmm_status_t upload(spmm_plan_s *p, const void *src, size_t bytes, void **dst) {
+  *dst = nullptr;
+  if (bytes == 0) bytes = 16;  // keep every table pointer valid
+  void *d = nullptr;
+  hipError_t e = hipMalloc(&d, bytes);
+  if (e != hipSuccess) return hip_fail(e, "hipMalloc");
+  p->allocations.push_back(d);
+  p->info.device_bytes += static_cast<int64_t>(bytes);
+  if (src) {
+    e = hipMemcpy(d, src, bytes, hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpy");
+  }
+  *dst = d;
+  return SPMM_OK;
+}
+
+template <class T>
+spmm_status_t upload_vec(spmm_plan_s *p, const std::vector<T> &v, T **dst) {
+  void *d = nullptr;
+  spmm_status_t s = upload(p, v.empty() ? nullptr : v.data(), v.size() * sizeof(T), &d);
+  *dst = static_cast<T *>(d);
+  return s;
+}
+
+// ---- BCSR plan ---------------------------------------------------------------
+spmm_status_t plan_bcsr(spmm_plan_s *p) {
+  const Matrix &a = *p->a;
+  if (a.bm != 64 || a.bk != 64)
+    return fail(SPMM_ERR_UNSUPPORTED, "spmm_plan: BCSR kernels take 64 x 64 blocks");
+  if (p->n % 8 != 0) return fail(SPMM_ERR_UNSUPPORTED, "spmm_plan: BCSR needs n % 8 == 0");
+  const int64_t nnzb = static_cast<int64_t>(a.bcol_idx.size());
+  std::vector<uint16_t> frag(a.bvals.size());
+  for (int64_t b = 0; b < nnzb; ++b) bcsr_fragment_order(a.bvals.data() + b * 4096, frag.data() + b * 4096);
+  BcsrLaunch &L = p->bcsr;
+  int32_t *rp = nullptr, *ci = nullptr;
+  uint16_t *fv = nullptr;
+  spmm_status_t s;
+  if ((s = upload_vec(p, a.brow_ptr, &rp)) != SPMM_OK) return s;
+  if ((s = upload_vec(p, a.bcol_idx, &ci)) != SPMM_OK) return s;
+  if ((s = upload_vec(p, frag, &fv)) != SPMM_OK) return s;
+  L.row_ptr = rp;
+  L.col_idx = ci;
+  L.frag = fv;
+  L.mb = static_cast<int32_t>(a.m / 64);
+  L.n = p->n;
+  p->info.tile_m = 64;
+  p->info.tile_n = bcsr_tile_n();
+  p->info.grid = bcsr_grid(L.mb, p->n);
+  return SPMM_OK;
+}
+
+// ---- WCSR plan: chunk descriptors, split rows and their partial slots ------
+spmm_status_t plan_wcsr(spmm_plan_s *p) {
+  const Matrix &a = *p->a;
+  const int64_t m = a.m, W = a.window_rows;
+  const int64_t C = static_cast<int64_t>(a.chunk_window.size());
+  const int64_t *rp = a.row_ptr.data();
+  std::vector<WcsrChunk> chunks(C);
+  std::vector<int32_t> slot_row;  // row of each partial slot, in slot order
+  for (int64_t c = 0; c < C; ++c) {
+    const int64_t w = a.chunk_window[c];
+    const int64_t r0 = w * W, r1 = std::min(m, r0 + W);
+    const int64_t b = a.chunk_begin[c], e = a.chunk_begin[c + 1];
+    const bool last_of_window = (e == rp[r1]);
+    int64_t rb = -1, re = -1;
+    for (int64_t r = r0; r < r1; ++r) {
+      const int64_t s0 = rp[r], s1 = rp[r + 1];
+      bool mine;
+      if (s0 == s1)  // empty row: owned by the chunk whose range holds its position
+        mine = (b <= s0 && s0 < e) || (s0 == e && last_of_window);
+      else
+        mine = s0 < e && s1 > b;
+      if (mine) {
+        if (rb < 0) rb = r;
+        re = r + 1;
+      }
+    }
+    if (rb < 0) return fail(SPMM_ERR_INTERNAL, "spmm_plan: chunk without rows");
+    WcsrChunk &d = chunks[c];
+    d.nz_begin = b;
+    d.nz_end = e;
+    d.row_begin = static_cast<int32_t>(rb);
+    d.row_end = static_cast<int32_t>(re);
+    d.slot_first = d.slot_last = -1;
+    auto split = [&](int64_t r) { return rp[r] != rp[r + 1] && (rp[r] < b || rp[r + 1] > e); };
+    if (split(rb)) {
+      d.slot_first = static_cast<int32_t>(slot_row.size());
+      slot_row.push_back(static_cast<int32_t>(rb));
+    }
+    if (re - 1 == rb) {
+      d.slot_last = d.slot_first;
+    } else if (split(re - 1)) {
+      d.slot_last = static_cast<int32_t>(slot_row.size());
+      slot_row.push_back(static_cast<int32_t>(re - 1));
+    }
+  }
+  // slots of one split row are consecutive: group them
+  std::vector<int32_t> merge_row, merge_slot;
+  for (size_t s = 0; s < slot_row.size(); ++s) {
+    if (s == 0 || slot_row[s] != slot_row[s - 1]) {
+      merge_row.push_back(slot_row[s]);
+      merge_slot.push_back(static_cast<int32_t>(s));
+    }
+  }
+  merge_slot.push_back(static_cast<int32_t>(slot_row.size()));
+  for (size_t q = 0; q + 1 < merge_slot.size(); ++q)
+    if (merge_slot[q + 1] - merge_slot[q] < 2)
+      return fail(SPMM_ERR_INTERNAL, "spmm_plan: split row with a single piece");
+
+  WcsrLaunch &L = p->wcsr;
+  spmm_status_t s;
+  WcsrChunk *dchunks = nullptr;
+  int64_t *drp = nullptr;
+  int32_t *dci = nullptr, *dmr = nullptr, *dms = nullptr;
+  float *dv = nullptr;
+  if ((s = upload_vec(p, chunks, &dchunks)) != SPMM_OK) return s;
+  if ((s = upload_vec(p, a.row_ptr, &drp)) != SPMM_OK) return s;
+  if ((s = upload_vec(p, a.col_idx, &dci)) != SPMM_OK) return s;
+  if ((s = upload_vec(p, a.vals, &dv)) != SPMM_OK) return s;
+  if ((s = upload_vec(p, merge_row, &dmr)) != SPMM_OK) return s;
+  if ((s = upload_vec(p, merge_slot, &dms)) != SPMM_OK) return s;
+  const int64_t ws_bytes = static_cast<int64_t>(slot_row.size()) * p->n * 4;
+  void *ws = nullptr;
+  if ((s = upload(p, nullptr, static_cast<size_t>(ws_bytes), &ws)) != SPMM_OK) return s;
+  p->info.device_bytes -= std::max<int64_t>(ws_bytes, 16);
+  L.chunks = dchunks;
+  L.num_chunks = C;
+  L.row_ptr = drp;
+  L.col_idx = dci;
+  L.vals = dv;
+  L.merge_row = dmr;
+  L.merge_slot = dms;
+  L.num_split_rows = static_cast<int64_t>(merge_row.size());
+  L.partial = static_cast<float *>(ws);
+  L.n = p->n;
+  p->info.workspace_bytes = ws_bytes;
+  p->info.num_split_rows = L.num_split_rows;
+  p->info.num_slots = static_cast<int64_t>(slot_row.size());
+  p->info.tile_m = 0;
+  p->info.tile_n = 0;
+  p->info.grid = wcsr_grid(C, p->n);
+  return SPMM_OK;
+}
+
+// ---- 2:4 plan: rows and k padded to whole tiles with zeros -----------------
+spmm_status_t plan_24(spmm_plan_s *p) {
+  const Matrix &a = *p->a;
+  if (p->n % 16 != 0) return fail(SPMM_ERR_UNSUPPORTED, "spmm_plan: 2:4 needs n % 16 == 0");
+  const int64_t TM = sp24_tile_m(), TK = sp24_tile_k();
+  const int64_t m_pad = (a.m + TM - 1) / TM * TM;
+  const int64_t k_pad = std::max<int64_t>(TK, (a.k + TK - 1) / TK * TK);
+  std::vector<int8_t> v(static_cast<size_t>(m_pad * (k_pad / 2)), 0);
+  std::vector<uint8_t> mt(static_cast<size_t>(m_pad * (k_pad / 8)), 0);
+  for (int64_t i = 0; i < a.m; ++i) {
+    std::memcpy(v.data() + i * (k_pad / 2), a.vals24.data() + i * (a.k / 2), a.k / 2);
+    std::memcpy(mt.data() + i * (k_pad / 8), a.meta24.data() + i * (a.k / 8), a.k / 8);
+  }
+  Sp24Launch &L = p->sp24;
+  spmm_status_t s;
+  int8_t *dv = nullptr;
+  uint8_t *dm = nullptr;
+  if ((s = upload_vec(p, v, &dv)) != SPMM_OK) return s;
+  if ((s = upload_vec(p, mt, &dm)) != SPMM_OK) return s;
+  L.vals = dv;
+  L.meta = dm;
+  L.m = a.m;
+  L.k = a.k;
+  L.n = p->n;
+  L.m_pad = m_pad;
+  L.k_pad = k_pad;
+  p->info.tile_m = sp24_tile_m();
+  p->info.tile_n = sp24_tile_n();
+  p->info.grid = sp24_grid(a.m, p->n);
+  return SPMM_OK;
+}
+
+bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+}  // namespace
+}  // namespace sdm
+
+using namespace sdm;
+
+extern "C" {
+
+const char *spmm_status_str(spmm_status_t s) {
+  switch (s) {
+    case SPMM_OK: return "SPMM_OK";
+    case SPMM_ERR_INVALID_ARG: return "SPMM_ERR_INVALID_ARG";
+    case SPMM_ERR_UNSUPPORTED: return "SPMM_ERR_UNSUPPORTED";
+    case SPMM_ERR_OUT_OF_MEMORY: return "SPMM_ERR_OUT_OF_MEMORY";
+    case SPMM_ERR_HIP: return "SPMM_ERR_HIP";
+    case SPMM_ERR_INTERNAL: return "SPMM_ERR_INTERNAL";
+  }
+  return "SPMM_ERR_UNKNOWN";
+}
+
+const char *spmm_last_error(void) { return g_last_error.c_str(); }
+
+spmm_status_t spmm_pack_bcsr(int64_t m, int64_t k, int32_t block_m, int32_t block_k,
+                             spmm_dtype_t dtype, const void *a_host, int64_t lda,
+                             spmm_matrix_t *out) {
+  if (!out) return fail(SPMM_ERR_INVALID_ARG, "spmm_pack_bcsr: out is NULL");
+  *out = nullptr;
+  if (dtype != SPMM_BF16) return fail(SPMM_ERR_UNSUPPORTED, "spmm_pack_bcsr: only bf16 values");
+  if (m < 0 || k < 0 || m > INT32_MAX || k > INT32_MAX || block_m <= 0 || block_k <= 0 ||
+      m % block_m != 0 || k % block_k != 0 || lda < k || (m * k > 0 && !a_host))
+    return fail(SPMM_ERR_INVALID_ARG, "spmm_pack_bcsr: bad shape, block, lda or pointer");
+  return guarded([&]() -> spmm_status_t {
+    auto *a = new spmm_matrix_s();
+    spmm_status_t s = pack_bcsr_bf16(m, k, block_m, block_k,
+                                     static_cast<const uint16_t *>(a_host), lda, *a);
+    if (s != SPMM_OK) {
+      delete a;
+      return s;
+    }
+    *out = a;
+    return SPMM_OK;
+  });
+}
+
+spmm_status_t spmm_pack_wcsr(int64_t m, int64_t k, spmm_dtype_t dtype,
+                             const int64_t *row_ptr, const int32_t *col_idx,
+                             const void *vals, int32_t window_rows,
+                             int64_t max_chunk_nnz, spmm_matrix_t *out) {
+  if (!out) return fail(SPMM_ERR_INVALID_ARG, "spmm_pack_wcsr: out is NULL");
+  *out = nullptr;
+  if (dtype != SPMM_F32) return fail(SPMM_ERR_UNSUPPORTED, "spmm_pack_wcsr: only fp32 values");
+  if (m < 0 || k < 0 || m > INT32_MAX - 1 || k > INT32_MAX || !row_ptr || window_rows <= 0 ||
+      max_chunk_nnz <= 0)
+    return fail(SPMM_ERR_INVALID_ARG, "spmm_pack_wcsr: bad shape, window, chunk bound or pointer");
+  return guarded([&]() -> spmm_status_t {
+    auto *a = new spmm_matrix_s();
+    spmm_status_t s = pack_wcsr_f32(m, k, row_ptr, col_idx, static_cast<const float *>(vals),
+                                    window_rows, max_chunk_nnz, *a);
+    if (s != SPMM_OK) {
+      delete a;
+      return s;
+    }
+    *out = a;
+    return SPMM_OK;
+  });
+}
+
+spmm_status_t spmm_pack_24(int64_t m, int64_t k, const int8_t *a_host, int64_t lda,
+                           spmm_matrix_t *out) {
+  if (!out) return fail(SPMM_ERR_INVALID_ARG, "spmm_pack_24: out is NULL");
+  *out = nullptr;
+  if (m < 0 || k < 0 || m > INT32_MAX || k > INT32_MAX || k % 8 != 0 || lda < k ||
+      (m * k > 0 && !a_host))
+    return fail(SPMM_ERR_INVALID_ARG, "spmm_pack_24: bad shape (k % 8 == 0 needed), lda or pointer");
+  return guarded([&]() -> spmm_status_t {
+    auto *a = new spmm_matrix_s();
+    spmm_status_t s = pack_24_i8(m, k, a_host, lda, *a);
+    if (s != SPMM_OK) {
+      delete a;
+      return s;
+    }
+    *out = a;
+    return SPMM_OK;
+  });
+}
+
+spmm_status_t spmm_matrix_info(spmm_matrix_t a, spmm_matrix_info_t *info) {
+  if (!a || !info) return fail(SPMM_ERR_INVALID_ARG, "spmm_matrix_info: NULL argument");
+  std::memset(info, 0, sizeof(*info));
+  info->format = a->format;
+  info->dtype = a->dtype;
+  info->m = a->m;
+  info->k = a->k;
+  info->nnz = a->nnz;
+  if (a->format == SPMM_FORMAT_BCSR) {
+    info->nnzb = static_cast<int64_t>(a->bcol_idx.size());
+    info->block_m = a->bm;
+    info->block_k = a->bk;
+  } else if (a->format == SPMM_FORMAT_WCSR) {
+    info->window_rows = a->window_rows;
+    info->max_chunk_nnz = a->max_chunk_nnz;
+    info->num_windows = (a->m + a->window_rows - 1) / a->window_rows;
+    info->num_chunks = static_cast<int64_t>(a->chunk_window.size());
+  }
+  return SPMM_OK;
+}
+
+spmm_status_t spmm_matrix_array(spmm_matrix_t a, int32_t which, const void **data,
+                                int64_t *count) {
+  if (!a || !data || !count) return fail(SPMM_ERR_INVALID_ARG, "spmm_matrix_array: NULL argument");
+  *data = nullptr;
+  *count = 0;
+  auto give = [&](const auto &v) {
+    *data = v.data();
+    *count = static_cast<int64_t>(v.size());
+    return SPMM_OK;
+  };
+  switch (a->format) {
+    case SPMM_FORMAT_BCSR:
+      if (which == SPMM_ARRAY_ROW_PTR) return give(a->brow_ptr);
+      if (which == SPMM_ARRAY_COL_IDX) return give(a->bcol_idx);
+      if (which == SPMM_ARRAY_VALS) return give(a->bvals);
+      break;
+    case SPMM_FORMAT_WCSR:
+      if (which == SPMM_ARRAY_ROW_PTR) return give(a->row_ptr);
+      if (which == SPMM_ARRAY_COL_IDX) return give(a->col_idx);
+      if (which == SPMM_ARRAY_VALS) return give(a->vals);
+      if (which == SPMM_ARRAY_CHUNK_WINDOW) return give(a->chunk_window);
+      if (which == SPMM_ARRAY_CHUNK_BEGIN) return give(a->chunk_begin);
+      break;
+    case SPMM_FORMAT_24:
+      if (which == SPMM_ARRAY_VALS) return give(a->vals24);
+      if (which == SPMM_ARRAY_META) return give(a->meta24);
+      break;
+  }
+  return fail(SPMM_ERR_INVALID_ARG, "spmm_matrix_array: no such array for this format");
+}
+
+void spmm_matrix_destroy(spmm_matrix_t a) { release(a); }
+
+spmm_status_t spmm_plan(spmm_matrix_t a, int64_t n, spmm_dtype_t b_dtype, spmm_dtype_t c_dtype,
+                        int32_t device, spmm_plan_t *out) {
+  if (!out) return fail(SPMM_ERR_INVALID_ARG, "spmm_plan: out is NULL");
+  *out = nullptr;
+  if (!a || n < 0 || n > INT32_MAX) return fail(SPMM_ERR_INVALID_ARG, "spmm_plan: bad matrix or n");
+  const bool ok_types =
+      (a->format == SPMM_FORMAT_BCSR && b_dtype == SPMM_BF16 && c_dtype == SPMM_BF16) ||
+      (a->format == SPMM_FORMAT_WCSR && b_dtype == SPMM_F32 && c_dtype == SPMM_F32) ||
+      (a->format == SPMM_FORMAT_24 && b_dtype == SPMM_I8 && c_dtype == SPMM_I32);
+  if (!ok_types) return fail(SPMM_ERR_UNSUPPORTED, "spmm_plan: unsupported (format, B, C) types");
+  int ndev = 0;
+  hipError_t e = hipGetDeviceCount(&ndev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceCount");
+  if (device < 0 || device >= ndev) return fail(SPMM_ERR_INVALID_ARG, "spmm_plan: no such device");
+  return guarded([&]() -> spmm_status_t {
+    DeviceScope ds(device);
+    if (ds.err != hipSuccess) return hip_fail(ds.err, "hipSetDevice");
+    auto *p = new spmm_plan_s();
+    retain(a);
+    p->a = a;
+    p->device = device;
+    p->n = n;
+    p->info.format = a->format;
+    p->info.device = device;
+    p->info.m = a->m;
+    p->info.k = a->k;
+    p->info.n = n;
+    spmm_status_t s = SPMM_ERR_INTERNAL;
+    try {
+      if (a->format == SPMM_FORMAT_BCSR) s = plan_bcsr(p);
+      else if (a->format == SPMM_FORMAT_WCSR) s = plan_wcsr(p);
+      else s = plan_24(p);
+    } catch (...) {
+      free_plan(p);
+      throw;
+    }
+    if (s == SPMM_OK) {
+      e = hipDeviceSynchronize();
+      if (e != hipSuccess) s = hip_fail(e, "hipDeviceSynchronize");
+    }
+    if (s != SPMM_OK) {
+      free_plan(p);
+      return s;
+    }
+    *out = p;
+    return SPMM_OK;
+  });
+}
+
+spmm_status_t spmm_plan_info(spmm_plan_t p, spmm_plan_info_t *info) {
+  if (!p || !info) return fail(SPMM_ERR_INVALID_ARG, "spmm_plan_info: NULL argument");
+  *info = p->info;
+  return SPMM_OK;
+}
+
+void spmm_plan_destroy(spmm_plan_t p) { free_plan(p); }
+
+spmm_status_t spmm_execute(spmm_plan_t p, const void *b_dev, int64_t ldb, void *c_dev,
+                           int64_t ldc, hipStream_t stream) {
+  if (!p) return fail(SPMM_ERR_INVALID_ARG, "spmm_execute: plan is NULL");
+  const Matrix &a = *p->a;
+  const int64_t n = p->n;
+  if (n == 0 || a.m == 0) return SPMM_OK;
+  const int64_t eb = a.format == SPMM_FORMAT_BCSR ? 2 : (a.format == SPMM_FORMAT_24 ? 1 : 4);
+  const int64_t ec = a.format == SPMM_FORMAT_BCSR ? 2 : 4;
+  if (!c_dev || (!b_dev && a.k > 0))
+    return fail(SPMM_ERR_INVALID_ARG, "spmm_execute: B or C is NULL");
+  if (!aligned16(b_dev) || !aligned16(c_dev) || ldb < n || ldc < n || (ldb * eb) % 16 != 0 ||
+      (ldc * ec) % 16 != 0)
+    return fail(SPMM_ERR_INVALID_ARG,
+                "spmm_execute: B/C must be 16-byte aligned with ld >= n and ld*elem % 16 == 0");
+  DeviceScope ds(p->device);
+  if (ds.err != hipSuccess) return hip_fail(ds.err, "hipSetDevice");
+  hipError_t e = hipSuccess;
+  if (a.format == SPMM_FORMAT_BCSR) {
+    BcsrLaunch L = p->bcsr;
+    L.B = static_cast<const uint16_t *>(b_dev);
+    L.ldb = ldb;
+    L.C = static_cast<uint16_t *>(c_dev);
+    L.ldc = ldc;
+    e = launch_bcsr_bf16(L, stream);
+  } else if (a.format == SPMM_FORMAT_WCSR) {
+    WcsrLaunch L = p->wcsr;
+    L.B = static_cast<const float *>(b_dev);
+    L.ldb = ldb;
+    L.C = static_cast<float *>(c_dev);
+    L.ldc = ldc;
+    e = launch_wcsr_f32(L, stream);
+  } else {
+    Sp24Launch L = p->sp24;
+    L.B = static_cast<const int8_t *>(b_dev);
+    L.ldb = ldb;
+    L.C = static_cast<int32_t *>(c_dev);
+    L.ldc = ldc;
+    e = launch_sp24_i8(L, stream);
+  }
+  if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  return SPMM_OK;
+}
+
+}  // extern "C"

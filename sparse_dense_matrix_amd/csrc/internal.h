@@ -1,0 +1,146 @@
+// internal.h -- objects behind the C ABI and the kernel launch interfaces.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../include/spmm.h"
+
+namespace sdm {
+
+// ---------------------------------------------------------------------------
+// errors
+// ---------------------------------------------------------------------------
+spmm_status_t fail(spmm_status_t s, const std::string &msg);
+spmm_status_t hip_fail(hipError_t e, const char *what);
+void clear_error();
+
+// ---------------------------------------------------------------------------
+// packed operand (host, canonical arrays)
+// ---------------------------------------------------------------------------
+struct Matrix {
+  std::atomic<int> refs{1};
+  spmm_format_t format = SPMM_FORMAT_BCSR;
+  spmm_dtype_t dtype = SPMM_F32;
+  int64_t m = 0, k = 0, nnz = 0;
+  // BCSR
+  int32_t bm = 0, bk = 0;
+  std::vector<int32_t> brow_ptr, bcol_idx;
+  std::vector<uint16_t> bvals;
+  // WCSR
+  int32_t window_rows = 0;
+  int64_t max_chunk_nnz = 0;
+  std::vector<int64_t> row_ptr;
+  std::vector<int32_t> col_idx;
+  std::vector<float> vals;
+  std::vector<int32_t> chunk_window;
+  std::vector<int64_t> chunk_begin;
+  // 2:4
+  std::vector<int8_t> vals24;
+  std::vector<uint8_t> meta24;
+};
+
+void retain(Matrix *a);
+void release(Matrix *a);
+
+// packers (pack.cpp); they fill `a` and return a status (message set on error)
+spmm_status_t pack_bcsr_bf16(int64_t m, int64_t k, int32_t bm, int32_t bk,
+                             const uint16_t *a, int64_t lda, Matrix &out);
+spmm_status_t pack_wcsr_f32(int64_t m, int64_t k, const int64_t *row_ptr,
+                            const int32_t *col_idx, const float *vals, int32_t W,
+                            int64_t T, Matrix &out);
+spmm_status_t pack_24_i8(int64_t m, int64_t k, const int8_t *a, int64_t lda, Matrix &out);
+
+// ---------------------------------------------------------------------------
+// device-side descriptors (plan-private layouts)
+// ---------------------------------------------------------------------------
+
+// One chunk of a row window: the stored entries [nz_begin, nz_end) it reduces
+// and the output rows [row_begin, row_end) it writes.  A row whose entries lie
+// inside the chunk (or an empty row the chunk owns) goes straight to C; the
+// first / last row may instead be a piece of a row split over several chunks
+// and then goes to partial row slot_first / slot_last (-1 when not split).
+struct WcsrChunk {
+  int64_t nz_begin, nz_end;
+  int32_t row_begin, row_end;
+  int32_t slot_first, slot_last;
+};
+static_assert(sizeof(WcsrChunk) == 32, "WcsrChunk layout");
+
+// ---------------------------------------------------------------------------
+// kernel launchers (one per format, in the .hip files)
+// ---------------------------------------------------------------------------
+struct BcsrLaunch {
+  const int32_t *row_ptr;   // [mb + 1]
+  const int32_t *col_idx;   // [nnzb]
+  const uint16_t *frag;     // [nnzb][4096] in MFMA fragment order
+  int32_t mb;               // block rows (64 rows each)
+  int64_t n;
+  const uint16_t *B;
+  int64_t ldb;
+  uint16_t *C;
+  int64_t ldc;
+};
+// Fragment order of one 64 x 64 block: [rb 2][s 4][lane 64][8 elements], lane l
+// holding row 32*rb + l%32, columns 16*s + 8*(l/32) + 0..7.
+void bcsr_fragment_order(const uint16_t *block_rowmajor, uint16_t *frag);
+int bcsr_tile_n();
+int64_t bcsr_grid(int32_t mb, int64_t n);
+hipError_t launch_bcsr_bf16(const BcsrLaunch &a, hipStream_t s);
+
+struct WcsrLaunch {
+  const WcsrChunk *chunks;
+  int64_t num_chunks;
+  const int64_t *row_ptr;
+  const int32_t *col_idx;
+  const float *vals;
+  const int32_t *merge_row;   // [num_split_rows]
+  const int32_t *merge_slot;  // [num_split_rows + 1]
+  int64_t num_split_rows;
+  float *partial;             // [num_slots][n]
+  int64_t n;
+  const float *B;
+  int64_t ldb;
+  float *C;
+  int64_t ldc;
+};
+hipError_t launch_wcsr_f32(const WcsrLaunch &a, hipStream_t s);
+int64_t wcsr_grid(int64_t num_chunks, int64_t n);
+
+struct Sp24Launch {
+  const int8_t *vals;   // [m_pad][k_pad/2]
+  const uint8_t *meta;  // [m_pad][k_pad/8]
+  int64_t m, k, n;
+  int64_t m_pad, k_pad;
+  const int8_t *B;
+  int64_t ldb;
+  int32_t *C;
+  int64_t ldc;
+};
+int sp24_tile_m();
+int sp24_tile_n();
+int sp24_tile_k();
+int64_t sp24_grid(int64_t m, int64_t n);
+hipError_t launch_sp24_i8(const Sp24Launch &a, hipStream_t s);
+
+}  // namespace sdm
+
+// ---------------------------------------------------------------------------
+// plan object
+// ---------------------------------------------------------------------------
+struct spmm_plan_s {
+  sdm::Matrix *a = nullptr;
+  int32_t device = 0;
+  int64_t n = 0;
+  spmm_plan_info_t info{};
+  std::vector<void *> allocations;
+  sdm::BcsrLaunch bcsr{};
+  sdm::WcsrLaunch wcsr{};
+  sdm::Sp24Launch sp24{};
+};
+
+struct spmm_matrix_s : sdm::Matrix {};

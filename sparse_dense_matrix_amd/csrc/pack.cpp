@@ -1,0 +1,151 @@
+// pack.cpp -- host packers into the canonical arrays of spmm.h.
+//
+// BCSR and the row-window CSR follow the AsyncSparse page (abstract; Figure 2
+// caption compares the two formats; the summary describes splitting long row
+// windows across thread blocks).  The 2:4 packer follows the tiled-GEMM page
+// (abstract: the 2:4 pattern of the sparse tensor core) and the N:M entry of
+// the search-results page.
+#include <algorithm>
+#include <cstring>
+
+#include "internal.h"
+
+namespace sdm {
+
+// ---------------------------------------------------------------------------
+// BCSR: one pass over each block row marks the block columns that hold a
+// nonzero (bf16 bits other than +0 / -0), then the marked blocks are copied.
+// ---------------------------------------------------------------------------
+spmm_status_t pack_bcsr_bf16(int64_t m, int64_t k, int32_t bm, int32_t bk,
+                             const uint16_t *a, int64_t lda, Matrix &out) {
+  const int64_t mb = m / bm, kb = k / bk;
+  out.format = SPMM_FORMAT_BCSR;
+  out.dtype = SPMM_BF16;
+  out.m = m;
+  out.k = k;
+  out.bm = bm;
+  out.bk = bk;
+  out.brow_ptr.assign(mb + 1, 0);
+  out.bcol_idx.clear();
+  std::vector<uint8_t> marked(kb);
+  for (int64_t br = 0; br < mb; ++br) {
+    std::fill(marked.begin(), marked.end(), 0);
+    for (int64_t i = br * bm; i < (br + 1) * bm; ++i) {
+      const uint16_t *row = a + i * lda;
+      for (int64_t j = 0; j < k; ++j)
+        if (row[j] & 0x7FFFu) marked[j / bk] = 1;
+    }
+    for (int64_t bc = 0; bc < kb; ++bc)
+      if (marked[bc]) out.bcol_idx.push_back(static_cast<int32_t>(bc));
+    if (out.bcol_idx.size() > static_cast<size_t>(INT32_MAX))
+      return fail(SPMM_ERR_UNSUPPORTED, "spmm_pack_bcsr: more than 2^31-1 blocks");
+    out.brow_ptr[br + 1] = static_cast<int32_t>(out.bcol_idx.size());
+  }
+  const int64_t nnzb = static_cast<int64_t>(out.bcol_idx.size());
+  const int64_t belems = static_cast<int64_t>(bm) * bk;
+  out.bvals.resize(static_cast<size_t>(nnzb * belems));
+  for (int64_t br = 0; br < mb; ++br)
+    for (int32_t p = out.brow_ptr[br]; p < out.brow_ptr[br + 1]; ++p) {
+      uint16_t *dst = out.bvals.data() + p * belems;
+      const uint16_t *src = a + br * bm * lda + static_cast<int64_t>(out.bcol_idx[p]) * bk;
+      for (int32_t i = 0; i < bm; ++i) std::memcpy(dst + i * bk, src + i * lda, bk * sizeof(uint16_t));
+    }
+  out.nnz = nnzb * belems;
+  return SPMM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// WCSR: validate the CSR, copy it, and cut each window of W rows into chunks
+// of at most T stored entries.
+// ---------------------------------------------------------------------------
+spmm_status_t pack_wcsr_f32(int64_t m, int64_t k, const int64_t *row_ptr,
+                            const int32_t *col_idx, const float *vals, int32_t W,
+                            int64_t T, Matrix &out) {
+  if (row_ptr[0] != 0) return fail(SPMM_ERR_INVALID_ARG, "spmm_pack_wcsr: row_ptr[0] != 0");
+  for (int64_t i = 0; i < m; ++i)
+    if (row_ptr[i + 1] < row_ptr[i])
+      return fail(SPMM_ERR_INVALID_ARG,
+                  "spmm_pack_wcsr: row_ptr decreases at row " + std::to_string(i));
+  const int64_t nnz = row_ptr[m];
+  if (nnz > 0 && (col_idx == nullptr || vals == nullptr))
+    return fail(SPMM_ERR_INVALID_ARG, "spmm_pack_wcsr: col_idx / vals is NULL");
+  for (int64_t i = 0; i < m; ++i) {
+    int64_t prev = -1;
+    for (int64_t p = row_ptr[i]; p < row_ptr[i + 1]; ++p) {
+      const int64_t c = col_idx[p];
+      if (c < 0 || c >= k)
+        return fail(SPMM_ERR_INVALID_ARG,
+                    "spmm_pack_wcsr: column out of range in row " + std::to_string(i));
+      if (c <= prev)
+        return fail(SPMM_ERR_INVALID_ARG,
+                    "spmm_pack_wcsr: columns not strictly ascending in row " +
+                        std::to_string(i));
+      prev = c;
+    }
+  }
+  out.format = SPMM_FORMAT_WCSR;
+  out.dtype = SPMM_F32;
+  out.m = m;
+  out.k = k;
+  out.nnz = nnz;
+  out.window_rows = W;
+  out.max_chunk_nnz = T;
+  out.row_ptr.assign(row_ptr, row_ptr + m + 1);
+  out.col_idx.assign(col_idx, col_idx + nnz);
+  out.vals.assign(vals, vals + nnz);
+  out.chunk_window.clear();
+  out.chunk_begin.clear();
+  const int64_t nwin = (m + W - 1) / W;
+  for (int64_t w = 0; w < nwin; ++w) {
+    const int64_t s = row_ptr[w * W];
+    const int64_t e = row_ptr[std::min<int64_t>(m, (w + 1) * W)];
+    const int64_t pieces = std::max<int64_t>(1, (e - s + T - 1) / T);
+    for (int64_t q = 0; q < pieces; ++q) {
+      out.chunk_window.push_back(static_cast<int32_t>(w));
+      out.chunk_begin.push_back(s + q * T);
+    }
+  }
+  out.chunk_begin.push_back(nnz);
+  return SPMM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// 2:4: in every group of four, the two largest of key = |a| * 4 + (3 - pos)
+// are kept (larger magnitude first, ties to the lower position), then stored
+// in ascending position.
+// ---------------------------------------------------------------------------
+spmm_status_t pack_24_i8(int64_t m, int64_t k, const int8_t *a, int64_t lda, Matrix &out) {
+  out.format = SPMM_FORMAT_24;
+  out.dtype = SPMM_I8;
+  out.m = m;
+  out.k = k;
+  out.nnz = m * (k / 2);
+  out.vals24.assign(static_cast<size_t>(m * (k / 2)), 0);
+  out.meta24.assign(static_cast<size_t>(m * (k / 8)), 0);
+  for (int64_t i = 0; i < m; ++i) {
+    const int8_t *row = a + i * lda;
+    int8_t *v = out.vals24.data() + i * (k / 2);
+    uint8_t *mt = out.meta24.data() + i * (k / 8);
+    for (int64_t g = 0; g < k / 4; ++g) {
+      int key[4];
+      for (int t = 0; t < 4; ++t) {
+        const int x = row[4 * g + t];
+        key[t] = (x < 0 ? -x : x) * 4 + (3 - t);
+      }
+      int first = 0;
+      for (int t = 1; t < 4; ++t)
+        if (key[t] > key[first]) first = t;
+      int second = first == 0 ? 1 : 0;
+      for (int t = 0; t < 4; ++t)
+        if (t != first && key[t] > key[second]) second = t;
+      const int lo = std::min(first, second), hi = std::max(first, second);
+      v[2 * g] = row[4 * g + lo];
+      v[2 * g + 1] = row[4 * g + hi];
+      const uint8_t nibble = static_cast<uint8_t>(lo | (hi << 2));
+      mt[g >> 1] = static_cast<uint8_t>(mt[g >> 1] | (nibble << ((g & 1) * 4)));
+    }
+  }
+  return SPMM_OK;
+}
+
+}  // namespace sdm

@@ -1,0 +1,342 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle
+on the same seeded inputs.
+
+Bars: int8 2:4 bit-exact; fp32 WCSR relative Frobenius error <= 1e-5; bf16
+BCSR (fp32 accumulate, bf16 round-to-nearest-even output) <= 2e-3.  Every
+element of C must be written (C is pre-filled with a sentinel).
+
+Formats: BCSR / WCSR from the AsyncSparse page (abstract, Figure 2 caption,
+row-window splitting in the summary); 2:4 from the tiled-GEMM page
+(abstract) and the N:M search-results entry; int8 SpMM from the Magicube
+page (abstract).
+"""
+import numpy as np
+import pytest
+
+import synth
+from gpu_helpers import TOL_BF16, TOL_F32, bf16_to_f64, run, to_dev, empty_out, from_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def S():
+    import sparse_dense_matrix_amd as S
+    import torch
+    assert torch.cuda.is_available()
+    return S
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# BCSR bf16
+# ---------------------------------------------------------------------------
+
+def bcsr_case(S, orc, a_bits, B_bits, rows=None, pad=0):
+    m, n = a_bits.shape[0], B_bits.shape[1]
+    M = S.spmm_pack_bcsr(a_bits, 64, 64)
+    P = S.spmm_plan(M, n, S.BF16, S.BF16)
+    got = run(S, P, B_bits, m, n, "bf16", pad)
+    rp, ci, v = orc.pack_bcsr(a_bits, 64, 64)
+    ref = orc.bcsr_spmm(64, 64, rp, ci, v, B_bits, rows=rows)
+    g = bf16_to_f64(got if rows is None else got[rows])
+    assert np.isfinite(g).all(), "unwritten or non-finite outputs"
+    return g, ref, got
+
+
+def test_bcsr_small_ragged_n(S, orc):
+    w = synth.SMALL["bcsr_small"]            # 640 x 512, n = 1000 (ragged tile)
+    a = synth.make_a(w)["dense"]
+    B = synth.make_b(w)
+    for pad in (0, 24):
+        g, ref, _ = bcsr_case(S, orc, a, B, pad=pad)
+        err = orc.rel_frobenius(g, ref)
+        _say(f"bcsr_small pad={pad} rel_frob={err:.3e}")
+        assert err <= TOL_BF16
+
+
+def test_bcsr_identity_exact(S, orc):
+    m = 256
+    eye = synth.f32_to_bf16_bits(np.eye(m, dtype=np.float32))
+    B = synth.dense_bf16_normal(m, 264, 77)
+    M = S.spmm_pack_bcsr(eye)
+    P = S.spmm_plan(M, 264, S.BF16, S.BF16)
+    got = run(S, P, B, m, 264, "bf16")
+    np.testing.assert_array_equal(got, B)
+
+
+def test_bcsr_single_nonzero_is_rne(S, orc):
+    # one product of two bf16 values is exact in fp32, so the output must be
+    # exactly its round-to-nearest-even bf16
+    m, k, n = 128, 192, 512
+    a = np.zeros((m, k), np.float32)
+    a[70, 100] = -1.3671875           # bf16-exact, many mantissa bits
+    a_bits = synth.f32_to_bf16_bits(a)
+    B = synth.dense_bf16_normal(k, n, 78)
+    M = S.spmm_pack_bcsr(a_bits)
+    P = S.spmm_plan(M, n, S.BF16, S.BF16)
+    got = run(S, P, B, m, n, "bf16")
+    exp = np.zeros((m, n), np.uint16)
+    prod = (np.float32(-1.3671875) * synth.bf16_bits_to_f32(B[100])).astype(np.float32)
+    exp[70] = synth.f32_to_bf16_bits(prod)
+    np.testing.assert_array_equal(got & 0x7FFF, exp & 0x7FFF)        # zeros may be -0
+    np.testing.assert_array_equal(got[70], exp[70])
+
+
+def test_bcsr_empty_and_dense_block_rows(S, orc):
+    m, k, n = 256, 512, 256
+    a = np.zeros((m, k), np.uint16)
+    a[64:128, :] = synth.dense_bf16_normal(64, k, 79, sigma=0.02)  # one full block row
+    B = synth.dense_bf16_normal(k, n, 80)
+    g, ref, got = bcsr_case(S, orc, a, B)
+    assert (got[:64] & 0x7FFF == 0).all() and (got[128:] & 0x7FFF == 0).all()
+    assert orc.rel_frobenius(g, ref) <= TOL_BF16
+    zero = np.zeros((m, k), np.uint16)
+    _, _, got0 = bcsr_case(S, orc, zero, B)
+    assert (got0 & 0x7FFF == 0).all()
+
+
+def test_bcsr_4096_config(S, orc):
+    w = synth.WORKLOADS["bcsr_4096_b64_90"]
+    a = synth.make_a(w)["dense"]
+    B = synth.make_b(w)
+    r = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(w.m - 64, w.m),
+                                     r.choice(w.m, 256, replace=False)])).astype(np.int64)
+    g, ref, _ = bcsr_case(S, orc, a, B, rows=rows)
+    err = orc.rel_frobenius(g, ref)
+    _say(f"bcsr_4096 rows={len(rows)} rel_frob={err:.3e}")
+    assert err <= TOL_BF16
+
+
+def test_bcsr_prefill_config_sampled(S, orc):
+    w = synth.WORKLOADS["bcsr_prefill_18944x3584"]
+    a = synth.make_a(w)["dense"]
+    B = synth.make_b(w)
+    r = np.random.default_rng(6)
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(w.m - 64, w.m),
+                                     r.choice(w.m, 64, replace=False)])).astype(np.int64)
+    g, ref, got = bcsr_case(S, orc, a, B, rows=rows)
+    err = orc.rel_frobenius(g, ref)
+    _say(f"bcsr_prefill rows={len(rows)} rel_frob={err:.3e}")
+    assert err <= TOL_BF16
+    assert (got != 0xFFFF).all(), "some C element was not written"
+
+
+def test_bcsr_deterministic(S, orc):
+    w = synth.SMALL["bcsr_small"]
+    a = synth.make_a(w)["dense"]
+    B = synth.make_b(w)
+    M = S.spmm_pack_bcsr(a)
+    P = S.spmm_plan(M, w.n, S.BF16, S.BF16)
+    x = run(S, P, B, w.m, w.n, "bf16")
+    y = run(S, P, B, w.m, w.n, "bf16")
+    np.testing.assert_array_equal(x, y)
+
+
+# ---------------------------------------------------------------------------
+# WCSR fp32
+# ---------------------------------------------------------------------------
+
+def wcsr_case(S, orc, m, k, rp, ci, v, B, W, T, rows=None, pad=0):
+    n = B.shape[1]
+    M = S.spmm_pack_wcsr(m, k, rp, ci, v, W, T)
+    P = S.spmm_plan(M, n, S.F32, S.F32)
+    got = run(S, P, B, m, n, "f32", pad)
+    ref = orc.csr_spmm(rp, ci, v, B, rows=rows)
+    g = got if rows is None else got[rows]
+    assert np.isfinite(got).all(), "unwritten or non-finite outputs"
+    return orc.rel_frobenius(g, ref), got, P
+
+
+def test_wcsr_tiny_config(S, orc):
+    w = synth.WORKLOADS["csr_tiny_256"]
+    a = synth.make_a(w)
+    B = synth.make_b(w)
+    err, _, _ = wcsr_case(S, orc, w.m, w.k, a["row_ptr"], a["col_idx"], a["vals"], B, 16, 512)
+    _say(f"csr_tiny rel_frob={err:.3e}")
+    assert err <= TOL_F32
+
+
+@pytest.mark.parametrize("W,T", [(16, 512), (1, 1), (3, 7), (64, 100), (16, 4096)])
+@pytest.mark.parametrize("name", ["csr_uniform_small", "csr_powerlaw_small"])
+def test_wcsr_small(S, orc, name, W, T):
+    w = synth.SMALL[name]
+    a = synth.make_a(w)
+    B = synth.make_b(w)
+    err, _, P = wcsr_case(S, orc, w.m, w.k, a["row_ptr"], a["col_idx"], a["vals"], B, W, T)
+    _say(f"{name} W={W} T={T} split_rows={P.info()['num_split_rows']} rel_frob={err:.3e}")
+    assert err <= TOL_F32
+
+
+@pytest.mark.parametrize("n", [1, 3, 64, 65, 129, 300])
+def test_wcsr_ragged_n(S, orc, n):
+    w = synth.SMALL["csr_uniform_small"]
+    a = synth.make_a(w)
+    B = synth.dense_f32_normal(w.k, n, 81)
+    # leading dimensions padded to whole 16-byte rows, as the ABI requires
+    err, _, _ = wcsr_case(S, orc, w.m, w.k, a["row_ptr"], a["col_idx"], a["vals"], B, 8, 37,
+                          pad=(-n) % 4 + 4)
+    assert err <= TOL_F32
+
+
+def test_wcsr_empty_and_giant_rows(S, orc):
+    k, n = 30000, 128
+    r = np.random.default_rng(9)
+    lens = np.zeros(50, np.int64)
+    lens[[3, 17, 18, 40]] = [20000, 5, 1, 7000]    # empty rows everywhere else
+    rp = np.zeros(51, np.int64)
+    np.cumsum(lens, out=rp[1:])
+    ci = np.concatenate([np.sort(r.choice(k, L, replace=False)) for L in lens if L]).astype(np.int32)
+    v = r.uniform(-1, 1, int(rp[-1])).astype(np.float32)
+    B = synth.dense_f32_normal(k, n, 82)
+    for W, T in ((16, 512), (4, 300), (50, 100000), (1, 64)):
+        err, got, P = wcsr_case(S, orc, 50, k, rp, ci, v, B, W, T)
+        _say(f"giant W={W} T={T} split_rows={P.info()['num_split_rows']} rel_frob={err:.3e}")
+        assert err <= TOL_F32
+        assert (got[lens == 0] == 0).all()
+    # all-empty matrix
+    rp0 = np.zeros(51, np.int64)
+    err, got, _ = wcsr_case(S, orc, 50, k, rp0, np.zeros(0, np.int32), np.zeros(0, np.float32),
+                            B, 16, 512)
+    assert (got == 0).all()
+
+
+def test_wcsr_powerlaw_1m_config_sampled(S, orc):
+    w = synth.WORKLOADS["csr_powerlaw_1m"]
+    a = synth.make_a(w)
+    B = synth.make_b(w)
+    lens = np.diff(a["row_ptr"])
+    r = np.random.default_rng(10)
+    rows = np.unique(np.concatenate([np.argsort(lens)[-300:], r.choice(w.m, 3000, replace=False),
+                                     np.arange(100), np.arange(w.m - 100, w.m)])).astype(np.int64)
+    err, got, P = wcsr_case(S, orc, w.m, w.k, a["row_ptr"], a["col_idx"], a["vals"], B, 16, 512,
+                            rows=rows)
+    _say(f"csr_powerlaw_1m rows={len(rows)} split_rows={P.info()['num_split_rows']} "
+         f"rel_frob={err:.3e}")
+    assert err <= TOL_F32
+
+
+def test_wcsr_deterministic(S, orc):
+    w = synth.SMALL["csr_powerlaw_small"]
+    a = synth.make_a(w)
+    B = synth.make_b(w)
+    M = S.spmm_pack_wcsr(w.m, w.k, a["row_ptr"], a["col_idx"], a["vals"], 16, 64)
+    P = S.spmm_plan(M, w.n, S.F32, S.F32)
+    x = run(S, P, B, w.m, w.n, "f32")
+    y = run(S, P, B, w.m, w.n, "f32")
+    np.testing.assert_array_equal(x.view(np.uint32), y.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# 2:4 int8
+# ---------------------------------------------------------------------------
+
+def sp24_case(S, orc, a, B, rows=None, pad=0):
+    m, n = a.shape[0], B.shape[1]
+    M = S.spmm_pack_24(a)
+    P = S.spmm_plan(M, n, S.I8, S.I32)
+    got = run(S, P, B, m, n, "i32", pad)
+    v, mt = orc.pack24(a)
+    ref = orc.sp24_spmm(v, mt, B, rows=rows)
+    return got if rows is None else got[rows], ref
+
+
+def test_sp24_small_ragged(S, orc):
+    w = synth.SMALL["sp24_small"]       # 320 x 512, n = 400: ragged m and n tiles
+    a = synth.make_a(w)["dense"]
+    B = synth.make_b(w)
+    for pad in (0, 32):
+        got, ref = sp24_case(S, orc, a, B, pad=pad)
+        np.testing.assert_array_equal(got, ref)
+
+
+@pytest.mark.parametrize("m,k,n", [(1, 8, 16), (17, 136, 48), (130, 264, 144), (64, 1024, 16)])
+def test_sp24_shapes(S, orc, m, k, n):
+    r = np.random.default_rng(m * 1000 + k)
+    a = synth.int8_uniform(r, (m, k))
+    B = synth.int8_uniform(r, (k, n))
+    got, ref = sp24_case(S, orc, a, B)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_sp24_identity_and_extremes(S, orc):
+    m = 256
+    B = synth.int8_uniform(np.random.default_rng(3), (m, 128))
+    got, _ = sp24_case(S, orc, np.eye(m, dtype=np.int8), B)
+    np.testing.assert_array_equal(got, B.astype(np.int32))
+    k = 8192
+    a = np.full((128, k), -128, np.int8)
+    Bm = np.full((k, 32), -128, np.int8)
+    got, ref = sp24_case(S, orc, a, Bm)
+    np.testing.assert_array_equal(got, np.full((128, 32), (k // 2) * 16384, np.int32))
+
+
+def test_sp24_8192_config_sampled(S, orc):
+    w = synth.WORKLOADS["sp24_i8_8192"]
+    a = synth.make_a(w)["dense"]
+    B = synth.make_b(w)
+    r = np.random.default_rng(11)
+    rows = np.unique(np.concatenate([np.arange(128), np.arange(w.m - 128, w.m),
+                                     r.choice(w.m, 256, replace=False)])).astype(np.int64)
+    got, ref = sp24_case(S, orc, a, B, rows=rows)
+    np.testing.assert_array_equal(got, ref)
+
+
+# ---------------------------------------------------------------------------
+# boundary behaviour on the device
+# ---------------------------------------------------------------------------
+
+def test_plan_rejects_unsupported(S):
+    a = np.zeros((64, 64), np.uint16)
+    M = S.spmm_pack_bcsr(a)
+    with pytest.raises(S.SpmmError) as ei:
+        S.spmm_plan(M, 12, S.BF16, S.BF16)          # n % 8 != 0
+    assert ei.value.name == "SPMM_ERR_UNSUPPORTED"
+    with pytest.raises(S.SpmmError) as ei:
+        S.spmm_plan(M, 16, S.F32, S.F32)
+    assert ei.value.name == "SPMM_ERR_UNSUPPORTED"
+    M24 = S.spmm_pack_24(np.zeros((16, 16), np.int8))
+    with pytest.raises(S.SpmmError) as ei:
+        S.spmm_plan(M24, 24, S.I8, S.I32)
+    assert ei.value.name == "SPMM_ERR_UNSUPPORTED"
+
+
+def test_execute_rejects_bad_layouts(S):
+    torch = pytest.importorskip("torch")
+    M = S.spmm_pack_bcsr(np.zeros((64, 64), np.uint16))
+    P = S.spmm_plan(M, 64, S.BF16, S.BF16)
+    B = torch.zeros((64, 72), dtype=torch.int16, device="cuda")
+    Cw = torch.zeros((64, 64), dtype=torch.int16, device="cuda")
+    with pytest.raises(S.SpmmError) as ei:          # misaligned B
+        S.spmm_execute(P, B.data_ptr() + 2, Cw.data_ptr(), ldb=72, ldc=64)
+    assert ei.value.name == "SPMM_ERR_INVALID_ARG"
+    with pytest.raises(S.SpmmError) as ei:          # ldb < n
+        S.spmm_execute(P, B.data_ptr(), Cw.data_ptr(), ldb=32, ldc=64)
+    assert ei.value.name == "SPMM_ERR_INVALID_ARG"
+
+
+def test_two_plans_two_streams(S, orc):
+    torch = pytest.importorskip("torch")
+    w1, w2 = synth.SMALL["csr_powerlaw_small"], synth.SMALL["bcsr_small"]
+    a1, a2 = synth.make_a(w1), synth.make_a(w2)["dense"]
+    B1, B2 = synth.make_b(w1), synth.make_b(w2)
+    P1 = S.spmm_plan(S.spmm_pack_wcsr(w1.m, w1.k, a1["row_ptr"], a1["col_idx"], a1["vals"], 16, 64),
+                     w1.n, S.F32, S.F32)
+    P2 = S.spmm_plan(S.spmm_pack_bcsr(a2), w2.n, S.BF16, S.BF16)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    Bt1, Bt2 = to_dev(B1), to_dev(B2)
+    C1, C2 = empty_out(w1.m, w1.n, "f32"), empty_out(w2.m, w2.n, "bf16")
+    torch.cuda.synchronize()
+    for _ in range(3):
+        S.spmm_execute(P1, Bt1, C1, stream=s1)
+        S.spmm_execute(P2, Bt2, C2, stream=s2)
+    torch.cuda.synchronize()
+    ref1 = orc.csr_spmm(a1["row_ptr"], a1["col_idx"], a1["vals"], B1)
+    assert orc.rel_frobenius(from_dev(C1, "f32"), ref1) <= TOL_F32
+    rp, ci, v = orc.pack_bcsr(a2, 64, 64)
+    ref2 = orc.bcsr_spmm(64, 64, rp, ci, v, B2)
+    assert orc.rel_frobenius(bf16_to_f64(from_dev(C2, "bf16")), ref2) <= TOL_BF16

@@ -27,7 +27,8 @@ __all__ = [
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libspmm.so")
+# SPMM_LIBRARY may point at another build of the same library
+LIB_PATH = os.environ.get("SPMM_LIBRARY") or os.path.join(HERE, "libspmm.so")
 
 F32, BF16, I8, I32 = 0, 1, 2, 3
 FORMAT_BCSR, FORMAT_WCSR, FORMAT_24 = 0, 1, 2

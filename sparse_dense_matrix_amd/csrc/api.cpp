@@ -3,6 +3,7 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "internal.h"
@@ -22,6 +23,24 @@ spmm_status_t hip_fail(hipError_t e, const char *what) {
 }
 
 void clear_error() { g_last_error.clear(); }
+
+hipError_t allow_dynamic_lds(const void *kernel, size_t bytes) {
+  struct Entry {
+    const void *kernel;
+    int device;
+  };
+  static std::mutex mu;
+  static std::vector<Entry> done;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const Entry &x : done)
+    if (x.kernel == kernel && x.device == dev) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
+  if (e == hipSuccess) done.push_back({kernel, dev});
+  return e;
+}
 
 void retain(Matrix *a) { a->refs.fetch_add(1, std::memory_order_relaxed); }
 
@@ -115,9 +134,13 @@ spmm_status_t plan_bcsr(spmm_plan_s *p) {
   L.frag = fv;
   L.mb = static_cast<int32_t>(a.m / 64);
   L.n = p->n;
+  int cus = 0;
+  hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, p->device);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+  L.cus = cus;
   p->info.tile_m = 64;
-  p->info.tile_n = bcsr_tile_n();
-  p->info.grid = bcsr_grid(L.mb, p->n);
+  p->info.tile_n = bcsr_tile_n(p->n);
+  p->info.grid = bcsr_grid(L.mb, p->n, cus);
   return SPMM_OK;
 }
 

@@ -1,22 +1,37 @@
 // bcsr_bf16.hip -- C = A * B with A in BCSR (64 x 64 bf16 blocks), B and C
 // dense row-major bf16, fp32 accumulation, round-to-nearest-even output.
 //
-// Block-structured SpMM of the AsyncSparse page (abstract; Figure 2 caption):
-// only the stored blocks of a block row are multiplied.  Design for gfx950:
-//   - one workgroup (4 waves) owns a 64-row block row and a 256-column tile
-//     of C; each wave owns 64 x 64 of it as 2 x 2 MFMA 32x32x16 bf16 tiles;
-//   - per stored block the B slab (64 k-rows x 256 columns) and the A block
-//     (8 KB, pre-arranged in MFMA fragment order by the plan) are staged in
-//     LDS; the next block's loads are issued to registers before the current
-//     block's MFMAs (software pipelining instead of the pages' TMA producer
-//     warps);
-//   - B is row-major (n contiguous) but the MFMA wants k contiguous per lane:
-//     the gfx950 LDS transpose read (ds_read_b64_tr_b16) delivers 4 k-values
-//     of one column per lane, two reads per operand;
-//   - workgroups are mapped so that each XCD walks contiguous tiles, block
-//     rows fastest: the workgroups resident on one XCD share the B column
-//     slab of one N tile in that XCD's L2.
+// Block-structured SpMM of the AsyncSparse page (abstract; Figure 2
+// caption): only the stored blocks of a block row are multiplied.  The page
+// overlaps TMA copies with WGMMA through producer/consumer warps; on gfx950
+// the same overlap comes from direct global->LDS loads (no registers in
+// between) into a ring of kStages LDS stages, every wave both issuing loads
+// and running MFMAs:
+//   - a tile is a 64-row block row times kTN (256 or 512) columns of C; each
+//     of the kTN/64 waves owns 64 x 64 of it as 2 x 2 MFMA 32x32x16 bf16
+//     tiles;
+//   - a stage holds one stored block: the B slab (64 k-rows x kTN columns,
+//     row-major) and the A block, pre-arranged by the plan in MFMA fragment
+//     order;
+//   - B is n-contiguous but the MFMA wants k-contiguous operands: the gfx950
+//     LDS transpose read (ds_read_b64_tr_b16) gives each lane 4 k-values of
+//     one column, two reads make an operand.  The slab's 16-byte pieces are
+//     XOR-swizzled by k-row so those reads hit 64 distinct banks;
+//   - the ring has two stages (80 KB at kTN = 256, so two workgroups share a
+//     CU and one hides the other's pipeline fill and epilogue);
+//   - the finished tile is rounded to bf16, staged in the (now idle) ring and
+//     written to C with 16-byte non-temporal stores, which keep the streaming
+//     C writes from evicting B from L2;
+//   - tiles are dealt so that each XCD walks a contiguous range, block rows
+//     fastest: the workgroups resident on one XCD share the B column slab of
+//     one N tile in that XCD's L2.
+// The kernel is bandwidth-bound by design: a 64-row block gives at most 64
+// flop per byte of B moved into LDS.
 #include "internal.h"
+
+// load_lds16 below names m0 as clobbered on purpose (it sets m0 for the
+// LDS-DMA instruction); clang warns about clobbering a reserved register.
+#pragma clang diagnostic ignored "-Winline-asm"
 
 namespace sdm {
 namespace {
@@ -25,70 +40,148 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int kBlk = 64;                        // block edge
-constexpr int kTN = 256;                        // C columns per workgroup
-constexpr int kThreads = 256;                   // 4 waves
-constexpr int kBPitch = kTN * 2 + 64;           // bytes per k-row of the LDS B slab
-constexpr int kBBytes = kBlk * kBPitch;         // 36,864
-constexpr int kABytes = kBlk * kBlk * 2;        // 8,192
-constexpr int kBPieces = kBlk * kTN * 2 / 16 / kThreads;  // 16-byte pieces per thread: 8
-constexpr int kAPieces = kABytes / 16 / kThreads;        // 2
+constexpr int kBlk = 64;                  // block edge
+constexpr int kStages = 2;                // one block in flight while one is used
+constexpr int kABytes = kBlk * kBlk * 2;  // 8 KB
+constexpr int kCPitch = 144;              // bytes per row of a wave's staged C tile
+
+// Tile geometry for kTN columns of C per workgroup (one wave per 64 columns).
+template <int kTN>
+struct Geo {
+  static constexpr int kWaves = kTN / 64;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kBRow = kTN * 2;           // bytes per k-row of the B slab
+  static constexpr int kBBytes = kBlk * kBRow;
+  static constexpr int kStageBytes = kBBytes + kABytes;
+  static constexpr int kBLoads = kBBytes / 1024 / kWaves;  // 1 KB wave loads per wave per stage
+  static constexpr int kALoads = kABytes / 1024 / kWaves;
+  static constexpr int kLdsBytes = kStages * kStageBytes;
+  static_assert(kBLoads * kWaves * 1024 == kBBytes && kALoads * kWaves * 1024 == kABytes, "split");
+  static_assert(kWaves * 64 * kCPitch <= kLdsBytes, "C staging fits in the ring");
+  static_assert(kLdsBytes <= 160 * 1024, "LDS");
+};
+
+// physical 16-byte piece of logical piece c in k-row r of the B slab
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r & 3) << 2); }
+
+// s_waitcnt vmcnt(n), leaving the other counters alone
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Direct global->LDS load of 16 bytes per lane: LDS[lds + 16 * lane] =
+// global[base + voff].  Issued as inline asm so the compiler neither waits
+// on it (the kernel counts vmcnt itself) nor assumes every later LDS read
+// depends on it.
+__device__ __forceinline__ void load_lds16(uint32_t lds, const void *base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds), "v"(voff), "s"(base)
+               : "memory", "m0");
+}
+
+// Workgroup barrier without the memory fence __syncthreads() adds (the fence
+// would wait for every in-flight load); LDS ordering is handled by the
+// explicit vmcnt / lgkmcnt waits around it.
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char *)(p)));
+}
 
 __device__ __forceinline__ unsigned short to_bf16_rne(float f) {
   // float -> bf16 conversion rounds to nearest even (v_cvt_pk_bf16_f32)
   return __builtin_bit_cast(unsigned short, static_cast<__bf16>(f));
 }
 
-__global__ __launch_bounds__(kThreads) void bcsr_bf16_mfma(
-    const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ col_idx,
-    const uint4 *__restrict__ frag, int32_t mb, int32_t tiles, int32_t per_xcd, int64_t n,
-    const uint16_t *__restrict__ B, int64_t ldb, uint16_t *__restrict__ C, int64_t ldc) {
-  __shared__ __attribute__((aligned(16))) char lds[kBBytes + kABytes];
+struct Operands {
+  bf16x8 a[2];
+  bf16x8 b[2];
+};
 
-  // XCD-aware tile order: workgroup b runs on XCD b % 8; give each XCD a
+template <int kTN>
+__global__ __launch_bounds__(Geo<kTN>::kThreads) void bcsr_bf16_mfma(
+    const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ col_idx,
+    const uint16_t *__restrict__ frag, int32_t mb, int32_t tiles, int32_t per_xcd, int64_t n,
+    const uint16_t *__restrict__ B, int64_t ldb, uint16_t *__restrict__ C, int64_t ldc) {
+  using G = Geo<kTN>;
+  constexpr int kBRow = G::kBRow, kBBytes = G::kBBytes, kStageBytes = G::kStageBytes;
+  constexpr int kBLoads = G::kBLoads, kALoads = G::kALoads;
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+
+  // XCD-aware tile order: workgroup b runs on XCD b % 8; each XCD gets a
   // contiguous range of logical tiles, block rows fastest.
-  const int bid = blockIdx.x;
-  const int t = (bid & 7) * per_xcd + (bid >> 3);
+  const int t = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (t >= tiles) return;
   const int br = t % mb;
   const int64_t n0 = static_cast<int64_t>(t / mb) * kTN;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int p0 = row_ptr[br], p1 = row_ptr[br + 1];
+  const int nblk = p1 - p0;
 
-  // global -> register staging: piece q = tid + 256 j of the B slab is row
-  // q / 32, 16-byte column piece q % 32 (32 threads cover a 512-byte row)
-  uint4 breg[kBPieces];
-  uint4 areg[kAPieces];
-  auto load_block = [&](int p) {
-    const int64_t kb = static_cast<int64_t>(col_idx[p]) * kBlk;
-    const uint16_t *src = B + kb * ldb + n0;
+  // Per-lane byte offsets of this wave's B loads relative to the block's
+  // first k-row; columns past n are read from column n0 of the same row
+  // (they only feed C columns that are never stored).
+  uint32_t boff[kBLoads];
 #pragma unroll
-    for (int j = 0; j < kBPieces; ++j) {
-      const int q = tid + kThreads * j;
-      const int row = q >> 5, cp = q & 31;
-      if (n0 + cp * 8 < n)
-        breg[j] = *reinterpret_cast<const uint4 *>(src + row * ldb + cp * 8);
-      else
-        breg[j] = make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < kBLoads; ++i) {
+    const int o = (wave * kBLoads + i) * 1024 + lane * 16;  // byte offset in the slab
+    const int r = o / kBRow;
+    const int c = swz(r, (o % kBRow) / 16) * 8;
+    const int64_t col = (n0 + c < n) ? n0 + c : n0;
+    boff[i] = static_cast<uint32_t>((r * ldb + col) * 2);
+  }
+  const uint32_t lds_base = lds_addr(lds);
+  auto issue = [&](int blk, int stage) {
+    const uint32_t sb = lds_base + stage * kStageBytes;
+    const uint16_t *bsrc = B + static_cast<int64_t>(col_idx[blk]) * kBlk * ldb;
+#pragma unroll
+    for (int i = 0; i < kBLoads; ++i) load_lds16(sb + (wave * kBLoads + i) * 1024, bsrc, boff[i]);
+    const uint16_t *asrc = frag + static_cast<int64_t>(blk) * (kABytes / 2);
+#pragma unroll
+    for (int i = 0; i < kALoads; ++i) {
+      const int o = (wave * kALoads + i) * 1024;
+      load_lds16(sb + kBBytes + o, asrc, static_cast<uint32_t>(o + lane * 16));
     }
-    const uint4 *asrc = frag + static_cast<int64_t>(p) * (kABytes / 16);
-#pragma unroll
-    for (int j = 0; j < kAPieces; ++j) areg[j] = asrc[tid + kThreads * j];
   };
-  auto store_block = [&]() {
+
+  // transpose-read addressing: within a 16-lane group, lane p supplies the
+  // 4 columns 4*(p%4).. of k-row p/4; lane i then holds k-rows 0..3 of
+  // column i.  Lanes 32..63 take k-rows 8..15 of each 16-row step.
+  const int g = lane >> 5;
+  const int pl = lane & 15;
+  const int tr_row = 8 * g + (pl >> 2);                                  // + 16 s + 4 h
+  const int tr_col = wave * 64 + ((lane >> 4) & 1) * 16 + 4 * (pl & 3);  // + 32 cb
+  auto read_ops = [&](const char *sb, int s) {
+    Operands o;
+    const bf16x8 *afr = reinterpret_cast<const bf16x8 *>(sb + kBBytes);
 #pragma unroll
-    for (int j = 0; j < kBPieces; ++j) {
-      const int q = tid + kThreads * j;
-      *reinterpret_cast<uint4 *>(lds + (q >> 5) * kBPitch + (q & 31) * 16) = breg[j];
+    for (int rb = 0; rb < 2; ++rb) o.a[rb] = afr[(rb * 4 + s) * 64 + lane];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      s16x4 part[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = 16 * s + tr_row + 4 * h;
+        const int c = tr_col + 32 * cb;
+        part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4 *)(sb + r * kBRow + swz(r, c >> 3) * 16 + (c & 7) * 2));
+      }
+      s16x8 bs;
+      bs[0] = part[0][0]; bs[1] = part[0][1]; bs[2] = part[0][2]; bs[3] = part[0][3];
+      bs[4] = part[1][0]; bs[5] = part[1][1]; bs[6] = part[1][2]; bs[7] = part[1][3];
+      o.b[cb] = __builtin_bit_cast(bf16x8, bs);
     }
-    uint4 *al = reinterpret_cast<uint4 *>(lds + kBBytes);
-#pragma unroll
-    for (int j = 0; j < kAPieces; ++j) al[tid + kThreads * j] = areg[j];
+    return o;
   };
 
   f32x16 acc[2][2];
@@ -99,62 +192,53 @@ __global__ __launch_bounds__(kThreads) void bcsr_bf16_mfma(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // transpose-read addressing: within a 16-lane group, lane p supplies the
-  // 4 columns 4*(p%4).. of k-row p/4; lane i then holds k-rows 0..3 of
-  // column i.  Lanes 32..63 take k-rows 8..15 of the 16-row step.
-  const int g = lane >> 5;
-  const int pl = lane & 15;
-  const int tr_row = 8 * g + (pl >> 2);
-  const int tr_col = wave * 64 + ((lane >> 4) & 1) * 16 + 4 * (pl & 3);
-
-  if (p0 < p1) {
-    load_block(p0);
-    store_block();
-  }
-  __syncthreads();
-  for (int p = p0; p < p1; ++p) {
-    if (p + 1 < p1) load_block(p + 1);
-    const bf16x8 *afr = reinterpret_cast<const bf16x8 *>(lds + kBBytes);
+  if (nblk > 0) issue(p0, 0);
+  for (int it = 0; it < nblk; ++it) {
+    wait_vm<0>();  // this block's loads have landed
+    barrier();     // ... for every wave; and the stage of block it-1 is free
+    if (it + 1 < nblk) issue(p0 + it + 1, (it + 1) & 1);
+    const char *sb = lds + (it & 1) * kStageBytes;
+    Operands cur = read_ops(sb, 0);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      bf16x8 af[2];
+      Operands nxt;
+      if (s < 3) nxt = read_ops(sb, s + 1);
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) af[rb] = afr[(rb * 4 + s) * 64 + lane];
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        const char *base = lds + (16 * s + tr_row) * kBPitch + (tr_col + 32 * cb) * 2;
-        s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(base));
-        s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(base + 4 * kBPitch));
-        s16x8 bs;
-        bs[0] = lo[0]; bs[1] = lo[1]; bs[2] = lo[2]; bs[3] = lo[3];
-        bs[4] = hi[0]; bs[5] = hi[1]; bs[6] = hi[2]; bs[7] = hi[3];
-        const bf16x8 bfr = __builtin_bit_cast(bf16x8, bs);
+      for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
-          acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rb], bfr, acc[rb][cb], 0, 0, 0);
-      }
+          acc[rb][cb] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a[rb], cur.b[cb], acc[rb][cb], 0, 0, 0);
+      if (s < 3) cur = nxt;
     }
-    __syncthreads();
-    if (p + 1 < p1) store_block();
-    __syncthreads();
   }
 
-  // epilogue: accumulator element r of lane l is row 8*(r/4) + 4*(l/32) + r%4,
-  // column l%32 of its 32 x 32 tile
-  const int64_t row0 = static_cast<int64_t>(br) * kBlk;
+  // epilogue: accumulator element r of lane l is row 8*(r/4) + 4*(l/32) +
+  // r%4, column l%32 of its 32 x 32 tile.  Round to bf16, stage the wave's
+  // 64 x 64 tile in the idle ring, then write 16-byte pieces of C rows.
+  barrier();  // every wave is done reading the ring
+  char *ct = lds + wave * 64 * kCPitch;
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      const int64_t col = n0 + wave * 64 + cb * 32 + (lane & 31);
-      if (col < n) {
+    for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t row = row0 + rb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          C[row * ldc + col] = to_bf16_rne(acc[rb][cb][r]);
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int row = rb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        const int col = cb * 32 + (lane & 31);
+        *reinterpret_cast<unsigned short *>(ct + row * kCPitch + col * 2) = to_bf16_rne(acc[rb][cb][r]);
       }
+  __builtin_amdgcn_wave_barrier();
+  const int64_t row0 = static_cast<int64_t>(br) * kBlk;
+  const int64_t col = n0 + wave * 64 + (lane & 7) * 8;
+  if (col < n) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int row = q * 8 + (lane >> 3);
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(ct + row * kCPitch + (lane & 7) * 16);
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(C + (row0 + row) * ldc + col));
     }
+  }
 }
 
 }  // namespace
@@ -168,24 +252,36 @@ void bcsr_fragment_order(const uint16_t *blk, uint16_t *frag) {
               blk[(32 * rb + (l & 31)) * kBlk + 16 * s + 8 * (l >> 5) + i];
 }
 
-int bcsr_tile_n() { return kTN; }
+// Wider tiles re-read each A block fewer times (once per kTN columns); for
+// small n the narrower tile gives more workgroups to fill the CUs.
+int bcsr_tile_n(int64_t n) { return n >= 8192 ? 512 : 256; }
 
-int64_t bcsr_grid(int32_t mb, int64_t n) {
-  const int64_t tiles = static_cast<int64_t>(mb) * ((n + kTN - 1) / kTN);
+int64_t bcsr_grid(int32_t mb, int64_t n, int /*cus*/) {
+  const int tn = bcsr_tile_n(n);
+  const int64_t tiles = static_cast<int64_t>(mb) * ((n + tn - 1) / tn);
   return 8 * ((tiles + 7) / 8);
 }
 
-hipError_t launch_bcsr_bf16(const BcsrLaunch &a, hipStream_t s) {
+namespace {
+template <int kTN>
+hipError_t launch_tn(const BcsrLaunch &a, hipStream_t s) {
+  using G = Geo<kTN>;
   const int64_t ntn = (a.n + kTN - 1) / kTN;
   const int64_t tiles = static_cast<int64_t>(a.mb) * ntn;
   if (tiles == 0) return hipSuccess;
-  if (tiles > INT32_MAX / 2) return hipErrorInvalidValue;
+  if (tiles > INT32_MAX / 2 || a.ldb > (1 << 24)) return hipErrorInvalidValue;
+  hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(&bcsr_bf16_mfma<kTN>), G::kLdsBytes);
+  if (e != hipSuccess) return e;
   const int64_t per_xcd = (tiles + 7) / 8;
-  hipLaunchKernelGGL(bcsr_bf16_mfma, dim3(static_cast<unsigned>(8 * per_xcd)), dim3(kThreads), 0, s,
-                     a.row_ptr, a.col_idx, reinterpret_cast<const uint4 *>(a.frag), a.mb,
-                     static_cast<int32_t>(tiles), static_cast<int32_t>(per_xcd), a.n, a.B, a.ldb,
-                     a.C, a.ldc);
+  hipLaunchKernelGGL(bcsr_bf16_mfma<kTN>, dim3(static_cast<unsigned>(8 * per_xcd)), dim3(G::kThreads),
+                     G::kLdsBytes, s, a.row_ptr, a.col_idx, a.frag, a.mb, static_cast<int32_t>(tiles),
+                     static_cast<int32_t>(per_xcd), a.n, a.B, a.ldb, a.C, a.ldc);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_bcsr_bf16(const BcsrLaunch &a, hipStream_t s) {
+  return bcsr_tile_n(a.n) == 512 ? launch_tn<512>(a, s) : launch_tn<256>(a, s);
 }
 
 }  // namespace sdm

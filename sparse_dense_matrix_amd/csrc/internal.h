@@ -71,6 +71,10 @@ struct WcsrChunk {
 };
 static_assert(sizeof(WcsrChunk) == 32, "WcsrChunk layout");
 
+// Raise a kernel's dynamic LDS limit to `bytes` on the current device (once
+// per kernel and device).
+hipError_t allow_dynamic_lds(const void *kernel, size_t bytes);
+
 // ---------------------------------------------------------------------------
 // kernel launchers (one per format, in the .hip files)
 // ---------------------------------------------------------------------------
@@ -80,6 +84,7 @@ struct BcsrLaunch {
   const uint16_t *frag;     // [nnzb][4096] in MFMA fragment order
   int32_t mb;               // block rows (64 rows each)
   int64_t n;
+  int32_t cus;              // compute units of the device (persistent grid)
   const uint16_t *B;
   int64_t ldb;
   uint16_t *C;
@@ -88,8 +93,8 @@ struct BcsrLaunch {
 // Fragment order of one 64 x 64 block: [rb 2][s 4][lane 64][8 elements], lane l
 // holding row 32*rb + l%32, columns 16*s + 8*(l/32) + 0..7.
 void bcsr_fragment_order(const uint16_t *block_rowmajor, uint16_t *frag);
-int bcsr_tile_n();
-int64_t bcsr_grid(int32_t mb, int64_t n);
+int bcsr_tile_n(int64_t n);
+int64_t bcsr_grid(int32_t mb, int64_t n, int cus);
 hipError_t launch_bcsr_bf16(const BcsrLaunch &a, hipStream_t s);
 
 struct WcsrLaunch {

@@ -15,9 +15,18 @@
 //     and 64+16*(l/16)+0..15, read out of the row-major LDS slab with the
 //     gfx950 transpose read ds_read_b64_tr_b8 (8 k-values per read);
 //   - D: 4 int32 per lane, rows 4*(l/16)+0..3, column l%16.
-// One workgroup (4 waves, 2 x 2) computes a 128 x 128 tile of C; k advances
-// 128 dense columns per step with register prefetch of the next step.
+// A workgroup of 8 waves computes a 256 x 256 tile of C (each wave 128 x 64,
+// 8 x 4 sparse MFMA tiles).  Operands go global -> LDS with direct loads
+// into a three-stage ring (two k-steps in flight): the A values land in MFMA fragment order because
+// each lane picks which row piece it fetches, the B slab's 16-byte pieces are
+// XOR-swizzled by k-row so the transpose reads are bank-conflict free.  The
+// tile order groups 4 row tiles with every column tile on one XCD, so A
+// panels are shared 8-fold and B panels 4-fold in that XCD's L2.
 #include "internal.h"
+
+// load_lds below names m0 as clobbered on purpose (it sets m0 for the
+// LDS-DMA instruction); clang warns about clobbering a reserved register.
+#pragma clang diagnostic ignored "-Winline-asm"
 
 namespace sdm {
 namespace {
@@ -27,139 +36,200 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
-constexpr int kTM = 128, kTN = 128, kTK = 128;  // dense k per step
-constexpr int kThreads = 256;
-constexpr int kBPitch = kTN + 16;               // bytes per k-row of the LDS B slab
-constexpr int kBBytes = kTK * kBPitch;          // 18,432
-constexpr int kABytes = kTM * kTK / 2;          // 8,192 compressed values
-constexpr int kMBytes = kTM * kTK / 8;          // 2,048 metadata
-constexpr int kAPieces = kABytes / 16 / kThreads;   // 2
-constexpr int kBPieces = kTK * kTN / 16 / kThreads; // 4
+constexpr int kTM = 256, kTN = 256, kTK = 128;  // dense k per step
+constexpr int kWaves = 8;                       // 2 (rows) x 4 (columns)
+constexpr int kThreads = 64 * kWaves;
+constexpr int kMG = 4;                          // row tiles grouped on one XCD
+constexpr int kAVBytes = kTM * kTK / 2;         // 16 KB compressed values
+constexpr int kAMBytes = kTM * kTK / 8;         // 4 KB metadata
+constexpr int kBBytes = kTK * kTN;              // 32 KB
+constexpr int kStageBytes = kAVBytes + kAMBytes + kBBytes;
+constexpr int kStages = 3;                      // two k-steps in flight
+constexpr int kLdsBytes = kStages * kStageBytes;  // 156 KB
+constexpr int kLoads = 7;                       // direct loads per wave per k-step
+static_assert(kLdsBytes <= 160 * 1024, "LDS");
+
+// physical 16-byte piece of logical piece c in k-row r of the B slab: the 16
+// rows one transpose read touches land in 16 distinct bank groups
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r & 7) | (((r >> 4) & 1) << 3)); }
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Direct global->LDS load of 16 bytes per lane: LDS[lds + 16 * lane] =
+// global[base + voff].  Inline asm so the compiler neither drains it at
+// barriers nor makes later LDS reads wait on it; the kernel counts vmcnt.
+__device__ __forceinline__ void load_lds16(uint32_t lds, const void *base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds), "v"(voff), "s"(base)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char *)(p)));
+}
+
+// exchange with the lane `xor` away inside a quad (DPP quad permutation)
+template <int kXor>
+__device__ __forceinline__ int quad_swap(int v) {
+  constexpr int perm = kXor == 1 ? 0xB1 : 0x4E;  // [1,0,3,2] or [2,3,0,1]
+  return __builtin_amdgcn_mov_dpp(v, perm, 0xF, 0xF, false);
+}
 
 __global__ __launch_bounds__(kThreads) void sp24_i8_smfmac(
     const int8_t *__restrict__ vals, const uint8_t *__restrict__ meta, int64_t m, int64_t k,
-    int64_t n, int64_t k_pad, int32_t mtiles, int32_t tiles, int32_t per_xcd,
+    int64_t n, int64_t k_pad, int32_t mtiles, int32_t ntiles, int32_t tiles, int32_t per_xcd,
     const int8_t *__restrict__ B, int64_t ldb, int32_t *__restrict__ C, int64_t ldc) {
-  __shared__ __attribute__((aligned(16))) char lds[kBBytes + kABytes + kMBytes];
-  char *const lds_b = lds;
-  char *const lds_a = lds + kBBytes;
-  char *const lds_m = lds + kBBytes + kABytes;
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
 
-  const int bid = blockIdx.x;
-  const int t = (bid & 7) * per_xcd + (bid >> 3);
+  // logical tile t: groups of kMG row tiles x every column tile, contiguous
+  // per XCD (workgroup b runs on XCD b % 8)
+  const int t = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (t >= tiles) return;
-  const int64_t m0 = static_cast<int64_t>(t % mtiles) * kTM;
-  const int64_t n0 = static_cast<int64_t>(t / mtiles) * kTN;
+  const int grp = t / (kMG * ntiles), rem = t % (kMG * ntiles);
+  const int gsize = min(kMG, mtiles - grp * kMG);
+  const int64_t m0 = static_cast<int64_t>(grp * kMG + rem % gsize) * kTM;
+  const int64_t n0 = static_cast<int64_t>(rem / gsize) * kTN;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
   const int64_t arow_bytes = k_pad / 2, mrow_bytes = k_pad / 8;
 
-  uint4 areg[kAPieces], breg[kBPieces], mreg;
-  auto load_step = [&](int64_t ks) {
-    // A: piece q -> row q/4, 16-byte piece q%4 (= lane group) of the row's 64
+  // Loads of one k-step, per wave: A values 2 x 1 KB (16 rows x 64 B each,
+  // lane l -> row l%16, piece l/16 = MFMA fragment order), B 4 x 1 KB (4
+  // k-rows x 256 B each); waves 0..3 also load the metadata, 64 rows x 16 B
+  // each (row-major, one 16-byte row per lane).
+  const uint32_t lds_base = lds_addr(lds);
+  uint32_t a_off[2], m_off, b_off[4];
 #pragma unroll
-    for (int j = 0; j < kAPieces; ++j) {
-      const int q = tid + kThreads * j;
-      areg[j] = *reinterpret_cast<const uint4 *>(vals + (m0 + (q >> 2)) * arow_bytes +
-                                                 ks * (kTK / 2) + (q & 3) * 16);
-    }
-    if (tid < kTM)
-      mreg = *reinterpret_cast<const uint4 *>(meta + (m0 + tid) * mrow_bytes + ks * (kTK / 8));
-    // B: piece q -> k-row q/8, 16-byte column piece q%8
+  for (int i = 0; i < 2; ++i) {
+    const int mt = wave * 2 + i;  // 16-row tile 0..15
+    const int64_t row = m0 + mt * 16 + (lane & 15);
+    a_off[i] = static_cast<uint32_t>(row * arow_bytes + (lane >> 4) * 16);
+  }
+  m_off = static_cast<uint32_t>((m0 + (wave & 3) * 64 + lane) * mrow_bytes);
 #pragma unroll
-    for (int j = 0; j < kBPieces; ++j) {
-      const int q = tid + kThreads * j;
-      const int64_t kr = ks * kTK + (q >> 3);
-      const int64_t cc = n0 + (q & 7) * 16;
-      if (kr < k && cc < n)
-        breg[j] = *reinterpret_cast<const uint4 *>(B + kr * ldb + cc);
-      else
-        breg[j] = make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < 4; ++i) {
+    const int r = (wave * 4 + i) * 4 + (lane >> 4);  // k-row of the slab
+    const int c = swz(r, lane & 15);                 // logical 16-byte piece
+    const int64_t col = (n0 + c * 16 < n) ? n0 + c * 16 : n0;
+    b_off[i] = static_cast<uint32_t>(r * ldb + col);
+  }
+  const int64_t ksteps = k_pad / kTK;
+  // load `part` (0..6) of k-step ks into stage `stage`: A values 0..1,
+  // metadata 2, B 3..6.  Every wave issues all kLoads parts per step (the
+  // vmcnt waits count them): waves 4..7 repeat the metadata load of 0..3.
+  auto issue_part = [&](int64_t ks, int stage, int part) {
+    const uint32_t sb = lds_base + stage * kStageBytes;
+    if (part < 2) {
+      load_lds16(sb + (wave * 2 + part) * 1024, vals + ks * (kTK / 2), a_off[part]);
+    } else if (part == 2) {
+      load_lds16(sb + kAVBytes + (wave & 3) * 1024, meta + ks * (kTK / 8), m_off);
+    } else {
+      // k-rows past k (the last step when k % 128 != 0) are read from row 0:
+      // the matching A values are zero-padded, so they add nothing
+      const int i = part - 3;
+      const int64_t krow0 = ks * kTK;
+      const int r = (wave * 4 + i) * 4 + (lane >> 4);
+      const uint32_t off = krow0 + r < k ? static_cast<uint32_t>(krow0 * ldb) + b_off[i]
+                                         : b_off[i] - static_cast<uint32_t>(r * ldb);
+      load_lds16(sb + kAVBytes + kAMBytes + (wave * 4 + i) * 1024, B, off);
     }
   };
-  auto store_step = [&]() {
+  auto issue = [&](int64_t ks, int stage) {
 #pragma unroll
-    for (int j = 0; j < kAPieces; ++j) {
-      const int q = tid + kThreads * j;
-      const int r = q >> 2, g = q & 3;
-      *reinterpret_cast<uint4 *>(lds_a + ((r >> 4) * 64 + g * 16 + (r & 15)) * 16) = areg[j];
-    }
-    if (tid < kTM) {
-      const int r = tid;
-      uint32_t *ml = reinterpret_cast<uint32_t *>(lds_m);
-      const int base = (r >> 4) * 64 + (r & 15);
-      ml[base + 0] = mreg.x;
-      ml[base + 16] = mreg.y;
-      ml[base + 32] = mreg.z;
-      ml[base + 48] = mreg.w;
-    }
-#pragma unroll
-    for (int j = 0; j < kBPieces; ++j) {
-      const int q = tid + kThreads * j;
-      *reinterpret_cast<uint4 *>(lds_b + (q >> 3) * kBPitch + (q & 7) * 16) = breg[j];
-    }
+    for (int part = 0; part < kLoads; ++part) issue_part(ks, stage, part);
   };
 
-  i32x4 acc[4][4];
+  i32x4 acc[8][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
 
-  // transpose-read addressing: in a 16-lane group, lane p supplies 8 columns
-  // 8*(p%2).. of k-row p/2; lane i then holds k-rows 0..7 of column i.
+  // transpose-read addressing: in a 16-lane group, lane p supplies the 8
+  // columns 8*(p%2).. of k-row p/2; lane i then holds k-rows 0..7 of column i
   const int g = lane >> 4;
   const int pl = lane & 15;
-  const int tr_row = 16 * g + (pl >> 1);
-  const int tr_col = wn * 64 + 8 * (pl & 1);
+  const int tr_row = 16 * g + (pl >> 1);  // + 0, 8, 64, 72
+  const int tr_colb = wn * 64 + 8 * (pl & 1);
 
-  const int64_t ksteps = k_pad / kTK;
-  load_step(0);
-  store_step();
-  __syncthreads();
+  for (int s = 0; s < kStages - 1; ++s)
+    if (s < ksteps) issue(s, s);
   for (int64_t ks = 0; ks < ksteps; ++ks) {
-    if (ks + 1 < ksteps) load_step(ks + 1);
+    // this step's loads have landed (the next step's may still be in flight)
+    if (ks + 1 < ksteps) wait_vm<kLoads>();
+    else wait_vm<0>();
+    barrier();  // ... for every wave; and the stage of step ks-1 is free
+    // the loads of step ks+2 are issued between this step's MFMAs, so the
+    // address unit works through them while the matrix cores run
+    const bool more = ks + kStages - 1 < ksteps;
+    const int64_t kn = ks + kStages - 1;
+    const int sn = static_cast<int>(kn % kStages);
+    const char *sb = lds + (ks % kStages) * kStageBytes;
+    const char *sbb = sb + kAVBytes + kAMBytes;
     i32x8 bop[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const char *base = lds_b + tr_row * kBPitch + tr_col + 16 * j;
-      const i32x2 q0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2 *)(base));
-      const i32x2 q1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2 *)(base + 8 * kBPitch));
-      const i32x2 q2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2 *)(base + 64 * kBPitch));
-      const i32x2 q3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2 *)(base + 72 * kBPitch));
-      bop[j] = i32x8{q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
-    }
-    const i32x4 *afr = reinterpret_cast<const i32x4 *>(lds_a);
-    const int *mfr = reinterpret_cast<const int *>(lds_m);
+      i32x2 q[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int mt = wm * 4 + i;
+      for (int h = 0; h < 4; ++h) {
+        const int r = tr_row + (h & 1) * 8 + (h >> 1) * 64;
+        const int c = tr_colb + 16 * j;  // byte column
+        q[h] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (lds_i32x2 *)(sbb + r * kTN + swz(r, c >> 4) * 16 + (c & 15)));
+      }
+      bop[j] = i32x8{q[0][0], q[0][1], q[1][0], q[1][1], q[2][0], q[2][1], q[3][0], q[3][1]};
+    }
+    const i32x4 *afr = reinterpret_cast<const i32x4 *>(sb);
+    const int *mfr = reinterpret_cast<const int *>(sb + kAVBytes);  // [row][4 words]
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int mt = wm * 8 + i;
       const i32x4 aop = afr[mt * 64 + lane];
-      const int idx = mfr[mt * 64 + lane];
+      const int idx = mfr[(mt * 16 + (lane & 15)) * 4 + (lane >> 4)];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         acc[i][j] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(aop, bop[j], acc[i][j], idx, 0, 0);
+      if (more && i < kLoads) issue_part(kn, sn, i);
     }
-    __syncthreads();
-    if (ks + 1 < ksteps) store_step();
-    __syncthreads();
   }
 
-  // D element r of lane l: row 4*(l/16) + r, column l%16 of the 16 x 16 tile
+  // D element r of lane l is row 4*(l/16) + r, column l%16 of its 16 x 16
+  // tile.  A 4 x 4 transpose inside each quad of lanes gives lane q of the
+  // quad row 4*(l/16) + q and the quad's 4 columns: one 16-byte store.
+  const int q = lane & 3;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int64_t col = n0 + wn * 64 + 16 * j + (lane & 15);
-      if (col >= n) continue;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t row = m0 + wm * 64 + 16 * i + 4 * g + r;
-        if (row < m) C[row * ldc + col] = acc[i][j][r];
+      int v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+      {  // exchange with lane ^ 1: elements 1,3 <-> 0,2
+        const bool hi = q & 1;
+        const int s0 = quad_swap<1>(hi ? v[0] : v[1]);
+        const int s1 = quad_swap<1>(hi ? v[2] : v[3]);
+        if (hi) { v[0] = s0; v[2] = s1; } else { v[1] = s0; v[3] = s1; }
       }
+      {  // exchange with lane ^ 2: elements 2,3 <-> 0,1
+        const bool hi = q & 2;
+        const int s0 = quad_swap<2>(hi ? v[0] : v[2]);
+        const int s1 = quad_swap<2>(hi ? v[1] : v[3]);
+        if (hi) { v[0] = s0; v[1] = s1; } else { v[2] = s0; v[3] = s1; }
+      }
+      const int64_t row = m0 + wm * 128 + i * 16 + 4 * g + q;
+      const int64_t col = n0 + wn * 64 + j * 16 + (lane & 12);
+      if (row < m && col < n)
+        __builtin_nontemporal_store(i32x4{v[0], v[1], v[2], v[3]},
+                                    reinterpret_cast<i32x4 *>(C + row * ldc + col));
     }
 }
 
@@ -176,12 +246,17 @@ int64_t sp24_grid(int64_t m, int64_t n) {
 
 hipError_t launch_sp24_i8(const Sp24Launch &a, hipStream_t s) {
   const int64_t mtiles = (a.m + kTM - 1) / kTM;
-  const int64_t tiles = mtiles * ((a.n + kTN - 1) / kTN);
+  const int64_t ntiles = (a.n + kTN - 1) / kTN;
+  const int64_t tiles = mtiles * ntiles;
   if (tiles == 0) return hipSuccess;
-  if (tiles > INT32_MAX / 2) return hipErrorInvalidValue;
+  if (tiles > INT32_MAX / 2 || a.k_pad / 2 * a.m_pad > UINT32_MAX || a.k_pad * a.ldb > UINT32_MAX)
+    return hipErrorInvalidValue;
+  hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(&sp24_i8_smfmac), kLdsBytes);
+  if (e != hipSuccess) return e;
   const int64_t per_xcd = (tiles + 7) / 8;
-  hipLaunchKernelGGL(sp24_i8_smfmac, dim3(static_cast<unsigned>(8 * per_xcd)), dim3(kThreads), 0, s,
-                     a.vals, a.meta, a.m, a.k, a.n, a.k_pad, static_cast<int32_t>(mtiles),
+  hipLaunchKernelGGL(sp24_i8_smfmac, dim3(static_cast<unsigned>(8 * per_xcd)), dim3(kThreads),
+                     kLdsBytes, s, a.vals, a.meta, a.m, a.k, a.n, a.k_pad,
+                     static_cast<int32_t>(mtiles), static_cast<int32_t>(ntiles),
                      static_cast<int32_t>(tiles), static_cast<int32_t>(per_xcd), a.B, a.ldb, a.C,
                      a.ldc);
   return hipGetLastError();

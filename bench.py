@@ -9,9 +9,13 @@ workloads of the catalogue run with --workload.
 
 Prints one JSON line:
   value      effective GFLOP/s = 2 * nnz * n / (time per step)
-  roofline   the dominant kernel against its bound (MFMA peak of its dtype,
-             or HBM bandwidth for the irregular CSR), from HIP events over
-             the timed region on the stream the kernels run on
+  roofline   the dominant kernel against its bound: the larger of the HBM
+             time (algorithmic bytes at 8 TB/s) and the MFMA time
+             (algorithmic flops at the dtype's dense peak), from HIP events
+             over the timed region on the stream the kernels run on;
+             `traffic` is the HBM bytes per launch the hardware counters saw
+             (profiles/hbm_traffic.md), or null when the library source has
+             changed since they were taken
   cpu_baseline  the CPU oracle timed on a bounded sample of rows of the same
              workload (a reported baseline, not a target)
 """
@@ -36,6 +40,11 @@ HEADLINE = "bcsr_4096_b64_90"
 PEAK_HBM_GBS = 8000.0
 PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "i8": 5000.0}
 
+# kernel whose launch dominates a step, per format
+DOMINANT_KERNEL = {"bcsr": "bcsr_bf16_mfma", "wcsr": "wcsr_stream", "sp24": "sp24_i8_smfmac"}
+TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+CSRC = os.path.join(ROOT, "sparse_dense_matrix_amd", "csrc")
+
 
 def log(msg: str):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -52,6 +61,12 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--window-rows", type=int, default=None)
     ap.add_argument("--max-chunk-nnz", type=int, default=None)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain device copy of 1 GiB (read 1 GiB, write 1 GiB), "
+                         "to scale the HBM byte counters")
+    ap.add_argument("--pmc-summary", metavar="DIR",
+                    help="print the mean per dispatch of every counter in the rocprofv3 "
+                         "counter CSVs under DIR, per kernel, and exit")
     return ap.parse_args()
 
 
@@ -110,6 +125,9 @@ def algorithmic(w, d):
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU: the multiply shards by columns "
                                    "of B with no communication, but only the one-GPU path is "
@@ -121,6 +139,9 @@ def main():
     if not torch.cuda.is_available():
         log("no GPU visible")
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(torch, args)
+        return
     cat = dict(synth.WORKLOADS)
     cat.update(synth.SMALL)
     if args.workload not in cat:
@@ -157,15 +178,7 @@ def main():
 
     flops, nbytes, dtype = algorithmic(w, d)
     gflops = flops / (ms_step * 1e-3) / 1e9
-    if w.fmt == "wcsr":
-        achieved = nbytes / (ms_step * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
-    else:
-        achieved = flops / (ms_step * 1e-3) / 1e12
-        peak = PEAK_MFMA_TFLOPS[dtype]
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None}
+    roof, other = roofline(w, flops, nbytes, dtype, ms_step)
     pinfo = S.spmm_plan_info(d["P"])
 
     cpu = None
@@ -191,14 +204,97 @@ def main():
                    "split_rows": pinfo["num_split_rows"], "grid": pinfo["grid"],
                    "parallelism": "single GPU"},
         "roofline": roof,
-        "hbm_compulsory": {"bytes": int(nbytes),
-                           "GB_s": round(nbytes / (ms_step * 1e-3) / 1e9, 1),
-                           "frac": round(nbytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "roofline_other_bound": other,
+        "algorithmic": {"flops": flops, "bytes": int(nbytes)},
         "one_time_s": {"generate": round(d["t_gen"], 3), "pack": round(d["t_pack"], 3),
                        "plan": round(d["t_plan"], 3)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def library_digest() -> str:
+    """sha256 (first 16 hex digits) over every library source file: traffic
+    counters taken with another digest no longer describe this build."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from profiles/hbm_traffic.md for (workload,
+    kernel), or None when absent or recorded for another library digest."""
+    if not os.path.exists(TRAFFIC_TABLE):
+        return None
+    digest = library_digest()
+    with open(TRAFFIC_TABLE) as f:
+        for line in f:
+            cells = [c.strip() for c in line.strip().strip("|").split("|")]
+            if len(cells) >= 7 and cells[0] == workload and cells[1] == kernel:
+                if cells[2] != digest:
+                    return None
+                try:
+                    return int(float(cells[6]))
+                except ValueError:
+                    return None
+    return None
+
+
+def roofline(w, flops, nbytes, dtype, ms_step):
+    """(roofline of the binding bound, the other bound).  The binding bound is
+    the one whose time at peak is longer."""
+    t = ms_step * 1e-3
+    traffic = measured_traffic(w.name, DOMINANT_KERNEL[w.fmt])
+    hbm = {"bound": "hbm", "achieved": round(nbytes / t / 1e9, 1), "peak": PEAK_HBM_GBS,
+           "unit": "GB/s", "frac": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4),
+           "traffic": traffic}
+    if traffic is not None:
+        hbm["traffic_GB_s"] = round(traffic / t / 1e9, 1)
+    if dtype not in PEAK_MFMA_TFLOPS:
+        return hbm, None
+    peak = PEAK_MFMA_TFLOPS[dtype]
+    mfma = {"bound": "mfma", "achieved": round(flops / t / 1e12, 2), "peak": peak,
+            "unit": "TFLOP/s", "frac": round(flops / t / 1e12 / peak, 4), "traffic": traffic}
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    t_mfma = flops / (peak * 1e12)
+    return (hbm, mfma) if t_hbm >= t_mfma else (mfma, hbm)
+
+
+def copy_calibration(torch, args):
+    """A plain elementwise copy kernel over 1 GiB of float32 (reads 1 GiB,
+    writes 1 GiB): what FETCH_SIZE / WRITE_SIZE read for it scales the
+    counters of the SpMM kernels to bytes."""
+    n = (1 << 30) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup + args.steps):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read": 1 << 30, "bytes_written": 1 << 30,
+                                           "launches": args.warmup + args.steps}}), flush=True)
+
+
+def pmc_summary(root):
+    """Mean per dispatch of each counter, per kernel, over rocprofv3 CSVs."""
+    import collections
+    import csv
+    agg = collections.defaultdict(list)
+    for dirpath, _, files in os.walk(root):
+        for fn in files:
+            if not fn.endswith("counter_collection.csv"):
+                continue
+            with open(os.path.join(dirpath, fn)) as f:
+                for r in csv.DictReader(f):
+                    name = r["Kernel_Name"].replace("(anonymous namespace)::", "")
+                    name = name.split("(")[0].split("::")[-1].split("<")[0]
+                    agg[(name, r["Counter_Name"])].append(float(r["Counter_Value"]))
+    print(f"library digest {library_digest()}")
+    for (k, c), v in sorted(agg.items()):
+        print(f"{k:32s} {c:32s} dispatches={len(v):4d} mean={sum(v) / len(v):.6g}")
 
 
 def cpu_baseline(w, d, target_s):

@@ -64,6 +64,9 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of 1 GiB (read 1 GiB, write 1 GiB), "
                          "to scale the HBM byte counters")
+    ap.add_argument("--trace-summary", metavar="DIR",
+                    help="print a markdown table of per-kernel durations from the rocprofv3 "
+                         "kernel-trace database(s) under DIR, and exit")
     ap.add_argument("--pmc-summary", metavar="DIR",
                     help="print the mean per dispatch of every counter in the rocprofv3 "
                          "counter CSVs under DIR, per kernel, and exit")
@@ -127,6 +130,9 @@ def main():
     args = parse()
     if args.pmc_summary:
         pmc_summary(args.pmc_summary)
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU: the multiply shards by columns "
@@ -276,6 +282,29 @@ def copy_calibration(torch, args):
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration": {"bytes_read": 1 << 30, "bytes_written": 1 << 30,
                                            "launches": args.warmup + args.steps}}), flush=True)
+
+
+def trace_summary(root):
+    """Per-kernel call count and duration statistics (microseconds) from the
+    rocprofv3 kernel-trace databases under root."""
+    import collections
+    import sqlite3
+    durs = collections.defaultdict(list)
+    for dirpath, _, files in os.walk(root):
+        for fn in files:
+            if not fn.endswith("_results.db"):
+                continue
+            con = sqlite3.connect(os.path.join(dirpath, fn))
+            for name, dur in con.execute("select name, duration from kernels"):
+                name = name.replace("(anonymous namespace)::", "")
+                durs[name.split("(")[0].split("::")[-1].split("<")[0]].append(dur / 1000.0)
+            con.close()
+    print("| kernel | calls | avg us | median us | min us | max us | total ms |")
+    print("|---|---|---|---|---|---|---|")
+    for name, v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
+        v = sorted(v)
+        print(f"| {name} | {len(v)} | {sum(v) / len(v):.2f} | {v[len(v) // 2]:.2f} | {v[0]:.2f} | "
+              f"{v[-1]:.2f} | {sum(v) / 1000:.3f} |")
 
 
 def pmc_summary(root):

@@ -21,7 +21,7 @@ namespace sdm {
 namespace {
 
 constexpr int kWavesPerBlock = 4;
-constexpr int kUnroll = 8;
+constexpr int kUnroll = 16;
 
 template <int V>
 struct Vec;
@@ -85,9 +85,13 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void wcsr_stream(
     const WcsrChunk *__restrict__ chunks, int64_t num_chunks, const int64_t *__restrict__ row_ptr,
     const int32_t *__restrict__ col_idx, const float *__restrict__ vals,
     const float *__restrict__ B, int64_t ldb, float *__restrict__ C, int64_t ldc,
-    float *__restrict__ partial, int64_t n) {
+    float *__restrict__ partial, int64_t n, int64_t per_xcd) {
   const int lane = threadIdx.x & 63;
-  const int64_t c = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + uniform(threadIdx.x >> 6);
+  // workgroup b runs on XCD b % 8: give each XCD a contiguous range of
+  // chunks, so the rows in flight on one XCD are neighbours and B rows that
+  // nearby rows share can be found in that XCD's L2
+  const int64_t lb = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  const int64_t c = lb * kWavesPerBlock + uniform(threadIdx.x >> 6);
   if (c >= num_chunks) return;
   const WcsrChunk d = chunks[c];
   const int64_t col = static_cast<int64_t>(blockIdx.y) * 64 * V + lane * V;
@@ -176,11 +180,13 @@ int pick_v(int64_t n) { return n <= 64 ? 1 : (n <= 128 ? 2 : 4); }
 template <int V>
 hipError_t launch_v(const WcsrLaunch &a, hipStream_t s) {
   const int64_t tiles = (a.n + 64 * V - 1) / (64 * V);
-  const int64_t grid = (a.num_chunks + kWavesPerBlock - 1) / kWavesPerBlock;
+  const int64_t blocks = (a.num_chunks + kWavesPerBlock - 1) / kWavesPerBlock;
+  const int64_t per_xcd = (blocks + 7) / 8;
+  const int64_t grid = 8 * per_xcd;
   if (grid > 0x7fffffff || tiles > 65535) return hipErrorInvalidValue;
   hipLaunchKernelGGL(wcsr_stream<V>, dim3(static_cast<unsigned>(grid), static_cast<unsigned>(tiles)),
                      dim3(64 * kWavesPerBlock), 0, s, a.chunks, a.num_chunks, a.row_ptr, a.col_idx,
-                     a.vals, a.B, a.ldb, a.C, a.ldc, a.partial, a.n);
+                     a.vals, a.B, a.ldb, a.C, a.ldc, a.partial, a.n, per_xcd);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_split_rows == 0) return e;
   const int64_t mgrid = (a.num_split_rows + kWavesPerBlock - 1) / kWavesPerBlock;

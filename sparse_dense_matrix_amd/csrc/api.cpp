@@ -244,12 +244,9 @@ spmm_status_t plan_24(spmm_plan_s *p) {
   const int64_t TM = sp24_tile_m(), TK = sp24_tile_k();
   const int64_t m_pad = (a.m + TM - 1) / TM * TM;
   const int64_t k_pad = std::max<int64_t>(TK, (a.k + TK - 1) / TK * TK);
-  std::vector<int8_t> v(static_cast<size_t>(m_pad * (k_pad / 2)), 0);
-  std::vector<uint8_t> mt(static_cast<size_t>(m_pad * (k_pad / 8)), 0);
-  for (int64_t i = 0; i < a.m; ++i) {
-    std::memcpy(v.data() + i * (k_pad / 2), a.vals24.data() + i * (a.k / 2), a.k / 2);
-    std::memcpy(mt.data() + i * (k_pad / 8), a.meta24.data() + i * (a.k / 8), a.k / 8);
-  }
+  std::vector<int8_t> v(static_cast<size_t>(m_pad * (k_pad / 2)));
+  std::vector<uint8_t> mt(static_cast<size_t>(m_pad * (k_pad / 8)));
+  sp24_tile_layout(a.vals24.data(), a.meta24.data(), a.m, a.k, m_pad, k_pad, v.data(), mt.data());
   Sp24Launch &L = p->sp24;
   spmm_status_t s;
   int8_t *dv = nullptr;

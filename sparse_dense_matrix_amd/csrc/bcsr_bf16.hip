@@ -198,19 +198,20 @@ __global__ __launch_bounds__(Geo<kTN>::kThreads) void bcsr_bf16_mfma(
     barrier();     // ... for every wave; and the stage of block it-1 is free
     if (it + 1 < nblk) issue(p0 + it + 1, (it + 1) & 1);
     const char *sb = lds + (it & 1) * kStageBytes;
-    Operands cur = read_ops(sb, 0);
+    // every operand of the block is read before the first MFMA, so the LDS
+    // latency is paid once per block instead of once per k-step
+    Operands ops[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      Operands nxt;
-      if (s < 3) nxt = read_ops(sb, s + 1);
+    for (int s = 0; s < 4; ++s) ops[s] = read_ops(sb, s);
+    __builtin_amdgcn_sched_barrier(0);  // keep the compiler from interleaving them again
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
           acc[rb][cb] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a[rb], cur.b[cb], acc[rb][cb], 0, 0, 0);
-      if (s < 3) cur = nxt;
-    }
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(ops[s].a[rb], ops[s].b[cb], acc[rb][cb], 0, 0, 0);
   }
 
   // epilogue: accumulator element r of lane l is row 8*(r/4) + 4*(l/32) +

@@ -117,8 +117,8 @@ hipError_t launch_wcsr_f32(const WcsrLaunch &a, hipStream_t s);
 int64_t wcsr_grid(int64_t num_chunks, int64_t n);
 
 struct Sp24Launch {
-  const int8_t *vals;   // [m_pad][k_pad/2]
-  const uint8_t *meta;  // [m_pad][k_pad/8]
+  const int8_t *vals;   // tiled copy of the values (sp24_tile_layout)
+  const uint8_t *meta;  // tiled copy of the index words
   int64_t m, k, n;
   int64_t m_pad, k_pad;
   const int8_t *B;
@@ -126,6 +126,12 @@ struct Sp24Launch {
   int32_t *C;
   int64_t ldc;
 };
+// Plan-private copies of the canonical 2:4 arrays, zero-padded to m_pad x
+// k_pad and laid out per 256-row tile and 128-deep k-step in the order the
+// kernel's shared-memory stages hold them (vals_tiled: m_pad * k_pad / 2
+// bytes, meta_tiled: m_pad * k_pad / 8 bytes).
+void sp24_tile_layout(const int8_t *vals, const uint8_t *meta, int64_t m, int64_t k,
+                      int64_t m_pad, int64_t k_pad, int8_t *vals_tiled, uint8_t *meta_tiled);
 int sp24_tile_m();
 int sp24_tile_n();
 int sp24_tile_k();

@@ -17,10 +17,13 @@
 //   - D: 4 int32 per lane, rows 4*(l/16)+0..3, column l%16.
 // A workgroup of 8 waves computes a 256 x 256 tile of C (each wave 128 x 64,
 // 8 x 4 sparse MFMA tiles).  Operands go global -> LDS with direct loads
-// into a three-stage ring (two k-steps in flight): the A values land in MFMA fragment order because
-// each lane picks which row piece it fetches, the B slab's 16-byte pieces are
-// XOR-swizzled by k-row so the transpose reads are bank-conflict free.  The
-// tile order groups 4 row tiles with every column tile on one XCD, so A
+// into a three-stage ring (two k-steps in flight).  The plan stores the
+// compressed values and the index words tiled: for each 256-row tile and
+// 128-deep k-step, one contiguous 16 KB piece of values already in MFMA
+// fragment order and one contiguous 4 KB piece of index words, so every
+// direct load reads 1 KB of consecutive bytes.  The B slab's 16-byte pieces
+// are XOR-swizzled by k-row so the transpose reads are bank-conflict free.
+// The tile order groups 4 row tiles with every column tile on one XCD, so A
 // panels are shared 8-fold and B panels 4-fold in that XCD's L2.
 #include "internal.h"
 
@@ -47,6 +50,7 @@ constexpr int kStageBytes = kAVBytes + kAMBytes + kBBytes;
 constexpr int kStages = 3;                      // two k-steps in flight
 constexpr int kLdsBytes = kStages * kStageBytes;  // 156 KB
 constexpr int kLoads = 7;                       // direct loads per wave per k-step
+constexpr int kMLanes = kAMBytes / kWaves / 16;  // lanes of a wave that load index words
 static_assert(kLdsBytes <= 160 * 1024, "LDS");
 
 // physical 16-byte piece of logical piece c in k-row r of the B slab: the 16
@@ -102,21 +106,16 @@ __global__ __launch_bounds__(kThreads) void sp24_i8_smfmac(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
-  const int64_t arow_bytes = k_pad / 2, mrow_bytes = k_pad / 8;
+  const int64_t ksteps = k_pad / kTK;
+  // this row tile's tiled values and index words
+  const int8_t *vt = vals + (m0 / kTM) * ksteps * kAVBytes;
+  const uint8_t *mtl = meta + (m0 / kTM) * ksteps * kAMBytes;
 
-  // Loads of one k-step, per wave: A values 2 x 1 KB (16 rows x 64 B each,
-  // lane l -> row l%16, piece l/16 = MFMA fragment order), B 4 x 1 KB (4
-  // k-rows x 256 B each); waves 0..3 also load the metadata, 64 rows x 16 B
-  // each (row-major, one 16-byte row per lane).
+  // Loads of one k-step, per wave: A values 2 x 1 KB and half a KB of index
+  // words, all consecutive bytes of the tiled copies; B 4 x 1 KB (4 k-rows x
+  // 256 B each).
   const uint32_t lds_base = lds_addr(lds);
-  uint32_t a_off[2], m_off, b_off[4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int mt = wave * 2 + i;  // 16-row tile 0..15
-    const int64_t row = m0 + mt * 16 + (lane & 15);
-    a_off[i] = static_cast<uint32_t>(row * arow_bytes + (lane >> 4) * 16);
-  }
-  m_off = static_cast<uint32_t>((m0 + (wave & 3) * 64 + lane) * mrow_bytes);
+  uint32_t b_off[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = (wave * 4 + i) * 4 + (lane >> 4);  // k-row of the slab
@@ -124,16 +123,17 @@ __global__ __launch_bounds__(kThreads) void sp24_i8_smfmac(
     const int64_t col = (n0 + c * 16 < n) ? n0 + c * 16 : n0;
     b_off[i] = static_cast<uint32_t>(r * ldb + col);
   }
-  const int64_t ksteps = k_pad / kTK;
   // load `part` (0..6) of k-step ks into stage `stage`: A values 0..1,
-  // metadata 2, B 3..6.  Every wave issues all kLoads parts per step (the
-  // vmcnt waits count them): waves 4..7 repeat the metadata load of 0..3.
+  // index words 2, B 3..6.  Every wave issues all kLoads parts per step (the
+  // vmcnt waits count them).
   auto issue_part = [&](int64_t ks, int stage, int part) {
     const uint32_t sb = lds_base + stage * kStageBytes;
     if (part < 2) {
-      load_lds16(sb + (wave * 2 + part) * 1024, vals + ks * (kTK / 2), a_off[part]);
+      const uint32_t o = (wave * 2 + part) * 1024;
+      load_lds16(sb + o, vt + ks * kAVBytes, o + lane * 16);
     } else if (part == 2) {
-      load_lds16(sb + kAVBytes + (wave & 3) * 1024, meta + ks * (kTK / 8), m_off);
+      const uint32_t o = wave * kMLanes * 16;
+      if (lane < kMLanes) load_lds16(sb + kAVBytes + o, mtl + ks * kAMBytes, o + lane * 16);
     } else {
       // k-rows past k (the last step when k % 128 != 0) are read from row 0:
       // the matching A values are zero-padded, so they add nothing
@@ -190,16 +190,25 @@ __global__ __launch_bounds__(kThreads) void sp24_i8_smfmac(
       }
       bop[j] = i32x8{q[0][0], q[0][1], q[1][0], q[1][1], q[2][0], q[2][1], q[3][0], q[3][1]};
     }
+    // The index words of a wave's 8 row tiles sit together per lane (two
+    // 16-byte reads); the A fragments of the first four row tiles are read
+    // with them, those of the last four behind the first 16 sparse MFMAs.
     const i32x4 *afr = reinterpret_cast<const i32x4 *>(sb);
-    const int *mfr = reinterpret_cast<const int *>(sb + kAVBytes);  // [row][4 words]
+    const i32x4 *mfr = reinterpret_cast<const i32x4 *>(sb + kAVBytes) + (wm * 64 + lane) * 2;
+    i32x4 aop[8];
+    const i32x4 idx_lo = mfr[0], idx_hi = mfr[1];
+    const int idx[8] = {idx_lo[0], idx_lo[1], idx_lo[2], idx_lo[3],
+                        idx_hi[0], idx_hi[1], idx_hi[2], idx_hi[3]};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) aop[i] = afr[(wm * 8 + i) * 64 + lane];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 4; i < 8; ++i) aop[i] = afr[(wm * 8 + i) * 64 + lane];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int mt = wm * 8 + i;
-      const i32x4 aop = afr[mt * 64 + lane];
-      const int idx = mfr[(mt * 16 + (lane & 15)) * 4 + (lane >> 4)];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(aop, bop[j], acc[i][j], idx, 0, 0);
+        acc[i][j] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(aop[i], bop[j], acc[i][j], idx[i], 0, 0);
       if (more && i < kLoads) issue_part(kn, sn, i);
     }
   }
@@ -235,6 +244,38 @@ __global__ __launch_bounds__(kThreads) void sp24_i8_smfmac(
 
 }  // namespace
 
+void sp24_tile_layout(const int8_t *vals, const uint8_t *meta, int64_t m, int64_t k,
+                      int64_t m_pad, int64_t k_pad, int8_t *vals_tiled, uint8_t *meta_tiled) {
+  const int64_t ksteps = k_pad / kTK;
+  for (int64_t t = 0; t < m_pad / kTM; ++t)
+    for (int64_t s = 0; s < ksteps; ++s) {
+      int8_t *vdst = vals_tiled + (t * ksteps + s) * kAVBytes;
+      uint8_t *mdst = meta_tiled + (t * ksteps + s) * kAMBytes;
+      // values: [16-row tile][lane][16 bytes], lane l holding row l%16 and
+      // bytes 16*(l/16).. of the step's 64 compressed bytes
+      for (int mt = 0; mt < kTM / 16; ++mt)
+        for (int l = 0; l < 64; ++l) {
+          const int64_t row = t * kTM + mt * 16 + (l & 15);
+          const int64_t c0 = s * (kTK / 2) + (l >> 4) * 16;
+          for (int b = 0; b < 16; ++b)
+            vdst[(mt * 64 + l) * 16 + b] =
+                (row < m && c0 + b < k / 2) ? vals[row * (k / 2) + c0 + b] : int8_t(0);
+        }
+      // index words: [row half wm 2][lane 64][row tile i 8][4 bytes]; lane l
+      // of row half wm gets, for its 8 row tiles, word l/16 of row
+      // (8*wm + i)*16 + l%16
+      for (int wm = 0; wm < 2; ++wm)
+        for (int l = 0; l < 64; ++l)
+          for (int i = 0; i < 8; ++i) {
+            const int64_t row = t * kTM + (wm * 8 + i) * 16 + (l & 15);
+            const int64_t c0 = s * (kTK / 8) + (l >> 4) * 4;
+            for (int b = 0; b < 4; ++b)
+              mdst[((wm * 64 + l) * 8 + i) * 4 + b] =
+                  (row < m && c0 + b < k / 8) ? meta[row * (k / 8) + c0 + b] : uint8_t(0);
+          }
+    }
+}
+
 int sp24_tile_m() { return kTM; }
 int sp24_tile_n() { return kTN; }
 int sp24_tile_k() { return kTK; }
@@ -249,7 +290,7 @@ hipError_t launch_sp24_i8(const Sp24Launch &a, hipStream_t s) {
   const int64_t ntiles = (a.n + kTN - 1) / kTN;
   const int64_t tiles = mtiles * ntiles;
   if (tiles == 0) return hipSuccess;
-  if (tiles > INT32_MAX / 2 || a.k_pad / 2 * a.m_pad > UINT32_MAX || a.k_pad * a.ldb > UINT32_MAX)
+  if (tiles > INT32_MAX / 2 || a.k_pad * a.ldb > UINT32_MAX)
     return hipErrorInvalidValue;
   hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(&sp24_i8_smfmac), kLdsBytes);
   if (e != hipSuccess) return e;

@@ -207,6 +207,8 @@ def main():
         "config": {"workload": w.name, "format": w.fmt, "m": w.m, "k": w.k, "n": w.n,
                    "nnz": d["info"]["nnz"], "nnzb": d["info"]["nnzb"],
                    "num_chunks": d["info"]["num_chunks"],
+                   "window_rows": d["info"]["window_rows"],
+                   "max_chunk_nnz": d["info"]["max_chunk_nnz"],
                    "split_rows": pinfo["num_split_rows"], "grid": pinfo["grid"],
                    "parallelism": "single GPU"},
         "roofline": roof,

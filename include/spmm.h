@@ -119,7 +119,9 @@ spmm_status_t spmm_pack_bcsr(int64_t m, int64_t k, int32_t block_m, int32_t bloc
  * INVALID_ARG, never silently fixed.  Rows are grouped into windows of
  * window_rows rows; a window holding at most max_chunk_nnz entries is one
  * chunk (even when empty), a longer one is cut into ceil(nnz_w / T) chunks of
- * T consecutive entries (the last one shorter).  dtype must be SPMM_F32. */
+ * T consecutive entries (the last one shorter).  window_rows = 0 picks
+ * min(16, max(1, m / 16384)) rows and max_chunk_nnz = 0 picks 512;
+ * spmm_matrix_info reports the values used.  dtype must be SPMM_F32. */
 spmm_status_t spmm_pack_wcsr(int64_t m, int64_t k, spmm_dtype_t dtype,
                              const int64_t *row_ptr, const int32_t *col_idx,
                              const void *vals, int32_t window_rows,

@@ -35,10 +35,10 @@ FORMAT_BCSR, FORMAT_WCSR, FORMAT_24 = 0, 1, 2
 (ARRAY_ROW_PTR, ARRAY_COL_IDX, ARRAY_VALS, ARRAY_META, ARRAY_CHUNK_WINDOW,
  ARRAY_CHUNK_BEGIN) = range(6)
 
-# Default row-window shape for WCSR: W rows per window, at most T stored
-# entries per chunk (one wavefront reduces one chunk).
-DEFAULT_WINDOW_ROWS = 16
-DEFAULT_MAX_CHUNK_NNZ = 512
+# Default row-window shape for WCSR: 0 lets the library choose (W rows per
+# window, at most T stored entries per chunk; one wavefront reduces one chunk).
+DEFAULT_WINDOW_ROWS = 0
+DEFAULT_MAX_CHUNK_NNZ = 0
 
 # every symbol include/spmm.h declares
 EXPORTS = (

@@ -318,9 +318,15 @@ spmm_status_t spmm_pack_wcsr(int64_t m, int64_t k, spmm_dtype_t dtype,
   if (!out) return fail(SPMM_ERR_INVALID_ARG, "spmm_pack_wcsr: out is NULL");
   *out = nullptr;
   if (dtype != SPMM_F32) return fail(SPMM_ERR_UNSUPPORTED, "spmm_pack_wcsr: only fp32 values");
-  if (m < 0 || k < 0 || m > INT32_MAX - 1 || k > INT32_MAX || !row_ptr || window_rows <= 0 ||
-      max_chunk_nnz <= 0)
+  if (m < 0 || k < 0 || m > INT32_MAX - 1 || k > INT32_MAX || !row_ptr || window_rows < 0 ||
+      max_chunk_nnz < 0)
     return fail(SPMM_ERR_INVALID_ARG, "spmm_pack_wcsr: bad shape, window, chunk bound or pointer");
+  // 0 selects the defaults: windows of 16 rows for large matrices, fewer
+  // (down to one row) below 16 x 16384 rows so that a small matrix still
+  // gives each CU several windows; chunks of at most 512 entries
+  if (window_rows == 0)
+    window_rows = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(16, m / 16384)));
+  if (max_chunk_nnz == 0) max_chunk_nnz = 512;
   return guarded([&]() -> spmm_status_t {
     auto *a = new spmm_matrix_s();
     spmm_status_t s = pack_wcsr_f32(m, k, row_ptr, col_idx, static_cast<const float *>(vals),

@@ -94,6 +94,21 @@ def test_pack_wcsr_matches_oracle(S, orc, name, W, T):
     assert info["num_chunks"] == len(cw) and info["num_windows"] == -(-w.m // W)
 
 
+@pytest.mark.parametrize("m,W_expected", [(256, 1), (20000, 1), (65536, 4), (1_000_000, 16)])
+def test_pack_wcsr_default_window(S, orc, m, W_expected):
+    # window_rows = 0 / max_chunk_nnz = 0 pick min(16, max(1, m / 16384)) and
+    # 512; the chunk tables are then the oracle's for those values
+    rp = (np.arange(m + 1, dtype=np.int64) * 3)
+    ci = np.tile(np.array([0, 5, 9], dtype=np.int32), m)
+    v = np.ones(3 * m, dtype=np.float32)
+    M = S.spmm_pack_wcsr(m, 10, rp, ci, v, 0, 0)
+    info = S.spmm_matrix_info(M)
+    assert info["window_rows"] == W_expected and info["max_chunk_nnz"] == 512
+    cw, cb = orc.wcsr_chunks(m, rp, W_expected, 512)
+    np.testing.assert_array_equal(S.spmm_matrix_array(M, S.ARRAY_CHUNK_WINDOW), cw)
+    np.testing.assert_array_equal(S.spmm_matrix_array(M, S.ARRAY_CHUNK_BEGIN), cb)
+
+
 @pytest.mark.parametrize("seed", range(12))
 def test_pack_24_matches_oracle(S, orc, seed):
     r = np.random.default_rng(40 + seed)
@@ -153,8 +168,8 @@ def test_wcsr_rejects_non_canonical(S):
     ]
     for r_, c_ in bad:
         assert _status(S, S.spmm_pack_wcsr, 3, 4, r_, c_, v, 2, 2) == "SPMM_ERR_INVALID_ARG"
-    assert _status(S, S.spmm_pack_wcsr, 3, 4, rp, ci, v, 0, 2) == "SPMM_ERR_INVALID_ARG"
-    assert _status(S, S.spmm_pack_wcsr, 3, 4, rp, ci, v, 2, 0) == "SPMM_ERR_INVALID_ARG"
+    assert _status(S, S.spmm_pack_wcsr, 3, 4, rp, ci, v, -1, 2) == "SPMM_ERR_INVALID_ARG"
+    assert _status(S, S.spmm_pack_wcsr, 3, 4, rp, ci, v, 2, -1) == "SPMM_ERR_INVALID_ARG"
     assert _status(S, S.spmm_pack_wcsr, 3, 4, rp, ci, v, 2, 2, S.BF16) == "SPMM_ERR_UNSUPPORTED"
 
 

@@ -5,8 +5,8 @@ CPU-baseline leg import this package.  It never imports the HIP library, and
 the HIP library never imports it.
 
 Sources are cited per function in oracle.h (AsyncSparse abstract and Figure 2;
-Magicube abstract; tiled-GEMM / tile-wise abstract; the N:M and SpMM entries of
-the search-results page).
+Magicube abstract, for SpMM on low-precision integers and for SDDMM; tiled-GEMM /
+tile-wise abstract; the N:M and SpMM entries of the search-results page).
 """
 from __future__ import annotations
 
@@ -58,6 +58,7 @@ def lib():
             "orc_csr_spmm_rows": (None, [P, P, P, P, i64, i64, P, i64, i64, P]),
             "orc_bcsr_spmm_rows": (None, [i32, i32, P, P, P, P, i64, i64, P, i64, i64, P]),
             "orc_sp24_spmm_rows": (i64, [i64, P, P, P, i64, i64, P, i64, i64, P]),
+            "orc_sddmm_rows": (None, [P, P, P, i64, P, i64, i64, i64, P, P]),
             "orc_gemm_f64": (None, [i64, i64, i64, P, P, P]),
             "orc_gemm_i8": (None, [i64, i64, i64, P, P, P]),
             "orc_num_threads": (C.c_int, []),
@@ -195,6 +196,23 @@ def sp24_spmm(vals, meta, B, rows=None, j0=0, j1=None):
                                   _p(out))
     if ov:
         raise OverflowError(f"{ov} int32 sums overflowed")
+    return out
+
+
+# ---- sampled dense-dense product (SDDMM) ------------------------------------------
+def sddmm(row_ptr, col_idx, X, Y, rows=None):
+    """Reference out (float64) of the CSR pattern sampled from X (float32
+    [m, kd]) times Y^T (Y float32 [k, kd]): the entries of `rows` (all rows
+    by default) in stored order."""
+    rp, ci = _c(row_ptr, np.int64), _c(col_idx, np.int32)
+    X, Y = _c(X, np.float32), _c(Y, np.float32)
+    if rows is None:
+        rows = np.arange(len(rp) - 1, dtype=np.int64)
+    rows = _c(rows, np.int64)
+    count = int((rp[rows + 1] - rp[rows]).sum())
+    out = np.empty(count, dtype=np.float64)
+    lib().orc_sddmm_rows(_p(rp), _p(ci), _p(X), X.shape[1], _p(Y), Y.shape[1], X.shape[1],
+                         len(rows), _p(rows), _p(out))
     return out
 
 

@@ -278,6 +278,32 @@ int64_t orc_sp24_spmm_rows(int64_t k, const int8_t *vals, const uint8_t *meta,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Sampled dense-dense product [MC abstract]: the dense product X * Y^T is   */
+/* evaluated only where the sparse pattern stores an entry.                  */
+/* ------------------------------------------------------------------------ */
+void orc_sddmm_rows(const int64_t *row_ptr, const int32_t *col_idx,
+                    const float *X, int64_t ldx, const float *Y, int64_t ldy, int64_t kd,
+                    int64_t nrows, const int64_t *rows, double *out) {
+  /* output offset of each requested row */
+  int64_t *off = (int64_t *)malloc(sizeof(int64_t) * (size_t)(nrows + 1));
+  off[0] = 0;
+  for (int64_t r = 0; r < nrows; ++r)
+    off[r + 1] = off[r] + (row_ptr[rows[r] + 1] - row_ptr[rows[r]]);
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t r = 0; r < nrows; ++r) {
+    const int64_t i = rows[r];
+    const float *x = X + i * ldx;
+    for (int64_t p = row_ptr[i]; p < row_ptr[i + 1]; ++p) {
+      const float *y = Y + (int64_t)col_idx[p] * ldy;
+      double s = 0.0;
+      for (int64_t t = 0; t < kd; ++t) s += (double)x[t] * (double)y[t];
+      out[off[r] + (p - row_ptr[i])] = s;
+    }
+  }
+  free(off);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Brute force: dense naive triple loops, i then j then k.                   */
 /* ------------------------------------------------------------------------ */
 void orc_gemm_f64(int64_t m, int64_t k, int64_t n, const double *A, const double *B,

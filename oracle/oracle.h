@@ -19,7 +19,8 @@
  *         (BCSR vs WCSR formats); summary paragraph "What carries the
  *         argument" (row-window splitting across thread blocks).
  *   [MC]  "Efficient Quantized Sparse Matrix Operations on Tensor Cores" --
- *         abstract (SpMM on low-precision integers).
+ *         abstract (SpMM on low-precision integers; SDDMM, the sampled
+ *         dense-dense product, as its companion operation).
  *   [TW]  "Accelerating Sparse DNNs Based on Tiled GEMM" -- abstract (the 2:4
  *         pattern of the sparse tensor core; tile-wise sparsity).
  *   [DP]  "Daily Papers" search page for sparse FP4 GEMM -- the entry on
@@ -99,6 +100,15 @@ int64_t orc_sp24_spmm_rows(int64_t k, const int8_t *vals, const uint8_t *meta,
                            const int8_t *B, int64_t ldb,
                            int64_t nrows, const int64_t *rows, int64_t j0, int64_t j1,
                            int32_t *out);
+
+/* ---- sampled dense-dense product [MC abstract: SDDMM] ---------------------- */
+/* out[p] = sum over t ascending of X[i][t] * Y[j][t] (fp64), for every stored
+ * entry p = (i, j) of the CSR pattern (row_ptr, col_idx) whose row i is in
+ * rows[0 .. nrows); out holds the entries of those rows in stored order.
+ * The pattern's values play no part: it is the sample mask. */
+void orc_sddmm_rows(const int64_t *row_ptr, const int32_t *col_idx,
+                    const float *X, int64_t ldx, const float *Y, int64_t ldy, int64_t kd,
+                    int64_t nrows, const int64_t *rows, double *out);
 
 /* ---- brute force (dense, naive triple loops) ---------------------------- */
 void orc_gemm_f64(int64_t m, int64_t k, int64_t n, const double *A, const double *B,

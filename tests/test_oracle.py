@@ -301,3 +301,46 @@ def test_rel_frobenius(orc):
     assert orc.rel_frobenius([3.0, 4.0 + 5e-3], [3.0, 4.0]) == pytest.approx(1e-3)
     assert orc.rel_frobenius([0.0], [0.0]) == 0.0
     assert orc.rel_frobenius([1.0], [0.0]) == float("inf")
+
+
+# ---------------------------------------------------------------------------
+# sampled dense-dense product (SDDMM): brute force and closed forms
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_sddmm_bruteforce(orc, seed):
+    # oracle vs numpy's dense X @ Y^T read at the pattern's positions
+    r = np.random.default_rng(700 + seed)
+    m, k, kd = (int(x) for x in r.integers(1, 80, size=3))
+    rp, ci, _ = synth.csr_uniform(m, k, float(r.uniform(0.0, 0.5)), 3000 + seed)
+    X = r.standard_normal((m, kd)).astype(np.float32)
+    Y = r.standard_normal((k, kd)).astype(np.float32)
+    got = orc.sddmm(rp, ci, X, Y)
+    rows = np.repeat(np.arange(m), np.diff(rp))
+    ref = (X.astype(np.float64) @ Y.astype(np.float64).T)[rows, ci]
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+    # a row subset gives those rows' entries, in stored order
+    sub = np.sort(r.choice(m, size=max(1, m // 2), replace=False)).astype(np.int64)
+    want = np.concatenate([got[rp[i]:rp[i + 1]] for i in sub])
+    np.testing.assert_array_equal(orc.sddmm(rp, ci, X, Y, rows=sub), want)
+
+
+def test_sddmm_closed_forms(orc):
+    r = np.random.default_rng(11)
+    m, kd = 40, 24
+    X = r.standard_normal((m, kd)).astype(np.float32)
+    # diagonal pattern with Y = X: squared row norms
+    rp = np.arange(m + 1, dtype=np.int64)
+    ci = np.arange(m, dtype=np.int32)
+    np.testing.assert_allclose(orc.sddmm(rp, ci, X, X),
+                               (X.astype(np.float64) ** 2).sum(axis=1), rtol=1e-13)
+    # one-hot rows of X pick single columns of Y: exact
+    Y = r.standard_normal((30, kd)).astype(np.float32)
+    hot = r.integers(0, kd, size=m)
+    Xh = np.zeros((m, kd), np.float32)
+    Xh[np.arange(m), hot] = 1.0
+    cols = r.integers(0, 30, size=m).astype(np.int32)
+    np.testing.assert_array_equal(orc.sddmm(rp, cols, Xh, Y), Y[cols, hot].astype(np.float64))
+    # an empty pattern gives nothing; empty rows are skipped
+    assert len(orc.sddmm(np.zeros(m + 1, np.int64), np.zeros(0, np.int32), X, X)) == 0

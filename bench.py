@@ -3,12 +3,14 @@
 
 A step is one spmm_execute (every kernel the plan launches) over one dense B
 that is already resident in HBM; packing and planning are one-time costs,
-reported separately.  The default workload is the 4096 x 4096 BCSR bf16
+reported separately.  For the sampled dense-dense workloads (format sddmm) a
+step is one spmm_execute_sddmm over resident X and Y, and n is the inner
+dimension kd.  The default workload is the 4096 x 4096 BCSR bf16
 matrix with 90% of its 64 x 64 blocks zero and B of 4096 columns; the other
 workloads of the catalogue run with --workload.
 
 Prints one JSON line:
-  value      effective GFLOP/s = 2 * nnz * n / (time per step)
+  value      effective GFLOP/s = 2 * nnz * n / (time per step)  (n = kd for sddmm)
   roofline   the dominant kernel against its bound: the larger of the HBM
              time (algorithmic bytes at 8 TB/s) and the MFMA time
              (algorithmic flops at the dtype's dense peak), from HIP events
@@ -41,7 +43,8 @@ PEAK_HBM_GBS = 8000.0
 PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "i8": 5000.0}
 
 # kernel whose launch dominates a step, per format
-DOMINANT_KERNEL = {"bcsr": "bcsr_bf16_mfma", "wcsr": "wcsr_stream", "sp24": "sp24_i8_smfmac"}
+DOMINANT_KERNEL = {"bcsr": "bcsr_bf16_mfma", "wcsr": "wcsr_stream", "sp24": "sp24_i8_smfmac",
+                   "sddmm": "sddmm_f32"}
 TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 CSRC = os.path.join(ROOT, "sparse_dense_matrix_amd", "csrc")
 
@@ -78,13 +81,13 @@ def setup(w, S, args):
     import synth
     t0 = time.perf_counter()
     a = synth.make_a(w)
-    B = synth.make_b(w)
+    B = synth.make_xy(w) if w.fmt == "sddmm" else synth.make_b(w)
     t_gen = time.perf_counter() - t0
     t0 = time.perf_counter()
     if w.fmt == "bcsr":
         M = S.spmm_pack_bcsr(a["dense"], w.block, w.block)
         types = (S.BF16, S.BF16)
-    elif w.fmt == "wcsr":
+    elif w.fmt in ("wcsr", "sddmm"):
         W = args.window_rows or S.DEFAULT_WINDOW_ROWS
         T = args.max_chunk_nnz or S.DEFAULT_MAX_CHUNK_NNZ
         M = S.spmm_pack_wcsr(w.m, w.k, a["row_ptr"], a["col_idx"], a["vals"], W, T)
@@ -94,7 +97,10 @@ def setup(w, S, args):
         types = (S.I8, S.I32)
     t_pack = time.perf_counter() - t0
     t0 = time.perf_counter()
-    P = S.spmm_plan(M, w.n, *types)
+    if w.fmt == "sddmm":
+        P = S.spmm_plan_sddmm(M, w.n)
+    else:
+        P = S.spmm_plan(M, w.n, *types)
     t_plan = time.perf_counter() - t0
     info = S.spmm_matrix_info(M)
     return {"a": a, "B": B, "M": M, "P": P, "info": info, "t_gen": t_gen, "t_pack": t_pack,
@@ -122,6 +128,13 @@ def algorithmic(w, d):
         touched = len(np.unique(d["a"]["col_idx"]))
         a_bytes = 8 * (w.m + 1) + 8 * nnz
         return flops, a_bytes + touched * n * 4 + w.m * n * 4, "f32"
+    if w.fmt == "sddmm":
+        # row_ptr, col_idx and out once; each X row with entries and each
+        # touched Y row once (n is the inner dimension kd)
+        nnz = info["nnz"]
+        x_rows = int(np.count_nonzero(np.diff(d["a"]["row_ptr"])))
+        y_rows = len(np.unique(d["a"]["col_idx"]))
+        return flops, 8 * (w.m + 1) + 8 * nnz + (x_rows + y_rows) * n * 4, "f32"
     a_bytes = w.m * w.k // 2 + w.m * w.k // 8
     return flops, a_bytes + w.k * n + w.m * n * 4, "i8"
 
@@ -159,22 +172,33 @@ def main():
     log(f"generated in {d['t_gen']:.1f}s, packed in {d['t_pack']:.2f}s, planned in {d['t_plan']:.2f}s")
 
     # device operands
-    B = d["B"]
-    Bh = torch.from_numpy(B.view(np.int16) if B.dtype == np.uint16 else B)
-    Bt = Bh.cuda()
-    cdt = {"bcsr": torch.int16, "wcsr": torch.float32, "sp24": torch.int32}[w.fmt]
-    Ct = torch.empty((w.m, w.n), dtype=cdt, device="cuda")
+    if w.fmt == "sddmm":
+        Xt = torch.from_numpy(d["B"][0]).cuda()
+        Yt = torch.from_numpy(d["B"][1]).cuda()
+        Ot = torch.empty(max(d["info"]["nnz"], 1), dtype=torch.float32, device="cuda")
+
+        def step(stream):
+            S.spmm_execute_sddmm(d["P"], Xt, Yt, Ot, stream=stream)
+    else:
+        B = d["B"]
+        Bh = torch.from_numpy(B.view(np.int16) if B.dtype == np.uint16 else B)
+        Bt = Bh.cuda()
+        cdt = {"bcsr": torch.int16, "wcsr": torch.float32, "sp24": torch.int32}[w.fmt]
+        Ct = torch.empty((w.m, w.n), dtype=cdt, device="cuda")
+
+        def step(stream):
+            S.spmm_execute(d["P"], Bt, Ct, stream=stream)
     stream = torch.cuda.Stream()
     torch.cuda.synchronize()
     for _ in range(args.warmup):
-        S.spmm_execute(d["P"], Bt, Ct, stream=stream)
+        step(stream)
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(args.steps):
-        S.spmm_execute(d["P"], Bt, Ct, stream=stream)
+        step(stream)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -345,6 +369,11 @@ def cpu_baseline(w, d, target_s):
 
         def run(rows):
             oracle.csr_spmm(a["row_ptr"], a["col_idx"], a["vals"], B, rows=rows)
+    elif w.fmt == "sddmm":
+        row_nnz = np.diff(a["row_ptr"])
+
+        def run(rows):
+            oracle.sddmm(a["row_ptr"], a["col_idx"], B[0], B[1], rows=rows)
     else:
         vals, meta = oracle.pack24(a["dense"])
         row_nnz = np.full(w.m, w.k // 2, dtype=np.int64)
@@ -367,7 +396,8 @@ def cpu_baseline(w, d, target_s):
     return {"value": round(flops / spent / 1e9, 3), "unit": "GFLOP/s",
             "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{len(rows)} of {w.m} rows (uniform without replacement, seed 0), "
-                      f"all {w.n} columns; fp64 accumulation"}
+                      + ("all their stored entries" if w.fmt == "sddmm" else f"all {w.n} columns")
+                      + "; fp64 accumulation"}
 
 
 if __name__ == "__main__":

@@ -158,7 +158,7 @@ spmm_status_t spmm_plan(spmm_matrix_t a, int64_t n, spmm_dtype_t b_dtype,
 typedef struct {
   int32_t format;
   int32_t device;
-  int64_t m, k, n;
+  int64_t m, k, n;           /* n: columns of B and C; kd for an SDDMM plan    */
   int64_t device_bytes;     /* packed operand + tables on the device          */
   int64_t workspace_bytes;  /* WCSR partial rows of split windows             */
   int64_t num_split_rows;   /* WCSR rows whose entries span several chunks    */
@@ -180,6 +180,28 @@ void spmm_plan_destroy(spmm_plan_t p);
  * time: concurrent streams need separate plans.  B and C must not overlap. */
 spmm_status_t spmm_execute(spmm_plan_t p, const void *b_dev, int64_t ldb, void *c_dev,
                            int64_t ldc, hipStream_t stream);
+
+/* ---- sampled dense-dense product (SDDMM) ---- */
+
+/* Plan out[p] = sum over t < kd of X[i][t] * Y[j][t] for every stored entry
+ * p = (i, j) of the WCSR matrix a: its stored pattern is the sample mask and
+ * its values play no part.  SDDMM is the companion of SpMM on the Magicube
+ * page ("Efficient Quantized Sparse Matrix Operations on Tensor Cores",
+ * abstract).  a must be WCSR and dtype SPMM_F32 (X, Y and out are fp32),
+ * else UNSUPPORTED; work is split by a's chunks.  Synchronous; the plan
+ * holds a reference on a.  kd = 0 is allowed (out becomes zeros). */
+spmm_status_t spmm_plan_sddmm(spmm_matrix_t a, int64_t kd, spmm_dtype_t dtype, int32_t device,
+                              spmm_plan_t *out);
+
+/* out_dev[p] for every stored entry p of the plan's pattern, in its stored
+ * order (float[nnz]), on `stream`.  x_dev [m x kd] and y_dev [k x kd] are
+ * row-major device arrays on the plan's device, 16-byte aligned, with
+ * ldx, ldy >= kd and ldx * 4, ldy * 4 multiples of 16 bytes (with kd = 0
+ * X, Y and their ld are not read); out_dev is 4-byte aligned.  Allocates
+ * nothing and does not synchronise.  Plans of
+ * spmm_plan are refused here and SDDMM plans by spmm_execute (INVALID_ARG). */
+spmm_status_t spmm_execute_sddmm(spmm_plan_t p, const void *x_dev, int64_t ldx, const void *y_dev,
+                                 int64_t ldy, void *out_dev, hipStream_t stream);
 
 /* ---- errors ---- */
 const char *spmm_status_str(spmm_status_t s);

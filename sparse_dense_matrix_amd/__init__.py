@@ -23,6 +23,7 @@ __all__ = [
     "ARRAY_CHUNK_WINDOW", "ARRAY_CHUNK_BEGIN",
     "spmm_pack_bcsr", "spmm_pack_wcsr", "spmm_pack_24", "spmm_matrix_info",
     "spmm_matrix_array", "spmm_plan", "spmm_plan_info", "spmm_execute",
+    "spmm_plan_sddmm", "spmm_execute_sddmm",
     "spmm_status_str", "spmm_last_error", "LIB_PATH", "EXPORTS",
 ]
 
@@ -44,7 +45,8 @@ DEFAULT_MAX_CHUNK_NNZ = 0
 EXPORTS = (
     "spmm_pack_bcsr", "spmm_pack_wcsr", "spmm_pack_24", "spmm_matrix_info",
     "spmm_matrix_array", "spmm_matrix_destroy", "spmm_plan", "spmm_plan_info",
-    "spmm_plan_destroy", "spmm_execute", "spmm_status_str", "spmm_last_error",
+    "spmm_plan_destroy", "spmm_execute", "spmm_plan_sddmm", "spmm_execute_sddmm",
+    "spmm_status_str", "spmm_last_error",
 )
 
 
@@ -89,6 +91,8 @@ def _load():
         "spmm_plan_info": (st, [P, C.POINTER(PlanInfo)]),
         "spmm_plan_destroy": (None, [P]),
         "spmm_execute": (st, [P, P, i64, P, i64, P]),
+        "spmm_plan_sddmm": (st, [P, i64, st, i32, C.POINTER(P)]),
+        "spmm_execute_sddmm": (st, [P, P, i64, P, i64, P, P]),
         "spmm_status_str": (C.c_char_p, [st]),
         "spmm_last_error": (C.c_char_p, []),
     }
@@ -239,7 +243,10 @@ def spmm_plan_info(plan: Plan) -> dict:
 
 
 def _dev_ptr_ld(t):
-    """(pointer, leading dimension) of a 2-D row-major torch tensor."""
+    """(pointer, leading dimension) of a 2-D row-major torch tensor.  A tensor
+    with no columns has no meaningful strides: its leading dimension is 0."""
+    if t.dim() == 2 and t.shape[1] == 0:
+        return t.data_ptr(), 0
     if t.dim() != 2 or t.stride(1) != 1:
         raise ValueError("dense operands must be 2-D row-major (stride(1) == 1)")
     return t.data_ptr(), t.stride(0)
@@ -266,3 +273,35 @@ def spmm_execute(plan: Plan, b, c, stream=None, ldb: int | None = None,
         stream = stream.cuda_stream
     _check(_lib.spmm_execute(plan.handle, C.c_void_p(bp), ldb, C.c_void_p(cp), ldc,
                              C.c_void_p(stream)), "spmm_execute")
+
+
+def spmm_plan_sddmm(mat: Matrix, kd: int, dtype: int = F32, device: int = 0) -> Plan:
+    """Plan the sampled product out[p] = X[i] . Y[j] over the stored entries
+    (i, j) of a WCSR matrix, inner dimension kd."""
+    h = C.c_void_p()
+    _check(_lib.spmm_plan_sddmm(mat.handle, kd, dtype, device, C.byref(h)), "spmm_plan_sddmm")
+    return Plan(h)
+
+
+def spmm_execute_sddmm(plan: Plan, x, y, out, stream=None, ldx: int | None = None,
+                       ldy: int | None = None):
+    """out[p] for every stored entry on `stream` (default: torch's current
+    stream).  x [m, kd] and y [k, kd] are 2-D row-major torch tensors (or raw
+    device pointers with ldx / ldy); out is a float32 tensor of nnz elements
+    (or a raw pointer)."""
+    if isinstance(x, int) or isinstance(y, int):
+        xp, yp = int(x), int(y)
+        if ldx is None or ldy is None:
+            raise ValueError("raw pointers need ldx and ldy")
+    else:
+        xp, ldx = _dev_ptr_ld(x)
+        yp, ldy = _dev_ptr_ld(y)
+    op = int(out) if isinstance(out, int) else out.data_ptr()
+    if stream is None:
+        import torch
+        dev = out.device if hasattr(out, "device") else None
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    _check(_lib.spmm_execute_sddmm(plan.handle, C.c_void_p(xp), ldx, C.c_void_p(yp), ldy,
+                                   C.c_void_p(op), C.c_void_p(stream)), "spmm_execute_sddmm")

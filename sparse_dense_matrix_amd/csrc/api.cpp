@@ -145,13 +145,15 @@ spmm_status_t plan_bcsr(spmm_plan_s *p) {
 }
 
 // ---- WCSR plan: chunk descriptors, split rows and their partial slots ------
-spmm_status_t plan_wcsr(spmm_plan_s *p) {
-  const Matrix &a = *p->a;
+}  // namespace
+
+spmm_status_t wcsr_chunk_descriptors(const Matrix &a, std::vector<WcsrChunk> &chunks,
+                                     std::vector<int32_t> &slot_row) {
   const int64_t m = a.m, W = a.window_rows;
   const int64_t C = static_cast<int64_t>(a.chunk_window.size());
   const int64_t *rp = a.row_ptr.data();
-  std::vector<WcsrChunk> chunks(C);
-  std::vector<int32_t> slot_row;  // row of each partial slot, in slot order
+  chunks.assign(C, WcsrChunk{});
+  slot_row.clear();
   for (int64_t c = 0; c < C; ++c) {
     const int64_t w = a.chunk_window[c];
     const int64_t r0 = w * W, r1 = std::min(m, r0 + W);
@@ -189,6 +191,18 @@ spmm_status_t plan_wcsr(spmm_plan_s *p) {
       slot_row.push_back(static_cast<int32_t>(re - 1));
     }
   }
+  return SPMM_OK;
+}
+
+namespace {
+
+spmm_status_t plan_wcsr(spmm_plan_s *p) {
+  const Matrix &a = *p->a;
+  const int64_t C = static_cast<int64_t>(a.chunk_window.size());
+  std::vector<WcsrChunk> chunks;
+  std::vector<int32_t> slot_row;  // row of each partial slot, in slot order
+  spmm_status_t st = wcsr_chunk_descriptors(a, chunks, slot_row);
+  if (st != SPMM_OK) return st;
   // slots of one split row are consecutive: group them
   std::vector<int32_t> merge_row, merge_slot;
   for (size_t s = 0; s < slot_row.size(); ++s) {
@@ -234,6 +248,29 @@ spmm_status_t plan_wcsr(spmm_plan_s *p) {
   p->info.tile_m = 0;
   p->info.tile_n = 0;
   p->info.grid = wcsr_grid(C, p->n);
+  return SPMM_OK;
+}
+
+// ---- SDDMM plan: the WCSR chunks, the pattern, no workspace ----------------
+spmm_status_t plan_sddmm(spmm_plan_s *p, int64_t kd) {
+  const Matrix &a = *p->a;
+  std::vector<WcsrChunk> chunks;
+  std::vector<int32_t> slot_row;  // unused: sampled entries are independent
+  spmm_status_t st = wcsr_chunk_descriptors(a, chunks, slot_row);
+  if (st != SPMM_OK) return st;
+  SddmmLaunch &L = p->sdd;
+  WcsrChunk *dchunks = nullptr;
+  int64_t *drp = nullptr;
+  int32_t *dci = nullptr;
+  if ((st = upload_vec(p, chunks, &dchunks)) != SPMM_OK) return st;
+  if ((st = upload_vec(p, a.row_ptr, &drp)) != SPMM_OK) return st;
+  if ((st = upload_vec(p, a.col_idx, &dci)) != SPMM_OK) return st;
+  L.chunks = dchunks;
+  L.num_chunks = static_cast<int64_t>(chunks.size());
+  L.row_ptr = drp;
+  L.col_idx = dci;
+  L.kd = kd;
+  p->info.grid = sddmm_grid(L.num_chunks);
   return SPMM_OK;
 }
 
@@ -473,6 +510,7 @@ void spmm_plan_destroy(spmm_plan_t p) { free_plan(p); }
 spmm_status_t spmm_execute(spmm_plan_t p, const void *b_dev, int64_t ldb, void *c_dev,
                            int64_t ldc, hipStream_t stream) {
   if (!p) return fail(SPMM_ERR_INVALID_ARG, "spmm_execute: plan is NULL");
+  if (p->sddmm) return fail(SPMM_ERR_INVALID_ARG, "spmm_execute: plan is an SDDMM plan");
   const Matrix &a = *p->a;
   const int64_t n = p->n;
   if (n == 0 || a.m == 0) return SPMM_OK;
@@ -509,6 +547,78 @@ spmm_status_t spmm_execute(spmm_plan_t p, const void *b_dev, int64_t ldb, void *
     L.ldc = ldc;
     e = launch_sp24_i8(L, stream);
   }
+  if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  return SPMM_OK;
+}
+
+spmm_status_t spmm_plan_sddmm(spmm_matrix_t a, int64_t kd, spmm_dtype_t dtype, int32_t device,
+                              spmm_plan_t *out) {
+  if (!out) return fail(SPMM_ERR_INVALID_ARG, "spmm_plan_sddmm: out is NULL");
+  *out = nullptr;
+  if (!a || kd < 0 || kd > INT32_MAX) return fail(SPMM_ERR_INVALID_ARG, "spmm_plan_sddmm: bad matrix or kd");
+  if (a->format != SPMM_FORMAT_WCSR || dtype != SPMM_F32)
+    return fail(SPMM_ERR_UNSUPPORTED, "spmm_plan_sddmm: needs a WCSR pattern and fp32 X, Y");
+  int ndev = 0;
+  hipError_t e = hipGetDeviceCount(&ndev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceCount");
+  if (device < 0 || device >= ndev) return fail(SPMM_ERR_INVALID_ARG, "spmm_plan_sddmm: no such device");
+  return guarded([&]() -> spmm_status_t {
+    DeviceScope ds(device);
+    if (ds.err != hipSuccess) return hip_fail(ds.err, "hipSetDevice");
+    auto *p = new spmm_plan_s();
+    retain(a);
+    p->a = a;
+    p->sddmm = true;
+    p->device = device;
+    p->n = kd;
+    p->info.format = a->format;
+    p->info.device = device;
+    p->info.m = a->m;
+    p->info.k = a->k;
+    p->info.n = kd;
+    spmm_status_t s = SPMM_ERR_INTERNAL;
+    try {
+      s = plan_sddmm(p, kd);
+    } catch (...) {
+      free_plan(p);
+      throw;
+    }
+    if (s == SPMM_OK) {
+      e = hipDeviceSynchronize();
+      if (e != hipSuccess) s = hip_fail(e, "hipDeviceSynchronize");
+    }
+    if (s != SPMM_OK) {
+      free_plan(p);
+      return s;
+    }
+    *out = p;
+    return SPMM_OK;
+  });
+}
+
+spmm_status_t spmm_execute_sddmm(spmm_plan_t p, const void *x_dev, int64_t ldx, const void *y_dev,
+                                 int64_t ldy, void *out_dev, hipStream_t stream) {
+  if (!p) return fail(SPMM_ERR_INVALID_ARG, "spmm_execute_sddmm: plan is NULL");
+  if (!p->sddmm) return fail(SPMM_ERR_INVALID_ARG, "spmm_execute_sddmm: plan is not an SDDMM plan");
+  const Matrix &a = *p->a;
+  const int64_t kd = p->n;
+  if (a.nnz == 0) return SPMM_OK;
+  if (!out_dev || (kd > 0 && (!x_dev || !y_dev)))
+    return fail(SPMM_ERR_INVALID_ARG, "spmm_execute_sddmm: X, Y or out is NULL");
+  if ((reinterpret_cast<uintptr_t>(out_dev) & 3u) ||
+      (kd > 0 && (!aligned16(x_dev) || !aligned16(y_dev) || ldx < kd || ldy < kd ||
+                  (ldx * 4) % 16 != 0 || (ldy * 4) % 16 != 0)))
+    return fail(SPMM_ERR_INVALID_ARG,
+                "spmm_execute_sddmm: X/Y must be 16-byte aligned with ld >= kd and ld*4 % 16 == 0");
+  DeviceScope ds(p->device);
+  if (ds.err != hipSuccess) return hip_fail(ds.err, "hipSetDevice");
+  SddmmLaunch L = p->sdd;
+  L.X = static_cast<const float *>(x_dev);
+  L.ldx = ldx;
+  L.Y = static_cast<const float *>(y_dev);
+  L.ldy = ldy;
+  L.out = static_cast<float *>(out_dev);
+  hipError_t e = launch_sddmm_f32(L, stream);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return SPMM_OK;
 }

@@ -116,6 +116,27 @@ struct WcsrLaunch {
 hipError_t launch_wcsr_f32(const WcsrLaunch &a, hipStream_t s);
 int64_t wcsr_grid(int64_t num_chunks, int64_t n);
 
+// Chunk descriptors of a WCSR matrix (row range of each chunk, and the
+// partial-row slots of rows split across chunks, slot_row[s] = row of slot
+// s in slot order).  Fails only on an internal inconsistency.
+spmm_status_t wcsr_chunk_descriptors(const Matrix &a, std::vector<WcsrChunk> &chunks,
+                                     std::vector<int32_t> &slot_row);
+
+struct SddmmLaunch {
+  const WcsrChunk *chunks;
+  int64_t num_chunks;
+  const int64_t *row_ptr;
+  const int32_t *col_idx;
+  int64_t kd;         // inner dimension
+  const float *X;     // [m][ldx]
+  int64_t ldx;
+  const float *Y;     // [k][ldy]
+  int64_t ldy;
+  float *out;         // [nnz]
+};
+hipError_t launch_sddmm_f32(const SddmmLaunch &a, hipStream_t s);
+int64_t sddmm_grid(int64_t num_chunks);
+
 struct Sp24Launch {
   const int8_t *vals;   // tiled copy of the values (sp24_tile_layout)
   const uint8_t *meta;  // tiled copy of the index words
@@ -145,6 +166,7 @@ hipError_t launch_sp24_i8(const Sp24Launch &a, hipStream_t s);
 // ---------------------------------------------------------------------------
 struct spmm_plan_s {
   sdm::Matrix *a = nullptr;
+  bool sddmm = false;  // plan of spmm_plan_sddmm rather than spmm_plan
   int32_t device = 0;
   int64_t n = 0;
   spmm_plan_info_t info{};
@@ -152,6 +174,7 @@ struct spmm_plan_s {
   sdm::BcsrLaunch bcsr{};
   sdm::WcsrLaunch wcsr{};
   sdm::Sp24Launch sp24{};
+  sdm::SddmmLaunch sdd{};
 };
 
 struct spmm_matrix_s : sdm::Matrix {};

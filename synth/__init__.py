@@ -25,7 +25,7 @@ from typing import Dict
 import numpy as np
 
 # stream ids: one independent Philox key per random quantity of a workload
-S_PATTERN, S_AVAL, S_BVAL, S_ROWLEN, S_COLS, S_BAND = 0, 1, 2, 3, 4, 5
+S_PATTERN, S_AVAL, S_BVAL, S_ROWLEN, S_COLS, S_BAND, S_YVAL = 0, 1, 2, 3, 4, 5, 6
 
 
 def rng(seed: int, stream: int) -> np.random.Generator:
@@ -176,7 +176,7 @@ def dense_f32_normal(rows: int, cols: int, seed: int, stream: int = S_BVAL) -> n
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    fmt: str            # "wcsr" | "bcsr" | "sp24"
+    fmt: str            # "wcsr" | "bcsr" | "sp24" | "sddmm" (n = inner dimension)
     m: int
     k: int
     n: int
@@ -210,6 +210,9 @@ WORKLOADS: Dict[str, Workload] = {
                                 powerlaw=True),
     "sp24_i8_8192": Workload("sp24_i8_8192", "sp24", 8192, 8192, 2048, 20260004),
     "bcsr_prefill_18944x3584": _bcsr("bcsr_prefill_18944x3584", 18944, 3584, 65536, 0.90, 20260005),
+    # the sampled dense-dense product on the power-law pattern, inner dimension 128
+    "sddmm_powerlaw_1m": Workload("sddmm_powerlaw_1m", "sddmm", 1_000_000, 1_000_000, 128, 20260003,
+                                  powerlaw=True),
 }
 
 # ... and smaller cases of the same construction for element-wise parity
@@ -221,13 +224,15 @@ SMALL: Dict[str, Workload] = {
     "bcsr_small": _bcsr("bcsr_small", 640, 512, 1000, 0.7, 33),
     "sp24_small": Workload("sp24_small", "sp24", 320, 512, 400, 34),
     "bcsr_prefill_slice": _bcsr("bcsr_prefill_slice", 18944, 3584, 4096 + 64 * 3, 0.90, 20260005),
+    "sddmm_small": Workload("sddmm_small", "sddmm", 20000, 20000, 96, 32, powerlaw=True, cap=3000,
+                            band_half=64),
 }
 
 
 def make_a(w: Workload) -> dict:
     """Draw the sparse operand.  wcsr -> CSR arrays; bcsr -> dense bf16 bits;
     sp24 -> dense int8 (not yet pruned: pruning is the packer's job)."""
-    if w.fmt == "wcsr":
+    if w.fmt in ("wcsr", "sddmm"):
         if w.powerlaw:
             rp, ci, v = csr_powerlaw(w.m, w.k, w.zipf, w.cap, w.band_frac, w.band_half, w.seed)
         else:
@@ -239,6 +244,13 @@ def make_a(w: Workload) -> dict:
     if w.fmt == "sp24":
         return {"dense": int8_uniform(rng(w.seed, S_AVAL), (w.m, w.k))}
     raise ValueError(w.fmt)
+
+
+def make_xy(w: Workload, kd: int | None = None):
+    """Draw the dense operands of the sampled product: X [m x kd] and
+    Y [k x kd], row-major float32 N(0, 1)."""
+    kd = w.n if kd is None else kd
+    return dense_f32_normal(w.m, kd, w.seed, S_BVAL), dense_f32_normal(w.k, kd, w.seed, S_YVAL)
 
 
 def make_b(w: Workload, n: int | None = None) -> np.ndarray:

@@ -340,3 +340,109 @@ def test_two_plans_two_streams(S, orc):
     rp, ci, v = orc.pack_bcsr(a2, 64, 64)
     ref2 = orc.bcsr_spmm(64, 64, rp, ci, v, B2)
     assert orc.rel_frobenius(bf16_to_f64(from_dev(C2, "bf16")), ref2) <= TOL_BF16
+
+
+# ---------------------------------------------------------------------------
+# SDDMM fp32: out[p] = X[i] . Y[j] over the stored entries of a WCSR pattern
+# ---------------------------------------------------------------------------
+
+def sddmm_case(S, orc, m, k, rp, ci, X, Y, W=0, T=0, rows=None, extra=0):
+    """X and Y go to the device as column slices of allocations whose rows are
+    whole 16-byte multiples (kd rounded up to 4 floats, plus `extra`)."""
+    torch = pytest.importorskip("torch")
+    M = S.spmm_pack_wcsr(m, k, rp, ci, np.ones(len(ci), np.float32), W, T)
+    kd = X.shape[1]
+    P = S.spmm_plan_sddmm(M, kd)
+    nnz = len(ci)
+    out = torch.full((max(nnz, 1),), float("nan"), dtype=torch.float32, device="cuda")
+    pad = (-kd) % 4 + extra
+    S.spmm_execute_sddmm(P, to_dev(X, pad), to_dev(Y, pad), out)
+    got = from_dev(out, "f32")[:nnz]
+    if rows is None:
+        ref = orc.sddmm(rp, ci, X, Y)
+        sel = got
+    else:
+        ref = orc.sddmm(rp, ci, X, Y, rows=rows)
+        sel = np.concatenate([got[rp[i]:rp[i + 1]] for i in rows]) if len(rows) else got[:0]
+    assert np.isfinite(got).all(), "unwritten or non-finite outputs"
+    return orc.rel_frobenius(sel, ref), got, P
+
+
+@pytest.mark.parametrize("kd", [1, 4, 63, 96, 128, 200, 300, 301, 1000])
+def test_sddmm_small(S, orc, kd):
+    w = synth.SMALL["sddmm_small"]          # 20000 x 20000 power-law pattern
+    a = synth.make_a(w)
+    X, Y = synth.make_xy(w, kd)
+    for W, T, extra in ((0, 0, 0), (16, 64, 4), (1, 5, 0)):
+        err, _, P = sddmm_case(S, orc, w.m, w.k, a["row_ptr"], a["col_idx"], X, Y, W, T,
+                               extra=extra)
+        _say(f"sddmm_small kd={kd} W={W} T={T} ld+{extra} grid={P.info()['grid']} "
+             f"rel_frob={err:.3e}")
+        assert err <= TOL_F32
+
+
+def test_sddmm_empty_giant_rows_and_kd0(S, orc):
+    k, kd = 30000, 128
+    r = np.random.default_rng(19)
+    lens = np.zeros(50, np.int64)
+    lens[[3, 17, 18, 40]] = [20000, 5, 1, 7000]
+    rp = np.zeros(51, np.int64)
+    np.cumsum(lens, out=rp[1:])
+    ci = np.concatenate([np.sort(r.choice(k, L, replace=False)) for L in lens if L]).astype(np.int32)
+    X = synth.dense_f32_normal(50, kd, 83)
+    Y = synth.dense_f32_normal(k, kd, 84)
+    for W, T in ((16, 512), (4, 300), (1, 64)):
+        err, _, _ = sddmm_case(S, orc, 50, k, rp, ci, X, Y, W, T)
+        assert err <= TOL_F32
+    # kd = 0: every sampled product is the empty sum
+    _, got, _ = sddmm_case(S, orc, 50, k, rp, ci, X[:, :0].copy(), Y[:, :0].copy(), 16, 512)
+    assert (got == 0).all()
+
+
+def test_sddmm_diagonal_closed_form(S, orc):
+    # diagonal pattern with Y = X: squared row norms
+    m, kd = 3000, 160
+    X = synth.dense_f32_normal(m, kd, 85)
+    rp = np.arange(m + 1, dtype=np.int64)
+    ci = np.arange(m, dtype=np.int32)
+    err, got, _ = sddmm_case(S, orc, m, m, rp, ci, X, X)
+    np.testing.assert_allclose(got, (X.astype(np.float64) ** 2).sum(axis=1), rtol=1e-5)
+    assert err <= TOL_F32
+
+
+def test_sddmm_powerlaw_1m_sampled(S, orc):
+    w = synth.WORKLOADS["sddmm_powerlaw_1m"]
+    a = synth.make_a(w)
+    X, Y = synth.make_xy(w)
+    lens = np.diff(a["row_ptr"])
+    r = np.random.default_rng(20)
+    rows = np.unique(np.concatenate([np.argsort(lens)[-200:], r.choice(w.m, 2000, replace=False),
+                                     np.arange(50), np.arange(w.m - 50, w.m)])).astype(np.int64)
+    err, _, P = sddmm_case(S, orc, w.m, w.k, a["row_ptr"], a["col_idx"], X, Y, rows=rows)
+    _say(f"sddmm_powerlaw_1m rows={len(rows)} grid={P.info()['grid']} rel_frob={err:.3e}")
+    assert err <= TOL_F32
+
+
+def test_sddmm_deterministic_and_plan_kinds(S, orc):
+    torch = pytest.importorskip("torch")
+    w = synth.SMALL["sddmm_small"]
+    a = synth.make_a(w)
+    X, Y = synth.make_xy(w)
+    _, x1, P = sddmm_case(S, orc, w.m, w.k, a["row_ptr"], a["col_idx"], X, Y, 16, 64)
+    _, x2, _ = sddmm_case(S, orc, w.m, w.k, a["row_ptr"], a["col_idx"], X, Y, 16, 64)
+    np.testing.assert_array_equal(x1.view(np.uint32), x2.view(np.uint32))
+    # an SDDMM plan is refused by spmm_execute, and an SpMM plan by the SDDMM call
+    Bt, Ct = to_dev(np.zeros((w.k, 16), np.float32)), empty_out(w.m, 16, "f32")
+    with pytest.raises(S.SpmmError) as ei:
+        S.spmm_execute(P, Bt, Ct)
+    assert ei.value.name == "SPMM_ERR_INVALID_ARG"
+    M = S.spmm_pack_wcsr(w.m, w.k, a["row_ptr"], a["col_idx"], a["vals"])
+    P2 = S.spmm_plan(M, 16, S.F32, S.F32)
+    out = torch.zeros(len(a["col_idx"]), dtype=torch.float32, device="cuda")
+    with pytest.raises(S.SpmmError) as ei:
+        S.spmm_execute_sddmm(P2, to_dev(X), to_dev(Y), out)
+    assert ei.value.name == "SPMM_ERR_INVALID_ARG"
+    # BCSR and 2:4 matrices have no SDDMM
+    with pytest.raises(S.SpmmError) as ei:
+        S.spmm_plan_sddmm(S.spmm_pack_bcsr(np.zeros((64, 64), np.uint16)), 32)
+    assert ei.value.name == "SPMM_ERR_UNSUPPORTED"

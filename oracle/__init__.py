@@ -59,6 +59,8 @@ def lib():
             "orc_bcsr_spmm_rows": (None, [i32, i32, P, P, P, P, i64, i64, P, i64, i64, P]),
             "orc_sp24_spmm_rows": (i64, [i64, P, P, P, i64, i64, P, i64, i64, P]),
             "orc_sddmm_rows": (None, [P, P, P, i64, P, i64, i64, i64, P, P]),
+            "orc_sddmm_bcsr_bf16": (None, [i32, i32, P, P, i64, P, i64, P, i64, i64, i64, P, P]),
+            "orc_sddmm_bcsr_i8": (i64, [i32, i32, P, P, i64, P, i64, P, i64, i64, i64, P, P]),
             "orc_gemm_f64": (None, [i64, i64, i64, P, P, P]),
             "orc_gemm_i8": (None, [i64, i64, i64, P, P, P]),
             "orc_num_threads": (C.c_int, []),
@@ -213,6 +215,33 @@ def sddmm(row_ptr, col_idx, X, Y, rows=None):
     out = np.empty(count, dtype=np.float64)
     lib().orc_sddmm_rows(_p(rp), _p(ci), _p(X), X.shape[1], _p(Y), Y.shape[1], X.shape[1],
                          len(rows), _p(rows), _p(out))
+    return out
+
+
+def sddmm_bcsr(bm, bk, row_ptr, col_idx, X, Y, blocks=None):
+    """Reference block values of the BCSR pattern (row_ptr, col_idx) sampled
+    from X [m, kd] times Y^T (Y [k, kd]): float64 [nsel, bm, bk] for bf16 bits
+    (uint16) operands, int32 for int8 operands (raises on int32 overflow).
+    `blocks` selects stored blocks (all by default)."""
+    rp, ci = _c(row_ptr, np.int32), _c(col_idx, np.int32)
+    nbrows = len(rp) - 1
+    if blocks is None:
+        blocks = np.arange(int(rp[-1]), dtype=np.int64)
+    blocks = _c(blocks, np.int64)
+    X = np.ascontiguousarray(X)
+    Y = np.ascontiguousarray(Y)
+    kd = X.shape[1]
+    if X.dtype == np.int8:
+        out = np.empty((len(blocks), bm, bk), dtype=np.int32)
+        ov = lib().orc_sddmm_bcsr_i8(bm, bk, _p(rp), _p(ci), nbrows, _p(X), X.shape[1], _p(Y),
+                                     Y.shape[1], kd, len(blocks), _p(blocks), _p(out))
+        if ov:
+            raise OverflowError(f"{ov} int32 sums overflowed")
+        return out
+    X, Y = _c(X, np.uint16), _c(Y, np.uint16)
+    out = np.empty((len(blocks), bm, bk), dtype=np.float64)
+    lib().orc_sddmm_bcsr_bf16(bm, bk, _p(rp), _p(ci), nbrows, _p(X), X.shape[1], _p(Y),
+                              Y.shape[1], kd, len(blocks), _p(blocks), _p(out))
     return out
 
 

@@ -303,6 +303,62 @@ void orc_sddmm_rows(const int64_t *row_ptr, const int32_t *col_idx,
   free(off);
 }
 
+/* Block-pattern SDDMM: the sample mask is a BCSR pattern, every element of */
+/* every stored block is sampled, and the result has the layout of the       */
+/* block values (block by block, row-major inside a block).                  */
+static int64_t *block_rows(const int32_t *row_ptr, int64_t nbrows) {
+  const int64_t nnzb = row_ptr[nbrows];
+  int64_t *br = (int64_t *)malloc(sizeof(int64_t) * (size_t)(nnzb > 0 ? nnzb : 1));
+  for (int64_t r = 0; r < nbrows; ++r)
+    for (int64_t b = row_ptr[r]; b < row_ptr[r + 1]; ++b) br[b] = r;
+  return br;
+}
+
+void orc_sddmm_bcsr_bf16(int32_t bm, int32_t bk, const int32_t *row_ptr, const int32_t *col_idx,
+                         int64_t nbrows, const uint16_t *X, int64_t ldx, const uint16_t *Y,
+                         int64_t ldy, int64_t kd, int64_t nsel, const int64_t *blocks,
+                         double *out) {
+  int64_t *br = block_rows(row_ptr, nbrows);
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t q = 0; q < nsel; ++q) {
+    const int64_t b = blocks[q];
+    for (int64_t i = 0; i < bm; ++i) {
+      const uint16_t *x = X + (br[b] * bm + i) * ldx;
+      for (int64_t j = 0; j < bk; ++j) {
+        const uint16_t *y = Y + ((int64_t)col_idx[b] * bk + j) * ldy;
+        double s = 0.0;
+        for (int64_t t = 0; t < kd; ++t) s += orc_bf16_to_double(x[t]) * orc_bf16_to_double(y[t]);
+        out[(q * bm + i) * bk + j] = s;
+      }
+    }
+  }
+  free(br);
+}
+
+int64_t orc_sddmm_bcsr_i8(int32_t bm, int32_t bk, const int32_t *row_ptr, const int32_t *col_idx,
+                          int64_t nbrows, const int8_t *X, int64_t ldx, const int8_t *Y,
+                          int64_t ldy, int64_t kd, int64_t nsel, const int64_t *blocks,
+                          int32_t *out) {
+  int64_t *br = block_rows(row_ptr, nbrows);
+  int64_t overflow = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(+ : overflow)
+  for (int64_t q = 0; q < nsel; ++q) {
+    const int64_t b = blocks[q];
+    for (int64_t i = 0; i < bm; ++i) {
+      const int8_t *x = X + (br[b] * bm + i) * ldx;
+      for (int64_t j = 0; j < bk; ++j) {
+        const int8_t *y = Y + ((int64_t)col_idx[b] * bk + j) * ldy;
+        int64_t s = 0;
+        for (int64_t t = 0; t < kd; ++t) s += (int64_t)((int32_t)x[t] * (int32_t)y[t]);
+        if (s >= 2147483648LL || s < -2147483648LL) ++overflow;
+        out[(q * bm + i) * bk + j] = (int32_t)s;
+      }
+    }
+  }
+  free(br);
+  return overflow;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Brute force: dense naive triple loops, i then j then k.                   */
 /* ------------------------------------------------------------------------ */

@@ -110,6 +110,21 @@ void orc_sddmm_rows(const int64_t *row_ptr, const int32_t *col_idx,
                     const float *X, int64_t ldx, const float *Y, int64_t ldy, int64_t kd,
                     int64_t nrows, const int64_t *rows, double *out);
 
+/* The same product with a BCSR block pattern (row_ptr over nbrows block rows,
+ * col_idx block columns) as the mask: for each block b in blocks[0 .. nsel),
+ * out[q][i][j] = sum over t ascending of X[I*bm + i][t] * Y[J*bk + j][t],
+ * with (I, J) the block's block row and column.  bf16 operands are widened
+ * exactly and summed in fp64; int8 products are formed in int32 and summed in
+ * int64 (the return value counts sums with |sum| >= 2^31; 0 when exact). */
+void orc_sddmm_bcsr_bf16(int32_t bm, int32_t bk, const int32_t *row_ptr, const int32_t *col_idx,
+                         int64_t nbrows, const uint16_t *X, int64_t ldx, const uint16_t *Y,
+                         int64_t ldy, int64_t kd, int64_t nsel, const int64_t *blocks,
+                         double *out);
+int64_t orc_sddmm_bcsr_i8(int32_t bm, int32_t bk, const int32_t *row_ptr, const int32_t *col_idx,
+                          int64_t nbrows, const int8_t *X, int64_t ldx, const int8_t *Y,
+                          int64_t ldy, int64_t kd, int64_t nsel, const int64_t *blocks,
+                          int32_t *out);
+
 /* ---- brute force (dense, naive triple loops) ---------------------------- */
 void orc_gemm_f64(int64_t m, int64_t k, int64_t n, const double *A, const double *B,
                   double *C);

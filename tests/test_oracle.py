@@ -344,3 +344,72 @@ def test_sddmm_closed_forms(orc):
     np.testing.assert_array_equal(orc.sddmm(rp, cols, Xh, Y), Y[cols, hot].astype(np.float64))
     # an empty pattern gives nothing; empty rows are skipped
     assert len(orc.sddmm(np.zeros(m + 1, np.int64), np.zeros(0, np.int32), X, X)) == 0
+
+
+def _block_pattern(r, mb, kb, bm, bk, density):
+    """A BCSR pattern from the oracle's own pack of a bf16 matrix whose
+    blocks are nonzero with the given probability."""
+    keep = r.random((mb, kb)) < density
+    a = np.zeros((mb * bm, kb * bk), np.uint16)
+    for I, J in zip(*np.nonzero(keep)):
+        a[I * bm + r.integers(bm), J * bk + r.integers(bk)] = 0x3F80   # 1.0
+    return a
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_sddmm_bcsr_bruteforce(orc, seed):
+    # oracle vs numpy's dense X @ Y^T cut into the stored blocks
+    r = np.random.default_rng(800 + seed)
+    bm, bk = (int(x) for x in r.choice([1, 2, 4, 8], size=2))
+    mb, kb, kd = int(r.integers(1, 7)), int(r.integers(1, 7)), int(r.integers(1, 70))
+    rp, ci, _ = orc.pack_bcsr(_block_pattern(r, mb, kb, bm, bk, 0.5), bm, bk)
+    brow = np.repeat(np.arange(mb), np.diff(rp))
+    # bf16 operands: exact widening, fp64 sums
+    Xb = synth.f32_to_bf16_bits(r.standard_normal((mb * bm, kd)).astype(np.float32))
+    Yb = synth.f32_to_bf16_bits(r.standard_normal((kb * bk, kd)).astype(np.float32))
+    full = synth.bf16_bits_to_f32(Xb).astype(np.float64) @ synth.bf16_bits_to_f32(Yb).astype(np.float64).T
+    ref = np.stack([full[I * bm:(I + 1) * bm, J * bk:(J + 1) * bk] for I, J in zip(brow, ci)]) \
+        if len(ci) else np.zeros((0, bm, bk))
+    got = orc.sddmm_bcsr(bm, bk, rp, ci, Xb, Yb)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+    # int8 operands: exact
+    Xi = r.integers(-128, 128, size=(mb * bm, kd)).astype(np.int8)
+    Yi = r.integers(-128, 128, size=(kb * bk, kd)).astype(np.int8)
+    fi = Xi.astype(np.int64) @ Yi.astype(np.int64).T
+    refi = np.stack([fi[I * bm:(I + 1) * bm, J * bk:(J + 1) * bk] for I, J in zip(brow, ci)]) \
+        if len(ci) else np.zeros((0, bm, bk))
+    np.testing.assert_array_equal(orc.sddmm_bcsr(bm, bk, rp, ci, Xi, Yi), refi)
+    # a block subset gives those blocks, in the order asked
+    if len(ci):
+        sub = r.permutation(len(ci))[: max(1, len(ci) // 2)].astype(np.int64)
+        np.testing.assert_array_equal(orc.sddmm_bcsr(bm, bk, rp, ci, Xb, Yb, blocks=sub), got[sub])
+
+
+def test_sddmm_bcsr_closed_forms(orc):
+    r = np.random.default_rng(12)
+    bm = bk = 64
+    rp, ci, _ = orc.pack_bcsr(_block_pattern(r, 3, 4, bm, bk, 0.6), bm, bk)
+    brow = np.repeat(np.arange(3), np.diff(rp))
+    kd = 96
+    # one-hot rows of X pick single elements of Y: exact
+    hot = r.integers(0, kd, size=3 * bm)
+    Xh = np.zeros((3 * bm, kd), np.uint16)
+    Xh[np.arange(3 * bm), hot] = 0x3F80
+    Yb = synth.dense_bf16_normal(4 * bk, kd, 90)
+    Yf = synth.bf16_bits_to_f32(Yb).astype(np.float64)
+    got = orc.sddmm_bcsr(bm, bk, rp, ci, Xh, Yb)
+    for q, (I, J) in enumerate(zip(brow, ci)):
+        rows = np.arange(I * bm, (I + 1) * bm)
+        np.testing.assert_array_equal(got[q], Yf[J * bk:(J + 1) * bk][:, hot[rows]].T)
+    # int8 extremes: all -128 gives kd * 16384 everywhere, exact
+    Xi = np.full((3 * bm, kd), -128, np.int8)
+    Yi = np.full((4 * bk, kd), -128, np.int8)
+    assert (orc.sddmm_bcsr(bm, bk, rp, ci, Xi, Yi) == kd * 16384).all()
+    # ... and an inner dimension past 2^31 / 16384 overflows int32: reported
+    big = 131073
+    rp1, ci1 = np.array([0, 1], np.int32), np.array([0], np.int32)
+    with pytest.raises(OverflowError):
+        orc.sddmm_bcsr(1, 1, rp1, ci1, np.full((1, big), -128, np.int8), np.full((1, big), -128, np.int8))
+    # an empty pattern gives no blocks
+    z = orc.sddmm_bcsr(bm, bk, np.zeros(4, np.int32), np.zeros(0, np.int32), Xh, Yb)
+    assert z.shape == (0, bm, bk)

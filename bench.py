@@ -44,7 +44,7 @@ PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "i8": 5000.0}
 
 # kernel whose launch dominates a step, per format
 DOMINANT_KERNEL = {"bcsr": "bcsr_bf16_mfma", "wcsr": "wcsr_stream", "sp24": "sp24_i8_smfmac",
-                   "sddmm": "sddmm_f32"}
+                   "sddmm": "sddmm_f32", "sddmm_bcsr": "sddmm_bcsr_mfma"}
 TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 CSRC = os.path.join(ROOT, "sparse_dense_matrix_amd", "csrc")
 
@@ -81,10 +81,10 @@ def setup(w, S, args):
     import synth
     t0 = time.perf_counter()
     a = synth.make_a(w)
-    B = synth.make_xy(w) if w.fmt == "sddmm" else synth.make_b(w)
+    B = synth.make_xy(w) if w.fmt in ("sddmm", "sddmm_bcsr") else synth.make_b(w)
     t_gen = time.perf_counter() - t0
     t0 = time.perf_counter()
-    if w.fmt == "bcsr":
+    if w.fmt in ("bcsr", "sddmm_bcsr"):
         M = S.spmm_pack_bcsr(a["dense"], w.block, w.block)
         types = (S.BF16, S.BF16)
     elif w.fmt in ("wcsr", "sddmm"):
@@ -99,6 +99,8 @@ def setup(w, S, args):
     t0 = time.perf_counter()
     if w.fmt == "sddmm":
         P = S.spmm_plan_sddmm(M, w.n)
+    elif w.fmt == "sddmm_bcsr":
+        P = S.spmm_plan_sddmm(M, w.n, S.BF16 if w.elem == "bf16" else S.I8)
     else:
         P = S.spmm_plan(M, w.n, *types)
     t_plan = time.perf_counter() - t0
@@ -114,6 +116,20 @@ def algorithmic(w, d):
     info = d["info"]
     n = w.n
     flops = 2.0 * info["nnz"] * n
+    if w.fmt == "sddmm_bcsr":
+        # every element of every stored block: 2 * nnzb * 4096 * kd; X rows of
+        # block rows with blocks and Y rows of block columns with blocks once,
+        # the block table and the output blocks once
+        import sparse_dense_matrix_amd as S
+        nnzb = info["nnzb"]
+        rp = np.asarray(S.spmm_matrix_array(d["M"], S.ARRAY_ROW_PTR))
+        ci = np.asarray(S.spmm_matrix_array(d["M"], S.ARRAY_COL_IDX))
+        e = 2 if w.elem == "bf16" else 1
+        x_rows = int(np.count_nonzero(np.diff(rp))) * w.block
+        y_rows = len(np.unique(ci)) * w.block
+        out_b = nnzb * w.block * w.block * (2 if w.elem == "bf16" else 4)
+        flops = 2.0 * nnzb * w.block * w.block * n
+        return flops, (x_rows + y_rows) * n * e + out_b + 4 * (len(rp) + nnzb), w.elem
     if w.fmt == "bcsr":
         nnzb = info["nnzb"]
         mb = w.m // w.block
@@ -172,10 +188,17 @@ def main():
     log(f"generated in {d['t_gen']:.1f}s, packed in {d['t_pack']:.2f}s, planned in {d['t_plan']:.2f}s")
 
     # device operands
-    if w.fmt == "sddmm":
-        Xt = torch.from_numpy(d["B"][0]).cuda()
-        Yt = torch.from_numpy(d["B"][1]).cuda()
-        Ot = torch.empty(max(d["info"]["nnz"], 1), dtype=torch.float32, device="cuda")
+    if w.fmt in ("sddmm", "sddmm_bcsr"):
+        Xh, Yh = d["B"]
+        if Xh.dtype == np.uint16:
+            Xh, Yh = Xh.view(np.int16), Yh.view(np.int16)
+        Xt = torch.from_numpy(Xh).cuda()
+        Yt = torch.from_numpy(Yh).cuda()
+        if w.fmt == "sddmm":
+            Ot = torch.empty(max(d["info"]["nnz"], 1), dtype=torch.float32, device="cuda")
+        else:
+            odt = torch.int16 if w.elem == "bf16" else torch.int32
+            Ot = torch.empty((max(d["info"]["nnzb"], 1), w.block, w.block), dtype=odt, device="cuda")
 
         def step(stream):
             S.spmm_execute_sddmm(d["P"], Xt, Yt, Ot, stream=stream)
@@ -310,6 +333,18 @@ def copy_calibration(torch, args):
                                            "launches": args.warmup + args.steps}}), flush=True)
 
 
+def short_kernel_name(name: str) -> str:
+    """Bare function name of a demangled kernel signature: no return type,
+    namespaces, template arguments or parameters."""
+    name = name.replace("(anonymous namespace)::", "")
+    depth, cut = 0, len(name)
+    for i, ch in enumerate(name):          # end of the name: first '<' or '(' at depth 0
+        if ch in "<(" and depth == 0:
+            cut = i
+            break
+    return name[:cut].split("::")[-1].split(" ")[-1]
+
+
 def trace_summary(root):
     """Per-kernel call count and duration statistics (microseconds) from the
     rocprofv3 kernel-trace databases under root."""
@@ -322,8 +357,7 @@ def trace_summary(root):
                 continue
             con = sqlite3.connect(os.path.join(dirpath, fn))
             for name, dur in con.execute("select name, duration from kernels"):
-                name = name.replace("(anonymous namespace)::", "")
-                durs[name.split("(")[0].split("::")[-1].split("<")[0]].append(dur / 1000.0)
+                durs[short_kernel_name(name)].append(dur / 1000.0)
             con.close()
     print("| kernel | calls | avg us | median us | min us | max us | total ms |")
     print("|---|---|---|---|---|---|---|")
@@ -344,8 +378,7 @@ def pmc_summary(root):
                 continue
             with open(os.path.join(dirpath, fn)) as f:
                 for r in csv.DictReader(f):
-                    name = r["Kernel_Name"].replace("(anonymous namespace)::", "")
-                    name = name.split("(")[0].split("::")[-1].split("<")[0]
+                    name = short_kernel_name(r["Kernel_Name"])
                     agg[(name, r["Counter_Name"])].append(float(r["Counter_Value"]))
     print(f"library digest {library_digest()}")
     for (k, c), v in sorted(agg.items()):
@@ -374,6 +407,27 @@ def cpu_baseline(w, d, target_s):
 
         def run(rows):
             oracle.sddmm(a["row_ptr"], a["col_idx"], B[0], B[1], rows=rows)
+    elif w.fmt == "sddmm_bcsr":
+        # the sample unit is a stored block (2 * 4096 * kd flop each)
+        rp, ci, _ = oracle.pack_bcsr(a["dense"], w.block, w.block)
+        units = len(ci)
+        perm = r.permutation(units).astype(np.int64)
+        count, spent = 1, 0.0
+        while True:
+            blocks = np.sort(perm[:count])
+            t0 = time.perf_counter()
+            oracle.sddmm_bcsr(w.block, w.block, rp, ci, B[0], B[1], blocks=blocks)
+            spent = time.perf_counter() - t0
+            if spent >= target_s or count >= units:
+                break
+            count = min(units, int(count * max(2.0, min(8.0, 0.9 * target_s / max(spent, 1e-3)))))
+        flops = 2.0 * count * w.block * w.block * w.n
+        log(f"cpu oracle: {count} blocks in {spent:.2f}s on {oracle.num_threads()} threads")
+        return {"value": round(flops / spent / 1e9, 3), "unit": "GFLOP/s",
+                "cores": oracle.num_threads(), "kind": "oracle",
+                "sample": f"{count} of {units} stored blocks (uniform without replacement, "
+                          f"seed 0), full inner dimension {w.n}; "
+                          + ("fp64" if w.elem == "bf16" else "int64") + " accumulation"}
     else:
         vals, meta = oracle.pack24(a["dense"])
         row_nnz = np.full(w.m, w.k // 2, dtype=np.int64)

@@ -184,22 +184,32 @@ spmm_status_t spmm_execute(spmm_plan_t p, const void *b_dev, int64_t ldb, void *
 /* ---- sampled dense-dense product (SDDMM) ---- */
 
 /* Plan out[p] = sum over t < kd of X[i][t] * Y[j][t] for every stored entry
- * p = (i, j) of the WCSR matrix a: its stored pattern is the sample mask and
- * its values play no part.  SDDMM is the companion of SpMM on the Magicube
- * page ("Efficient Quantized Sparse Matrix Operations on Tensor Cores",
- * abstract).  a must be WCSR and dtype SPMM_F32 (X, Y and out are fp32),
- * else UNSUPPORTED; work is split by a's chunks.  Synchronous; the plan
- * holds a reference on a.  kd = 0 is allowed (out becomes zeros). */
+ * p = (i, j) of the matrix a: its stored pattern is the sample mask and its
+ * values play no part.  SDDMM is the companion of SpMM on the Magicube page
+ * ("Efficient Quantized Sparse Matrix Operations on Tensor Cores",
+ * abstract), which runs both on low-precision integers.  Two patterns:
+ *   - WCSR with dtype SPMM_F32: X, Y and out fp32; out holds one value per
+ *     stored entry in stored order (float[nnz]); work is split by a's chunks;
+ *   - BCSR of 64 x 64 blocks with dtype SPMM_BF16 (X, Y bf16; fp32 sums;
+ *     out bf16, rounded to nearest even) or SPMM_I8 (X, Y int8; out int32,
+ *     exact while |sum| < 2^31): every element of every stored block is
+ *     sampled and out has the layout of the block values, [nnzb][64][64]
+ *     row-major inside a block, in stored block order.  The plan may hold a
+ *     workspace of fp32 / int32 partial blocks (workspace_bytes).
+ * Anything else is UNSUPPORTED.  Synchronous; the plan holds a reference on
+ * a.  kd = 0 is allowed (out becomes zeros). */
 spmm_status_t spmm_plan_sddmm(spmm_matrix_t a, int64_t kd, spmm_dtype_t dtype, int32_t device,
                               spmm_plan_t *out);
 
-/* out_dev[p] for every stored entry p of the plan's pattern, in its stored
- * order (float[nnz]), on `stream`.  x_dev [m x kd] and y_dev [k x kd] are
- * row-major device arrays on the plan's device, 16-byte aligned, with
- * ldx, ldy >= kd and ldx * 4, ldy * 4 multiples of 16 bytes (with kd = 0
- * X, Y and their ld are not read); out_dev is 4-byte aligned.  Allocates
- * nothing and does not synchronise.  Plans of
- * spmm_plan are refused here and SDDMM plans by spmm_execute (INVALID_ARG). */
+/* out_dev for every stored entry of the plan's pattern, on `stream`.
+ * x_dev [m x kd] and y_dev [k x kd] are row-major device arrays of the plan's
+ * element type on the plan's device, 16-byte aligned, with ldx, ldy >= kd
+ * (elements) and ldx * elem, ldy * elem multiples of 16 bytes (with kd = 0
+ * X, Y and their ld are not read); for a BCSR pattern 64 * ldx * elem and
+ * 64 * ldy * elem must stay below 4 GiB (else UNSUPPORTED).  out_dev is 4-byte aligned (WCSR) or
+ * 16-byte aligned (BCSR).  Allocates nothing and does not synchronise; one
+ * execute in flight per plan (the workspace).  Plans of spmm_plan are
+ * refused here and SDDMM plans by spmm_execute (INVALID_ARG). */
 spmm_status_t spmm_execute_sddmm(spmm_plan_t p, const void *x_dev, int64_t ldx, const void *y_dev,
                                  int64_t ldy, void *out_dev, hipStream_t stream);
 

@@ -274,6 +274,62 @@ spmm_status_t plan_sddmm(spmm_plan_s *p, int64_t kd) {
   return SPMM_OK;
 }
 
+// ---- SDDMM plan on a BCSR pattern: block groups and inner-dimension ranges ---
+#ifndef SDM_SDDMM_UNITS
+#define SDM_SDDMM_UNITS 2048
+#endif
+spmm_status_t plan_sddmm_bcsr(spmm_plan_s *p, int64_t kd, bool int8) {
+  const Matrix &a = *p->a;
+  const int64_t nnzb = static_cast<int64_t>(a.bcol_idx.size());
+  const int G = sddmm_bcsr_group();
+  // groups of up to G consecutive stored blocks of one block row
+  std::vector<int32_t> groups;
+  for (int64_t r = 0; r + 1 < static_cast<int64_t>(a.brow_ptr.size()); ++r)
+    for (int32_t b = a.brow_ptr[r]; b < a.brow_ptr[r + 1]; b += G)
+      groups.insert(groups.end(),
+                    {static_cast<int32_t>(r), b, std::min<int32_t>(G, a.brow_ptr[r + 1] - b), 0});
+  const int64_t ngroups = static_cast<int64_t>(groups.size() / 4);
+  // ranges of the inner dimension: enough workgroups for the chip (about
+  // SDM_SDDMM_UNITS), each range at least 16 chunks long
+  const int64_t chunk = sddmm_bcsr_chunk(int8);
+  const int64_t chunks = (kd + chunk - 1) / chunk;
+  int64_t nsplit = 1;
+  if (ngroups > 0 && chunks > 0) {
+    nsplit = std::min<int64_t>((SDM_SDDMM_UNITS + ngroups - 1) / ngroups,
+                               std::max<int64_t>(1, chunks / 16));
+    nsplit = std::max<int64_t>(1, nsplit);
+  }
+  const int64_t ksplit = std::max<int64_t>(1, (chunks + nsplit - 1) / nsplit) * chunk;
+  if (kd > 0) nsplit = (kd + ksplit - 1) / ksplit;
+  if (ngroups * 8 * nsplit > INT32_MAX) return fail(SPMM_ERR_UNSUPPORTED, "spmm_plan_sddmm: too many blocks");
+
+  SddmmBcsrLaunch &L = p->sddb;
+  spmm_status_t st;
+  int32_t *dg = nullptr, *dci = nullptr;
+  if ((st = upload_vec(p, groups, &dg)) != SPMM_OK) return st;
+  if ((st = upload_vec(p, a.bcol_idx, &dci)) != SPMM_OK) return st;
+  const int64_t ws_bytes = nsplit > 1 ? nsplit * nnzb * 64 * 64 * 4 : 0;
+  void *ws = nullptr;
+  if (ws_bytes > 0) {
+    if ((st = upload(p, nullptr, static_cast<size_t>(ws_bytes), &ws)) != SPMM_OK) return st;
+    p->info.device_bytes -= ws_bytes;
+  }
+  L.groups = reinterpret_cast<const int4 *>(dg);
+  L.ngroups = static_cast<int32_t>(ngroups);
+  L.col_idx = dci;
+  L.nnzb = nnzb;
+  L.kd = kd;
+  L.ksplit = ksplit;
+  L.nsplit = static_cast<int32_t>(nsplit);
+  L.int8 = int8;
+  L.partial = ws;
+  p->info.workspace_bytes = ws_bytes;
+  p->info.tile_m = 64;
+  p->info.tile_n = 64;
+  p->info.grid = 8 * ((ngroups + 7) / 8) * nsplit;
+  return SPMM_OK;
+}
+
 // ---- 2:4 plan: rows and k padded to whole tiles with zeros -----------------
 spmm_status_t plan_24(spmm_plan_s *p) {
   const Matrix &a = *p->a;
@@ -556,8 +612,14 @@ spmm_status_t spmm_plan_sddmm(spmm_matrix_t a, int64_t kd, spmm_dtype_t dtype, i
   if (!out) return fail(SPMM_ERR_INVALID_ARG, "spmm_plan_sddmm: out is NULL");
   *out = nullptr;
   if (!a || kd < 0 || kd > INT32_MAX) return fail(SPMM_ERR_INVALID_ARG, "spmm_plan_sddmm: bad matrix or kd");
-  if (a->format != SPMM_FORMAT_WCSR || dtype != SPMM_F32)
-    return fail(SPMM_ERR_UNSUPPORTED, "spmm_plan_sddmm: needs a WCSR pattern and fp32 X, Y");
+  const bool wcsr = a->format == SPMM_FORMAT_WCSR && dtype == SPMM_F32;
+  const bool bcsr = a->format == SPMM_FORMAT_BCSR && (dtype == SPMM_BF16 || dtype == SPMM_I8);
+  if (!wcsr && !bcsr)
+    return fail(SPMM_ERR_UNSUPPORTED,
+                "spmm_plan_sddmm: needs a WCSR pattern with fp32 X, Y or a BCSR pattern with "
+                "bf16 or int8 X, Y");
+  if (bcsr && (a->bm != 64 || a->bk != 64))
+    return fail(SPMM_ERR_UNSUPPORTED, "spmm_plan_sddmm: BCSR patterns take 64 x 64 blocks");
   int ndev = 0;
   hipError_t e = hipGetDeviceCount(&ndev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDeviceCount");
@@ -569,6 +631,7 @@ spmm_status_t spmm_plan_sddmm(spmm_matrix_t a, int64_t kd, spmm_dtype_t dtype, i
     retain(a);
     p->a = a;
     p->sddmm = true;
+    p->sddmm_dtype = dtype;
     p->device = device;
     p->n = kd;
     p->info.format = a->format;
@@ -578,7 +641,7 @@ spmm_status_t spmm_plan_sddmm(spmm_matrix_t a, int64_t kd, spmm_dtype_t dtype, i
     p->info.n = kd;
     spmm_status_t s = SPMM_ERR_INTERNAL;
     try {
-      s = plan_sddmm(p, kd);
+      s = wcsr ? plan_sddmm(p, kd) : plan_sddmm_bcsr(p, kd, dtype == SPMM_I8);
     } catch (...) {
       free_plan(p);
       throw;
@@ -602,23 +665,41 @@ spmm_status_t spmm_execute_sddmm(spmm_plan_t p, const void *x_dev, int64_t ldx, 
   if (!p->sddmm) return fail(SPMM_ERR_INVALID_ARG, "spmm_execute_sddmm: plan is not an SDDMM plan");
   const Matrix &a = *p->a;
   const int64_t kd = p->n;
-  if (a.nnz == 0) return SPMM_OK;
+  const bool bcsr = a.format == SPMM_FORMAT_BCSR;
+  const int64_t elem = p->sddmm_dtype == SPMM_F32 ? 4 : (p->sddmm_dtype == SPMM_BF16 ? 2 : 1);
+  if (bcsr ? a.bcol_idx.empty() : a.nnz == 0) return SPMM_OK;
   if (!out_dev || (kd > 0 && (!x_dev || !y_dev)))
     return fail(SPMM_ERR_INVALID_ARG, "spmm_execute_sddmm: X, Y or out is NULL");
-  if ((reinterpret_cast<uintptr_t>(out_dev) & 3u) ||
+  const uintptr_t out_align = bcsr ? 15u : 3u;
+  if ((reinterpret_cast<uintptr_t>(out_dev) & out_align) ||
       (kd > 0 && (!aligned16(x_dev) || !aligned16(y_dev) || ldx < kd || ldy < kd ||
-                  (ldx * 4) % 16 != 0 || (ldy * 4) % 16 != 0)))
+                  (ldx * elem) % 16 != 0 || (ldy * elem) % 16 != 0)))
     return fail(SPMM_ERR_INVALID_ARG,
-                "spmm_execute_sddmm: X/Y must be 16-byte aligned with ld >= kd and ld*4 % 16 == 0");
+                "spmm_execute_sddmm: X/Y must be 16-byte aligned with ld >= kd and ld*elem % 16 "
+                "== 0; out aligned to 16 bytes (BCSR) or 4 bytes (WCSR)");
+  // a BCSR workgroup addresses its 64 rows of X and of Y with 32-bit byte offsets
+  if (bcsr && kd > 0 && 64 * std::max(ldx, ldy) * elem >= (int64_t(1) << 32))
+    return fail(SPMM_ERR_UNSUPPORTED, "spmm_execute_sddmm: rows of X or Y longer than 64 MiB");
   DeviceScope ds(p->device);
   if (ds.err != hipSuccess) return hip_fail(ds.err, "hipSetDevice");
-  SddmmLaunch L = p->sdd;
-  L.X = static_cast<const float *>(x_dev);
-  L.ldx = ldx;
-  L.Y = static_cast<const float *>(y_dev);
-  L.ldy = ldy;
-  L.out = static_cast<float *>(out_dev);
-  hipError_t e = launch_sddmm_f32(L, stream);
+  hipError_t e;
+  if (bcsr) {
+    SddmmBcsrLaunch L = p->sddb;
+    L.X = x_dev;
+    L.ldx = ldx;
+    L.Y = y_dev;
+    L.ldy = ldy;
+    L.out = out_dev;
+    e = launch_sddmm_bcsr(L, stream);
+  } else {
+    SddmmLaunch L = p->sdd;
+    L.X = static_cast<const float *>(x_dev);
+    L.ldx = ldx;
+    L.Y = static_cast<const float *>(y_dev);
+    L.ldy = ldy;
+    L.out = static_cast<float *>(out_dev);
+    e = launch_sddmm_f32(L, stream);
+  }
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return SPMM_OK;
 }

@@ -86,8 +86,10 @@ __device__ __forceinline__ void load_lds16(uint32_t lds, const void *base, uint3
 }
 
 // Workgroup barrier without the memory fence __syncthreads() adds (the fence
-// would wait for every in-flight load); LDS ordering is handled by the
-// explicit vmcnt / lgkmcnt waits around it.
+// would wait for every in-flight load); global loads are ordered by the
+// explicit vmcnt waits before it.  Every LDS read of a block feeds that
+// block's MFMAs, so its wait comes before the loop's back edge and no read of
+// a stage is in flight when the next block refills it.
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {

@@ -137,6 +137,29 @@ struct SddmmLaunch {
 hipError_t launch_sddmm_f32(const SddmmLaunch &a, hipStream_t s);
 int64_t sddmm_grid(int64_t num_chunks);
 
+// SDDMM with a BCSR pattern of 64 x 64 blocks: a workgroup serves a group of
+// up to sddmm_bcsr_group() stored blocks of one block row over one range of
+// the inner dimension (ksplit elements, a multiple of sddmm_bcsr_chunk()).
+struct SddmmBcsrLaunch {
+  const int4 *groups;       // [ngroups] (block row, first block, block count, 0)
+  int32_t ngroups;
+  const int32_t *col_idx;   // [nnzb]
+  int64_t nnzb;
+  int64_t kd;               // inner dimension
+  int64_t ksplit;           // elements per range
+  int32_t nsplit;           // ranges; > 1 goes through `partial`
+  bool int8;                // int8 X, Y -> int32 out; else bf16 -> bf16
+  const void *X;            // [m][ldx]
+  int64_t ldx;              // elements
+  const void *Y;            // [k][ldy]
+  int64_t ldy;
+  void *out;                // [nnzb][64][64]
+  void *partial;            // [nsplit][nnzb][64][64] fp32 / int32 when nsplit > 1
+};
+int sddmm_bcsr_chunk(bool int8);
+int sddmm_bcsr_group();
+hipError_t launch_sddmm_bcsr(const SddmmBcsrLaunch &a, hipStream_t s);
+
 struct Sp24Launch {
   const int8_t *vals;   // tiled copy of the values (sp24_tile_layout)
   const uint8_t *meta;  // tiled copy of the index words
@@ -167,6 +190,7 @@ hipError_t launch_sp24_i8(const Sp24Launch &a, hipStream_t s);
 struct spmm_plan_s {
   sdm::Matrix *a = nullptr;
   bool sddmm = false;  // plan of spmm_plan_sddmm rather than spmm_plan
+  spmm_dtype_t sddmm_dtype = SPMM_F32;  // element type of X and Y
   int32_t device = 0;
   int64_t n = 0;
   spmm_plan_info_t info{};
@@ -175,6 +199,7 @@ struct spmm_plan_s {
   sdm::WcsrLaunch wcsr{};
   sdm::Sp24Launch sp24{};
   sdm::SddmmLaunch sdd{};
+  sdm::SddmmBcsrLaunch sddb{};
 };
 
 struct spmm_matrix_s : sdm::Matrix {};

@@ -73,6 +73,9 @@ __device__ __forceinline__ void load_lds16(uint32_t lds, const void *base, uint3
                : "memory", "m0");
 }
 
+// Workgroup barrier without a memory fence.  Every LDS read of a k-step
+// feeds that step's MFMAs, so its wait comes before the loop's back edge
+// and no read of a stage is in flight when the next step refills it.
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {

@@ -176,7 +176,7 @@ def dense_f32_normal(rows: int, cols: int, seed: int, stream: int = S_BVAL) -> n
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    fmt: str            # "wcsr" | "bcsr" | "sp24" | "sddmm" (n = inner dimension)
+    fmt: str            # "wcsr" | "bcsr" | "sp24" | "sddmm" | "sddmm_bcsr" (n = inner dimension)
     m: int
     k: int
     n: int
@@ -190,16 +190,17 @@ class Workload:
     block: int = 64               # bcsr
     nblocks: int = 0
     sigma: float = 0.02
+    elem: str = ""                # sddmm_bcsr: "bf16" | "i8" operands X, Y
 
     @property
     def describe(self) -> str:
         return f"{self.name} ({self.fmt}, m={self.m}, k={self.k}, n={self.n})"
 
 
-def _bcsr(name, m, k, n, zero_frac, seed, block=64):
+def _bcsr(name, m, k, n, zero_frac, seed, block=64, fmt="bcsr", elem=""):
     total = (m // block) * (k // block)
-    return Workload(name, "bcsr", m, k, n, seed, block=block,
-                    nblocks=int(round((1.0 - zero_frac) * total)))
+    return Workload(name, fmt, m, k, n, seed, block=block,
+                    nblocks=int(round((1.0 - zero_frac) * total)), elem=elem)
 
 
 # The five benchmark shapes (seed 20260000 + index) ...
@@ -213,6 +214,12 @@ WORKLOADS: Dict[str, Workload] = {
     # the sampled dense-dense product on the power-law pattern, inner dimension 128
     "sddmm_powerlaw_1m": Workload("sddmm_powerlaw_1m", "sddmm", 1_000_000, 1_000_000, 128, 20260003,
                                   powerlaw=True),
+    # the same product on the block pattern of the 18944 x 3584 layer: the
+    # layer's weight gradient over one GPU's share (8192) of 65536 tokens
+    "sddmm_bcsr_prefill_kd8192": _bcsr("sddmm_bcsr_prefill_kd8192", 18944, 3584, 8192, 0.90,
+                                       20260005, fmt="sddmm_bcsr", elem="bf16"),
+    "sddmm_i8_prefill_kd8192": _bcsr("sddmm_i8_prefill_kd8192", 18944, 3584, 8192, 0.90,
+                                     20260005, fmt="sddmm_bcsr", elem="i8"),
 }
 
 # ... and smaller cases of the same construction for element-wise parity
@@ -226,6 +233,8 @@ SMALL: Dict[str, Workload] = {
     "bcsr_prefill_slice": _bcsr("bcsr_prefill_slice", 18944, 3584, 4096 + 64 * 3, 0.90, 20260005),
     "sddmm_small": Workload("sddmm_small", "sddmm", 20000, 20000, 96, 32, powerlaw=True, cap=3000,
                             band_half=64),
+    "sddmm_bcsr_small": _bcsr("sddmm_bcsr_small", 640, 512, 1000, 0.7, 35, fmt="sddmm_bcsr",
+                              elem="bf16"),
 }
 
 
@@ -238,7 +247,7 @@ def make_a(w: Workload) -> dict:
         else:
             rp, ci, v = csr_uniform(w.m, w.k, w.density, w.seed)
         return {"row_ptr": rp, "col_idx": ci, "vals": v}
-    if w.fmt == "bcsr":
+    if w.fmt in ("bcsr", "sddmm_bcsr"):
         a, ids = block_sparse_dense_bf16(w.m, w.k, w.block, w.block, w.nblocks, w.sigma, w.seed)
         return {"dense": a, "block_ids": ids}
     if w.fmt == "sp24":
@@ -246,10 +255,18 @@ def make_a(w: Workload) -> dict:
     raise ValueError(w.fmt)
 
 
-def make_xy(w: Workload, kd: int | None = None):
+def make_xy(w: Workload, kd: int | None = None, elem: str | None = None):
     """Draw the dense operands of the sampled product: X [m x kd] and
-    Y [k x kd], row-major float32 N(0, 1)."""
+    Y [k x kd], row-major; float32 N(0, 1) for the CSR pattern, bf16 bits
+    N(0, 1) or int8 uniform on {-127 ... 127} for the block pattern."""
     kd = w.n if kd is None else kd
+    elem = w.elem if elem is None else elem
+    if w.fmt == "sddmm_bcsr" and elem == "bf16":
+        return (dense_bf16_normal(w.m, kd, w.seed, S_BVAL),
+                dense_bf16_normal(w.k, kd, w.seed, S_YVAL))
+    if w.fmt == "sddmm_bcsr" and elem == "i8":
+        return (int8_uniform(rng(w.seed, S_BVAL), (w.m, kd)),
+                int8_uniform(rng(w.seed, S_YVAL), (w.k, kd)))
     return dense_f32_normal(w.m, kd, w.seed, S_BVAL), dense_f32_normal(w.k, kd, w.seed, S_YVAL)
 
 

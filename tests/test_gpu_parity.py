@@ -446,3 +446,101 @@ def test_sddmm_deterministic_and_plan_kinds(S, orc):
     with pytest.raises(S.SpmmError) as ei:
         S.spmm_plan_sddmm(S.spmm_pack_bcsr(np.zeros((64, 64), np.uint16)), 32)
     assert ei.value.name == "SPMM_ERR_UNSUPPORTED"
+
+
+# ---------------------------------------------------------------------------
+# SDDMM on a BCSR block pattern: bf16 -> bf16 and int8 -> int32
+# ---------------------------------------------------------------------------
+
+I32_SENTINEL = 0x7ABCDEF1
+
+
+def sddmm_bcsr_case(S, orc, a_bits, X, Y, elem, blocks=None, extra=0):
+    """Run the block-pattern SDDMM and return (got [nnzb, 64, 64], ref for
+    `blocks` (all by default), plan).  X and Y go to the device as column
+    slices with whole 16-byte rows plus `extra` padding columns."""
+    torch = pytest.importorskip("torch")
+    M = S.spmm_pack_bcsr(a_bits)
+    kd = X.shape[1]
+    P = S.spmm_plan_sddmm(M, kd, S.BF16 if elem == "bf16" else S.I8)
+    rp, ci, _ = orc.pack_bcsr(a_bits, 64, 64)
+    nnzb = len(ci)
+    if elem == "bf16":
+        out = torch.full((max(nnzb, 1), 64, 64), -1, dtype=torch.int16, device="cuda")   # 0xFFFF
+        pad = (-kd) % 8 + extra
+    else:
+        out = torch.full((max(nnzb, 1), 64, 64), I32_SENTINEL, dtype=torch.int32, device="cuda")
+        pad = (-kd) % 16 + extra
+    S.spmm_execute_sddmm(P, to_dev(X, pad), to_dev(Y, pad), out)
+    got = out.cpu().numpy()[:nnzb]
+    if elem == "bf16":
+        got = got.view(np.uint16)
+        assert (got != 0xFFFF).all(), "some output element was not written"
+    ref = orc.sddmm_bcsr(64, 64, rp, ci, X, Y, blocks=blocks)
+    return got, ref, P
+
+
+def _check_sddmm_bcsr(orc, got, ref, elem, blocks=None):
+    g = got if blocks is None else got[blocks]
+    if elem == "bf16":
+        err = orc.rel_frobenius(bf16_to_f64(g), ref)
+        assert err <= TOL_BF16, err
+        return err
+    np.testing.assert_array_equal(g, ref)
+    return 0.0
+
+
+@pytest.mark.parametrize("elem,kd", [("bf16", 8), ("bf16", 64), ("bf16", 1000), ("bf16", 4104),
+                                     ("i8", 16), ("i8", 128), ("i8", 1000), ("i8", 8200)])
+def test_sddmm_bcsr_small(S, orc, elem, kd):
+    w = synth.SMALL["sddmm_bcsr_small"]       # 640 x 512, 24 of 80 blocks stored
+    a = synth.make_a(w)["dense"]
+    X, Y = synth.make_xy(w, kd, elem)
+    got, ref, P = sddmm_bcsr_case(S, orc, a, X, Y, elem)
+    err = _check_sddmm_bcsr(orc, got, ref, elem)
+    _say(f"sddmm_bcsr_small {elem} kd={kd} grid={P.info()['grid']} "
+         f"ws={P.info()['workspace_bytes']} rel_frob={err:.3e}")
+
+
+@pytest.mark.parametrize("elem", ["bf16", "i8"])
+def test_sddmm_bcsr_ld_kd0_and_repeat(S, orc, elem):
+    w = synth.SMALL["sddmm_bcsr_small"]
+    a = synth.make_a(w)["dense"]
+    X, Y = synth.make_xy(w, 200, elem)
+    g1, ref, _ = sddmm_bcsr_case(S, orc, a, X, Y, elem, extra=32)      # ld > kd
+    _check_sddmm_bcsr(orc, g1, ref, elem)
+    g2, _, _ = sddmm_bcsr_case(S, orc, a, X, Y, elem)
+    np.testing.assert_array_equal(g1, g2)                              # bitwise repeatable
+    gz, _, _ = sddmm_bcsr_case(S, orc, a, X[:, :0].copy(), Y[:, :0].copy(), elem)
+    assert (gz & (0x7FFF if elem == "bf16" else -1) == 0).all()        # kd = 0: zeros
+
+
+def test_sddmm_bcsr_dense_row_and_empty(S, orc):
+    # one block row stored in full (8 blocks: two groups of four), the rest
+    # empty; and an all-zero pattern, which has nothing to compute
+    torch = pytest.importorskip("torch")
+    a = np.zeros((256, 512), np.uint16)
+    a[64:128, :] = 0x3F80
+    X = synth.dense_bf16_normal(256, 320, 91)
+    Y = synth.dense_bf16_normal(512, 320, 92)
+    got, ref, _ = sddmm_bcsr_case(S, orc, a, X, Y, "bf16")
+    assert got.shape == (8, 64, 64)
+    _check_sddmm_bcsr(orc, got, ref, "bf16")
+    M = S.spmm_pack_bcsr(np.zeros((128, 128), np.uint16))
+    P = S.spmm_plan_sddmm(M, 64, S.BF16)
+    out = torch.zeros(16, dtype=torch.int16, device="cuda")
+    S.spmm_execute_sddmm(P, to_dev(X[:128, :64]), to_dev(Y[:128, :64]), out)
+
+
+@pytest.mark.parametrize("name", ["sddmm_bcsr_prefill_kd8192", "sddmm_i8_prefill_kd8192"])
+def test_sddmm_bcsr_prefill_sampled(S, orc, name):
+    w = synth.WORKLOADS[name]
+    a = synth.make_a(w)["dense"]
+    X, Y = synth.make_xy(w)
+    nnzb = w.nblocks
+    r = np.random.default_rng(21)
+    blocks = np.unique(np.concatenate([[0, nnzb - 1], r.choice(nnzb, 14, replace=False)])).astype(np.int64)
+    got, ref, P = sddmm_bcsr_case(S, orc, a, X, Y, w.elem, blocks=blocks)
+    err = _check_sddmm_bcsr(orc, got, ref, w.elem, blocks)
+    _say(f"{name} blocks={len(blocks)} grid={P.info()['grid']} ws={P.info()['workspace_bytes']} "
+         f"rel_frob={err:.3e}")

@@ -62,6 +62,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dense-baseline", action="store_true",
+                    help="BCSR workloads: also time the dense product of the same shape "
+                         "(torch.matmul on the zero-filled bf16 A) to show where block "
+                         "sparsity stops paying")
     ap.add_argument("--window-rows", type=int, default=None)
     ap.add_argument("--max-chunk-nnz", type=int, default=None)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -237,6 +241,9 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, d, args.cpu_seconds)
+    dense = None
+    if args.dense_baseline and w.fmt == "bcsr":
+        dense = dense_baseline(torch, w, d, Bt, stream, args, ms_step)
 
     out = {
         "metric": METRIC,
@@ -265,6 +272,8 @@ def main():
                        "plan": round(d["t_plan"], 3)},
         "cpu_baseline": cpu,
     }
+    if dense is not None:
+        out["dense_baseline"] = dense
     print(json.dumps(out), flush=True)
 
 
@@ -296,6 +305,34 @@ def measured_traffic(workload: str, kernel: str):
                 except ValueError:
                     return None
     return None
+
+
+def dense_baseline(torch, w, d, Bt, stream, args, ms_sparse):
+    """Time the dense bf16 product of the same shape (the zero-filled A times
+    B, torch.matmul) on the same stream; a comparison point, not part of the
+    library."""
+    A = torch.from_numpy(d["a"]["dense"].view(np.int16)).cuda().view(torch.bfloat16)
+    B = Bt.view(torch.bfloat16)
+    C = torch.empty((w.m, w.n), dtype=torch.bfloat16, device="cuda")
+    with torch.cuda.stream(stream):
+        for _ in range(max(2, args.warmup)):
+            torch.matmul(A, B, out=C)
+    torch.cuda.synchronize()
+    steps = max(5, args.steps // 4)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        for _ in range(steps):
+            torch.matmul(A, B, out=C)
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    flops = 2.0 * w.m * w.k * w.n
+    log(f"dense bf16 product of the same shape: {ms:.3f} ms")
+    return {"ms_per_step": round(ms, 6), "tflops_dense": round(flops / (ms * 1e-3) / 1e12, 2),
+            "sparse_speedup": round(ms / ms_sparse, 3), "steps": steps,
+            "what": "torch.matmul on the zero-filled bf16 A, same B, bf16 C"}
 
 
 def roofline(w, flops, nbytes, dtype, ms_step):

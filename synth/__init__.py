@@ -211,6 +211,11 @@ WORKLOADS: Dict[str, Workload] = {
                                 powerlaw=True),
     "sp24_i8_8192": Workload("sp24_i8_8192", "sp24", 8192, 8192, 2048, 20260004),
     "bcsr_prefill_18944x3584": _bcsr("bcsr_prefill_18944x3584", 18944, 3584, 65536, 0.90, 20260005),
+    # the same layer at milder block sparsity (50% and 70% of the blocks zero)
+    "bcsr_prefill_18944x3584_z50": _bcsr("bcsr_prefill_18944x3584_z50", 18944, 3584, 65536, 0.50,
+                                         20260006),
+    "bcsr_prefill_18944x3584_z70": _bcsr("bcsr_prefill_18944x3584_z70", 18944, 3584, 65536, 0.70,
+                                         20260007),
     # the sampled dense-dense product on the power-law pattern, inner dimension 128
     "sddmm_powerlaw_1m": Workload("sddmm_powerlaw_1m", "sddmm", 1_000_000, 1_000_000, 128, 20260003,
                                   powerlaw=True),

@@ -112,18 +112,27 @@ def test_bcsr_4096_config(S, orc):
     assert err <= TOL_BF16
 
 
-def test_bcsr_prefill_config_sampled(S, orc):
-    w = synth.WORKLOADS["bcsr_prefill_18944x3584"]
+@pytest.mark.parametrize("name", ["bcsr_prefill_18944x3584", "bcsr_prefill_18944x3584_z70",
+                                  "bcsr_prefill_18944x3584_z50"])
+def test_bcsr_prefill_config_sampled(S, orc, name):
+    w = synth.WORKLOADS[name]
     a = synth.make_a(w)["dense"]
     B = synth.make_b(w)
     r = np.random.default_rng(6)
     rows = np.unique(np.concatenate([np.arange(64), np.arange(w.m - 64, w.m),
                                      r.choice(w.m, 64, replace=False)])).astype(np.int64)
-    g, ref, got = bcsr_case(S, orc, a, B, rows=rows)
-    err = orc.rel_frobenius(g, ref)
-    _say(f"bcsr_prefill rows={len(rows)} rel_frob={err:.3e}")
-    assert err <= TOL_BF16
+    M = S.spmm_pack_bcsr(a, 64, 64)
+    P = S.spmm_plan(M, w.n, S.BF16, S.BF16)
+    got = run(S, P, B, w.m, w.n, "bf16")
     assert (got != 0xFFFF).all(), "some C element was not written"
+    rp, ci, v = orc.pack_bcsr(a, 64, 64)
+    # the sampled rows over the first and the last 2048 columns (C's columns
+    # are independent, so slabs check the same sums as whole rows)
+    for j0, j1 in ((0, 2048), (w.n - 2048, w.n)):
+        ref = orc.bcsr_spmm(64, 64, rp, ci, v, B, rows=rows, j0=j0, j1=j1)
+        err = orc.rel_frobenius(bf16_to_f64(got[rows][:, j0:j1]), ref)
+        _say(f"{name} rows={len(rows)} cols=[{j0},{j1}) rel_frob={err:.3e}")
+        assert err <= TOL_BF16
 
 
 def test_bcsr_deterministic(S, orc):

@@ -44,7 +44,7 @@ PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "i8": 5000.0}
 
 # kernel whose launch dominates a step, per format
 DOMINANT_KERNEL = {"bcsr": "bcsr_bf16_mfma", "wcsr": "wcsr_stream", "sp24": "sp24_i8_smfmac",
-                   "sddmm": "sddmm_f32", "sddmm_bcsr": "sddmm_bcsr_mfma"}
+                   "sddmm": "sddmm_f32", "sddmm_bcsr": "sddmm_bcsr_mfma", "bcsr_csr": "bcsr_bf16_mfma"}
 TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 CSRC = os.path.join(ROOT, "sparse_dense_matrix_amd", "csrc")
 
@@ -91,6 +91,10 @@ def setup(w, S, args):
     if w.fmt in ("bcsr", "sddmm_bcsr"):
         M = S.spmm_pack_bcsr(a["dense"], w.block, w.block)
         types = (S.BF16, S.BF16)
+    elif w.fmt == "bcsr_csr":
+        M = S.spmm_pack_bcsr_csr(w.m, w.k, a["row_ptr"], a["col_idx"], a["vals_bf16"],
+                                 reorder=w.reorder)
+        types = (S.BF16, S.BF16)
     elif w.fmt in ("wcsr", "sddmm"):
         W = args.window_rows or S.DEFAULT_WINDOW_ROWS
         T = args.max_chunk_nnz or S.DEFAULT_MAX_CHUNK_NNZ
@@ -120,6 +124,16 @@ def algorithmic(w, d):
     info = d["info"]
     n = w.n
     flops = 2.0 * info["nnz"] * n
+    if w.fmt == "bcsr_csr":
+        # effective work counts the CSR entries (the stored zeros of the blocks
+        # are overhead); bytes as for BCSR: the packed blocks, the B rows of
+        # touched block columns and C once
+        import sparse_dense_matrix_amd as S
+        nnzb = info["nnzb"]
+        cols = np.unique(S.spmm_matrix_array(d["M"], S.ARRAY_COL_IDX))
+        flops = 2.0 * int(d["a"]["row_ptr"][-1]) * n
+        a_bytes = nnzb * w.block * w.block * 2 + 4 * (w.m // w.block + 1) + 4 * nnzb
+        return flops, a_bytes + len(cols) * w.block * n * 2 + w.m * n * 2, "bf16"
     if w.fmt == "sddmm_bcsr":
         # every element of every stored block: 2 * nnzb * 4096 * kd; X rows of
         # block rows with blocks and Y rows of block columns with blocks once,
@@ -210,7 +224,8 @@ def main():
         B = d["B"]
         Bh = torch.from_numpy(B.view(np.int16) if B.dtype == np.uint16 else B)
         Bt = Bh.cuda()
-        cdt = {"bcsr": torch.int16, "wcsr": torch.float32, "sp24": torch.int32}[w.fmt]
+        cdt = {"bcsr": torch.int16, "bcsr_csr": torch.int16, "wcsr": torch.float32,
+               "sp24": torch.int32}[w.fmt]
         Ct = torch.empty((w.m, w.n), dtype=cdt, device="cuda")
 
         def step(stream):
@@ -264,6 +279,8 @@ def main():
                    "window_rows": d["info"]["window_rows"],
                    "max_chunk_nnz": d["info"]["max_chunk_nnz"],
                    "split_rows": pinfo["num_split_rows"], "grid": pinfo["grid"],
+                   **({"csr_nnz": int(d["a"]["row_ptr"][-1]), "reordered": w.reorder,
+                       "scramble_seed": w.scramble} if w.scramble else {}),
                    "parallelism": "single GPU"},
         "roofline": roof,
         "roofline_other_bound": other,
@@ -422,6 +439,12 @@ def pmc_summary(root):
         print(f"{k:32s} {c:32s} dispatches={len(v):4d} mean={sum(v) / len(v):.6g}")
 
 
+def synth_f32(B):
+    """B as float32 for the CSR oracle (bf16 bit patterns widen exactly)."""
+    import synth
+    return synth.bf16_bits_to_f32(B) if B.dtype == np.uint16 else B
+
+
 def cpu_baseline(w, d, target_s):
     """Time the oracle on a growing sample of rows until it takes about
     target_s; report effective GFLOP/s over the sampled rows."""
@@ -434,11 +457,12 @@ def cpu_baseline(w, d, target_s):
 
         def run(rows):
             oracle.bcsr_spmm(w.block, w.block, rp, ci, v, B, rows=rows)
-    elif w.fmt == "wcsr":
+    elif w.fmt in ("wcsr", "bcsr_csr"):
         row_nnz = np.diff(a["row_ptr"])
+        Bf = synth_f32(B)
 
         def run(rows):
-            oracle.csr_spmm(a["row_ptr"], a["col_idx"], a["vals"], B, rows=rows)
+            oracle.csr_spmm(a["row_ptr"], a["col_idx"], a["vals"], Bf, rows=rows)
     elif w.fmt == "sddmm":
         row_nnz = np.diff(a["row_ptr"])
 

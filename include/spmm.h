@@ -81,6 +81,11 @@ typedef struct {
  *    SPMM_ARRAY_ROW_PTR   int32[mb + 1]   blocks of block row r: [row_ptr[r], row_ptr[r+1])
  *    SPMM_ARRAY_COL_IDX   int32[nnzb]     block column, ascending within a block row
  *    SPMM_ARRAY_VALS      bf16 bits, uint16[nnzb * bm * bk], each block row-major
+ *    SPMM_ARRAY_ROW_PERM  int32[m]        (spmm_pack_bcsr_csr with reordering) original
+ *                                         row of each row of the packed matrix; count 0
+ *                                         when rows keep their order
+ *    SPMM_ARRAY_COL_PERM  int32[k]        original column of each packed column; count 0
+ *                                         when columns keep their order
  *  WCSR
  *    SPMM_ARRAY_ROW_PTR   int64[m + 1]
  *    SPMM_ARRAY_COL_IDX   int32[nnz]      strictly ascending within a row
@@ -98,7 +103,9 @@ typedef enum {
   SPMM_ARRAY_VALS = 2,
   SPMM_ARRAY_META = 3,
   SPMM_ARRAY_CHUNK_WINDOW = 4,
-  SPMM_ARRAY_CHUNK_BEGIN = 5
+  SPMM_ARRAY_CHUNK_BEGIN = 5,
+  SPMM_ARRAY_ROW_PERM = 6,
+  SPMM_ARRAY_COL_PERM = 7
 } spmm_array_t;
 
 /* ---- packing (host only; inputs are borrowed for the call and copied) ---- */
@@ -112,6 +119,25 @@ typedef enum {
 spmm_status_t spmm_pack_bcsr(int64_t m, int64_t k, int32_t block_m, int32_t block_k,
                              spmm_dtype_t dtype, const void *a_host, int64_t lda,
                              spmm_matrix_t *out);
+
+/* BCSR from a canonical CSR on the host (row_ptr, col_idx as for
+ * spmm_pack_wcsr; vals bf16 bit patterns, uint16[nnz]).  A block is stored
+ * when a CSR entry falls in it (structural: an explicit zero still makes a
+ * block).  reorder = 0 keeps rows and columns in place; reorder = 1 first
+ * permutes rows and columns so the entries fall into fewer blocks, the
+ * row/column permutation before BCSR named on the "Daily Papers" search page
+ * (entry on block-sparse SpMM on tensor cores for unstructured matrices):
+ * columns ordered by their sorted row lists, then rows by their sorted lists
+ * of block columns, both lexicographically; the original order is kept when
+ * the permutation does not reduce the block count.  The packed matrix is
+ * P_r A P_c^T; the permutations are readable as SPMM_ARRAY_ROW_PERM /
+ * SPMM_ARRAY_COL_PERM, and spmm_execute applies them, so C = A * B in the
+ * original row and column order.  dtype must be SPMM_BF16; m % block_m == 0
+ * and k % block_k == 0; reorder must be 0 or 1 (else INVALID_ARG). */
+spmm_status_t spmm_pack_bcsr_csr(int64_t m, int64_t k, spmm_dtype_t dtype,
+                                 const int64_t *row_ptr, const int32_t *col_idx,
+                                 const void *vals, int32_t block_m, int32_t block_k,
+                                 int32_t reorder, spmm_matrix_t *out);
 
 /* WCSR from a canonical CSR on the host: row_ptr int64[m+1] with row_ptr[0] = 0,
  * non-decreasing; col_idx int32[nnz] strictly ascending within each row and in

@@ -21,7 +21,7 @@ __all__ = [
     "FORMAT_BCSR", "FORMAT_WCSR", "FORMAT_24",
     "ARRAY_ROW_PTR", "ARRAY_COL_IDX", "ARRAY_VALS", "ARRAY_META",
     "ARRAY_CHUNK_WINDOW", "ARRAY_CHUNK_BEGIN",
-    "spmm_pack_bcsr", "spmm_pack_wcsr", "spmm_pack_24", "spmm_matrix_info",
+    "spmm_pack_bcsr", "spmm_pack_bcsr_csr", "spmm_pack_wcsr", "spmm_pack_24", "spmm_matrix_info",
     "spmm_matrix_array", "spmm_plan", "spmm_plan_info", "spmm_execute",
     "spmm_plan_sddmm", "spmm_execute_sddmm",
     "spmm_status_str", "spmm_last_error", "LIB_PATH", "EXPORTS",
@@ -34,7 +34,7 @@ LIB_PATH = os.environ.get("SPMM_LIBRARY") or os.path.join(HERE, "libspmm.so")
 F32, BF16, I8, I32 = 0, 1, 2, 3
 FORMAT_BCSR, FORMAT_WCSR, FORMAT_24 = 0, 1, 2
 (ARRAY_ROW_PTR, ARRAY_COL_IDX, ARRAY_VALS, ARRAY_META, ARRAY_CHUNK_WINDOW,
- ARRAY_CHUNK_BEGIN) = range(6)
+ ARRAY_CHUNK_BEGIN, ARRAY_ROW_PERM, ARRAY_COL_PERM) = range(8)
 
 # Default row-window shape for WCSR: 0 lets the library choose (W rows per
 # window, at most T stored entries per chunk; one wavefront reduces one chunk).
@@ -43,7 +43,7 @@ DEFAULT_MAX_CHUNK_NNZ = 0
 
 # every symbol include/spmm.h declares
 EXPORTS = (
-    "spmm_pack_bcsr", "spmm_pack_wcsr", "spmm_pack_24", "spmm_matrix_info",
+    "spmm_pack_bcsr", "spmm_pack_bcsr_csr", "spmm_pack_wcsr", "spmm_pack_24", "spmm_matrix_info",
     "spmm_matrix_array", "spmm_matrix_destroy", "spmm_plan", "spmm_plan_info",
     "spmm_plan_destroy", "spmm_execute", "spmm_plan_sddmm", "spmm_execute_sddmm",
     "spmm_status_str", "spmm_last_error",
@@ -83,6 +83,7 @@ def _load():
     sig = {
         "spmm_pack_bcsr": (st, [i64, i64, i32, i32, st, P, i64, C.POINTER(P)]),
         "spmm_pack_wcsr": (st, [i64, i64, st, P, P, P, i32, i64, C.POINTER(P)]),
+        "spmm_pack_bcsr_csr": (st, [i64, i64, st, P, P, P, i32, i32, i32, C.POINTER(P)]),
         "spmm_pack_24": (st, [i64, i64, P, i64, C.POINTER(P)]),
         "spmm_matrix_info": (st, [P, C.POINTER(MatrixInfo)]),
         "spmm_matrix_array": (st, [P, i32, C.POINTER(P), C.POINTER(i64)]),
@@ -177,6 +178,22 @@ def spmm_pack_bcsr(a_bits: np.ndarray, block_m: int = 64, block_k: int = 64,
     return Matrix(h)
 
 
+def spmm_pack_bcsr_csr(m: int, k: int, row_ptr, col_idx, vals_bits, reorder: bool = False,
+                       block_m: int = 64, block_k: int = 64, dtype: int = BF16) -> Matrix:
+    """BCSR from a canonical CSR with bf16 values (uint16 bit patterns),
+    optionally after the row/column permutation that clusters entries into
+    fewer blocks (read back with ARRAY_ROW_PERM / ARRAY_COL_PERM)."""
+    rp = np.ascontiguousarray(row_ptr, dtype=np.int64)
+    ci = np.ascontiguousarray(col_idx, dtype=np.int32)
+    v = np.ascontiguousarray(vals_bits, dtype=np.uint16)
+    if len(rp) != m + 1:
+        raise ValueError("row_ptr must have m + 1 entries")
+    h = C.c_void_p()
+    _check(_lib.spmm_pack_bcsr_csr(m, k, dtype, _ptr(rp), _ptr(ci), _ptr(v), block_m, block_k,
+                                   int(bool(reorder)), C.byref(h)), "spmm_pack_bcsr_csr")
+    return Matrix(h)
+
+
 def spmm_pack_wcsr(m: int, k: int, row_ptr, col_idx, vals,
                    window_rows: int = DEFAULT_WINDOW_ROWS,
                    max_chunk_nnz: int = DEFAULT_MAX_CHUNK_NNZ, dtype: int = F32) -> Matrix:
@@ -209,7 +226,8 @@ def spmm_matrix_info(mat: Matrix) -> dict:
 
 _ARRAY_DTYPES = {
     (FORMAT_BCSR, ARRAY_ROW_PTR): np.int32, (FORMAT_BCSR, ARRAY_COL_IDX): np.int32,
-    (FORMAT_BCSR, ARRAY_VALS): np.uint16,
+    (FORMAT_BCSR, ARRAY_VALS): np.uint16, (FORMAT_BCSR, ARRAY_ROW_PERM): np.int32,
+    (FORMAT_BCSR, ARRAY_COL_PERM): np.int32,
     (FORMAT_WCSR, ARRAY_ROW_PTR): np.int64, (FORMAT_WCSR, ARRAY_COL_IDX): np.int32,
     (FORMAT_WCSR, ARRAY_VALS): np.float32, (FORMAT_WCSR, ARRAY_CHUNK_WINDOW): np.int32,
     (FORMAT_WCSR, ARRAY_CHUNK_BEGIN): np.int64,

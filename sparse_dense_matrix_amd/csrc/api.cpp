@@ -134,6 +134,26 @@ spmm_status_t plan_bcsr(spmm_plan_s *p) {
   L.frag = fv;
   L.mb = static_cast<int32_t>(a.m / 64);
   L.n = p->n;
+  L.k_rows = a.k;
+  L.col_perm = nullptr;
+  L.b_perm = nullptr;
+  L.c_rows = nullptr;
+  if (!a.col_perm.empty()) {
+    int32_t *cp = nullptr;
+    void *ws = nullptr;
+    const int64_t ws_bytes = a.k * p->n * 2;
+    if ((s = upload_vec(p, a.col_perm, &cp)) != SPMM_OK) return s;
+    if ((s = upload(p, nullptr, static_cast<size_t>(ws_bytes), &ws)) != SPMM_OK) return s;
+    p->info.device_bytes -= std::max<int64_t>(ws_bytes, 16);
+    p->info.workspace_bytes = ws_bytes;
+    L.col_perm = cp;
+    L.b_perm = static_cast<uint16_t *>(ws);
+  }
+  if (!a.row_perm.empty()) {
+    int32_t *rows = nullptr;
+    if ((s = upload_vec(p, a.row_perm, &rows)) != SPMM_OK) return s;
+    L.c_rows = rows;
+  }
   int cus = 0;
   hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, p->device);
   if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
@@ -404,6 +424,29 @@ spmm_status_t spmm_pack_bcsr(int64_t m, int64_t k, int32_t block_m, int32_t bloc
   });
 }
 
+spmm_status_t spmm_pack_bcsr_csr(int64_t m, int64_t k, spmm_dtype_t dtype,
+                                 const int64_t *row_ptr, const int32_t *col_idx,
+                                 const void *vals, int32_t block_m, int32_t block_k,
+                                 int32_t reorder, spmm_matrix_t *out) {
+  if (!out) return fail(SPMM_ERR_INVALID_ARG, "spmm_pack_bcsr_csr: out is NULL");
+  *out = nullptr;
+  if (dtype != SPMM_BF16) return fail(SPMM_ERR_UNSUPPORTED, "spmm_pack_bcsr_csr: only bf16 values");
+  if (m < 0 || k < 0 || m > INT32_MAX || k > INT32_MAX || !row_ptr || block_m <= 0 ||
+      block_k <= 0 || m % block_m != 0 || k % block_k != 0 || (reorder != 0 && reorder != 1))
+    return fail(SPMM_ERR_INVALID_ARG, "spmm_pack_bcsr_csr: bad shape, block, reorder or pointer");
+  return guarded([&]() -> spmm_status_t {
+    auto *a = new spmm_matrix_s();
+    spmm_status_t s = pack_bcsr_csr_bf16(m, k, row_ptr, col_idx, static_cast<const uint16_t *>(vals),
+                                         block_m, block_k, reorder == 1, *a);
+    if (s != SPMM_OK) {
+      delete a;
+      return s;
+    }
+    *out = a;
+    return SPMM_OK;
+  });
+}
+
 spmm_status_t spmm_pack_wcsr(int64_t m, int64_t k, spmm_dtype_t dtype,
                              const int64_t *row_ptr, const int32_t *col_idx,
                              const void *vals, int32_t window_rows,
@@ -488,6 +531,8 @@ spmm_status_t spmm_matrix_array(spmm_matrix_t a, int32_t which, const void **dat
       if (which == SPMM_ARRAY_ROW_PTR) return give(a->brow_ptr);
       if (which == SPMM_ARRAY_COL_IDX) return give(a->bcol_idx);
       if (which == SPMM_ARRAY_VALS) return give(a->bvals);
+      if (which == SPMM_ARRAY_ROW_PERM) return give(a->row_perm);
+      if (which == SPMM_ARRAY_COL_PERM) return give(a->col_perm);
       break;
     case SPMM_FORMAT_WCSR:
       if (which == SPMM_ARRAY_ROW_PTR) return give(a->row_ptr);
@@ -620,6 +665,8 @@ spmm_status_t spmm_plan_sddmm(spmm_matrix_t a, int64_t kd, spmm_dtype_t dtype, i
                 "bf16 or int8 X, Y");
   if (bcsr && (a->bm != 64 || a->bk != 64))
     return fail(SPMM_ERR_UNSUPPORTED, "spmm_plan_sddmm: BCSR patterns take 64 x 64 blocks");
+  if (bcsr && (!a->row_perm.empty() || !a->col_perm.empty()))
+    return fail(SPMM_ERR_UNSUPPORTED, "spmm_plan_sddmm: not for a reordered BCSR pattern");
   int ndev = 0;
   hipError_t e = hipGetDeviceCount(&ndev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDeviceCount");

@@ -111,7 +111,8 @@ template <int kTN>
 __global__ __launch_bounds__(Geo<kTN>::kThreads) void bcsr_bf16_mfma(
     const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ col_idx,
     const uint16_t *__restrict__ frag, int32_t mb, int32_t tiles, int32_t per_xcd, int64_t n,
-    const uint16_t *__restrict__ B, int64_t ldb, uint16_t *__restrict__ C, int64_t ldc) {
+    const uint16_t *__restrict__ B, int64_t ldb, uint16_t *__restrict__ C, int64_t ldc,
+    const int32_t *__restrict__ c_rows) {
   using G = Geo<kTN>;
   constexpr int kBRow = G::kBRow, kBBytes = G::kBBytes, kStageBytes = G::kStageBytes;
   constexpr int kBLoads = G::kBLoads, kALoads = G::kALoads;
@@ -238,8 +239,10 @@ __global__ __launch_bounds__(Geo<kTN>::kThreads) void bcsr_bf16_mfma(
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int row = q * 8 + (lane >> 3);
+      // packed row -> row of C (the identity unless A was packed permuted)
+      const int64_t crow = c_rows ? c_rows[row0 + row] : row0 + row;
       const u32x4 v = *reinterpret_cast<const u32x4 *>(ct + row * kCPitch + (lane & 7) * 16);
-      __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(C + (row0 + row) * ldc + col));
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(C + crow * ldc + col));
     }
   }
 }
@@ -278,12 +281,36 @@ hipError_t launch_tn(const BcsrLaunch &a, hipStream_t s) {
   const int64_t per_xcd = (tiles + 7) / 8;
   hipLaunchKernelGGL(bcsr_bf16_mfma<kTN>, dim3(static_cast<unsigned>(8 * per_xcd)), dim3(G::kThreads),
                      G::kLdsBytes, s, a.row_ptr, a.col_idx, a.frag, a.mb, static_cast<int32_t>(tiles),
-                     static_cast<int32_t>(per_xcd), a.n, a.B, a.ldb, a.C, a.ldc);
+                     static_cast<int32_t>(per_xcd), a.n, a.B, a.ldb, a.C, a.ldc, a.c_rows);
   return hipGetLastError();
+}
+
+// Bp[j] = B[perm[j]] for the k rows of B, n (a multiple of 8) columns each:
+// one workgroup per row, 16-byte pieces
+__global__ __launch_bounds__(256) void gather_rows_bf16(const uint16_t *__restrict__ B, int64_t ldb,
+                                                        const int32_t *__restrict__ perm, int64_t n,
+                                                        uint16_t *__restrict__ Bp) {
+  const int64_t j = blockIdx.x;
+  const u32x4 *src = reinterpret_cast<const u32x4 *>(B + static_cast<int64_t>(perm[j]) * ldb);
+  u32x4 *dst = reinterpret_cast<u32x4 *>(Bp + j * n);
+  for (int64_t c = threadIdx.x; c < n / 8; c += 256) dst[c] = src[c];
 }
 }  // namespace
 
-hipError_t launch_bcsr_bf16(const BcsrLaunch &a, hipStream_t s) {
+hipError_t launch_bcsr_bf16(const BcsrLaunch &a0, hipStream_t s) {
+  BcsrLaunch a = a0;
+  if (a.col_perm) {
+    // B's rows in the packed column order, then the multiply reads that copy
+    const int64_t k = a.k_rows;
+    if (k > 0 && a.n > 0) {
+      hipLaunchKernelGGL(gather_rows_bf16, dim3(static_cast<unsigned>(k)), dim3(256), 0, s, a.B,
+                         a.ldb, a.col_perm, a.n, a.b_perm);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    a.B = a.b_perm;
+    a.ldb = a.n;
+  }
   return bcsr_tile_n(a.n) == 512 ? launch_tn<512>(a, s) : launch_tn<256>(a, s);
 }
 

@@ -31,6 +31,9 @@ struct Matrix {
   int32_t bm = 0, bk = 0;
   std::vector<int32_t> brow_ptr, bcol_idx;
   std::vector<uint16_t> bvals;
+  // BCSR of a permuted CSR matrix: original row of each row / original
+  // column of each column of the packed matrix (empty: original order)
+  std::vector<int32_t> row_perm, col_perm;
   // WCSR
   int32_t window_rows = 0;
   int64_t max_chunk_nnz = 0;
@@ -54,6 +57,9 @@ spmm_status_t pack_wcsr_f32(int64_t m, int64_t k, const int64_t *row_ptr,
                             const int32_t *col_idx, const float *vals, int32_t W,
                             int64_t T, Matrix &out);
 spmm_status_t pack_24_i8(int64_t m, int64_t k, const int8_t *a, int64_t lda, Matrix &out);
+spmm_status_t pack_bcsr_csr_bf16(int64_t m, int64_t k, const int64_t *row_ptr,
+                                 const int32_t *col_idx, const uint16_t *vals, int32_t bm,
+                                 int32_t bk, bool reorder, Matrix &out);
 
 // ---------------------------------------------------------------------------
 // device-side descriptors (plan-private layouts)
@@ -89,6 +95,13 @@ struct BcsrLaunch {
   int64_t ldb;
   uint16_t *C;
   int64_t ldc;
+  // A packed with its rows and columns permuted (spmm_pack_bcsr_csr): B's
+  // rows are gathered into b_perm (k x n, ld n) in the packed column order
+  // first, and packed row i is written to C row c_rows[i]; null otherwise
+  int64_t k_rows;           // k: rows of B
+  const int32_t *col_perm;  // [k] original row of B for each packed column
+  uint16_t *b_perm;         // [k][n] workspace
+  const int32_t *c_rows;    // [m] original row of C for each packed row
 };
 // Fragment order of one 64 x 64 block: [rb 2][s 4][lane 64][8 elements], lane l
 // holding row 32*rb + l%32, columns 16*s + 8*(l/32) + 0..7.

@@ -58,31 +58,39 @@ spmm_status_t pack_bcsr_bf16(int64_t m, int64_t k, int32_t bm, int32_t bk,
 // WCSR: validate the CSR, copy it, and cut each window of W rows into chunks
 // of at most T stored entries.
 // ---------------------------------------------------------------------------
-spmm_status_t pack_wcsr_f32(int64_t m, int64_t k, const int64_t *row_ptr,
-                            const int32_t *col_idx, const float *vals, int32_t W,
-                            int64_t T, Matrix &out) {
-  if (row_ptr[0] != 0) return fail(SPMM_ERR_INVALID_ARG, "spmm_pack_wcsr: row_ptr[0] != 0");
+// A canonical CSR: row_ptr starts at 0 and never decreases, columns lie in
+// [0, k) and strictly ascend within a row.  Nothing is ever fixed silently.
+static spmm_status_t check_csr(const char *who, int64_t m, int64_t k, const int64_t *row_ptr,
+                               const int32_t *col_idx, const void *vals) {
+  const std::string w(who);
+  if (row_ptr[0] != 0) return fail(SPMM_ERR_INVALID_ARG, w + ": row_ptr[0] != 0");
   for (int64_t i = 0; i < m; ++i)
     if (row_ptr[i + 1] < row_ptr[i])
-      return fail(SPMM_ERR_INVALID_ARG,
-                  "spmm_pack_wcsr: row_ptr decreases at row " + std::to_string(i));
+      return fail(SPMM_ERR_INVALID_ARG, w + ": row_ptr decreases at row " + std::to_string(i));
   const int64_t nnz = row_ptr[m];
   if (nnz > 0 && (col_idx == nullptr || vals == nullptr))
-    return fail(SPMM_ERR_INVALID_ARG, "spmm_pack_wcsr: col_idx / vals is NULL");
+    return fail(SPMM_ERR_INVALID_ARG, w + ": col_idx / vals is NULL");
   for (int64_t i = 0; i < m; ++i) {
     int64_t prev = -1;
     for (int64_t p = row_ptr[i]; p < row_ptr[i + 1]; ++p) {
       const int64_t c = col_idx[p];
       if (c < 0 || c >= k)
-        return fail(SPMM_ERR_INVALID_ARG,
-                    "spmm_pack_wcsr: column out of range in row " + std::to_string(i));
+        return fail(SPMM_ERR_INVALID_ARG, w + ": column out of range in row " + std::to_string(i));
       if (c <= prev)
         return fail(SPMM_ERR_INVALID_ARG,
-                    "spmm_pack_wcsr: columns not strictly ascending in row " +
-                        std::to_string(i));
+                    w + ": columns not strictly ascending in row " + std::to_string(i));
       prev = c;
     }
   }
+  return SPMM_OK;
+}
+
+spmm_status_t pack_wcsr_f32(int64_t m, int64_t k, const int64_t *row_ptr,
+                            const int32_t *col_idx, const float *vals, int32_t W,
+                            int64_t T, Matrix &out) {
+  spmm_status_t st = check_csr("spmm_pack_wcsr", m, k, row_ptr, col_idx, vals);
+  if (st != SPMM_OK) return st;
+  const int64_t nnz = row_ptr[m];
   out.format = SPMM_FORMAT_WCSR;
   out.dtype = SPMM_F32;
   out.m = m;
@@ -106,6 +114,165 @@ spmm_status_t pack_wcsr_f32(int64_t m, int64_t k, const int64_t *row_ptr,
     }
   }
   out.chunk_begin.push_back(nnz);
+  return SPMM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// BCSR from a CSR matrix, optionally after permuting rows and columns so the
+// entries fall into fewer blocks (the row/column permutation that minimises
+// nonzero blocks, on the search page's entry about block-sparse SpMM on
+// tensor cores for unstructured matrices).  The permutation used here:
+//   1. columns are ordered by their sorted lists of rows, compared
+//      lexicographically (ties by column index), so columns used by the same
+//      rows become neighbours and land in the same block columns;
+//   2. rows are then ordered by their sorted lists of block columns under the
+//      new column order (ties by row index), so rows touching the same block
+//      columns share block rows.
+// When the permuted matrix needs no fewer blocks than the original, the
+// original order is kept.  row_perm[i'] is the original row of row i',
+// col_perm[j'] the original column of column j'; both are empty when the
+// order is the original one.
+// ---------------------------------------------------------------------------
+namespace {
+
+// lexicographic order of variable-length sorted lists, ties by index
+struct ListOrder {
+  const std::vector<int64_t> &ptr;
+  const std::vector<int32_t> &val;
+  bool operator()(int32_t a, int32_t b) const {
+    const int32_t *pa = val.data() + ptr[a], *ea = val.data() + ptr[a + 1];
+    const int32_t *pb = val.data() + ptr[b], *eb = val.data() + ptr[b + 1];
+    for (; pa != ea && pb != eb; ++pa, ++pb)
+      if (*pa != *pb) return *pa < *pb;
+    if (pa != ea || pb != eb) return pa == ea;  // the shorter (prefix) list first
+    return a < b;
+  }
+};
+
+// blocks a permuted CSR pattern occupies (newcol[c]: position of column c)
+int64_t count_blocks(int64_t m, const int64_t *row_ptr, const int32_t *col_idx,
+                     const std::vector<int32_t> &row_perm, const std::vector<int32_t> &newcol,
+                     int32_t bm, int32_t bk, int64_t kb) {
+  std::vector<int64_t> seen(kb, -1);
+  int64_t blocks = 0;
+  for (int64_t ip = 0; ip < m; ++ip) {
+    const int64_t i = row_perm.empty() ? ip : row_perm[ip];
+    const int64_t br = ip / bm;
+    for (int64_t p = row_ptr[i]; p < row_ptr[i + 1]; ++p) {
+      const int64_t bc = (newcol.empty() ? col_idx[p] : newcol[col_idx[p]]) / bk;
+      if (seen[bc] != br) {
+        seen[bc] = br;
+        ++blocks;
+      }
+    }
+  }
+  return blocks;
+}
+
+void cluster_order(int64_t m, int64_t k, const int64_t *row_ptr, const int32_t *col_idx,
+                   int32_t bk, std::vector<int32_t> &row_perm, std::vector<int32_t> &col_perm) {
+  const int64_t nnz = row_ptr[m];
+  // 1. columns by their row lists (a CSC view; rows come out ascending)
+  std::vector<int64_t> cptr(k + 1, 0);
+  for (int64_t p = 0; p < nnz; ++p) ++cptr[col_idx[p] + 1];
+  for (int64_t c = 0; c < k; ++c) cptr[c + 1] += cptr[c];
+  std::vector<int32_t> crow(nnz);
+  {
+    std::vector<int64_t> fill(cptr.begin(), cptr.end() - 1);
+    for (int64_t i = 0; i < m; ++i)
+      for (int64_t p = row_ptr[i]; p < row_ptr[i + 1]; ++p) crow[fill[col_idx[p]]++] = static_cast<int32_t>(i);
+  }
+  col_perm.resize(k);
+  for (int64_t c = 0; c < k; ++c) col_perm[c] = static_cast<int32_t>(c);
+  std::sort(col_perm.begin(), col_perm.end(), ListOrder{cptr, crow});
+  std::vector<int32_t> newcol(k);
+  for (int64_t j = 0; j < k; ++j) newcol[col_perm[j]] = static_cast<int32_t>(j);
+  // 2. rows by their sorted, distinct block columns under the new order
+  std::vector<int64_t> rptr(m + 1, 0);
+  std::vector<int32_t> rblk;
+  rblk.reserve(nnz);
+  std::vector<int32_t> tmp;
+  for (int64_t i = 0; i < m; ++i) {
+    tmp.clear();
+    for (int64_t p = row_ptr[i]; p < row_ptr[i + 1]; ++p) tmp.push_back(newcol[col_idx[p]] / bk);
+    std::sort(tmp.begin(), tmp.end());
+    tmp.erase(std::unique(tmp.begin(), tmp.end()), tmp.end());
+    rblk.insert(rblk.end(), tmp.begin(), tmp.end());
+    rptr[i + 1] = static_cast<int64_t>(rblk.size());
+  }
+  row_perm.resize(m);
+  for (int64_t i = 0; i < m; ++i) row_perm[i] = static_cast<int32_t>(i);
+  std::sort(row_perm.begin(), row_perm.end(), ListOrder{rptr, rblk});
+}
+
+}  // namespace
+
+spmm_status_t pack_bcsr_csr_bf16(int64_t m, int64_t k, const int64_t *row_ptr,
+                                 const int32_t *col_idx, const uint16_t *vals, int32_t bm,
+                                 int32_t bk, bool reorder, Matrix &out) {
+  spmm_status_t st = check_csr("spmm_pack_bcsr_csr", m, k, row_ptr, col_idx, vals);
+  if (st != SPMM_OK) return st;
+  const int64_t mb = m / bm, kb = k / bk;
+  std::vector<int32_t> row_perm, col_perm, newcol;
+  if (reorder && row_ptr[m] > 0) {
+    cluster_order(m, k, row_ptr, col_idx, bk, row_perm, col_perm);
+    newcol.resize(k);
+    for (int64_t j = 0; j < k; ++j) newcol[col_perm[j]] = static_cast<int32_t>(j);
+    const int64_t before = count_blocks(m, row_ptr, col_idx, {}, {}, bm, bk, kb);
+    const int64_t after = count_blocks(m, row_ptr, col_idx, row_perm, newcol, bm, bk, kb);
+    if (after >= before) {
+      row_perm.clear();
+      col_perm.clear();
+      newcol.clear();
+    }
+  }
+  out.format = SPMM_FORMAT_BCSR;
+  out.dtype = SPMM_BF16;
+  out.m = m;
+  out.k = k;
+  out.bm = bm;
+  out.bk = bk;
+  out.row_perm = row_perm;
+  out.col_perm = col_perm;
+  out.brow_ptr.assign(mb + 1, 0);
+  out.bcol_idx.clear();
+  out.bvals.clear();
+  const int64_t belems = static_cast<int64_t>(bm) * bk;
+  std::vector<int32_t> slot(kb, -1);  // block column -> block index within the block row
+  std::vector<int32_t> cols;
+  for (int64_t br = 0; br < mb; ++br) {
+    cols.clear();
+    for (int64_t ip = br * bm; ip < (br + 1) * bm; ++ip) {
+      const int64_t i = row_perm.empty() ? ip : row_perm[ip];
+      for (int64_t p = row_ptr[i]; p < row_ptr[i + 1]; ++p) {
+        const int32_t bc = (newcol.empty() ? col_idx[p] : newcol[col_idx[p]]) / bk;
+        if (slot[bc] < 0) {
+          slot[bc] = 0;
+          cols.push_back(bc);
+        }
+      }
+    }
+    std::sort(cols.begin(), cols.end());
+    const int64_t first = static_cast<int64_t>(out.bcol_idx.size());
+    if (first + static_cast<int64_t>(cols.size()) > INT32_MAX)
+      return fail(SPMM_ERR_UNSUPPORTED, "spmm_pack_bcsr_csr: more than 2^31-1 blocks");
+    for (size_t q = 0; q < cols.size(); ++q) {
+      slot[cols[q]] = static_cast<int32_t>(q);
+      out.bcol_idx.push_back(cols[q]);
+    }
+    out.bvals.resize(static_cast<size_t>((first + static_cast<int64_t>(cols.size())) * belems), 0);
+    for (int64_t ip = br * bm; ip < (br + 1) * bm; ++ip) {
+      const int64_t i = row_perm.empty() ? ip : row_perm[ip];
+      for (int64_t p = row_ptr[i]; p < row_ptr[i + 1]; ++p) {
+        const int64_t jn = newcol.empty() ? col_idx[p] : newcol[col_idx[p]];
+        const int64_t b = first + slot[jn / bk];
+        out.bvals[static_cast<size_t>(b * belems + (ip - br * bm) * bk + jn % bk)] = vals[p];
+      }
+    }
+    for (int32_t bc : cols) slot[bc] = -1;
+    out.brow_ptr[br + 1] = static_cast<int32_t>(out.bcol_idx.size());
+  }
+  out.nnz = static_cast<int64_t>(out.bcol_idx.size()) * belems;
   return SPMM_OK;
 }
 

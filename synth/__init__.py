@@ -25,7 +25,7 @@ from typing import Dict
 import numpy as np
 
 # stream ids: one independent Philox key per random quantity of a workload
-S_PATTERN, S_AVAL, S_BVAL, S_ROWLEN, S_COLS, S_BAND, S_YVAL = 0, 1, 2, 3, 4, 5, 6
+S_PATTERN, S_AVAL, S_BVAL, S_ROWLEN, S_COLS, S_BAND, S_YVAL, S_PERM = 0, 1, 2, 3, 4, 5, 6, 7
 
 
 def rng(seed: int, stream: int) -> np.random.Generator:
@@ -154,6 +154,23 @@ def block_sparse_dense_bf16(m: int, k: int, bm: int, bk: int, nblocks: int,
     return a, ids
 
 
+def scrambled_csr_bf16(a_bits: np.ndarray, seed: int):
+    """A dense bf16 matrix (uint16 bits) with its rows and columns shuffled by
+    seeded random permutations, as a canonical CSR (row_ptr int64, col_idx
+    int32, vals uint16 bits): block structure that is there but not visible.
+    Also returns the two permutations (new -> original)."""
+    m, k = a_bits.shape
+    g = rng(seed, S_PERM)
+    rperm = g.permutation(m)
+    cperm = g.permutation(k)
+    a = a_bits[rperm][:, cperm]
+    nz = (a & 0x7FFF) != 0
+    row_ptr = np.zeros(m + 1, dtype=np.int64)
+    np.cumsum(nz.sum(axis=1), out=row_ptr[1:])
+    rows, cols = np.nonzero(nz)
+    return row_ptr, cols.astype(np.int32), a[rows, cols].astype(np.uint16), rperm, cperm
+
+
 def dense_bf16_normal(rows: int, cols: int, seed: int, stream: int = S_BVAL,
                       sigma: float = 1.0, chunk_rows: int = 256) -> np.ndarray:
     """Dense row-major bf16 (uint16 bits) N(0, sigma), drawn in row slabs to
@@ -176,7 +193,7 @@ def dense_f32_normal(rows: int, cols: int, seed: int, stream: int = S_BVAL) -> n
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    fmt: str            # "wcsr" | "bcsr" | "sp24" | "sddmm" | "sddmm_bcsr" (n = inner dimension)
+    fmt: str            # "wcsr" | "bcsr" | "bcsr_csr" | "sp24" | "sddmm" | "sddmm_bcsr"
     m: int
     k: int
     n: int
@@ -191,6 +208,9 @@ class Workload:
     nblocks: int = 0
     sigma: float = 0.02
     elem: str = ""                # sddmm_bcsr: "bf16" | "i8" operands X, Y
+    scramble: int = 0             # > 0: a block-sparse matrix with rows and columns
+                                  # shuffled (this seed), given as CSR
+    reorder: bool = False         # bcsr_csr: pack after the row/column reordering
 
     @property
     def describe(self) -> str:
@@ -216,6 +236,15 @@ WORKLOADS: Dict[str, Workload] = {
                                          20260006),
     "bcsr_prefill_18944x3584_z70": _bcsr("bcsr_prefill_18944x3584_z70", 18944, 3584, 65536, 0.70,
                                          20260007),
+    # the 4096 block-sparse matrix with rows and columns shuffled, given as
+    # CSR: packed as BCSR with and without the reordering, and as WCSR
+    "scrambled_4096_bcsr_reordered": Workload("scrambled_4096_bcsr_reordered", "bcsr_csr", 4096,
+                                              4096, 4096, 20260002, nblocks=410,
+                                              scramble=20260008, reorder=True),
+    "scrambled_4096_bcsr_plain": Workload("scrambled_4096_bcsr_plain", "bcsr_csr", 4096, 4096,
+                                          4096, 20260002, nblocks=410, scramble=20260008),
+    "scrambled_4096_wcsr": Workload("scrambled_4096_wcsr", "wcsr", 4096, 4096, 4096, 20260002,
+                                    nblocks=410, scramble=20260008),
     # the sampled dense-dense product on the power-law pattern, inner dimension 128
     "sddmm_powerlaw_1m": Workload("sddmm_powerlaw_1m", "sddmm", 1_000_000, 1_000_000, 128, 20260003,
                                   powerlaw=True),
@@ -240,12 +269,21 @@ SMALL: Dict[str, Workload] = {
                             band_half=64),
     "sddmm_bcsr_small": _bcsr("sddmm_bcsr_small", 640, 512, 1000, 0.7, 35, fmt="sddmm_bcsr",
                               elem="bf16"),
+    "scrambled_small": Workload("scrambled_small", "bcsr_csr", 1024, 768, 520, 36, nblocks=30,
+                                scramble=37, reorder=True),
 }
 
 
 def make_a(w: Workload) -> dict:
     """Draw the sparse operand.  wcsr -> CSR arrays; bcsr -> dense bf16 bits;
     sp24 -> dense int8 (not yet pruned: pruning is the packer's job)."""
+    if w.scramble:
+        dense, _ = block_sparse_dense_bf16(w.m, w.k, w.block, w.block, w.nblocks, w.sigma, w.seed)
+        rp, ci, v, rperm, cperm = scrambled_csr_bf16(dense, w.scramble)
+        out = {"row_ptr": rp, "col_idx": ci, "vals_bf16": v, "row_shuffle": rperm,
+               "col_shuffle": cperm}
+        out["vals"] = bf16_bits_to_f32(v)            # the same values, for fp32 paths
+        return out
     if w.fmt in ("wcsr", "sddmm"):
         if w.powerlaw:
             rp, ci, v = csr_powerlaw(w.m, w.k, w.zipf, w.cap, w.band_frac, w.band_half, w.seed)
@@ -278,6 +316,9 @@ def make_xy(w: Workload, kd: int | None = None, elem: str | None = None):
 def make_b(w: Workload, n: int | None = None) -> np.ndarray:
     """Draw the dense operand B [k x n] row-major."""
     n = w.n if n is None else n
+    if w.scramble:
+        bits = dense_bf16_normal(w.k, n, w.seed)
+        return bf16_bits_to_f32(bits) if w.fmt == "wcsr" else bits   # the same values
     if w.fmt == "wcsr":
         return dense_f32_normal(w.k, n, w.seed)
     if w.fmt == "bcsr":

@@ -553,3 +553,53 @@ def test_sddmm_bcsr_prefill_sampled(S, orc, name):
     err = _check_sddmm_bcsr(orc, got, ref, w.elem, blocks)
     _say(f"{name} blocks={len(blocks)} grid={P.info()['grid']} ws={P.info()['workspace_bytes']} "
          f"rel_frob={err:.3e}")
+
+
+# ---------------------------------------------------------------------------
+# BCSR of a CSR matrix after the row/column reordering
+# ---------------------------------------------------------------------------
+
+def _reordered_case(S, orc, w, rows=None):
+    a = synth.make_a(w)
+    B = synth.make_b(w)
+    M = S.spmm_pack_bcsr_csr(w.m, w.k, a["row_ptr"], a["col_idx"], a["vals_bf16"],
+                             reorder=w.reorder)
+    P = S.spmm_plan(M, w.n, S.BF16, S.BF16)
+    got = run(S, P, B, w.m, w.n, "bf16")
+    assert (got != 0xFFFF).all(), "some C element was not written"
+    ref = orc.csr_spmm(a["row_ptr"], a["col_idx"], a["vals"], synth.bf16_bits_to_f32(B), rows=rows)
+    g = got if rows is None else got[rows]
+    return orc.rel_frobenius(bf16_to_f64(g), ref), M, P
+
+
+@pytest.mark.parametrize("reorder", [True, False])
+def test_reordered_bcsr_small(S, orc, reorder):
+    import dataclasses
+    w = dataclasses.replace(synth.SMALL["scrambled_small"], reorder=reorder)   # 1024 x 768, n = 520
+    err, M, P = _reordered_case(S, orc, w)
+    info = S.spmm_matrix_info(M)
+    _say(f"scrambled_small reorder={reorder} nnzb={info['nnzb']} ws={P.info()['workspace_bytes']} "
+         f"rel_frob={err:.3e}")
+    assert err <= TOL_BF16
+    if reorder:
+        assert info["nnzb"] == w.nblocks          # the hidden blocks, found again
+        assert len(S.spmm_matrix_array(M, S.ARRAY_ROW_PERM)) == w.m
+
+
+def test_reordered_bcsr_4096_sampled(S, orc):
+    w = synth.WORKLOADS["scrambled_4096_bcsr_reordered"]
+    r = np.random.default_rng(22)
+    rows = np.unique(np.concatenate([np.arange(32), r.choice(w.m, 200, replace=False)])).astype(np.int64)
+    err, M, _ = _reordered_case(S, orc, w, rows=rows)
+    _say(f"scrambled_4096 nnzb={S.spmm_matrix_info(M)['nnzb']} rel_frob={err:.3e}")
+    assert err <= TOL_BF16
+    assert S.spmm_matrix_info(M)["nnzb"] == w.nblocks
+
+
+def test_reordered_pattern_has_no_sddmm(S, orc):
+    w = synth.SMALL["scrambled_small"]
+    a = synth.make_a(w)
+    M = S.spmm_pack_bcsr_csr(w.m, w.k, a["row_ptr"], a["col_idx"], a["vals_bf16"], reorder=True)
+    with pytest.raises(S.SpmmError) as ei:
+        S.spmm_plan_sddmm(M, 64, S.BF16)
+    assert ei.value.name == "SPMM_ERR_UNSUPPORTED"

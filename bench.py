@@ -44,7 +44,8 @@ PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "i8": 5000.0}
 
 # kernel whose launch dominates a step, per format
 DOMINANT_KERNEL = {"bcsr": "bcsr_bf16_mfma", "wcsr": "wcsr_stream", "sp24": "sp24_i8_smfmac",
-                   "sddmm": "sddmm_f32", "sddmm_bcsr": "sddmm_bcsr_mfma", "bcsr_csr": "bcsr_bf16_mfma"}
+                   "sddmm": "sddmm_f32", "sddmm_bcsr": "sddmm_bcsr_mfma", "bcsr_csr": "bcsr_bf16_mfma",
+                   "tvw": "sp24_i8_smfmac"}
 TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 CSRC = os.path.join(ROOT, "sparse_dense_matrix_amd", "csrc")
 
@@ -100,6 +101,9 @@ def setup(w, S, args):
         T = args.max_chunk_nnz or S.DEFAULT_MAX_CHUNK_NNZ
         M = S.spmm_pack_wcsr(w.m, w.k, a["row_ptr"], a["col_idx"], a["vals"], W, T)
         types = (S.F32, S.F32)
+    elif w.fmt == "tvw":
+        M = S.spmm_pack_tvw(a["dense"], synth.TVW_TILE_M, synth.TVW_TILE_K)
+        types = (S.I8, S.I32)
     else:
         M = S.spmm_pack_24(a["dense"])
         types = (S.I8, S.I32)
@@ -169,6 +173,13 @@ def algorithmic(w, d):
         x_rows = int(np.count_nonzero(np.diff(d["a"]["row_ptr"])))
         y_rows = len(np.unique(d["a"]["col_idx"]))
         return flops, 8 * (w.m + 1) + 8 * nnz + (x_rows + y_rows) * n * 4, "f32"
+    if w.fmt == "tvw":
+        # the stored tiles (kept values and index bytes), the B rows of
+        # k-steps any tile row stores, C once
+        import sparse_dense_matrix_amd as S
+        steps = np.unique(S.spmm_matrix_array(d["M"], S.ARRAY_COL_IDX))
+        a_bytes = info["nnz"] + info["nnz"] // 4 + 4 * (w.m // synth_tile_m() + 1 + info["nnzb"])
+        return flops, a_bytes + len(steps) * synth_tile_k() * n + w.m * n * 4, "i8"
     a_bytes = w.m * w.k // 2 + w.m * w.k // 8
     return flops, a_bytes + w.k * n + w.m * n * 4, "i8"
 
@@ -225,7 +236,7 @@ def main():
         Bh = torch.from_numpy(B.view(np.int16) if B.dtype == np.uint16 else B)
         Bt = Bh.cuda()
         cdt = {"bcsr": torch.int16, "bcsr_csr": torch.int16, "wcsr": torch.float32,
-               "sp24": torch.int32}[w.fmt]
+               "sp24": torch.int32, "tvw": torch.int32}[w.fmt]
         Ct = torch.empty((w.m, w.n), dtype=cdt, device="cuda")
 
         def step(stream):
@@ -259,6 +270,8 @@ def main():
     dense = None
     if args.dense_baseline and w.fmt == "bcsr":
         dense = dense_baseline(torch, w, d, Bt, stream, args, ms_step)
+    elif args.dense_baseline and w.fmt in ("tvw", "sp24"):
+        dense = dense_baseline_i8(torch, w, d, Bt, stream, args, ms_step)
 
     out = {
         "metric": METRIC,
@@ -352,6 +365,39 @@ def dense_baseline(torch, w, d, Bt, stream, args, ms_sparse):
             "what": "torch.matmul on the zero-filled bf16 A, same B, bf16 C"}
 
 
+def dense_baseline_i8(torch, w, d, Bt, stream, args, ms_sparse):
+    """Time the dense int8 product of the same shape (torch._int_mm on the
+    unpruned A) on the same stream; a comparison point, not part of the
+    library.  None when this torch build has no int8 matrix product."""
+    if not hasattr(torch, "_int_mm"):
+        return None
+    A = torch.from_numpy(d["a"]["dense"]).cuda()
+    C = torch.empty((w.m, w.n), dtype=torch.int32, device="cuda")
+    try:
+        with torch.cuda.stream(stream):
+            for _ in range(max(2, args.warmup)):
+                torch._int_mm(A, Bt, out=C)
+        torch.cuda.synchronize()
+    except (RuntimeError, TypeError) as e:
+        log(f"dense int8 product unavailable: {e}")
+        return None
+    steps = max(5, args.steps // 4)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        for _ in range(steps):
+            torch._int_mm(A, Bt, out=C)
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    ops = 2.0 * w.m * w.k * w.n
+    log(f"dense int8 product of the same shape: {ms:.3f} ms")
+    return {"ms_per_step": round(ms, 6), "tops_dense": round(ops / (ms * 1e-3) / 1e12, 2),
+            "sparse_speedup": round(ms / ms_sparse, 3), "steps": steps,
+            "what": "torch._int_mm on the unpruned int8 A, same B, int32 C"}
+
+
 def roofline(w, flops, nbytes, dtype, ms_step):
     """(roofline of the binding bound, the other bound).  The binding bound is
     the one whose time at peak is longer."""
@@ -439,6 +485,16 @@ def pmc_summary(root):
         print(f"{k:32s} {c:32s} dispatches={len(v):4d} mean={sum(v) / len(v):.6g}")
 
 
+def synth_tile_m():
+    import synth
+    return synth.TVW_TILE_M
+
+
+def synth_tile_k():
+    import synth
+    return synth.TVW_TILE_K
+
+
 def synth_f32(B):
     """B as float32 for the CSR oracle (bf16 bit patterns widen exactly)."""
     import synth
@@ -491,7 +547,14 @@ def cpu_baseline(w, d, target_s):
                           + ("fp64" if w.elem == "bf16" else "int64") + " accumulation"}
     else:
         vals, meta = oracle.pack24(a["dense"])
-        row_nnz = np.full(w.m, w.k // 2, dtype=np.int64)
+        # kept values per row: all k/2 for 2:4; for the tile pattern the kept
+        # values of the stored tiles only (the oracle still walks every group)
+        if w.fmt == "tvw":
+            import sparse_dense_matrix_amd as S
+            rp = S.spmm_matrix_array(d["M"], S.ARRAY_ROW_PTR).astype(np.int64)
+            row_nnz = np.repeat(np.diff(rp) * (synth_tile_k() // 2), synth_tile_m())
+        else:
+            row_nnz = np.full(w.m, w.k // 2, dtype=np.int64)
 
         def run(rows):
             oracle.sp24_spmm(vals, meta, B, rows=rows)

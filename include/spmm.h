@@ -56,7 +56,12 @@ typedef enum {
 
 typedef enum { SPMM_F32 = 0, SPMM_BF16 = 1, SPMM_I8 = 2, SPMM_I32 = 3 } spmm_dtype_t;
 
-typedef enum { SPMM_FORMAT_BCSR = 0, SPMM_FORMAT_WCSR = 1, SPMM_FORMAT_24 = 2 } spmm_format_t;
+typedef enum {
+  SPMM_FORMAT_BCSR = 0,
+  SPMM_FORMAT_WCSR = 1,
+  SPMM_FORMAT_24 = 2,
+  SPMM_FORMAT_TVW = 3  /* tile-vector-wise: 2:4 inside the stored tiles of a tile grid */
+} spmm_format_t;
 
 /* Packed sparse operand: immutable host arrays in the canonical layout below,
  * reference counted (a plan holds a reference). */
@@ -96,7 +101,13 @@ typedef struct {
  *    SPMM_ARRAY_VALS      int8[m * k/2]   the two kept values of group g of row i at
  *                                         [i*k/2 + 2g], [i*k/2 + 2g + 1], ascending position
  *    SPMM_ARRAY_META      uint8[m * k/8]  nibble (i0 | i1 << 2) of group g in byte
- *                                         i*k/8 + g/2, low nibble for even g            */
+ *                                         i*k/8 + g/2, low nibble for even g
+ *  TVW (nt stored tiles of tm x tk, mt = m / tm tile rows)
+ *    SPMM_ARRAY_ROW_PTR   int32[mt + 1]   stored tiles of tile row T: [row_ptr[T], row_ptr[T+1])
+ *    SPMM_ARRAY_COL_IDX   int32[nt]       tile column (k / tk units), ascending in a tile row
+ *    SPMM_ARRAY_VALS      int8[nt * tm * tk/2]  each stored tile in the 2:4 layout above,
+ *                                         tile row-major, rows of tk/2 kept values
+ *    SPMM_ARRAY_META      uint8[nt * tm * tk/8] each stored tile's nibbles, rows of tk/8 */
 typedef enum {
   SPMM_ARRAY_ROW_PTR = 0,
   SPMM_ARRAY_COL_IDX = 1,
@@ -119,6 +130,17 @@ typedef enum {
 spmm_status_t spmm_pack_bcsr(int64_t m, int64_t k, int32_t block_m, int32_t block_k,
                              spmm_dtype_t dtype, const void *a_host, int64_t lda,
                              spmm_matrix_t *out);
+
+/* Tile-vector-wise (the tile-wise pattern combined with 2:4 of "Accelerating
+ * Sparse DNNs Based on Tiled GEMM", abstract) from a dense row-major int8
+ * matrix a_host [m x k] (lda >= k): A is cut into tile_m x tile_k tiles, a
+ * tile is stored when any element is nonzero, and a stored tile is pruned
+ * 2:4 along k by the rule of spmm_pack_24.  The product is therefore the 2:4
+ * product with the zero tiles skipped.  Requires m % tile_m == 0,
+ * k % tile_k == 0 and tile_k % 8 == 0 (else INVALID_ARG); the kernels take
+ * 256 x 128 tiles (spmm_plan returns UNSUPPORTED for others). */
+spmm_status_t spmm_pack_tvw(int64_t m, int64_t k, const int8_t *a_host, int64_t lda, int32_t tile_m,
+                            int32_t tile_k, spmm_matrix_t *out);
 
 /* BCSR from a canonical CSR on the host (row_ptr, col_idx as for
  * spmm_pack_wcsr; vals bf16 bit patterns, uint16[nnz]).  A block is stored
@@ -177,7 +199,9 @@ void spmm_matrix_destroy(spmm_matrix_t a);
  *   BCSR (64 x 64 blocks): (BF16, BF16), n % 8 == 0
  *   WCSR:                  (F32, F32), any n >= 1
  *   2:4:                   (I8, I32), n % 16 == 0
- * anything else is UNSUPPORTED.  n = 0 is allowed (execute does nothing). */
+ *   TVW (256 x 128 tiles): (I8, I32), n % 16 == 0
+ * A BCSR matrix packed with reordering also gets a workspace for B's rows in
+ * the packed column order (k * n * 2 bytes).  Anything else is UNSUPPORTED.  n = 0 is allowed (execute does nothing). */
 spmm_status_t spmm_plan(spmm_matrix_t a, int64_t n, spmm_dtype_t b_dtype,
                         spmm_dtype_t c_dtype, int32_t device, spmm_plan_t *out);
 

@@ -373,6 +373,42 @@ spmm_status_t plan_24(spmm_plan_s *p) {
   L.n = p->n;
   L.m_pad = m_pad;
   L.k_pad = k_pad;
+  L.tile_ptr = nullptr;
+  L.tile_step = nullptr;
+  p->info.tile_m = sp24_tile_m();
+  p->info.tile_n = sp24_tile_n();
+  p->info.grid = sp24_grid(a.m, p->n);
+  return SPMM_OK;
+}
+
+// ---- tile-vector-wise plan: the stored tiles in the 2:4 kernel's layout ------
+spmm_status_t plan_tvw(spmm_plan_s *p) {
+  const Matrix &a = *p->a;
+  if (p->n % 16 != 0) return fail(SPMM_ERR_UNSUPPORTED, "spmm_plan: TVW needs n % 16 == 0");
+  if (a.bm != sp24_tile_m() || a.bk != sp24_tile_k())
+    return fail(SPMM_ERR_UNSUPPORTED, "spmm_plan: TVW kernels take 256 x 128 tiles");
+  const int64_t ntiles = static_cast<int64_t>(a.bcol_idx.size());
+  std::vector<int8_t> v(static_cast<size_t>(ntiles * a.bm * (a.bk / 2)));
+  std::vector<uint8_t> mt(static_cast<size_t>(ntiles * a.bm * (a.bk / 8)));
+  tvw_tile_layout(a.vals24.data(), a.meta24.data(), ntiles, v.data(), mt.data());
+  Sp24Launch &L = p->sp24;
+  spmm_status_t s;
+  int8_t *dv = nullptr;
+  uint8_t *dm = nullptr;
+  int32_t *tp = nullptr, *ts = nullptr;
+  if ((s = upload_vec(p, v, &dv)) != SPMM_OK) return s;
+  if ((s = upload_vec(p, mt, &dm)) != SPMM_OK) return s;
+  if ((s = upload_vec(p, a.brow_ptr, &tp)) != SPMM_OK) return s;
+  if ((s = upload_vec(p, a.bcol_idx, &ts)) != SPMM_OK) return s;
+  L.vals = dv;
+  L.meta = dm;
+  L.tile_ptr = tp;
+  L.tile_step = ts;
+  L.m = a.m;
+  L.k = a.k;
+  L.n = p->n;
+  L.m_pad = a.m;
+  L.k_pad = a.k;
   p->info.tile_m = sp24_tile_m();
   p->info.tile_n = sp24_tile_n();
   p->info.grid = sp24_grid(a.m, p->n);
@@ -415,6 +451,25 @@ spmm_status_t spmm_pack_bcsr(int64_t m, int64_t k, int32_t block_m, int32_t bloc
     auto *a = new spmm_matrix_s();
     spmm_status_t s = pack_bcsr_bf16(m, k, block_m, block_k,
                                      static_cast<const uint16_t *>(a_host), lda, *a);
+    if (s != SPMM_OK) {
+      delete a;
+      return s;
+    }
+    *out = a;
+    return SPMM_OK;
+  });
+}
+
+spmm_status_t spmm_pack_tvw(int64_t m, int64_t k, const int8_t *a_host, int64_t lda, int32_t tile_m,
+                            int32_t tile_k, spmm_matrix_t *out) {
+  if (!out) return fail(SPMM_ERR_INVALID_ARG, "spmm_pack_tvw: out is NULL");
+  *out = nullptr;
+  if (m < 0 || k < 0 || m > INT32_MAX || k > INT32_MAX || tile_m <= 0 || tile_k <= 0 ||
+      tile_k % 8 != 0 || m % tile_m != 0 || k % tile_k != 0 || lda < k || (m * k > 0 && !a_host))
+    return fail(SPMM_ERR_INVALID_ARG, "spmm_pack_tvw: bad shape, tile, lda or pointer");
+  return guarded([&]() -> spmm_status_t {
+    auto *a = new spmm_matrix_s();
+    spmm_status_t s = pack_tvw_i8(m, k, a_host, lda, tile_m, tile_k, *a);
     if (s != SPMM_OK) {
       delete a;
       return s;
@@ -503,7 +558,7 @@ spmm_status_t spmm_matrix_info(spmm_matrix_t a, spmm_matrix_info_t *info) {
   info->m = a->m;
   info->k = a->k;
   info->nnz = a->nnz;
-  if (a->format == SPMM_FORMAT_BCSR) {
+  if (a->format == SPMM_FORMAT_BCSR || a->format == SPMM_FORMAT_TVW) {
     info->nnzb = static_cast<int64_t>(a->bcol_idx.size());
     info->block_m = a->bm;
     info->block_k = a->bk;
@@ -545,6 +600,12 @@ spmm_status_t spmm_matrix_array(spmm_matrix_t a, int32_t which, const void **dat
       if (which == SPMM_ARRAY_VALS) return give(a->vals24);
       if (which == SPMM_ARRAY_META) return give(a->meta24);
       break;
+    case SPMM_FORMAT_TVW:
+      if (which == SPMM_ARRAY_ROW_PTR) return give(a->brow_ptr);
+      if (which == SPMM_ARRAY_COL_IDX) return give(a->bcol_idx);
+      if (which == SPMM_ARRAY_VALS) return give(a->vals24);
+      if (which == SPMM_ARRAY_META) return give(a->meta24);
+      break;
   }
   return fail(SPMM_ERR_INVALID_ARG, "spmm_matrix_array: no such array for this format");
 }
@@ -559,7 +620,8 @@ spmm_status_t spmm_plan(spmm_matrix_t a, int64_t n, spmm_dtype_t b_dtype, spmm_d
   const bool ok_types =
       (a->format == SPMM_FORMAT_BCSR && b_dtype == SPMM_BF16 && c_dtype == SPMM_BF16) ||
       (a->format == SPMM_FORMAT_WCSR && b_dtype == SPMM_F32 && c_dtype == SPMM_F32) ||
-      (a->format == SPMM_FORMAT_24 && b_dtype == SPMM_I8 && c_dtype == SPMM_I32);
+      ((a->format == SPMM_FORMAT_24 || a->format == SPMM_FORMAT_TVW) && b_dtype == SPMM_I8 &&
+       c_dtype == SPMM_I32);
   if (!ok_types) return fail(SPMM_ERR_UNSUPPORTED, "spmm_plan: unsupported (format, B, C) types");
   int ndev = 0;
   hipError_t e = hipGetDeviceCount(&ndev);
@@ -582,6 +644,7 @@ spmm_status_t spmm_plan(spmm_matrix_t a, int64_t n, spmm_dtype_t b_dtype, spmm_d
     try {
       if (a->format == SPMM_FORMAT_BCSR) s = plan_bcsr(p);
       else if (a->format == SPMM_FORMAT_WCSR) s = plan_wcsr(p);
+      else if (a->format == SPMM_FORMAT_TVW) s = plan_tvw(p);
       else s = plan_24(p);
     } catch (...) {
       free_plan(p);
@@ -615,7 +678,9 @@ spmm_status_t spmm_execute(spmm_plan_t p, const void *b_dev, int64_t ldb, void *
   const Matrix &a = *p->a;
   const int64_t n = p->n;
   if (n == 0 || a.m == 0) return SPMM_OK;
-  const int64_t eb = a.format == SPMM_FORMAT_BCSR ? 2 : (a.format == SPMM_FORMAT_24 ? 1 : 4);
+  const int64_t eb = a.format == SPMM_FORMAT_BCSR
+                         ? 2
+                         : ((a.format == SPMM_FORMAT_24 || a.format == SPMM_FORMAT_TVW) ? 1 : 4);
   const int64_t ec = a.format == SPMM_FORMAT_BCSR ? 2 : 4;
   if (!c_dev || (!b_dev && a.k > 0))
     return fail(SPMM_ERR_INVALID_ARG, "spmm_execute: B or C is NULL");

@@ -42,7 +42,8 @@ struct Matrix {
   std::vector<float> vals;
   std::vector<int32_t> chunk_window;
   std::vector<int64_t> chunk_begin;
-  // 2:4
+  // 2:4 (and the stored tiles of tile-vector-wise: brow_ptr / bcol_idx over
+  // tiles of bm x bk, vals24 / meta24 tile after tile)
   std::vector<int8_t> vals24;
   std::vector<uint8_t> meta24;
 };
@@ -57,6 +58,8 @@ spmm_status_t pack_wcsr_f32(int64_t m, int64_t k, const int64_t *row_ptr,
                             const int32_t *col_idx, const float *vals, int32_t W,
                             int64_t T, Matrix &out);
 spmm_status_t pack_24_i8(int64_t m, int64_t k, const int8_t *a, int64_t lda, Matrix &out);
+spmm_status_t pack_tvw_i8(int64_t m, int64_t k, const int8_t *a, int64_t lda, int32_t tm,
+                          int32_t tk, Matrix &out);
 spmm_status_t pack_bcsr_csr_bf16(int64_t m, int64_t k, const int64_t *row_ptr,
                                  const int32_t *col_idx, const uint16_t *vals, int32_t bm,
                                  int32_t bk, bool reorder, Matrix &out);
@@ -174,8 +177,12 @@ int sddmm_bcsr_group();
 hipError_t launch_sddmm_bcsr(const SddmmBcsrLaunch &a, hipStream_t s);
 
 struct Sp24Launch {
-  const int8_t *vals;   // tiled copy of the values (sp24_tile_layout)
+  const int8_t *vals;   // tiled copy of the values (sp24_tile_layout / tvw_tile_layout)
   const uint8_t *meta;  // tiled copy of the index words
+  // tile-vector-wise A: stored k-steps of row tile T are
+  // tile_step[tile_ptr[T] .. tile_ptr[T+1]); null for a plain 2:4 A
+  const int32_t *tile_ptr;
+  const int32_t *tile_step;
   int64_t m, k, n;
   int64_t m_pad, k_pad;
   const int8_t *B;
@@ -189,6 +196,11 @@ struct Sp24Launch {
 // bytes, meta_tiled: m_pad * k_pad / 8 bytes).
 void sp24_tile_layout(const int8_t *vals, const uint8_t *meta, int64_t m, int64_t k,
                       int64_t m_pad, int64_t k_pad, int8_t *vals_tiled, uint8_t *meta_tiled);
+// The same layout for the stored tiles of a tile-vector-wise matrix, given
+// per tile as [256][64] values and [256][16] index bytes (ntiles * 16 KB and
+// ntiles * 4 KB out).
+void tvw_tile_layout(const int8_t *tile_vals, const uint8_t *tile_meta, int64_t ntiles,
+                     int8_t *vals_tiled, uint8_t *meta_tiled);
 int sp24_tile_m();
 int sp24_tile_n();
 int sp24_tile_k();

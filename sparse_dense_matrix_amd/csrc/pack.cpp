@@ -281,6 +281,33 @@ spmm_status_t pack_bcsr_csr_bf16(int64_t m, int64_t k, const int64_t *row_ptr,
 // are kept (larger magnitude first, ties to the lower position), then stored
 // in ascending position.
 // ---------------------------------------------------------------------------
+static inline void prune_group(const int8_t *grp, int8_t *kept, uint8_t &nibble) {
+  int key[4];
+  for (int t = 0; t < 4; ++t) {
+    const int x = grp[t];
+    key[t] = (x < 0 ? -x : x) * 4 + (3 - t);
+  }
+  int first = 0;
+  for (int t = 1; t < 4; ++t)
+    if (key[t] > key[first]) first = t;
+  int second = first == 0 ? 1 : 0;
+  for (int t = 0; t < 4; ++t)
+    if (t != first && key[t] > key[second]) second = t;
+  const int lo = std::min(first, second), hi = std::max(first, second);
+  kept[0] = grp[lo];
+  kept[1] = grp[hi];
+  nibble = static_cast<uint8_t>(lo | (hi << 2));
+}
+
+// one row of `len` elements (len % 8 == 0) into len/2 values and len/8 bytes
+static void prune_row(const int8_t *row, int64_t len, int8_t *v, uint8_t *mt) {
+  for (int64_t g = 0; g < len / 4; ++g) {
+    uint8_t nibble;
+    prune_group(row + 4 * g, v + 2 * g, nibble);
+    mt[g >> 1] = static_cast<uint8_t>(mt[g >> 1] | (nibble << ((g & 1) * 4)));
+  }
+}
+
 spmm_status_t pack_24_i8(int64_t m, int64_t k, const int8_t *a, int64_t lda, Matrix &out) {
   out.format = SPMM_FORMAT_24;
   out.dtype = SPMM_I8;
@@ -289,29 +316,57 @@ spmm_status_t pack_24_i8(int64_t m, int64_t k, const int8_t *a, int64_t lda, Mat
   out.nnz = m * (k / 2);
   out.vals24.assign(static_cast<size_t>(m * (k / 2)), 0);
   out.meta24.assign(static_cast<size_t>(m * (k / 8)), 0);
-  for (int64_t i = 0; i < m; ++i) {
-    const int8_t *row = a + i * lda;
-    int8_t *v = out.vals24.data() + i * (k / 2);
-    uint8_t *mt = out.meta24.data() + i * (k / 8);
-    for (int64_t g = 0; g < k / 4; ++g) {
-      int key[4];
-      for (int t = 0; t < 4; ++t) {
-        const int x = row[4 * g + t];
-        key[t] = (x < 0 ? -x : x) * 4 + (3 - t);
+  for (int64_t i = 0; i < m; ++i)
+    prune_row(a + i * lda, k, out.vals24.data() + i * (k / 2), out.meta24.data() + i * (k / 8));
+  return SPMM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Tile-vector-wise (the tiled-GEMM page, abstract): A is cut into tm x tk
+// tiles; a tile is stored when any element is nonzero, and a stored tile is
+// pruned 2:4 along k exactly as above.  Since 2:4 pruning maps a zero tile
+// to zero and keeps a nonzero in every nonzero group, the stored product is
+// the 2:4 product of A with the zero tiles skipped.
+// ---------------------------------------------------------------------------
+spmm_status_t pack_tvw_i8(int64_t m, int64_t k, const int8_t *a, int64_t lda, int32_t tm,
+                          int32_t tk, Matrix &out) {
+  const int64_t mt = m / tm, kt = k / tk;
+  out.format = SPMM_FORMAT_TVW;
+  out.dtype = SPMM_I8;
+  out.m = m;
+  out.k = k;
+  out.bm = tm;
+  out.bk = tk;
+  out.brow_ptr.assign(mt + 1, 0);
+  out.bcol_idx.clear();
+  out.vals24.clear();
+  out.meta24.clear();
+  const int64_t tv = static_cast<int64_t>(tm) * (tk / 2), tmeta = static_cast<int64_t>(tm) * (tk / 8);
+  for (int64_t T = 0; T < mt; ++T) {
+    for (int64_t s = 0; s < kt; ++s) {
+      bool any = false;
+      for (int64_t i = T * tm; i < (T + 1) * tm && !any; ++i) {
+        const int8_t *row = a + i * lda + s * tk;
+        for (int32_t j = 0; j < tk; ++j)
+          if (row[j] != 0) {
+            any = true;
+            break;
+          }
       }
-      int first = 0;
-      for (int t = 1; t < 4; ++t)
-        if (key[t] > key[first]) first = t;
-      int second = first == 0 ? 1 : 0;
-      for (int t = 0; t < 4; ++t)
-        if (t != first && key[t] > key[second]) second = t;
-      const int lo = std::min(first, second), hi = std::max(first, second);
-      v[2 * g] = row[4 * g + lo];
-      v[2 * g + 1] = row[4 * g + hi];
-      const uint8_t nibble = static_cast<uint8_t>(lo | (hi << 2));
-      mt[g >> 1] = static_cast<uint8_t>(mt[g >> 1] | (nibble << ((g & 1) * 4)));
+      if (!any) continue;
+      if (out.bcol_idx.size() >= static_cast<size_t>(INT32_MAX))
+        return fail(SPMM_ERR_UNSUPPORTED, "spmm_pack_tvw: more than 2^31-1 tiles");
+      const size_t v0 = out.vals24.size(), m0 = out.meta24.size();
+      out.vals24.resize(v0 + static_cast<size_t>(tv), 0);
+      out.meta24.resize(m0 + static_cast<size_t>(tmeta), 0);
+      for (int32_t r = 0; r < tm; ++r)
+        prune_row(a + (T * tm + r) * lda + s * tk, tk, out.vals24.data() + v0 + r * (tk / 2),
+                  out.meta24.data() + m0 + r * (tk / 8));
+      out.bcol_idx.push_back(static_cast<int32_t>(s));
     }
+    out.brow_ptr[T + 1] = static_cast<int32_t>(out.bcol_idx.size());
   }
+  out.nnz = static_cast<int64_t>(out.bcol_idx.size()) * tv;
   return SPMM_OK;
 }
 

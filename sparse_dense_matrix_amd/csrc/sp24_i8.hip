@@ -25,6 +25,13 @@
 // are XOR-swizzled by k-row so the transpose reads are bank-conflict free.
 // The tile order groups 4 row tiles with every column tile on one XCD, so A
 // panels are shared 8-fold and B panels 4-fold in that XCD's L2.
+//
+// The same kernel runs the tile-vector-wise pattern of the tiled-GEMM page
+// (abstract: tile-wise sparsity at the global-memory level combined with 2:4
+// at the register level): A is cut into tiles of one row tile (256 rows) by
+// one k-step (128), only the tiles holding a nonzero are stored (2:4 inside),
+// and a per-row-tile table lists their k-steps; the kernel walks that list
+// instead of every k-step, so a zero tile is never loaded.
 #include "internal.h"
 
 // load_lds below names m0 as clobbered on purpose (it sets m0 for the
@@ -90,10 +97,16 @@ __device__ __forceinline__ int quad_swap(int v) {
   return __builtin_amdgcn_mov_dpp(v, perm, 0xF, 0xF, false);
 }
 
+// kTiles: A is tile-vector-wise; row tile T holds the stored k-steps
+// tile_step[tile_ptr[T] .. tile_ptr[T+1]), their values and index words in
+// that order.  Otherwise every k-step of every row tile is stored.
+template <bool kTiles>
 __global__ __launch_bounds__(kThreads) void sp24_i8_smfmac(
-    const int8_t *__restrict__ vals, const uint8_t *__restrict__ meta, int64_t m, int64_t k,
-    int64_t n, int64_t k_pad, int32_t mtiles, int32_t ntiles, int32_t tiles, int32_t per_xcd,
-    const int8_t *__restrict__ B, int64_t ldb, int32_t *__restrict__ C, int64_t ldc) {
+    const int8_t *__restrict__ vals, const uint8_t *__restrict__ meta,
+    const int32_t *__restrict__ tile_ptr, const int32_t *__restrict__ tile_step, int64_t m,
+    int64_t k, int64_t n, int64_t k_pad, int32_t mtiles, int32_t ntiles, int32_t tiles,
+    int32_t per_xcd, const int8_t *__restrict__ B, int64_t ldb, int32_t *__restrict__ C,
+    int64_t ldc) {
   extern __shared__ __attribute__((aligned(1024))) char lds[];
 
   // logical tile t: groups of kMG row tiles x every column tile, contiguous
@@ -109,10 +122,22 @@ __global__ __launch_bounds__(kThreads) void sp24_i8_smfmac(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
-  const int64_t ksteps = k_pad / kTK;
-  // this row tile's tiled values and index words
-  const int8_t *vt = vals + (m0 / kTM) * ksteps * kAVBytes;
-  const uint8_t *mtl = meta + (m0 / kTM) * ksteps * kAMBytes;
+  // this row tile's stored k-steps and their tiled values and index words
+  int64_t first, ksteps;
+  if constexpr (kTiles) {
+    first = tile_ptr[m0 / kTM];
+    ksteps = tile_ptr[m0 / kTM + 1] - first;
+  } else {
+    ksteps = k_pad / kTK;
+    first = (m0 / kTM) * ksteps;
+  }
+  const int8_t *vt = vals + first * kAVBytes;
+  const uint8_t *mtl = meta + first * kAMBytes;
+  // k-step of B for the ks-th stored step
+  auto kstep = [&](int64_t ks) -> int64_t {
+    if constexpr (kTiles) return tile_step[first + ks];
+    else return ks;
+  };
 
   // Loads of one k-step, per wave: A values 2 x 1 KB and half a KB of index
   // words, all consecutive bytes of the tiled copies; B 4 x 1 KB (4 k-rows x
@@ -141,7 +166,7 @@ __global__ __launch_bounds__(kThreads) void sp24_i8_smfmac(
       // k-rows past k (the last step when k % 128 != 0) are read from row 0:
       // the matching A values are zero-padded, so they add nothing
       const int i = part - 3;
-      const int64_t krow0 = ks * kTK;
+      const int64_t krow0 = kstep(ks) * kTK;
       const int r = (wave * 4 + i) * 4 + (lane >> 4);
       const uint32_t off = krow0 + r < k ? static_cast<uint32_t>(krow0 * ldb) + b_off[i]
                                          : b_off[i] - static_cast<uint32_t>(r * ldb);
@@ -247,36 +272,51 @@ __global__ __launch_bounds__(kThreads) void sp24_i8_smfmac(
 
 }  // namespace
 
+// One (row tile, k-step) piece of the plan layout.  v points at the piece's
+// first compressed value (row stride vs bytes), mt at its first index byte
+// (row stride ms); rows >= rows_ok and value / index columns >= vcols /
+// mcols read as zero.
+static void sp24_piece(const int8_t *v, int64_t vs, const uint8_t *mt, int64_t ms, int64_t rows_ok,
+                       int64_t vcols, int64_t mcols, int8_t *vdst, uint8_t *mdst) {
+  // values: [16-row tile][lane][16 bytes], lane l holding row l%16 and
+  // bytes 16*(l/16).. of the step's 64 compressed bytes
+  for (int t16 = 0; t16 < kTM / 16; ++t16)
+    for (int l = 0; l < 64; ++l) {
+      const int64_t row = t16 * 16 + (l & 15);
+      const int64_t c0 = (l >> 4) * 16;
+      for (int b = 0; b < 16; ++b)
+        vdst[(t16 * 64 + l) * 16 + b] =
+            (row < rows_ok && c0 + b < vcols) ? v[row * vs + c0 + b] : int8_t(0);
+    }
+  // index words: [row half wm 2][lane 64][row tile i 8][4 bytes]; lane l of
+  // row half wm gets, for its 8 row tiles, word l/16 of row (8*wm + i)*16 + l%16
+  for (int wm = 0; wm < 2; ++wm)
+    for (int l = 0; l < 64; ++l)
+      for (int i = 0; i < 8; ++i) {
+        const int64_t row = (wm * 8 + i) * 16 + (l & 15);
+        const int64_t c0 = (l >> 4) * 4;
+        for (int b = 0; b < 4; ++b)
+          mdst[((wm * 64 + l) * 8 + i) * 4 + b] =
+              (row < rows_ok && c0 + b < mcols) ? mt[row * ms + c0 + b] : uint8_t(0);
+      }
+}
+
 void sp24_tile_layout(const int8_t *vals, const uint8_t *meta, int64_t m, int64_t k,
                       int64_t m_pad, int64_t k_pad, int8_t *vals_tiled, uint8_t *meta_tiled) {
   const int64_t ksteps = k_pad / kTK;
   for (int64_t t = 0; t < m_pad / kTM; ++t)
-    for (int64_t s = 0; s < ksteps; ++s) {
-      int8_t *vdst = vals_tiled + (t * ksteps + s) * kAVBytes;
-      uint8_t *mdst = meta_tiled + (t * ksteps + s) * kAMBytes;
-      // values: [16-row tile][lane][16 bytes], lane l holding row l%16 and
-      // bytes 16*(l/16).. of the step's 64 compressed bytes
-      for (int mt = 0; mt < kTM / 16; ++mt)
-        for (int l = 0; l < 64; ++l) {
-          const int64_t row = t * kTM + mt * 16 + (l & 15);
-          const int64_t c0 = s * (kTK / 2) + (l >> 4) * 16;
-          for (int b = 0; b < 16; ++b)
-            vdst[(mt * 64 + l) * 16 + b] =
-                (row < m && c0 + b < k / 2) ? vals[row * (k / 2) + c0 + b] : int8_t(0);
-        }
-      // index words: [row half wm 2][lane 64][row tile i 8][4 bytes]; lane l
-      // of row half wm gets, for its 8 row tiles, word l/16 of row
-      // (8*wm + i)*16 + l%16
-      for (int wm = 0; wm < 2; ++wm)
-        for (int l = 0; l < 64; ++l)
-          for (int i = 0; i < 8; ++i) {
-            const int64_t row = t * kTM + (wm * 8 + i) * 16 + (l & 15);
-            const int64_t c0 = s * (kTK / 8) + (l >> 4) * 4;
-            for (int b = 0; b < 4; ++b)
-              mdst[((wm * 64 + l) * 8 + i) * 4 + b] =
-                  (row < m && c0 + b < k / 8) ? meta[row * (k / 8) + c0 + b] : uint8_t(0);
-          }
-    }
+    for (int64_t s = 0; s < ksteps; ++s)
+      sp24_piece(vals + t * kTM * (k / 2) + s * (kTK / 2), k / 2,
+                 meta + t * kTM * (k / 8) + s * (kTK / 8), k / 8, m - t * kTM,
+                 k / 2 - s * (kTK / 2), k / 8 - s * (kTK / 8),
+                 vals_tiled + (t * ksteps + s) * kAVBytes, meta_tiled + (t * ksteps + s) * kAMBytes);
+}
+
+void tvw_tile_layout(const int8_t *tile_vals, const uint8_t *tile_meta, int64_t ntiles,
+                     int8_t *vals_tiled, uint8_t *meta_tiled) {
+  for (int64_t t = 0; t < ntiles; ++t)
+    sp24_piece(tile_vals + t * kTM * (kTK / 2), kTK / 2, tile_meta + t * kTM * (kTK / 8), kTK / 8,
+               kTM, kTK / 2, kTK / 8, vals_tiled + t * kAVBytes, meta_tiled + t * kAMBytes);
 }
 
 int sp24_tile_m() { return kTM; }
@@ -288,22 +328,28 @@ int64_t sp24_grid(int64_t m, int64_t n) {
   return 8 * ((tiles + 7) / 8);
 }
 
-hipError_t launch_sp24_i8(const Sp24Launch &a, hipStream_t s) {
+template <bool kTiles>
+hipError_t launch(const Sp24Launch &a, hipStream_t s) {
   const int64_t mtiles = (a.m + kTM - 1) / kTM;
   const int64_t ntiles = (a.n + kTN - 1) / kTN;
   const int64_t tiles = mtiles * ntiles;
   if (tiles == 0) return hipSuccess;
   if (tiles > INT32_MAX / 2 || a.k_pad * a.ldb > UINT32_MAX)
     return hipErrorInvalidValue;
-  hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(&sp24_i8_smfmac), kLdsBytes);
+  hipError_t e =
+      allow_dynamic_lds(reinterpret_cast<const void *>(&sp24_i8_smfmac<kTiles>), kLdsBytes);
   if (e != hipSuccess) return e;
   const int64_t per_xcd = (tiles + 7) / 8;
-  hipLaunchKernelGGL(sp24_i8_smfmac, dim3(static_cast<unsigned>(8 * per_xcd)), dim3(kThreads),
-                     kLdsBytes, s, a.vals, a.meta, a.m, a.k, a.n, a.k_pad,
-                     static_cast<int32_t>(mtiles), static_cast<int32_t>(ntiles),
+  hipLaunchKernelGGL(sp24_i8_smfmac<kTiles>, dim3(static_cast<unsigned>(8 * per_xcd)),
+                     dim3(kThreads), kLdsBytes, s, a.vals, a.meta, a.tile_ptr, a.tile_step, a.m,
+                     a.k, a.n, a.k_pad, static_cast<int32_t>(mtiles), static_cast<int32_t>(ntiles),
                      static_cast<int32_t>(tiles), static_cast<int32_t>(per_xcd), a.B, a.ldb, a.C,
                      a.ldc);
   return hipGetLastError();
+}
+
+hipError_t launch_sp24_i8(const Sp24Launch &a, hipStream_t s) {
+  return a.tile_ptr ? launch<true>(a, s) : launch<false>(a, s);
 }
 
 }  // namespace sdm

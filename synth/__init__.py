@@ -154,6 +154,20 @@ def block_sparse_dense_bf16(m: int, k: int, bm: int, bk: int, nblocks: int,
     return a, ids
 
 
+def tile_sparse_i8(m: int, k: int, tm: int, tk: int, ntiles: int, seed: int) -> np.ndarray:
+    """Dense int8 [m x k] that is zero except on exactly `ntiles` tm x tk
+    tiles chosen uniformly without replacement, whose values are uniform on
+    {-127 ... 127}.  (The 2:4 pruning inside the tiles is the packer's job.)"""
+    mt, kt = m // tm, k // tk
+    ids = np.sort(rng(seed, S_PATTERN).choice(mt * kt, size=ntiles, replace=False))
+    vals = int8_uniform(rng(seed, S_AVAL), (ntiles, tm, tk))
+    a = np.zeros((m, k), dtype=np.int8)
+    for t, b in enumerate(ids):
+        r, c = divmod(int(b), kt)
+        a[r * tm:(r + 1) * tm, c * tk:(c + 1) * tk] = vals[t]
+    return a
+
+
 def scrambled_csr_bf16(a_bits: np.ndarray, seed: int):
     """A dense bf16 matrix (uint16 bits) with its rows and columns shuffled by
     seeded random permutations, as a canonical CSR (row_ptr int64, col_idx
@@ -193,7 +207,7 @@ def dense_f32_normal(rows: int, cols: int, seed: int, stream: int = S_BVAL) -> n
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    fmt: str            # "wcsr" | "bcsr" | "bcsr_csr" | "sp24" | "sddmm" | "sddmm_bcsr"
+    fmt: str            # "wcsr" | "bcsr" | "bcsr_csr" | "sp24" | "tvw" | "sddmm" | "sddmm_bcsr"
     m: int
     k: int
     n: int
@@ -223,6 +237,9 @@ def _bcsr(name, m, k, n, zero_frac, seed, block=64, fmt="bcsr", elem=""):
                     nblocks=int(round((1.0 - zero_frac) * total)), elem=elem)
 
 
+# tile shape of the tile-vector-wise workloads (the 2:4 kernel's A tile)
+TVW_TILE_M, TVW_TILE_K = 256, 128
+
 # The five benchmark shapes (seed 20260000 + index) ...
 WORKLOADS: Dict[str, Workload] = {
     "csr_tiny_256": Workload("csr_tiny_256", "wcsr", 256, 256, 64, 20260001, density=0.05),
@@ -236,6 +253,10 @@ WORKLOADS: Dict[str, Workload] = {
                                          20260006),
     "bcsr_prefill_18944x3584_z70": _bcsr("bcsr_prefill_18944x3584_z70", 18944, 3584, 65536, 0.70,
                                          20260007),
+    # tile-vector-wise: the 8192 x 8192 int8 weight with half / three quarters
+    # of its 256 x 128 tiles zero (2:4 inside the rest), same B as the 2:4 case
+    "tvw_i8_8192_t50": Workload("tvw_i8_8192_t50", "tvw", 8192, 8192, 2048, 20260009, nblocks=1024),
+    "tvw_i8_8192_t75": Workload("tvw_i8_8192_t75", "tvw", 8192, 8192, 2048, 20260010, nblocks=512),
     # the 4096 block-sparse matrix with rows and columns shuffled, given as
     # CSR: packed as BCSR with and without the reordering, and as WCSR
     "scrambled_4096_bcsr_reordered": Workload("scrambled_4096_bcsr_reordered", "bcsr_csr", 4096,
@@ -269,6 +290,7 @@ SMALL: Dict[str, Workload] = {
                             band_half=64),
     "sddmm_bcsr_small": _bcsr("sddmm_bcsr_small", 640, 512, 1000, 0.7, 35, fmt="sddmm_bcsr",
                               elem="bf16"),
+    "tvw_small": Workload("tvw_small", "tvw", 512, 1024, 272, 38, nblocks=6),
     "scrambled_small": Workload("scrambled_small", "bcsr_csr", 1024, 768, 520, 36, nblocks=30,
                                 scramble=37, reorder=True),
 }
@@ -295,6 +317,8 @@ def make_a(w: Workload) -> dict:
         return {"dense": a, "block_ids": ids}
     if w.fmt == "sp24":
         return {"dense": int8_uniform(rng(w.seed, S_AVAL), (w.m, w.k))}
+    if w.fmt == "tvw":
+        return {"dense": tile_sparse_i8(w.m, w.k, TVW_TILE_M, TVW_TILE_K, w.nblocks, w.seed)}
     raise ValueError(w.fmt)
 
 
@@ -323,6 +347,6 @@ def make_b(w: Workload, n: int | None = None) -> np.ndarray:
         return dense_f32_normal(w.k, n, w.seed)
     if w.fmt == "bcsr":
         return dense_bf16_normal(w.k, n, w.seed)
-    if w.fmt == "sp24":
+    if w.fmt in ("sp24", "tvw"):
         return int8_uniform(rng(w.seed, S_BVAL), (w.k, n))
     raise ValueError(w.fmt)

@@ -603,3 +603,62 @@ def test_reordered_pattern_has_no_sddmm(S, orc):
     with pytest.raises(S.SpmmError) as ei:
         S.spmm_plan_sddmm(M, 64, S.BF16)
     assert ei.value.name == "SPMM_ERR_UNSUPPORTED"
+
+
+# ---------------------------------------------------------------------------
+# tile-vector-wise int8: the 2:4 kernel walking only the stored tiles
+# ---------------------------------------------------------------------------
+
+def tvw_case(S, orc, a, B, rows=None, pad=0):
+    m, n = a.shape[0], B.shape[1]
+    M = S.spmm_pack_tvw(a, 256, 128)
+    P = S.spmm_plan(M, n, S.I8, S.I32)
+    got = run(S, P, B, m, n, "i32", pad)
+    v, mt = orc.pack24(a)
+    ref = orc.sp24_spmm(v, mt, B, rows=rows)
+    np.testing.assert_array_equal(got if rows is None else got[rows], ref)
+    return M
+
+
+def test_tvw_small(S, orc):
+    w = synth.SMALL["tvw_small"]        # 512 x 1024, 6 of 16 tiles stored, n = 272
+    a = synth.make_a(w)["dense"]
+    B = synth.make_b(w)
+    for pad in (0, 16):
+        M = tvw_case(S, orc, a, B, pad=pad)
+    assert S.spmm_matrix_info(M)["nnzb"] == w.nblocks
+
+
+def test_tvw_empty_rows_full_rows_and_extremes(S, orc):
+    # tile row 0 empty, tile row 1 full, tile row 2 a single tile of -128s
+    a = np.zeros((768, 512), np.int8)
+    a[256:512] = synth.int8_uniform(np.random.default_rng(4), (256, 512))
+    a[512:768, 128:256] = -128
+    B = np.full((512, 64), -128, np.int8)
+    B[:, 32:] = synth.int8_uniform(np.random.default_rng(5), (512, 32))
+    tvw_case(S, orc, a, B)
+    # no stored tile at all: C is zero
+    Z = np.zeros((256, 256), np.int8)
+    M = S.spmm_pack_tvw(Z, 256, 128)
+    P = S.spmm_plan(M, 32, S.I8, S.I32)
+    got = run(S, P, synth.int8_uniform(np.random.default_rng(6), (256, 32)), 256, 32, "i32")
+    assert (got == 0).all()
+
+
+def test_tvw_unsupported_tile(S, orc):
+    M = S.spmm_pack_tvw(np.ones((128, 128), np.int8), 64, 64)
+    with pytest.raises(S.SpmmError) as ei:
+        S.spmm_plan(M, 32, S.I8, S.I32)
+    assert ei.value.name == "SPMM_ERR_UNSUPPORTED"
+
+
+@pytest.mark.parametrize("name", ["tvw_i8_8192_t50", "tvw_i8_8192_t75"])
+def test_tvw_8192_sampled(S, orc, name):
+    w = synth.WORKLOADS[name]
+    a = synth.make_a(w)["dense"]
+    B = synth.make_b(w)
+    r = np.random.default_rng(23)
+    rows = np.unique(np.concatenate([np.arange(16), np.arange(w.m - 16, w.m),
+                                     r.choice(w.m, 96, replace=False)])).astype(np.int64)
+    M = tvw_case(S, orc, a, B, rows=rows)
+    _say(f"{name} tiles={S.spmm_matrix_info(M)['nnzb']} rows={len(rows)} exact")

@@ -55,6 +55,7 @@ def lib():
             "orc_csr_densify": (None, [i64, i64, P, P, P, P]),
             "orc_pack24": (C.c_int, [i64, i64, P, i64, P, P]),
             "orc_densify24": (None, [i64, i64, P, P, P]),
+            "orc_prune_nm": (C.c_int, [i64, i64, P, i64, C.c_int, C.c_int, P]),
             "orc_csr_spmm_rows": (None, [P, P, P, P, i64, i64, P, i64, i64, P]),
             "orc_bcsr_spmm_rows": (None, [i32, i32, P, P, P, P, i64, i64, P, i64, i64, P]),
             "orc_sp24_spmm_rows": (i64, [i64, P, P, P, i64, i64, P, i64, i64, P]),
@@ -181,6 +182,17 @@ def densify24(vals, meta) -> np.ndarray:
     m, k = v.shape[0], v.shape[1] * 2
     out = np.empty((m, k), dtype=np.int8)
     lib().orc_densify24(m, k, _p(v), _p(mt), _p(out))
+    return out
+
+
+def prune_nm(a: np.ndarray, keep: int, group: int) -> np.ndarray:
+    """Dense int8 with only the `keep` largest |a| of every `group`
+    consecutive elements of a row kept (ties to the lower position)."""
+    a = _c(a, np.int8)
+    m, k = a.shape
+    out = np.empty((m, k), dtype=np.int8)
+    if lib().orc_prune_nm(m, k, _p(a), k, keep, group, _p(out)) != 0:
+        raise ValueError("k must be a multiple of the group, group <= 64")
     return out
 
 

@@ -359,6 +359,32 @@ int64_t orc_sddmm_bcsr_i8(int32_t bm, int32_t bk, const int32_t *row_ptr, const 
   return overflow;
 }
 
+/* N:M pruning [DP N:M entry; the (2N-2):2N family on the same page]: in    */
+/* every group of `group` consecutive elements of a row keep the `keep` of   */
+/* largest |a| (as integers: |-128| = 128), ties to the lower position; the  */
+/* others become zero.  keep = 2, group = 4 is the 2:4 rule above.            */
+int orc_prune_nm(int64_t m, int64_t k, const int8_t *a, int64_t lda, int keep, int group,
+                 int8_t *out) {
+  if (group <= 0 || group > 64 || keep < 0 || keep > group || k % group != 0 || lda < k) return -1;
+  for (int64_t i = 0; i < m; ++i)
+    for (int64_t g = 0; g < k / group; ++g) {
+      const int8_t *grp = a + i * lda + g * group;
+      int8_t *dst = out + i * k + g * group;
+      /* position t is kept iff fewer than `keep` positions rank before it,
+         where u ranks before t when |a_u| > |a_t|, or equal and u < t */
+      for (int t = 0; t < group; ++t) {
+        int before = 0;
+        const int at = abs((int)grp[t]);
+        for (int u = 0; u < group; ++u) {
+          const int au = abs((int)grp[u]);
+          if (au > at || (au == at && u < t)) ++before;
+        }
+        dst[t] = before < keep ? grp[t] : 0;
+      }
+    }
+  return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Brute force: dense naive triple loops, i then j then k.                   */
 /* ------------------------------------------------------------------------ */

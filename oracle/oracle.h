@@ -82,6 +82,12 @@ int orc_pack24(int64_t m, int64_t k, const int8_t *a, int64_t lda,
 void orc_densify24(int64_t m, int64_t k, const int8_t *vals, const uint8_t *meta,
                    int8_t *out);
 
+/* N:M pruning: keep the `keep` largest |a| of every `group` consecutive
+ * elements of a row (ties to the lower position), zero the rest; out is
+ * dense int8 [m][k].  Returns -1 for a bad group (k % group != 0, group > 64). */
+int orc_prune_nm(int64_t m, int64_t k, const int8_t *a, int64_t lda, int keep, int group,
+                 int8_t *out);
+
 /* ---- reference products [AS abstract; MC abstract; DP SpMM entry] ------- */
 /* out[r][j - j0] = sum over stored (rows[r], c) in ascending c of
  * A[rows[r]][c] * B[c][j], for j in [j0, j1).  out is row-major with

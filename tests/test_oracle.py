@@ -413,3 +413,47 @@ def test_sddmm_bcsr_closed_forms(orc):
     # an empty pattern gives no blocks
     z = orc.sddmm_bcsr(bm, bk, np.zeros(4, np.int32), np.zeros(0, np.int32), Xh, Yb)
     assert z.shape == (0, bm, bk)
+
+
+# ---- N:M pruning (the (2N-2):2N family) -------------------------------------
+
+def test_prune_nm_is_the_24_rule_at_2_of_4(orc):
+    for seed in range(10):
+        a = synth.int8_uniform(np.random.default_rng(1100 + seed), (int(5 + seed), 64))
+        a[0, :8] = [-128, 127, 127, -128, 0, 0, 0, 5]        # ties and -128
+        v, m = orc.pack24(a)
+        np.testing.assert_array_equal(orc.prune_nm(a, 2, 4), orc.densify24(v, m))
+
+
+@pytest.mark.parametrize("keep,group", [(6, 8), (4, 6), (14, 16), (1, 2), (3, 3), (0, 4)])
+def test_prune_nm_invariants(orc, keep, group):
+    r = np.random.default_rng(keep * 100 + group)
+    a = r.integers(-128, 128, size=(40, group * 12)).astype(np.int8)
+    a[::3] = r.integers(-3, 4, size=a[::3].shape)            # many ties
+    out = orc.prune_nm(a, keep, group)
+    ga = a.reshape(40, -1, group).astype(np.int64)
+    go = out.reshape(40, -1, group).astype(np.int64)
+    kept = (go == ga) & ((go != 0) | (ga == 0))
+    for i in range(40):
+        for g in range(ga.shape[1]):
+            vals = np.abs(ga[i, g])
+            # the kept set: `keep` positions, by (larger |a|, lower position)
+            order = sorted(range(group), key=lambda t: (-vals[t], t))[:keep]
+            mask = np.zeros(group, bool)
+            mask[order] = True
+            np.testing.assert_array_equal(go[i, g][mask], ga[i, g][mask])
+            assert (go[i, g][~mask] == 0).all()
+            if keep and (~mask).any():
+                assert vals[mask].min() >= vals[~mask].max()
+    assert kept.shape == ga.shape
+
+
+def test_prune_nm_hand_cases(orc):
+    a = np.array([[3, -3, 3, -3, 1, 0, -128, 127]], np.int8)
+    np.testing.assert_array_equal(orc.prune_nm(a, 6, 8), [[3, -3, 3, -3, 0, 0, -128, 127]])
+    a = np.array([[0, 0, 0, 0, 0, 0, 0, 1]], np.int8)
+    np.testing.assert_array_equal(orc.prune_nm(a, 6, 8), a)    # zeros kept as zeros
+    a = np.array([[5, 5, 5, 5, 5, 5, 5, 5]], np.int8)           # all tie: lowest six survive
+    np.testing.assert_array_equal(orc.prune_nm(a, 6, 8), [[5, 5, 5, 5, 5, 5, 0, 0]])
+    with pytest.raises(ValueError):
+        orc.prune_nm(np.zeros((1, 12), np.int8), 6, 8)

@@ -45,7 +45,7 @@ PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "i8": 5000.0}
 # kernel whose launch dominates a step, per format
 DOMINANT_KERNEL = {"bcsr": "bcsr_bf16_mfma", "wcsr": "wcsr_stream", "sp24": "sp24_i8_smfmac",
                    "sddmm": "sddmm_f32", "sddmm_bcsr": "sddmm_bcsr_mfma", "bcsr_csr": "bcsr_bf16_mfma",
-                   "tvw": "sp24_i8_smfmac"}
+                   "tvw": "sp24_i8_smfmac", "slide": "sp24_i8_smfmac"}
 TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 CSRC = os.path.join(ROOT, "sparse_dense_matrix_amd", "csrc")
 
@@ -103,6 +103,9 @@ def setup(w, S, args):
         types = (S.F32, S.F32)
     elif w.fmt == "tvw":
         M = S.spmm_pack_tvw(a["dense"], synth.TVW_TILE_M, synth.TVW_TILE_K)
+        types = (S.I8, S.I32)
+    elif w.fmt == "slide":
+        M = S.spmm_pack_slide(a["dense"], w.nm_group)
         types = (S.I8, S.I32)
     else:
         M = S.spmm_pack_24(a["dense"])
@@ -173,6 +176,12 @@ def algorithmic(w, d):
         x_rows = int(np.count_nonzero(np.diff(d["a"]["row_ptr"])))
         y_rows = len(np.unique(d["a"]["col_idx"]))
         return flops, 8 * (w.m + 1) + 8 * nnz + (x_rows + y_rows) * n * 4, "f32"
+    if w.fmt == "slide":
+        # effective work counts the kept (2N-2)/2N of A; bytes: the lifted 2:4
+        # operand (values and index bytes), B and C once
+        kept = w.m * w.k * (w.nm_group - 2) // w.nm_group
+        lifted = info["nnz"]                     # m * k_lift / 2 kept values
+        return 2.0 * kept * n, lifted + lifted // 4 + w.k * n + w.m * n * 4, "i8"
     if w.fmt == "tvw":
         # the stored tiles (kept values and index bytes), the B rows of
         # k-steps any tile row stores, C once
@@ -236,7 +245,7 @@ def main():
         Bh = torch.from_numpy(B.view(np.int16) if B.dtype == np.uint16 else B)
         Bt = Bh.cuda()
         cdt = {"bcsr": torch.int16, "bcsr_csr": torch.int16, "wcsr": torch.float32,
-               "sp24": torch.int32, "tvw": torch.int32}[w.fmt]
+               "sp24": torch.int32, "tvw": torch.int32, "slide": torch.int32}[w.fmt]
         Ct = torch.empty((w.m, w.n), dtype=cdt, device="cuda")
 
         def step(stream):
@@ -270,7 +279,7 @@ def main():
     dense = None
     if args.dense_baseline and w.fmt == "bcsr":
         dense = dense_baseline(torch, w, d, Bt, stream, args, ms_step)
-    elif args.dense_baseline and w.fmt in ("tvw", "sp24"):
+    elif args.dense_baseline and w.fmt in ("tvw", "sp24", "slide"):
         dense = dense_baseline_i8(torch, w, d, Bt, stream, args, ms_step)
 
     out = {
@@ -524,6 +533,12 @@ def cpu_baseline(w, d, target_s):
 
         def run(rows):
             oracle.sddmm(a["row_ptr"], a["col_idx"], B[0], B[1], rows=rows)
+    elif w.fmt == "slide":
+        pruned = oracle.prune_nm(a["dense"], w.nm_group - 2, w.nm_group)
+        row_nnz = np.full(w.m, w.k * (w.nm_group - 2) // w.nm_group, dtype=np.int64)
+
+        def run(rows):
+            oracle.gemm_i8(pruned[rows], B)
     elif w.fmt == "sddmm_bcsr":
         # the sample unit is a stored block (2 * 4096 * kd flop each)
         rp, ci, _ = oracle.pack_bcsr(a["dense"], w.block, w.block)

@@ -60,7 +60,8 @@ typedef enum {
   SPMM_FORMAT_BCSR = 0,
   SPMM_FORMAT_WCSR = 1,
   SPMM_FORMAT_24 = 2,
-  SPMM_FORMAT_TVW = 3  /* tile-vector-wise: 2:4 inside the stored tiles of a tile grid */
+  SPMM_FORMAT_TVW = 3,   /* tile-vector-wise: 2:4 inside the stored tiles of a tile grid */
+  SPMM_FORMAT_SLIDE = 4  /* (2N-2):2N as overlapping 2:4 windows                        */
 } spmm_format_t;
 
 /* Packed sparse operand: immutable host arrays in the canonical layout below,
@@ -102,6 +103,9 @@ typedef struct {
  *                                         [i*k/2 + 2g], [i*k/2 + 2g + 1], ascending position
  *    SPMM_ARRAY_META      uint8[m * k/8]  nibble (i0 | i1 << 2) of group g in byte
  *                                         i*k/8 + g/2, low nibble for even g
+ *  SLIDE ((2N-2):2N as overlapping 2:4 windows, group = 2N, k_lift = 4(N-1) k / 2N)
+ *    SPMM_ARRAY_VALS      int8[m * k_lift/2]   the lifted 2:4 matrix, layout as for 2:4
+ *    SPMM_ARRAY_META      uint8[m * k_lift/8]  its nibbles
  *  TVW (nt stored tiles of tm x tk, mt = m / tm tile rows)
  *    SPMM_ARRAY_ROW_PTR   int32[mt + 1]   stored tiles of tile row T: [row_ptr[T], row_ptr[T+1])
  *    SPMM_ARRAY_COL_IDX   int32[nt]       tile column (k / tk units), ascending in a tile row
@@ -130,6 +134,21 @@ typedef enum {
 spmm_status_t spmm_pack_bcsr(int64_t m, int64_t k, int32_t block_m, int32_t block_k,
                              spmm_dtype_t dtype, const void *a_host, int64_t lda,
                              spmm_matrix_t *out);
+
+/* (2N-2):2N weights as overlapping 2:4 windows (the sliding-window
+ * decomposition of the (2N-2):2N family on the "Daily Papers" search page):
+ * from a dense int8 a_host [m x k], every group of `group` = 2N consecutive
+ * elements of a row keeps its 2N-2 largest |a| (as integers, ties to the
+ * lower position; the rest are dropped) and the kept elements are dealt, in
+ * ascending position, to the lowest of the N-1 windows of four (window w
+ * covers positions 2w .. 2w+3) that covers them and has room; each window is
+ * then one 2:4 group.  The product is that of the pruned A.  Lifted column
+ * 4w + j of group g multiplies B's row 2N g + 2w + j; spmm_execute gathers
+ * those rows into a plan workspace (k_lift * n bytes) first.  Requires
+ * group even in [4, 64], k % group == 0 and k_lift % 8 == 0 (else
+ * INVALID_ARG); spmm_matrix_info reports group as block_k. */
+spmm_status_t spmm_pack_slide(int64_t m, int64_t k, const int8_t *a_host, int64_t lda, int32_t group,
+                              spmm_matrix_t *out);
 
 /* Tile-vector-wise (the tile-wise pattern combined with 2:4 of "Accelerating
  * Sparse DNNs Based on Tiled GEMM", abstract) from a dense row-major int8
@@ -200,6 +219,7 @@ void spmm_matrix_destroy(spmm_matrix_t a);
  *   WCSR:                  (F32, F32), any n >= 1
  *   2:4:                   (I8, I32), n % 16 == 0
  *   TVW (256 x 128 tiles): (I8, I32), n % 16 == 0
+ *   SLIDE:                 (I8, I32), n % 16 == 0 (plus a k_lift * n workspace)
  * A BCSR matrix packed with reordering also gets a workspace for B's rows in
  * the packed column order (k * n * 2 bytes).  Anything else is UNSUPPORTED.  n = 0 is allowed (execute does nothing). */
 spmm_status_t spmm_plan(spmm_matrix_t a, int64_t n, spmm_dtype_t b_dtype,

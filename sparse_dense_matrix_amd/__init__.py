@@ -18,10 +18,10 @@ import numpy as np
 
 __all__ = [
     "SpmmError", "Matrix", "Plan", "F32", "BF16", "I8", "I32",
-    "FORMAT_BCSR", "FORMAT_WCSR", "FORMAT_24", "FORMAT_TVW",
+    "FORMAT_BCSR", "FORMAT_WCSR", "FORMAT_24", "FORMAT_TVW", "FORMAT_SLIDE",
     "ARRAY_ROW_PTR", "ARRAY_COL_IDX", "ARRAY_VALS", "ARRAY_META",
     "ARRAY_CHUNK_WINDOW", "ARRAY_CHUNK_BEGIN", "ARRAY_ROW_PERM", "ARRAY_COL_PERM",
-    "spmm_pack_bcsr", "spmm_pack_bcsr_csr", "spmm_pack_wcsr", "spmm_pack_24", "spmm_pack_tvw",
+    "spmm_pack_bcsr", "spmm_pack_bcsr_csr", "spmm_pack_wcsr", "spmm_pack_24", "spmm_pack_tvw", "spmm_pack_slide",
     "spmm_matrix_info",
     "spmm_matrix_array", "spmm_plan", "spmm_plan_info", "spmm_execute",
     "spmm_plan_sddmm", "spmm_execute_sddmm",
@@ -33,7 +33,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("SPMM_LIBRARY") or os.path.join(HERE, "libspmm.so")
 
 F32, BF16, I8, I32 = 0, 1, 2, 3
-FORMAT_BCSR, FORMAT_WCSR, FORMAT_24, FORMAT_TVW = 0, 1, 2, 3
+FORMAT_BCSR, FORMAT_WCSR, FORMAT_24, FORMAT_TVW, FORMAT_SLIDE = 0, 1, 2, 3, 4
 (ARRAY_ROW_PTR, ARRAY_COL_IDX, ARRAY_VALS, ARRAY_META, ARRAY_CHUNK_WINDOW,
  ARRAY_CHUNK_BEGIN, ARRAY_ROW_PERM, ARRAY_COL_PERM) = range(8)
 
@@ -44,7 +44,7 @@ DEFAULT_MAX_CHUNK_NNZ = 0
 
 # every symbol include/spmm.h declares
 EXPORTS = (
-    "spmm_pack_bcsr", "spmm_pack_bcsr_csr", "spmm_pack_wcsr", "spmm_pack_24", "spmm_pack_tvw",
+    "spmm_pack_bcsr", "spmm_pack_bcsr_csr", "spmm_pack_wcsr", "spmm_pack_24", "spmm_pack_tvw", "spmm_pack_slide",
     "spmm_matrix_info",
     "spmm_matrix_array", "spmm_matrix_destroy", "spmm_plan", "spmm_plan_info",
     "spmm_plan_destroy", "spmm_execute", "spmm_plan_sddmm", "spmm_execute_sddmm",
@@ -88,6 +88,7 @@ def _load():
         "spmm_pack_bcsr_csr": (st, [i64, i64, st, P, P, P, i32, i32, i32, C.POINTER(P)]),
         "spmm_pack_24": (st, [i64, i64, P, i64, C.POINTER(P)]),
         "spmm_pack_tvw": (st, [i64, i64, P, i64, i32, i32, C.POINTER(P)]),
+        "spmm_pack_slide": (st, [i64, i64, P, i64, i32, C.POINTER(P)]),
         "spmm_matrix_info": (st, [P, C.POINTER(MatrixInfo)]),
         "spmm_matrix_array": (st, [P, i32, C.POINTER(P), C.POINTER(i64)]),
         "spmm_matrix_destroy": (None, [P]),
@@ -181,6 +182,18 @@ def spmm_pack_bcsr(a_bits: np.ndarray, block_m: int = 64, block_k: int = 64,
     return Matrix(h)
 
 
+def spmm_pack_slide(a: np.ndarray, group: int = 8) -> Matrix:
+    """(group-2):group weights (group = 2N) as N-1 overlapping 2:4 windows per
+    group, from a dense int8 matrix."""
+    a = np.ascontiguousarray(a, dtype=np.int8)
+    if a.ndim != 2:
+        raise ValueError("a must be 2-D")
+    h = C.c_void_p()
+    _check(_lib.spmm_pack_slide(a.shape[0], a.shape[1], _ptr(a), a.shape[1], group, C.byref(h)),
+           "spmm_pack_slide")
+    return Matrix(h)
+
+
 def spmm_pack_tvw(a: np.ndarray, tile_m: int = 256, tile_k: int = 128) -> Matrix:
     """Tile-vector-wise from a dense int8 matrix: tiles with a nonzero are
     stored, 2:4-pruned along k."""
@@ -249,6 +262,7 @@ _ARRAY_DTYPES = {
     (FORMAT_24, ARRAY_VALS): np.int8, (FORMAT_24, ARRAY_META): np.uint8,
     (FORMAT_TVW, ARRAY_ROW_PTR): np.int32, (FORMAT_TVW, ARRAY_COL_IDX): np.int32,
     (FORMAT_TVW, ARRAY_VALS): np.int8, (FORMAT_TVW, ARRAY_META): np.uint8,
+    (FORMAT_SLIDE, ARRAY_VALS): np.int8, (FORMAT_SLIDE, ARRAY_META): np.uint8,
 }
 
 

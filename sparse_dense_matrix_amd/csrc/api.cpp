@@ -354,12 +354,15 @@ spmm_status_t plan_sddmm_bcsr(spmm_plan_s *p, int64_t kd, bool int8) {
 spmm_status_t plan_24(spmm_plan_s *p) {
   const Matrix &a = *p->a;
   if (p->n % 16 != 0) return fail(SPMM_ERR_UNSUPPORTED, "spmm_plan: 2:4 needs n % 16 == 0");
+  // a sliding-window matrix is the 2:4 matrix of its lifted columns
+  const bool slide = a.format == SPMM_FORMAT_SLIDE;
+  const int64_t k = slide ? a.k_lift : a.k;
   const int64_t TM = sp24_tile_m(), TK = sp24_tile_k();
   const int64_t m_pad = (a.m + TM - 1) / TM * TM;
-  const int64_t k_pad = std::max<int64_t>(TK, (a.k + TK - 1) / TK * TK);
+  const int64_t k_pad = std::max<int64_t>(TK, (k + TK - 1) / TK * TK);
   std::vector<int8_t> v(static_cast<size_t>(m_pad * (k_pad / 2)));
   std::vector<uint8_t> mt(static_cast<size_t>(m_pad * (k_pad / 8)));
-  sp24_tile_layout(a.vals24.data(), a.meta24.data(), a.m, a.k, m_pad, k_pad, v.data(), mt.data());
+  sp24_tile_layout(a.vals24.data(), a.meta24.data(), a.m, k, m_pad, k_pad, v.data(), mt.data());
   Sp24Launch &L = p->sp24;
   spmm_status_t s;
   int8_t *dv = nullptr;
@@ -369,12 +372,27 @@ spmm_status_t plan_24(spmm_plan_s *p) {
   L.vals = dv;
   L.meta = dm;
   L.m = a.m;
-  L.k = a.k;
+  L.k = k;
   L.n = p->n;
   L.m_pad = m_pad;
   L.k_pad = k_pad;
   L.tile_ptr = nullptr;
   L.tile_step = nullptr;
+  L.b_rows = nullptr;
+  L.b_lift = nullptr;
+  if (slide) {
+    std::vector<int32_t> rows(static_cast<size_t>(k));
+    for (int64_t j = 0; j < k; ++j) rows[j] = static_cast<int32_t>(slide_source_row(j, a.slide_group));
+    int32_t *dr = nullptr;
+    void *ws = nullptr;
+    const int64_t ws_bytes = k * p->n;
+    if ((s = upload_vec(p, rows, &dr)) != SPMM_OK) return s;
+    if ((s = upload(p, nullptr, static_cast<size_t>(ws_bytes), &ws)) != SPMM_OK) return s;
+    p->info.device_bytes -= std::max<int64_t>(ws_bytes, 16);
+    p->info.workspace_bytes = ws_bytes;
+    L.b_rows = dr;
+    L.b_lift = static_cast<int8_t *>(ws);
+  }
   p->info.tile_m = sp24_tile_m();
   p->info.tile_n = sp24_tile_n();
   p->info.grid = sp24_grid(a.m, p->n);
@@ -404,6 +422,8 @@ spmm_status_t plan_tvw(spmm_plan_s *p) {
   L.meta = dm;
   L.tile_ptr = tp;
   L.tile_step = ts;
+  L.b_rows = nullptr;
+  L.b_lift = nullptr;
   L.m = a.m;
   L.k = a.k;
   L.n = p->n;
@@ -451,6 +471,28 @@ spmm_status_t spmm_pack_bcsr(int64_t m, int64_t k, int32_t block_m, int32_t bloc
     auto *a = new spmm_matrix_s();
     spmm_status_t s = pack_bcsr_bf16(m, k, block_m, block_k,
                                      static_cast<const uint16_t *>(a_host), lda, *a);
+    if (s != SPMM_OK) {
+      delete a;
+      return s;
+    }
+    *out = a;
+    return SPMM_OK;
+  });
+}
+
+spmm_status_t spmm_pack_slide(int64_t m, int64_t k, const int8_t *a_host, int64_t lda, int32_t group,
+                              spmm_matrix_t *out) {
+  if (!out) return fail(SPMM_ERR_INVALID_ARG, "spmm_pack_slide: out is NULL");
+  *out = nullptr;
+  // group = 2N with N >= 2; the lifted row (4(N-1) columns per group) must
+  // hold whole bytes of 2:4 metadata
+  if (m < 0 || k < 0 || m > INT32_MAX || k > INT32_MAX || group < 4 || group > 64 || group % 2 != 0 ||
+      k % group != 0 || ((k / group) * 4 * (group / 2 - 1)) % 8 != 0 || lda < k ||
+      (m * k > 0 && !a_host))
+    return fail(SPMM_ERR_INVALID_ARG, "spmm_pack_slide: bad shape, group, lda or pointer");
+  return guarded([&]() -> spmm_status_t {
+    auto *a = new spmm_matrix_s();
+    spmm_status_t s = pack_slide_i8(m, k, a_host, lda, group, *a);
     if (s != SPMM_OK) {
       delete a;
       return s;
@@ -562,6 +604,8 @@ spmm_status_t spmm_matrix_info(spmm_matrix_t a, spmm_matrix_info_t *info) {
     info->nnzb = static_cast<int64_t>(a->bcol_idx.size());
     info->block_m = a->bm;
     info->block_k = a->bk;
+  } else if (a->format == SPMM_FORMAT_SLIDE) {
+    info->block_k = a->slide_group;
   } else if (a->format == SPMM_FORMAT_WCSR) {
     info->window_rows = a->window_rows;
     info->max_chunk_nnz = a->max_chunk_nnz;
@@ -600,6 +644,10 @@ spmm_status_t spmm_matrix_array(spmm_matrix_t a, int32_t which, const void **dat
       if (which == SPMM_ARRAY_VALS) return give(a->vals24);
       if (which == SPMM_ARRAY_META) return give(a->meta24);
       break;
+    case SPMM_FORMAT_SLIDE:
+      if (which == SPMM_ARRAY_VALS) return give(a->vals24);
+      if (which == SPMM_ARRAY_META) return give(a->meta24);
+      break;
     case SPMM_FORMAT_TVW:
       if (which == SPMM_ARRAY_ROW_PTR) return give(a->brow_ptr);
       if (which == SPMM_ARRAY_COL_IDX) return give(a->bcol_idx);
@@ -620,8 +668,9 @@ spmm_status_t spmm_plan(spmm_matrix_t a, int64_t n, spmm_dtype_t b_dtype, spmm_d
   const bool ok_types =
       (a->format == SPMM_FORMAT_BCSR && b_dtype == SPMM_BF16 && c_dtype == SPMM_BF16) ||
       (a->format == SPMM_FORMAT_WCSR && b_dtype == SPMM_F32 && c_dtype == SPMM_F32) ||
-      ((a->format == SPMM_FORMAT_24 || a->format == SPMM_FORMAT_TVW) && b_dtype == SPMM_I8 &&
-       c_dtype == SPMM_I32);
+      ((a->format == SPMM_FORMAT_24 || a->format == SPMM_FORMAT_TVW ||
+        a->format == SPMM_FORMAT_SLIDE) &&
+       b_dtype == SPMM_I8 && c_dtype == SPMM_I32);
   if (!ok_types) return fail(SPMM_ERR_UNSUPPORTED, "spmm_plan: unsupported (format, B, C) types");
   int ndev = 0;
   hipError_t e = hipGetDeviceCount(&ndev);
@@ -645,7 +694,7 @@ spmm_status_t spmm_plan(spmm_matrix_t a, int64_t n, spmm_dtype_t b_dtype, spmm_d
       if (a->format == SPMM_FORMAT_BCSR) s = plan_bcsr(p);
       else if (a->format == SPMM_FORMAT_WCSR) s = plan_wcsr(p);
       else if (a->format == SPMM_FORMAT_TVW) s = plan_tvw(p);
-      else s = plan_24(p);
+      else s = plan_24(p);  // 2:4 and sliding-window
     } catch (...) {
       free_plan(p);
       throw;
@@ -680,7 +729,10 @@ spmm_status_t spmm_execute(spmm_plan_t p, const void *b_dev, int64_t ldb, void *
   if (n == 0 || a.m == 0) return SPMM_OK;
   const int64_t eb = a.format == SPMM_FORMAT_BCSR
                          ? 2
-                         : ((a.format == SPMM_FORMAT_24 || a.format == SPMM_FORMAT_TVW) ? 1 : 4);
+                         : ((a.format == SPMM_FORMAT_24 || a.format == SPMM_FORMAT_TVW ||
+                             a.format == SPMM_FORMAT_SLIDE)
+                                ? 1
+                                : 4);
   const int64_t ec = a.format == SPMM_FORMAT_BCSR ? 2 : 4;
   if (!c_dev || (!b_dev && a.k > 0))
     return fail(SPMM_ERR_INVALID_ARG, "spmm_execute: B or C is NULL");

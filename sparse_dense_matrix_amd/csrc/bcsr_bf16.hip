@@ -285,16 +285,6 @@ hipError_t launch_tn(const BcsrLaunch &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Bp[j] = B[perm[j]] for the k rows of B, n (a multiple of 8) columns each:
-// one workgroup per row, 16-byte pieces
-__global__ __launch_bounds__(256) void gather_rows_bf16(const uint16_t *__restrict__ B, int64_t ldb,
-                                                        const int32_t *__restrict__ perm, int64_t n,
-                                                        uint16_t *__restrict__ Bp) {
-  const int64_t j = blockIdx.x;
-  const u32x4 *src = reinterpret_cast<const u32x4 *>(B + static_cast<int64_t>(perm[j]) * ldb);
-  u32x4 *dst = reinterpret_cast<u32x4 *>(Bp + j * n);
-  for (int64_t c = threadIdx.x; c < n / 8; c += 256) dst[c] = src[c];
-}
 }  // namespace
 
 hipError_t launch_bcsr_bf16(const BcsrLaunch &a0, hipStream_t s) {
@@ -302,12 +292,8 @@ hipError_t launch_bcsr_bf16(const BcsrLaunch &a0, hipStream_t s) {
   if (a.col_perm) {
     // B's rows in the packed column order, then the multiply reads that copy
     const int64_t k = a.k_rows;
-    if (k > 0 && a.n > 0) {
-      hipLaunchKernelGGL(gather_rows_bf16, dim3(static_cast<unsigned>(k)), dim3(256), 0, s, a.B,
-                         a.ldb, a.col_perm, a.n, a.b_perm);
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
+    hipError_t e = launch_gather_rows(a.B, a.ldb * 2, a.col_perm, k, a.n * 2, a.b_perm, a.n * 2, s);
+    if (e != hipSuccess) return e;
     a.B = a.b_perm;
     a.ldb = a.n;
   }

@@ -34,6 +34,10 @@ struct Matrix {
   // BCSR of a permuted CSR matrix: original row of each row / original
   // column of each column of the packed matrix (empty: original order)
   std::vector<int32_t> row_perm, col_perm;
+  // sliding-window 2:4 ((2N-2):2N weights): group width 2N; vals24 / meta24
+  // hold the lifted 2:4 matrix of m x k_lift columns
+  int32_t slide_group = 0;
+  int64_t k_lift = 0;
   // WCSR
   int32_t window_rows = 0;
   int64_t max_chunk_nnz = 0;
@@ -58,6 +62,10 @@ spmm_status_t pack_wcsr_f32(int64_t m, int64_t k, const int64_t *row_ptr,
                             const int32_t *col_idx, const float *vals, int32_t W,
                             int64_t T, Matrix &out);
 spmm_status_t pack_24_i8(int64_t m, int64_t k, const int8_t *a, int64_t lda, Matrix &out);
+spmm_status_t pack_slide_i8(int64_t m, int64_t k, const int8_t *a, int64_t lda, int32_t group,
+                            Matrix &out);
+// lifted row j of a sliding-window matrix -> row of B it multiplies
+int64_t slide_source_row(int64_t j, int32_t group);
 spmm_status_t pack_tvw_i8(int64_t m, int64_t k, const int8_t *a, int64_t lda, int32_t tm,
                           int32_t tk, Matrix &out);
 spmm_status_t pack_bcsr_csr_bf16(int64_t m, int64_t k, const int64_t *row_ptr,
@@ -79,6 +87,11 @@ struct WcsrChunk {
   int32_t slot_first, slot_last;
 };
 static_assert(sizeof(WcsrChunk) == 32, "WcsrChunk layout");
+
+// dst row j = src row map[j] for j < rows, row_bytes (a multiple of 16)
+// bytes each; leading dimensions in bytes, 16-byte aligned.
+hipError_t launch_gather_rows(const void *src, int64_t ld_bytes, const int32_t *map, int64_t rows,
+                              int64_t row_bytes, void *dst, int64_t dst_ld_bytes, hipStream_t s);
 
 // Raise a kernel's dynamic LDS limit to `bytes` on the current device (once
 // per kernel and device).
@@ -183,6 +196,11 @@ struct Sp24Launch {
   // tile_step[tile_ptr[T] .. tile_ptr[T+1]); null for a plain 2:4 A
   const int32_t *tile_ptr;
   const int32_t *tile_step;
+  // sliding-window A: the kernel multiplies by B's rows in window order,
+  // b_lift[j] = B[b_rows[j]] for the k (= lifted) rows, gathered first from
+  // the caller's B of k_src rows; null otherwise
+  const int32_t *b_rows;
+  int8_t *b_lift;
   int64_t m, k, n;
   int64_t m_pad, k_pad;
   const int8_t *B;

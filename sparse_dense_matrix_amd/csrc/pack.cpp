@@ -6,6 +6,7 @@
 // (abstract: the 2:4 pattern of the sparse tensor core) and the N:M entry of
 // the search-results page.
 #include <algorithm>
+#include <cstdlib>
 #include <cstring>
 
 #include "internal.h"
@@ -318,6 +319,88 @@ spmm_status_t pack_24_i8(int64_t m, int64_t k, const int8_t *a, int64_t lda, Mat
   out.meta24.assign(static_cast<size_t>(m * (k / 8)), 0);
   for (int64_t i = 0; i < m; ++i)
     prune_row(a + i * lda, k, out.vals24.data() + i * (k / 2), out.meta24.data() + i * (k / 8));
+  return SPMM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Sliding-window decomposition of (2N-2):2N weights (the search page's entry
+// on the (2N-2):2N family): every group of 2N elements keeps its 2N-2 largest
+// |a| (ties to the lower position), and the kept elements are dealt to N-1
+// overlapping windows of four (window w covers positions 2w .. 2w+3), two per
+// window, so the group becomes N-1 2:4 groups.  The lifted row has 4(N-1)
+// columns per group; lifted column 4w + j of group g multiplies B's row
+// 2N g + 2w + j.  Kept positions are dealt in ascending order to the lower
+// window while it has room: positions 2w and 2w+1 belong to windows w-1 and
+// w, the two ends to one window only.
+// ---------------------------------------------------------------------------
+int64_t slide_source_row(int64_t j, int32_t group) {
+  const int64_t per = 2 * (group - 2);  // lifted columns per group: 4 (N - 1)
+  const int64_t g = j / per, o = j % per;
+  return g * group + 2 * (o / 4) + (o % 4);
+}
+
+spmm_status_t pack_slide_i8(int64_t m, int64_t k, const int8_t *a, int64_t lda, int32_t group,
+                            Matrix &out) {
+  const int32_t N = group / 2, keep = group - 2, windows = N - 1;
+  const int64_t groups = k / group;
+  const int64_t k_lift = groups * 4 * windows;
+  out.format = SPMM_FORMAT_SLIDE;
+  out.dtype = SPMM_I8;
+  out.m = m;
+  out.k = k;
+  out.slide_group = group;
+  out.k_lift = k_lift;
+  out.nnz = m * (k_lift / 2);
+  out.vals24.assign(static_cast<size_t>(m * (k_lift / 2)), 0);
+  out.meta24.assign(static_cast<size_t>(m * (k_lift / 8)), 0);
+  std::vector<int> rank_key(group);
+  std::vector<int8_t> lifted(static_cast<size_t>(4 * windows));
+  std::vector<int> wcount(windows);
+  std::vector<uint8_t> taken(4 * windows);
+  for (int64_t i = 0; i < m; ++i) {
+    const int8_t *row = a + i * lda;
+    int8_t *v = out.vals24.data() + i * (k_lift / 2);
+    uint8_t *mt = out.meta24.data() + i * (k_lift / 8);
+    for (int64_t g = 0; g < groups; ++g) {
+      const int8_t *grp = row + g * group;
+      std::fill(wcount.begin(), wcount.end(), 0);
+      std::fill(taken.begin(), taken.end(), 0);
+      std::fill(lifted.begin(), lifted.end(), 0);
+      for (int32_t p = 0; p < group; ++p) {
+        // kept iff fewer than `keep` positions rank before p
+        int before = 0;
+        const int ap = std::abs(static_cast<int>(grp[p]));
+        for (int32_t u = 0; u < group; ++u) {
+          const int au = std::abs(static_cast<int>(grp[u]));
+          if (au > ap || (au == ap && u < p)) ++before;
+        }
+        if (before >= keep) continue;
+        const int w_lo = p / 2 - 1, w_hi = p / 2;
+        int w = -1;
+        if (w_lo >= 0 && w_lo < windows && wcount[w_lo] < 2) w = w_lo;
+        else if (w_hi < windows && wcount[w_hi] < 2) w = w_hi;
+        if (w < 0) return fail(SPMM_ERR_INTERNAL, "spmm_pack_slide: window assignment failed");
+        ++wcount[w];
+        const int j = p - 2 * w;
+        taken[4 * w + j] = 1;
+        lifted[4 * w + j] = grp[p];
+      }
+      // every window is a 2:4 group: its two taken positions (every window
+      // is full, since 2N-2 elements fill N-1 windows of two)
+      for (int32_t w = 0; w < windows; ++w) {
+        int pos[2], q = 0;
+        for (int j = 0; j < 4 && q < 2; ++j)
+          if (taken[4 * w + j]) pos[q++] = j;
+        for (int j = 0; j < 4 && q < 2; ++j)  // (unreachable) pad with an untaken slot
+          if (!taken[4 * w + j] && (q == 0 || j > pos[0])) pos[q++] = j;
+        const int64_t lg = g * windows + w;  // 2:4 group index in the lifted row
+        v[2 * lg] = lifted[4 * w + pos[0]];
+        v[2 * lg + 1] = lifted[4 * w + pos[1]];
+        const uint8_t nibble = static_cast<uint8_t>(pos[0] | (pos[1] << 2));
+        mt[lg >> 1] = static_cast<uint8_t>(mt[lg >> 1] | (nibble << ((lg & 1) * 4)));
+      }
+    }
+  }
   return SPMM_OK;
 }
 

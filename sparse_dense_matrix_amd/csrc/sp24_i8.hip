@@ -348,7 +348,15 @@ hipError_t launch(const Sp24Launch &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_sp24_i8(const Sp24Launch &a, hipStream_t s) {
+hipError_t launch_sp24_i8(const Sp24Launch &a0, hipStream_t s) {
+  Sp24Launch a = a0;
+  if (a.b_rows) {
+    // sliding-window A: B's rows in lifted order first (a.k lifted rows)
+    hipError_t e = launch_gather_rows(a.B, a.ldb, a.b_rows, a.k, a.n, a.b_lift, a.n, s);
+    if (e != hipSuccess) return e;
+    a.B = a.b_lift;
+    a.ldb = a.n;
+  }
   return a.tile_ptr ? launch<true>(a, s) : launch<false>(a, s);
 }
 

@@ -207,7 +207,7 @@ def dense_f32_normal(rows: int, cols: int, seed: int, stream: int = S_BVAL) -> n
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    fmt: str            # "wcsr" | "bcsr" | "bcsr_csr" | "sp24" | "tvw" | "sddmm" | "sddmm_bcsr"
+    fmt: str            # "wcsr" | "bcsr" | "bcsr_csr" | "sp24" | "tvw" | "slide" | "sddmm" | "sddmm_bcsr"
     m: int
     k: int
     n: int
@@ -225,6 +225,7 @@ class Workload:
     scramble: int = 0             # > 0: a block-sparse matrix with rows and columns
                                   # shuffled (this seed), given as CSR
     reorder: bool = False         # bcsr_csr: pack after the row/column reordering
+    nm_group: int = 0             # slide: group width 2N of the (2N-2):2N pattern
 
     @property
     def describe(self) -> str:
@@ -257,6 +258,9 @@ WORKLOADS: Dict[str, Workload] = {
     # of its 256 x 128 tiles zero (2:4 inside the rest), same B as the 2:4 case
     "tvw_i8_8192_t50": Workload("tvw_i8_8192_t50", "tvw", 8192, 8192, 2048, 20260009, nblocks=1024),
     "tvw_i8_8192_t75": Workload("tvw_i8_8192_t75", "tvw", 8192, 8192, 2048, 20260010, nblocks=512),
+    # the 2:4 case's shapes with a milder pattern: 6 of every 8 kept, as
+    # overlapping 2:4 windows
+    "slide68_i8_8192": Workload("slide68_i8_8192", "slide", 8192, 8192, 2048, 20260011, nm_group=8),
     # the 4096 block-sparse matrix with rows and columns shuffled, given as
     # CSR: packed as BCSR with and without the reordering, and as WCSR
     "scrambled_4096_bcsr_reordered": Workload("scrambled_4096_bcsr_reordered", "bcsr_csr", 4096,
@@ -291,6 +295,7 @@ SMALL: Dict[str, Workload] = {
     "sddmm_bcsr_small": _bcsr("sddmm_bcsr_small", 640, 512, 1000, 0.7, 35, fmt="sddmm_bcsr",
                               elem="bf16"),
     "tvw_small": Workload("tvw_small", "tvw", 512, 1024, 272, 38, nblocks=6),
+    "slide_small": Workload("slide_small", "slide", 320, 512, 400, 39, nm_group=8),
     "scrambled_small": Workload("scrambled_small", "bcsr_csr", 1024, 768, 520, 36, nblocks=30,
                                 scramble=37, reorder=True),
 }
@@ -315,7 +320,7 @@ def make_a(w: Workload) -> dict:
     if w.fmt in ("bcsr", "sddmm_bcsr"):
         a, ids = block_sparse_dense_bf16(w.m, w.k, w.block, w.block, w.nblocks, w.sigma, w.seed)
         return {"dense": a, "block_ids": ids}
-    if w.fmt == "sp24":
+    if w.fmt in ("sp24", "slide"):
         return {"dense": int8_uniform(rng(w.seed, S_AVAL), (w.m, w.k))}
     if w.fmt == "tvw":
         return {"dense": tile_sparse_i8(w.m, w.k, TVW_TILE_M, TVW_TILE_K, w.nblocks, w.seed)}
@@ -347,6 +352,6 @@ def make_b(w: Workload, n: int | None = None) -> np.ndarray:
         return dense_f32_normal(w.k, n, w.seed)
     if w.fmt == "bcsr":
         return dense_bf16_normal(w.k, n, w.seed)
-    if w.fmt in ("sp24", "tvw"):
+    if w.fmt in ("sp24", "tvw", "slide"):
         return int8_uniform(rng(w.seed, S_BVAL), (w.k, n))
     raise ValueError(w.fmt)

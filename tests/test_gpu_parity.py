@@ -662,3 +662,47 @@ def test_tvw_8192_sampled(S, orc, name):
                                      r.choice(w.m, 96, replace=False)])).astype(np.int64)
     M = tvw_case(S, orc, a, B, rows=rows)
     _say(f"{name} tiles={S.spmm_matrix_info(M)['nnzb']} rows={len(rows)} exact")
+
+
+# ---------------------------------------------------------------------------
+# (2N-2):2N weights as overlapping 2:4 windows, on the 2:4 kernel
+# ---------------------------------------------------------------------------
+
+def slide_case(S, orc, a, B, group, rows=None, pad=0):
+    m, n = a.shape[0], B.shape[1]
+    M = S.spmm_pack_slide(a, group)
+    P = S.spmm_plan(M, n, S.I8, S.I32)
+    got = run(S, P, B, m, n, "i32", pad)
+    pruned = orc.prune_nm(a, group - 2, group)
+    ref = orc.gemm_i8(pruned if rows is None else pruned[rows], B)
+    g = got if rows is None else got[rows]
+    np.testing.assert_array_equal(g.astype(np.int64), ref)
+    return P
+
+
+@pytest.mark.parametrize("group", [8, 6, 16, 4])
+def test_slide_small(S, orc, group):
+    w = synth.SMALL["slide_small"]       # 320 x 512 (k = 528 for 6 and 16), n = 400
+    k = w.k if (w.k // group * 4 * (group // 2 - 1)) % 8 == 0 and w.k % group == 0 else 528
+    a = synth.int8_uniform(np.random.default_rng(40 + group), (w.m, k))
+    B = synth.int8_uniform(np.random.default_rng(41 + group), (k, w.n))
+    for pad in (0, 16):
+        P = slide_case(S, orc, a, B, group, pad=pad)
+    _say(f"slide {group - 2}:{group} ws={P.info()['workspace_bytes']} exact")
+
+
+def test_slide_extremes(S, orc):
+    # all -128: every kept product is 16384, a row sums 6/8 of k of them
+    k = 4096
+    a = np.full((256, k), -128, np.int8)
+    B = np.full((k, 32), -128, np.int8)
+    slide_case(S, orc, a, B, 8)
+
+
+def test_slide68_8192_sampled(S, orc):
+    w = synth.WORKLOADS["slide68_i8_8192"]
+    a = synth.make_a(w)["dense"]
+    B = synth.make_b(w)
+    r = np.random.default_rng(24)
+    rows = np.unique(np.concatenate([np.arange(8), r.choice(w.m, 56, replace=False)])).astype(np.int64)
+    slide_case(S, orc, a, B, w.nm_group, rows=rows)

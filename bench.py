@@ -47,6 +47,12 @@ DOMINANT_KERNEL = {"bcsr": "bcsr_bf16_mfma", "wcsr": "wcsr_stream", "sp24": "sp2
                    "sddmm": "sddmm_f32", "sddmm_bcsr": "sddmm_bcsr_mfma", "bcsr_csr": "bcsr_bf16_mfma",
                    "tvw": "sp24_i8_smfmac", "slide": "sp24_i8_smfmac"}
 TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+
+
+def dominant_kernel(w) -> str:
+    if w.fmt == "tvw" and w.elem == "bf16":
+        return "sp24_bf16_smfmac"
+    return DOMINANT_KERNEL[w.fmt]
 CSRC = os.path.join(ROOT, "sparse_dense_matrix_amd", "csrc")
 
 
@@ -103,7 +109,7 @@ def setup(w, S, args):
         types = (S.F32, S.F32)
     elif w.fmt == "tvw":
         M = S.spmm_pack_tvw(a["dense"], synth.TVW_TILE_M, synth.TVW_TILE_K)
-        types = (S.I8, S.I32)
+        types = (S.BF16, S.BF16) if w.elem == "bf16" else (S.I8, S.I32)
     elif w.fmt == "slide":
         M = S.spmm_pack_slide(a["dense"], w.nm_group)
         types = (S.I8, S.I32)
@@ -186,9 +192,11 @@ def algorithmic(w, d):
         # the stored tiles (kept values and index bytes), the B rows of
         # k-steps any tile row stores, C once
         import sparse_dense_matrix_amd as S
+        e, ec = (2, 2) if w.elem == "bf16" else (1, 4)
         steps = np.unique(S.spmm_matrix_array(d["M"], S.ARRAY_COL_IDX))
-        a_bytes = info["nnz"] + info["nnz"] // 4 + 4 * (w.m // synth_tile_m() + 1 + info["nnzb"])
-        return flops, a_bytes + len(steps) * synth_tile_k() * n + w.m * n * 4, "i8"
+        a_bytes = info["nnz"] * e + info["nnz"] // 4 + 4 * (w.m // synth_tile_m() + 1 + info["nnzb"])
+        return (flops, a_bytes + len(steps) * synth_tile_k() * n * e + w.m * n * ec,
+                "bf16" if w.elem == "bf16" else "i8")
     a_bytes = w.m * w.k // 2 + w.m * w.k // 8
     return flops, a_bytes + w.k * n + w.m * n * 4, "i8"
 
@@ -246,6 +254,8 @@ def main():
         Bt = Bh.cuda()
         cdt = {"bcsr": torch.int16, "bcsr_csr": torch.int16, "wcsr": torch.float32,
                "sp24": torch.int32, "tvw": torch.int32, "slide": torch.int32}[w.fmt]
+        if w.fmt == "tvw" and w.elem == "bf16":
+            cdt = torch.int16
         Ct = torch.empty((w.m, w.n), dtype=cdt, device="cuda")
 
         def step(stream):
@@ -277,7 +287,7 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, d, args.cpu_seconds)
     dense = None
-    if args.dense_baseline and w.fmt == "bcsr":
+    if args.dense_baseline and (w.fmt == "bcsr" or (w.fmt == "tvw" and w.elem == "bf16")):
         dense = dense_baseline(torch, w, d, Bt, stream, args, ms_step)
     elif args.dense_baseline and w.fmt in ("tvw", "sp24", "slide"):
         dense = dense_baseline_i8(torch, w, d, Bt, stream, args, ms_step)
@@ -411,7 +421,7 @@ def roofline(w, flops, nbytes, dtype, ms_step):
     """(roofline of the binding bound, the other bound).  The binding bound is
     the one whose time at peak is longer."""
     t = ms_step * 1e-3
-    traffic = measured_traffic(w.name, DOMINANT_KERNEL[w.fmt])
+    traffic = measured_traffic(w.name, dominant_kernel(w))
     hbm = {"bound": "hbm", "achieved": round(nbytes / t / 1e9, 1), "peak": PEAK_HBM_GBS,
            "unit": "GB/s", "frac": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4),
            "traffic": traffic}
@@ -560,6 +570,16 @@ def cpu_baseline(w, d, target_s):
                 "sample": f"{count} of {units} stored blocks (uniform without replacement, "
                           f"seed 0), full inner dimension {w.n}; "
                           + ("fp64" if w.elem == "bf16" else "int64") + " accumulation"}
+    elif w.fmt == "tvw" and w.elem == "bf16":
+        # the oracle's 2:4 pruning, then its BCSR product over tiles of
+        # 256 x 128 (every element of a stored tile, pruned or not, is walked)
+        pruned = oracle.prune_nm(a["dense"], 2, 4)
+        tm, tk = synth_tile_m(), synth_tile_k()
+        rp, ci, v = oracle.pack_bcsr(pruned, tm, tk)
+        row_nnz = np.repeat(np.diff(rp).astype(np.int64) * (tk // 2), tm)
+
+        def run(rows):
+            oracle.bcsr_spmm(tm, tk, rp, ci, v, B, rows=rows)
     else:
         vals, meta = oracle.pack24(a["dense"])
         # kept values per row: all k/2 for 2:4; for the tile pattern the kept

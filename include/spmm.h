@@ -109,8 +109,9 @@ typedef struct {
  *  TVW (nt stored tiles of tm x tk, mt = m / tm tile rows)
  *    SPMM_ARRAY_ROW_PTR   int32[mt + 1]   stored tiles of tile row T: [row_ptr[T], row_ptr[T+1])
  *    SPMM_ARRAY_COL_IDX   int32[nt]       tile column (k / tk units), ascending in a tile row
- *    SPMM_ARRAY_VALS      int8[nt * tm * tk/2]  each stored tile in the 2:4 layout above,
- *                                         tile row-major, rows of tk/2 kept values
+ *    SPMM_ARRAY_VALS      int8 or bf16 (uint16)[nt * tm * tk/2]  each stored tile in the
+ *                                         2:4 layout above, tile row-major, rows of tk/2
+ *                                         kept values
  *    SPMM_ARRAY_META      uint8[nt * tm * tk/8] each stored tile's nibbles, rows of tk/8 */
 typedef enum {
   SPMM_ARRAY_ROW_PTR = 0,
@@ -151,15 +152,18 @@ spmm_status_t spmm_pack_slide(int64_t m, int64_t k, const int8_t *a_host, int64_
                               spmm_matrix_t *out);
 
 /* Tile-vector-wise (the tile-wise pattern combined with 2:4 of "Accelerating
- * Sparse DNNs Based on Tiled GEMM", abstract) from a dense row-major int8
- * matrix a_host [m x k] (lda >= k): A is cut into tile_m x tile_k tiles, a
- * tile is stored when any element is nonzero, and a stored tile is pruned
- * 2:4 along k by the rule of spmm_pack_24.  The product is therefore the 2:4
- * product with the zero tiles skipped.  Requires m % tile_m == 0,
- * k % tile_k == 0 and tile_k % 8 == 0 (else INVALID_ARG); the kernels take
- * 256 x 128 tiles (spmm_plan returns UNSUPPORTED for others). */
-spmm_status_t spmm_pack_tvw(int64_t m, int64_t k, const int8_t *a_host, int64_t lda, int32_t tile_m,
-                            int32_t tile_k, spmm_matrix_t *out);
+ * Sparse DNNs Based on Tiled GEMM", abstract) from a dense row-major matrix
+ * a_host [m x k] (lda >= k) of dtype SPMM_I8 (int8) or SPMM_BF16 (uint16 bit
+ * patterns; else UNSUPPORTED): A is cut into tile_m x tile_k tiles, a tile is
+ * stored when any element is nonzero (bf16: +0 and -0 are zero, NaN is not),
+ * and a stored tile is pruned 2:4 along k by the rule of spmm_pack_24 (for
+ * bf16, |a| in magnitude order, every NaN above infinity and NaNs equal).  The product is
+ * therefore the 2:4 product of the pruned A with the zero tiles skipped.
+ * Requires m % tile_m == 0, k % tile_k == 0 and tile_k % 8 == 0 (else
+ * INVALID_ARG); the kernels take tile_m = 256 and tile_k a multiple of 128
+ * (int8) or 64 (bf16) (spmm_plan returns UNSUPPORTED for others). */
+spmm_status_t spmm_pack_tvw(int64_t m, int64_t k, spmm_dtype_t dtype, const void *a_host,
+                            int64_t lda, int32_t tile_m, int32_t tile_k, spmm_matrix_t *out);
 
 /* BCSR from a canonical CSR on the host (row_ptr, col_idx as for
  * spmm_pack_wcsr; vals bf16 bit patterns, uint16[nnz]).  A block is stored
@@ -218,7 +222,9 @@ void spmm_matrix_destroy(spmm_matrix_t a);
  *   BCSR (64 x 64 blocks): (BF16, BF16), n % 8 == 0
  *   WCSR:                  (F32, F32), any n >= 1
  *   2:4:                   (I8, I32), n % 16 == 0
- *   TVW (256 x 128 tiles): (I8, I32), n % 16 == 0
+ *   TVW, int8 (256 x 128j tiles):  (I8, I32), n % 16 == 0
+ *   TVW, bf16 (256 x 64j tiles):   (BF16, BF16), n % 16 == 0; fp32 sums rounded to
+ *                                  nearest even
  *   SLIDE:                 (I8, I32), n % 16 == 0 (plus a k_lift * n workspace)
  * A BCSR matrix packed with reordering also gets a workspace for B's rows in
  * the packed column order (k * n * 2 bytes).  Anything else is UNSUPPORTED.  n = 0 is allowed (execute does nothing). */

@@ -25,7 +25,7 @@ def build(verbose: bool = False) -> str:
     """Compile liboracle.so with gcc (no -ffast-math; OpenMP over rows)."""
     tmp = LIB_PATH + ".tmp"
     cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
-           "-o", tmp, _SRC]
+           "-o", tmp, _SRC, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
@@ -56,6 +56,7 @@ def lib():
             "orc_pack24": (C.c_int, [i64, i64, P, i64, P, P]),
             "orc_densify24": (None, [i64, i64, P, P, P]),
             "orc_prune_nm": (C.c_int, [i64, i64, P, i64, C.c_int, C.c_int, P]),
+            "orc_prune_nm_bf16": (C.c_int, [i64, i64, P, i64, C.c_int, C.c_int, P]),
             "orc_csr_spmm_rows": (None, [P, P, P, P, i64, i64, P, i64, i64, P]),
             "orc_bcsr_spmm_rows": (None, [i32, i32, P, P, P, P, i64, i64, P, i64, i64, P]),
             "orc_sp24_spmm_rows": (i64, [i64, P, P, P, i64, i64, P, i64, i64, P]),
@@ -186,12 +187,16 @@ def densify24(vals, meta) -> np.ndarray:
 
 
 def prune_nm(a: np.ndarray, keep: int, group: int) -> np.ndarray:
-    """Dense int8 with only the `keep` largest |a| of every `group`
-    consecutive elements of a row kept (ties to the lower position)."""
-    a = _c(a, np.int8)
+    """Dense int8, or bf16 bit patterns (uint16), with only the `keep` largest
+    |a| of every `group` consecutive elements of a row kept (ties to the lower
+    position; for bf16 NaN ranks above every number)."""
+    a = np.asarray(a)
+    bf16 = a.dtype == np.uint16
+    a = _c(a, np.uint16 if bf16 else np.int8)
     m, k = a.shape
-    out = np.empty((m, k), dtype=np.int8)
-    if lib().orc_prune_nm(m, k, _p(a), k, keep, group, _p(out)) != 0:
+    out = np.empty((m, k), dtype=a.dtype)
+    fn = lib().orc_prune_nm_bf16 if bf16 else lib().orc_prune_nm
+    if fn(m, k, _p(a), k, keep, group, _p(out)) != 0:
         raise ValueError("k must be a multiple of the group, group <= 64")
     return out
 

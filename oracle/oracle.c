@@ -7,6 +7,7 @@
  */
 #include "oracle.h"
 
+#include <math.h>
 #include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
@@ -380,6 +381,35 @@ int orc_prune_nm(int64_t m, int64_t k, const int8_t *a, int64_t lda, int keep, i
           if (au > at || (au == at && u < t)) ++before;
         }
         dst[t] = before < keep ? grp[t] : 0;
+      }
+    }
+  return 0;
+}
+
+/* 1 when bf16 u has the larger magnitude than bf16 t: compared as real
+ * numbers in double, a NaN above every number, two NaNs equal */
+static int bf16_mag_above(uint16_t u, uint16_t t) {
+  const double du = orc_bf16_to_double(u), dt = orc_bf16_to_double(t);
+  const int nu = du != du, nt = dt != dt;
+  if (nu || nt) return nu && !nt;
+  return fabs(du) > fabs(dt);
+}
+
+int orc_prune_nm_bf16(int64_t m, int64_t k, const uint16_t *a, int64_t lda, int keep, int group,
+                      uint16_t *out) {
+  if (group <= 0 || group > 64 || keep < 0 || keep > group || k % group != 0 || lda < k) return -1;
+#pragma omp parallel for
+  for (int64_t i = 0; i < m; ++i)
+    for (int64_t g = 0; g < k / group; ++g) {
+      const uint16_t *grp = a + i * lda + g * group;
+      uint16_t *dst = out + i * k + g * group;
+      /* as for int8: t is kept iff fewer than `keep` positions rank before it */
+      for (int t = 0; t < group; ++t) {
+        int before = 0;
+        for (int u = 0; u < group; ++u)
+          if (bf16_mag_above(grp[u], grp[t]) || (!bf16_mag_above(grp[t], grp[u]) && u < t))
+            ++before;
+        dst[t] = before < keep ? grp[t] : (uint16_t)0;
       }
     }
   return 0;

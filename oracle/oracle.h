@@ -88,6 +88,12 @@ void orc_densify24(int64_t m, int64_t k, const int8_t *vals, const uint8_t *meta
 int orc_prune_nm(int64_t m, int64_t k, const int8_t *a, int64_t lda, int keep, int group,
                  int8_t *out);
 
+/* The same rule for bf16 bit patterns [TW abstract; DP N:M entry]: rank by
+ * |a| as a real number, NaN above every number and NaNs equal, ties to the
+ * lower position; dropped elements become +0 (bits 0).  Same return codes. */
+int orc_prune_nm_bf16(int64_t m, int64_t k, const uint16_t *a, int64_t lda, int keep, int group,
+                      uint16_t *out);
+
 /* ---- reference products [AS abstract; MC abstract; DP SpMM entry] ------- */
 /* out[r][j - j0] = sum over stored (rows[r], c) in ascending c of
  * A[rows[r]][c] * B[c][j], for j in [j0, j1).  out is row-major with

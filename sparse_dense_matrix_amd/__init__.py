@@ -87,7 +87,7 @@ def _load():
         "spmm_pack_wcsr": (st, [i64, i64, st, P, P, P, i32, i64, C.POINTER(P)]),
         "spmm_pack_bcsr_csr": (st, [i64, i64, st, P, P, P, i32, i32, i32, C.POINTER(P)]),
         "spmm_pack_24": (st, [i64, i64, P, i64, C.POINTER(P)]),
-        "spmm_pack_tvw": (st, [i64, i64, P, i64, i32, i32, C.POINTER(P)]),
+        "spmm_pack_tvw": (st, [i64, i64, i32, P, i64, i32, i32, C.POINTER(P)]),
         "spmm_pack_slide": (st, [i64, i64, P, i64, i32, C.POINTER(P)]),
         "spmm_matrix_info": (st, [P, C.POINTER(MatrixInfo)]),
         "spmm_matrix_array": (st, [P, i32, C.POINTER(P), C.POINTER(i64)]),
@@ -195,13 +195,20 @@ def spmm_pack_slide(a: np.ndarray, group: int = 8) -> Matrix:
 
 
 def spmm_pack_tvw(a: np.ndarray, tile_m: int = 256, tile_k: int = 128) -> Matrix:
-    """Tile-vector-wise from a dense int8 matrix: tiles with a nonzero are
-    stored, 2:4-pruned along k."""
-    a = np.ascontiguousarray(a, dtype=np.int8)
+    """Tile-vector-wise from a dense matrix: int8, or bf16 given as uint16
+    bit patterns.  Tiles with a nonzero are stored, 2:4-pruned along k."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        dtype = BF16
+    elif a.dtype == np.int8:
+        dtype = I8
+    else:
+        raise TypeError("spmm_pack_tvw takes int8 or uint16 (bf16 bits) values")
+    a = np.ascontiguousarray(a)
     if a.ndim != 2:
         raise ValueError("a must be 2-D")
     h = C.c_void_p()
-    _check(_lib.spmm_pack_tvw(a.shape[0], a.shape[1], _ptr(a), a.shape[1], tile_m, tile_k,
+    _check(_lib.spmm_pack_tvw(a.shape[0], a.shape[1], dtype, _ptr(a), a.shape[1], tile_m, tile_k,
                               C.byref(h)), "spmm_pack_tvw")
     return Matrix(h)
 
@@ -271,8 +278,11 @@ def spmm_matrix_array(mat: Matrix, which: int) -> np.ndarray:
     data, count = C.c_void_p(), C.c_int64()
     _check(_lib.spmm_matrix_array(mat.handle, which, C.byref(data), C.byref(count)),
            "spmm_matrix_array")
-    fmt = spmm_matrix_info(mat)["format"]
+    info = spmm_matrix_info(mat)
+    fmt = info["format"]
     dt = np.dtype(_ARRAY_DTYPES[(fmt, which)])
+    if fmt == FORMAT_TVW and which == ARRAY_VALS and info["dtype"] == BF16:
+        dt = np.dtype(np.uint16)
     if count.value == 0:
         return np.zeros(0, dtype=dt)
     buf = (C.c_char * (count.value * dt.itemsize)).from_address(data.value)

@@ -357,13 +357,15 @@ spmm_status_t plan_24(spmm_plan_s *p) {
   // a sliding-window matrix is the 2:4 matrix of its lifted columns
   const bool slide = a.format == SPMM_FORMAT_SLIDE;
   const int64_t k = slide ? a.k_lift : a.k;
-  const int64_t TM = sp24_tile_m(), TK = sp24_tile_k();
+  const int64_t TM = sp24_tile_m(), TK = sp24_tile_k(false);
   const int64_t m_pad = (a.m + TM - 1) / TM * TM;
   const int64_t k_pad = std::max<int64_t>(TK, (k + TK - 1) / TK * TK);
   std::vector<int8_t> v(static_cast<size_t>(m_pad * (k_pad / 2)));
   std::vector<uint8_t> mt(static_cast<size_t>(m_pad * (k_pad / 8)));
-  sp24_tile_layout(a.vals24.data(), a.meta24.data(), a.m, k, m_pad, k_pad, v.data(), mt.data());
+  sp24_tile_layout(a.vals24.data(), a.meta24.data(), a.m, k, m_pad, k_pad, false, v.data(),
+                   mt.data());
   Sp24Launch &L = p->sp24;
+  L.bf16 = false;
   spmm_status_t s;
   int8_t *dv = nullptr;
   uint8_t *dm = nullptr;
@@ -400,15 +402,28 @@ spmm_status_t plan_24(spmm_plan_s *p) {
 }
 
 // ---- tile-vector-wise plan: the stored tiles in the 2:4 kernel's layout ------
+// A stored tile of tk columns becomes tk / TK consecutive k-steps of the
+// kernel (TK = 128 int8, 64 bf16).
 spmm_status_t plan_tvw(spmm_plan_s *p) {
   const Matrix &a = *p->a;
+  const bool bf16 = a.dtype == SPMM_BF16;
+  const int64_t TK = sp24_tile_k(bf16), elem = bf16 ? 2 : 1;
   if (p->n % 16 != 0) return fail(SPMM_ERR_UNSUPPORTED, "spmm_plan: TVW needs n % 16 == 0");
-  if (a.bm != sp24_tile_m() || a.bk != sp24_tile_k())
-    return fail(SPMM_ERR_UNSUPPORTED, "spmm_plan: TVW kernels take 256 x 128 tiles");
+  if (a.bm != sp24_tile_m() || a.bk % TK != 0)
+    return fail(SPMM_ERR_UNSUPPORTED,
+                "spmm_plan: TVW kernels take tiles of 256 rows and a multiple of 128 (int8) or "
+                "64 (bf16) columns");
   const int64_t ntiles = static_cast<int64_t>(a.bcol_idx.size());
-  std::vector<int8_t> v(static_cast<size_t>(ntiles * a.bm * (a.bk / 2)));
+  const int64_t per = a.bk / TK;
+  std::vector<int8_t> v(static_cast<size_t>(ntiles * a.bm * (a.bk / 2) * elem));
   std::vector<uint8_t> mt(static_cast<size_t>(ntiles * a.bm * (a.bk / 8)));
-  tvw_tile_layout(a.vals24.data(), a.meta24.data(), ntiles, v.data(), mt.data());
+  const void *src = bf16 ? static_cast<const void *>(a.vals24_bf16.data())
+                         : static_cast<const void *>(a.vals24.data());
+  tvw_tile_layout(src, a.meta24.data(), ntiles, a.bk, bf16, v.data(), mt.data());
+  std::vector<int32_t> ptr(a.brow_ptr.size()), step(static_cast<size_t>(ntiles * per));
+  for (size_t T = 0; T < a.brow_ptr.size(); ++T) ptr[T] = static_cast<int32_t>(a.brow_ptr[T] * per);
+  for (int64_t t = 0; t < ntiles; ++t)
+    for (int64_t s = 0; s < per; ++s) step[t * per + s] = static_cast<int32_t>(a.bcol_idx[t] * per + s);
   Sp24Launch &L = p->sp24;
   spmm_status_t s;
   int8_t *dv = nullptr;
@@ -416,8 +431,9 @@ spmm_status_t plan_tvw(spmm_plan_s *p) {
   int32_t *tp = nullptr, *ts = nullptr;
   if ((s = upload_vec(p, v, &dv)) != SPMM_OK) return s;
   if ((s = upload_vec(p, mt, &dm)) != SPMM_OK) return s;
-  if ((s = upload_vec(p, a.brow_ptr, &tp)) != SPMM_OK) return s;
-  if ((s = upload_vec(p, a.bcol_idx, &ts)) != SPMM_OK) return s;
+  if ((s = upload_vec(p, ptr, &tp)) != SPMM_OK) return s;
+  if ((s = upload_vec(p, step, &ts)) != SPMM_OK) return s;
+  L.bf16 = bf16;
   L.vals = dv;
   L.meta = dm;
   L.tile_ptr = tp;
@@ -502,16 +518,18 @@ spmm_status_t spmm_pack_slide(int64_t m, int64_t k, const int8_t *a_host, int64_
   });
 }
 
-spmm_status_t spmm_pack_tvw(int64_t m, int64_t k, const int8_t *a_host, int64_t lda, int32_t tile_m,
-                            int32_t tile_k, spmm_matrix_t *out) {
+spmm_status_t spmm_pack_tvw(int64_t m, int64_t k, spmm_dtype_t dtype, const void *a_host,
+                            int64_t lda, int32_t tile_m, int32_t tile_k, spmm_matrix_t *out) {
   if (!out) return fail(SPMM_ERR_INVALID_ARG, "spmm_pack_tvw: out is NULL");
   *out = nullptr;
+  if (dtype != SPMM_I8 && dtype != SPMM_BF16)
+    return fail(SPMM_ERR_UNSUPPORTED, "spmm_pack_tvw: int8 or bf16 values only");
   if (m < 0 || k < 0 || m > INT32_MAX || k > INT32_MAX || tile_m <= 0 || tile_k <= 0 ||
       tile_k % 8 != 0 || m % tile_m != 0 || k % tile_k != 0 || lda < k || (m * k > 0 && !a_host))
     return fail(SPMM_ERR_INVALID_ARG, "spmm_pack_tvw: bad shape, tile, lda or pointer");
   return guarded([&]() -> spmm_status_t {
     auto *a = new spmm_matrix_s();
-    spmm_status_t s = pack_tvw_i8(m, k, a_host, lda, tile_m, tile_k, *a);
+    spmm_status_t s = pack_tvw(m, k, dtype, a_host, lda, tile_m, tile_k, *a);
     if (s != SPMM_OK) {
       delete a;
       return s;
@@ -651,7 +669,8 @@ spmm_status_t spmm_matrix_array(spmm_matrix_t a, int32_t which, const void **dat
     case SPMM_FORMAT_TVW:
       if (which == SPMM_ARRAY_ROW_PTR) return give(a->brow_ptr);
       if (which == SPMM_ARRAY_COL_IDX) return give(a->bcol_idx);
-      if (which == SPMM_ARRAY_VALS) return give(a->vals24);
+      if (which == SPMM_ARRAY_VALS)
+        return a->dtype == SPMM_BF16 ? give(a->vals24_bf16) : give(a->vals24);
       if (which == SPMM_ARRAY_META) return give(a->meta24);
       break;
   }
@@ -670,7 +689,9 @@ spmm_status_t spmm_plan(spmm_matrix_t a, int64_t n, spmm_dtype_t b_dtype, spmm_d
       (a->format == SPMM_FORMAT_WCSR && b_dtype == SPMM_F32 && c_dtype == SPMM_F32) ||
       ((a->format == SPMM_FORMAT_24 || a->format == SPMM_FORMAT_TVW ||
         a->format == SPMM_FORMAT_SLIDE) &&
-       b_dtype == SPMM_I8 && c_dtype == SPMM_I32);
+       a->dtype == SPMM_I8 && b_dtype == SPMM_I8 && c_dtype == SPMM_I32) ||
+      (a->format == SPMM_FORMAT_TVW && a->dtype == SPMM_BF16 && b_dtype == SPMM_BF16 &&
+       c_dtype == SPMM_BF16);
   if (!ok_types) return fail(SPMM_ERR_UNSUPPORTED, "spmm_plan: unsupported (format, B, C) types");
   int ndev = 0;
   hipError_t e = hipGetDeviceCount(&ndev);
@@ -727,13 +748,10 @@ spmm_status_t spmm_execute(spmm_plan_t p, const void *b_dev, int64_t ldb, void *
   const Matrix &a = *p->a;
   const int64_t n = p->n;
   if (n == 0 || a.m == 0) return SPMM_OK;
-  const int64_t eb = a.format == SPMM_FORMAT_BCSR
-                         ? 2
-                         : ((a.format == SPMM_FORMAT_24 || a.format == SPMM_FORMAT_TVW ||
-                             a.format == SPMM_FORMAT_SLIDE)
-                                ? 1
-                                : 4);
-  const int64_t ec = a.format == SPMM_FORMAT_BCSR ? 2 : 4;
+  const bool bf16 = a.format == SPMM_FORMAT_BCSR || a.dtype == SPMM_BF16;
+  const bool i8 = a.dtype == SPMM_I8;
+  const int64_t eb = bf16 ? 2 : (i8 ? 1 : 4);  // B: bf16, int8 or fp32
+  const int64_t ec = bf16 ? 2 : 4;              // C: bf16, int32 or fp32
   if (!c_dev || (!b_dev && a.k > 0))
     return fail(SPMM_ERR_INVALID_ARG, "spmm_execute: B or C is NULL");
   if (!aligned16(b_dev) || !aligned16(c_dev) || ldb < n || ldc < n || (ldb * eb) % 16 != 0 ||
@@ -759,11 +777,11 @@ spmm_status_t spmm_execute(spmm_plan_t p, const void *b_dev, int64_t ldb, void *
     e = launch_wcsr_f32(L, stream);
   } else {
     Sp24Launch L = p->sp24;
-    L.B = static_cast<const int8_t *>(b_dev);
+    L.B = b_dev;
     L.ldb = ldb;
-    L.C = static_cast<int32_t *>(c_dev);
+    L.C = c_dev;
     L.ldc = ldc;
-    e = launch_sp24_i8(L, stream);
+    e = launch_sp24(L, stream);
   }
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return SPMM_OK;

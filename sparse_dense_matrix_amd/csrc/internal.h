@@ -47,8 +47,10 @@ struct Matrix {
   std::vector<int32_t> chunk_window;
   std::vector<int64_t> chunk_begin;
   // 2:4 (and the stored tiles of tile-vector-wise: brow_ptr / bcol_idx over
-  // tiles of bm x bk, vals24 / meta24 tile after tile)
+  // tiles of bm x bk, vals24 / meta24 tile after tile); bf16 values of a
+  // bf16 tile-vector-wise matrix go to vals24_bf16 instead of vals24
   std::vector<int8_t> vals24;
+  std::vector<uint16_t> vals24_bf16;
   std::vector<uint8_t> meta24;
 };
 
@@ -66,8 +68,9 @@ spmm_status_t pack_slide_i8(int64_t m, int64_t k, const int8_t *a, int64_t lda, 
                             Matrix &out);
 // lifted row j of a sliding-window matrix -> row of B it multiplies
 int64_t slide_source_row(int64_t j, int32_t group);
-spmm_status_t pack_tvw_i8(int64_t m, int64_t k, const int8_t *a, int64_t lda, int32_t tm,
-                          int32_t tk, Matrix &out);
+// dtype SPMM_I8 (a: int8) or SPMM_BF16 (a: bf16 bit patterns)
+spmm_status_t pack_tvw(int64_t m, int64_t k, spmm_dtype_t dtype, const void *a, int64_t lda,
+                       int32_t tm, int32_t tk, Matrix &out);
 spmm_status_t pack_bcsr_csr_bf16(int64_t m, int64_t k, const int64_t *row_ptr,
                                  const int32_t *col_idx, const uint16_t *vals, int32_t bm,
                                  int32_t bk, bool reorder, Matrix &out);
@@ -190,7 +193,8 @@ int sddmm_bcsr_group();
 hipError_t launch_sddmm_bcsr(const SddmmBcsrLaunch &a, hipStream_t s);
 
 struct Sp24Launch {
-  const int8_t *vals;   // tiled copy of the values (sp24_tile_layout / tvw_tile_layout)
+  bool bf16;            // bf16 A, B and C (else int8 A, B and int32 C)
+  const void *vals;     // tiled copy of the values (sp24_tile_layout / tvw_tile_layout)
   const uint8_t *meta;  // tiled copy of the index words
   // tile-vector-wise A: stored k-steps of row tile T are
   // tile_step[tile_ptr[T] .. tile_ptr[T+1]); null for a plain 2:4 A
@@ -200,30 +204,31 @@ struct Sp24Launch {
   // b_lift[j] = B[b_rows[j]] for the k (= lifted) rows, gathered first from
   // the caller's B of k_src rows; null otherwise
   const int32_t *b_rows;
-  int8_t *b_lift;
+  void *b_lift;
   int64_t m, k, n;
   int64_t m_pad, k_pad;
-  const int8_t *B;
-  int64_t ldb;
-  int32_t *C;
-  int64_t ldc;
+  const void *B;
+  int64_t ldb;  // elements
+  void *C;
+  int64_t ldc;  // elements
 };
-// Plan-private copies of the canonical 2:4 arrays, zero-padded to m_pad x
-// k_pad and laid out per 256-row tile and 128-deep k-step in the order the
-// kernel's shared-memory stages hold them (vals_tiled: m_pad * k_pad / 2
-// bytes, meta_tiled: m_pad * k_pad / 8 bytes).
-void sp24_tile_layout(const int8_t *vals, const uint8_t *meta, int64_t m, int64_t k,
-                      int64_t m_pad, int64_t k_pad, int8_t *vals_tiled, uint8_t *meta_tiled);
+// Plan-private copies of the canonical 2:4 arrays (values int8 or bf16),
+// zero-padded to m_pad x k_pad and laid out per 256-row tile and k-step
+// (sp24_tile_k) in the order the kernel's shared-memory stages hold them
+// (vals_tiled: m_pad * k_pad / 2 elements, meta_tiled: m_pad * k_pad / 8
+// bytes).
+void sp24_tile_layout(const void *vals, const uint8_t *meta, int64_t m, int64_t k, int64_t m_pad,
+                      int64_t k_pad, bool bf16, void *vals_tiled, uint8_t *meta_tiled);
 // The same layout for the stored tiles of a tile-vector-wise matrix, given
-// per tile as [256][64] values and [256][16] index bytes (ntiles * 16 KB and
-// ntiles * 4 KB out).
-void tvw_tile_layout(const int8_t *tile_vals, const uint8_t *tile_meta, int64_t ntiles,
-                     int8_t *vals_tiled, uint8_t *meta_tiled);
+// per tile as [256][tk/2] values and [256][tk/8] index bytes, tk a multiple
+// of sp24_tile_k; every tile becomes tk / sp24_tile_k consecutive k-steps.
+void tvw_tile_layout(const void *tile_vals, const uint8_t *tile_meta, int64_t ntiles, int32_t tk,
+                     bool bf16, void *vals_tiled, uint8_t *meta_tiled);
 int sp24_tile_m();
 int sp24_tile_n();
-int sp24_tile_k();
+int sp24_tile_k(bool bf16);  // dense k per step: 128 int8, 64 bf16
 int64_t sp24_grid(int64_t m, int64_t n);
-hipError_t launch_sp24_i8(const Sp24Launch &a, hipStream_t s);
+hipError_t launch_sp24(const Sp24Launch &a, hipStream_t s);
 
 }  // namespace sdm
 

@@ -278,16 +278,23 @@ spmm_status_t pack_bcsr_csr_bf16(int64_t m, int64_t k, const int64_t *row_ptr,
 }
 
 // ---------------------------------------------------------------------------
-// 2:4: in every group of four, the two largest of key = |a| * 4 + (3 - pos)
+// 2:4: in every group of four, the two largest of key = mag(a) * 4 + (3 - pos)
 // are kept (larger magnitude first, ties to the lower position), then stored
-// in ascending position.
+// in ascending position.  mag is |a| for int8 (|-128| = 128); for bf16 it is
+// the bit pattern with the sign cleared, which orders finite values and
+// infinities by magnitude, with every NaN mapped to one rank above infinity
+// (so NaNs tie with each other).
 // ---------------------------------------------------------------------------
-static inline void prune_group(const int8_t *grp, int8_t *kept, uint8_t &nibble) {
+static inline int mag(int8_t x) { return x < 0 ? -x : x; }
+static inline int mag(uint16_t x) {
+  const int v = x & 0x7fff;
+  return v > 0x7f80 ? 0x7f81 : v;
+}
+
+template <class T>
+static inline void prune_group(const T *grp, T *kept, uint8_t &nibble) {
   int key[4];
-  for (int t = 0; t < 4; ++t) {
-    const int x = grp[t];
-    key[t] = (x < 0 ? -x : x) * 4 + (3 - t);
-  }
+  for (int t = 0; t < 4; ++t) key[t] = mag(grp[t]) * 4 + (3 - t);
   int first = 0;
   for (int t = 1; t < 4; ++t)
     if (key[t] > key[first]) first = t;
@@ -301,7 +308,8 @@ static inline void prune_group(const int8_t *grp, int8_t *kept, uint8_t &nibble)
 }
 
 // one row of `len` elements (len % 8 == 0) into len/2 values and len/8 bytes
-static void prune_row(const int8_t *row, int64_t len, int8_t *v, uint8_t *mt) {
+template <class T>
+static void prune_row(const T *row, int64_t len, T *v, uint8_t *mt) {
   for (int64_t g = 0; g < len / 4; ++g) {
     uint8_t nibble;
     prune_group(row + 4 * g, v + 2 * g, nibble);
@@ -406,32 +414,33 @@ spmm_status_t pack_slide_i8(int64_t m, int64_t k, const int8_t *a, int64_t lda, 
 
 // ---------------------------------------------------------------------------
 // Tile-vector-wise (the tiled-GEMM page, abstract): A is cut into tm x tk
-// tiles; a tile is stored when any element is nonzero, and a stored tile is
-// pruned 2:4 along k exactly as above.  Since 2:4 pruning maps a zero tile
-// to zero and keeps a nonzero in every nonzero group, the stored product is
-// the 2:4 product of A with the zero tiles skipped.
+// tiles; a tile is stored when any element is nonzero (for bf16, +0 and -0
+// are zero and NaN is not), and a stored tile is pruned 2:4 along k exactly
+// as above.  Since 2:4 pruning maps a zero tile to zero and keeps a nonzero
+// in every nonzero group, the stored product is the 2:4 product of A with
+// the zero tiles skipped.
 // ---------------------------------------------------------------------------
-spmm_status_t pack_tvw_i8(int64_t m, int64_t k, const int8_t *a, int64_t lda, int32_t tm,
-                          int32_t tk, Matrix &out) {
+template <class V>
+static spmm_status_t pack_tvw_t(int64_t m, int64_t k, const V *a, int64_t lda, int32_t tm,
+                                int32_t tk, std::vector<V> &vals, Matrix &out) {
   const int64_t mt = m / tm, kt = k / tk;
   out.format = SPMM_FORMAT_TVW;
-  out.dtype = SPMM_I8;
   out.m = m;
   out.k = k;
   out.bm = tm;
   out.bk = tk;
   out.brow_ptr.assign(mt + 1, 0);
   out.bcol_idx.clear();
-  out.vals24.clear();
+  vals.clear();
   out.meta24.clear();
   const int64_t tv = static_cast<int64_t>(tm) * (tk / 2), tmeta = static_cast<int64_t>(tm) * (tk / 8);
   for (int64_t T = 0; T < mt; ++T) {
     for (int64_t s = 0; s < kt; ++s) {
       bool any = false;
       for (int64_t i = T * tm; i < (T + 1) * tm && !any; ++i) {
-        const int8_t *row = a + i * lda + s * tk;
+        const V *row = a + i * lda + s * tk;
         for (int32_t j = 0; j < tk; ++j)
-          if (row[j] != 0) {
+          if (mag(row[j]) != 0) {
             any = true;
             break;
           }
@@ -439,11 +448,11 @@ spmm_status_t pack_tvw_i8(int64_t m, int64_t k, const int8_t *a, int64_t lda, in
       if (!any) continue;
       if (out.bcol_idx.size() >= static_cast<size_t>(INT32_MAX))
         return fail(SPMM_ERR_UNSUPPORTED, "spmm_pack_tvw: more than 2^31-1 tiles");
-      const size_t v0 = out.vals24.size(), m0 = out.meta24.size();
-      out.vals24.resize(v0 + static_cast<size_t>(tv), 0);
+      const size_t v0 = vals.size(), m0 = out.meta24.size();
+      vals.resize(v0 + static_cast<size_t>(tv), 0);
       out.meta24.resize(m0 + static_cast<size_t>(tmeta), 0);
       for (int32_t r = 0; r < tm; ++r)
-        prune_row(a + (T * tm + r) * lda + s * tk, tk, out.vals24.data() + v0 + r * (tk / 2),
+        prune_row(a + (T * tm + r) * lda + s * tk, tk, vals.data() + v0 + r * (tk / 2),
                   out.meta24.data() + m0 + r * (tk / 8));
       out.bcol_idx.push_back(static_cast<int32_t>(s));
     }
@@ -451,6 +460,16 @@ spmm_status_t pack_tvw_i8(int64_t m, int64_t k, const int8_t *a, int64_t lda, in
   }
   out.nnz = static_cast<int64_t>(out.bcol_idx.size()) * tv;
   return SPMM_OK;
+}
+
+spmm_status_t pack_tvw(int64_t m, int64_t k, spmm_dtype_t dtype, const void *a, int64_t lda,
+                       int32_t tm, int32_t tk, Matrix &out) {
+  out.dtype = dtype;
+  out.vals24.clear();
+  out.vals24_bf16.clear();
+  if (dtype == SPMM_BF16)
+    return pack_tvw_t(m, k, static_cast<const uint16_t *>(a), lda, tm, tk, out.vals24_bf16, out);
+  return pack_tvw_t(m, k, static_cast<const int8_t *>(a), lda, tm, tk, out.vals24, out);
 }
 
 }  // namespace sdm

@@ -221,7 +221,8 @@ class Workload:
     block: int = 64               # bcsr
     nblocks: int = 0
     sigma: float = 0.02
-    elem: str = ""                # sddmm_bcsr: "bf16" | "i8" operands X, Y
+    elem: str = ""                # sddmm_bcsr: "bf16" | "i8" operands X, Y; tvw: "bf16"
+                                  # A and B (default int8)
     scramble: int = 0             # > 0: a block-sparse matrix with rows and columns
                                   # shuffled (this seed), given as CSR
     reorder: bool = False         # bcsr_csr: pack after the row/column reordering
@@ -258,6 +259,11 @@ WORKLOADS: Dict[str, Workload] = {
     # of its 256 x 128 tiles zero (2:4 inside the rest), same B as the 2:4 case
     "tvw_i8_8192_t50": Workload("tvw_i8_8192_t50", "tvw", 8192, 8192, 2048, 20260009, nblocks=1024),
     "tvw_i8_8192_t75": Workload("tvw_i8_8192_t75", "tvw", 8192, 8192, 2048, 20260010, nblocks=512),
+    # the same shapes and tile counts in bf16 (weights N(0, 0.02), B N(0, 1))
+    "tvw_bf16_8192_t50": Workload("tvw_bf16_8192_t50", "tvw", 8192, 8192, 2048, 20260012,
+                                  nblocks=1024, elem="bf16"),
+    "tvw_bf16_8192_t75": Workload("tvw_bf16_8192_t75", "tvw", 8192, 8192, 2048, 20260013,
+                                  nblocks=512, elem="bf16"),
     # the 2:4 case's shapes with a milder pattern: 6 of every 8 kept, as
     # overlapping 2:4 windows
     "slide68_i8_8192": Workload("slide68_i8_8192", "slide", 8192, 8192, 2048, 20260011, nm_group=8),
@@ -295,6 +301,7 @@ SMALL: Dict[str, Workload] = {
     "sddmm_bcsr_small": _bcsr("sddmm_bcsr_small", 640, 512, 1000, 0.7, 35, fmt="sddmm_bcsr",
                               elem="bf16"),
     "tvw_small": Workload("tvw_small", "tvw", 512, 1024, 272, 38, nblocks=6),
+    "tvw_bf16_small": Workload("tvw_bf16_small", "tvw", 512, 1024, 272, 40, nblocks=6, elem="bf16"),
     "slide_small": Workload("slide_small", "slide", 320, 512, 400, 39, nm_group=8),
     "scrambled_small": Workload("scrambled_small", "bcsr_csr", 1024, 768, 520, 36, nblocks=30,
                                 scramble=37, reorder=True),
@@ -322,6 +329,9 @@ def make_a(w: Workload) -> dict:
         return {"dense": a, "block_ids": ids}
     if w.fmt in ("sp24", "slide"):
         return {"dense": int8_uniform(rng(w.seed, S_AVAL), (w.m, w.k))}
+    if w.fmt == "tvw" and w.elem == "bf16":
+        a, _ = block_sparse_dense_bf16(w.m, w.k, TVW_TILE_M, TVW_TILE_K, w.nblocks, w.sigma, w.seed)
+        return {"dense": a}
     if w.fmt == "tvw":
         return {"dense": tile_sparse_i8(w.m, w.k, TVW_TILE_M, TVW_TILE_K, w.nblocks, w.seed)}
     raise ValueError(w.fmt)
@@ -350,7 +360,7 @@ def make_b(w: Workload, n: int | None = None) -> np.ndarray:
         return bf16_bits_to_f32(bits) if w.fmt == "wcsr" else bits   # the same values
     if w.fmt == "wcsr":
         return dense_f32_normal(w.k, n, w.seed)
-    if w.fmt == "bcsr":
+    if w.fmt == "bcsr" or (w.fmt == "tvw" and w.elem == "bf16"):
         return dense_bf16_normal(w.k, n, w.seed)
     if w.fmt in ("sp24", "tvw", "slide"):
         return int8_uniform(rng(w.seed, S_BVAL), (w.k, n))

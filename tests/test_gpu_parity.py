@@ -664,6 +664,108 @@ def test_tvw_8192_sampled(S, orc, name):
     _say(f"{name} tiles={S.spmm_matrix_info(M)['nnzb']} rows={len(rows)} exact")
 
 
+def test_tvw_i8_wide_tiles(S, orc):
+    # 256 x 256 tiles: each stored tile is two consecutive k-steps of the kernel
+    a = synth.tile_sparse_i8(768, 1024, 256, 256, 5, 41)
+    B = synth.int8_uniform(np.random.default_rng(42), (1024, 144))
+    M = S.spmm_pack_tvw(a, 256, 256)
+    P = S.spmm_plan(M, 144, S.I8, S.I32)
+    got = run(S, P, B, 768, 144, "i32")
+    v, mt = orc.pack24(a)
+    np.testing.assert_array_equal(got, orc.sp24_spmm(v, mt, B))
+
+
+# ---------------------------------------------------------------------------
+# tile-vector-wise bf16: the 2:4 kernel on the bf16 sparse MFMA
+# ---------------------------------------------------------------------------
+
+def tvw_bf16_case(S, orc, a_bits, B_bits, tk=128, rows=None, pad=0):
+    """GPU result (uint16 bits) and the oracle's fp64 product of the 2:4-pruned
+    A (its pruning, then its BCSR product over tiles of 256 x tk)."""
+    m, n = a_bits.shape[0], B_bits.shape[1]
+    M = S.spmm_pack_tvw(a_bits, 256, tk)
+    P = S.spmm_plan(M, n, S.BF16, S.BF16)
+    got = run(S, P, B_bits, m, n, "bf16", pad)
+    pruned = orc.prune_nm(a_bits, 2, 4)
+    rp, ci, v = orc.pack_bcsr(pruned, 256, tk)
+    ref = orc.bcsr_spmm(256, tk, rp, ci, v, B_bits, rows=rows)
+    g = bf16_to_f64(got if rows is None else got[rows])
+    assert np.isfinite(g).all(), "unwritten or non-finite outputs"
+    return g, ref, got, M
+
+
+@pytest.mark.parametrize("tk", [128, 64])
+def test_tvw_bf16_small(S, orc, tk):
+    w = synth.SMALL["tvw_bf16_small"]   # 512 x 1024, 6 of 16 tiles of 256 x 128, n = 272
+    a = synth.make_a(w)["dense"]
+    B = synth.make_b(w)
+    for pad in (0, 16):
+        g, ref, _, M = tvw_bf16_case(S, orc, a, B, tk=tk, pad=pad)
+        err = orc.rel_frobenius(g, ref)
+        assert err <= TOL_BF16, err
+    _say(f"tvw_bf16_small tk={tk} tiles={S.spmm_matrix_info(M)['nnzb']} rel={err:.2e}")
+
+
+def test_tvw_bf16_integer_values_are_exact(S, orc):
+    # small integers: every fp32 partial sum is exact, so C must be exactly
+    # the round-to-nearest-even bf16 of the exact sum; pins the index words,
+    # the k order of B and the epilogue bit for bit
+    r = np.random.default_rng(43)
+    m, k, n = 768, 512, 336
+    a = r.integers(-3, 4, size=(m, k)).astype(np.float32)
+    a[0:256, 128:384] = 0                       # tile row 0: two zero tiles
+    a[512:768] = 0
+    a[600, 77] = -2.0                           # tile row 2: one tile, one entry
+    a_bits = synth.f32_to_bf16_bits(a)
+    B = synth.f32_to_bf16_bits(r.integers(-4, 5, size=(k, n)).astype(np.float32))
+    _, ref, got, M = tvw_bf16_case(S, orc, a_bits, B)
+    assert np.abs(ref).max() < 2 ** 24
+    np.testing.assert_array_equal(got & 0x7FFF, synth.f32_to_bf16_bits(ref.astype(np.float32)) & 0x7FFF)
+    nz = ref != 0
+    np.testing.assert_array_equal(got[nz], synth.f32_to_bf16_bits(ref[nz].astype(np.float32)))
+    assert S.spmm_matrix_info(M)["nnzb"] == 4 + 2 + 1
+
+
+def test_tvw_bf16_identity_and_no_tiles(S, orc):
+    m = 512
+    eye = synth.f32_to_bf16_bits(np.eye(m, dtype=np.float32))   # one nonzero per group: kept
+    B = synth.dense_bf16_normal(m, 272, 44)
+    _, _, got, _ = tvw_bf16_case(S, orc, eye, B, tk=64)
+    np.testing.assert_array_equal(got, B)
+    Z = np.zeros((256, 256), np.uint16)
+    M = S.spmm_pack_tvw(Z, 256, 128)
+    P = S.spmm_plan(M, 32, S.BF16, S.BF16)
+    got = run(S, P, synth.dense_bf16_normal(256, 32, 45), 256, 32, "bf16")
+    assert (got & 0x7FFF == 0).all()
+
+
+def test_tvw_bf16_plan_checks(S, orc):
+    a = synth.f32_to_bf16_bits(np.ones((256, 96), np.float32))
+    M = S.spmm_pack_tvw(a, 256, 96)              # 96 is not a multiple of the k-step
+    with pytest.raises(S.SpmmError) as ei:
+        S.spmm_plan(M, 32, S.BF16, S.BF16)
+    assert ei.value.name == "SPMM_ERR_UNSUPPORTED"
+    M = S.spmm_pack_tvw(synth.f32_to_bf16_bits(np.ones((256, 128), np.float32)), 256, 128)
+    for types in ((S.I8, S.I32), (S.BF16, S.F32)):
+        with pytest.raises(S.SpmmError) as ei:
+            S.spmm_plan(M, 32, *types)
+        assert ei.value.name == "SPMM_ERR_UNSUPPORTED"
+
+
+@pytest.mark.parametrize("name", ["tvw_bf16_8192_t50", "tvw_bf16_8192_t75"])
+def test_tvw_bf16_8192_sampled(S, orc, name):
+    w = synth.WORKLOADS[name]
+    a = synth.make_a(w)["dense"]
+    B = synth.make_b(w)
+    r = np.random.default_rng(24)
+    rows = np.unique(np.concatenate([np.arange(16), np.arange(w.m - 16, w.m),
+                                     r.choice(w.m, 64, replace=False)])).astype(np.int64)
+    g, ref, _, M = tvw_bf16_case(S, orc, a, B, rows=rows)
+    err = orc.rel_frobenius(g, ref)
+    assert err <= TOL_BF16, err
+    _say(f"{name} tiles={S.spmm_matrix_info(M)['nnzb']} rows={len(rows)} rel={err:.2e}")
+
+
 # ---------------------------------------------------------------------------
 # (2N-2):2N weights as overlapping 2:4 windows, on the 2:4 kernel
 # ---------------------------------------------------------------------------

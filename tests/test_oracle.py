@@ -457,3 +457,73 @@ def test_prune_nm_hand_cases(orc):
     np.testing.assert_array_equal(orc.prune_nm(a, 6, 8), [[5, 5, 5, 5, 5, 5, 0, 0]])
     with pytest.raises(ValueError):
         orc.prune_nm(np.zeros((1, 12), np.int8), 6, 8)
+
+
+# ---- N:M pruning of bf16 (the 2:4 pattern of tile-vector-wise bf16) ------------
+
+def _bf(x):
+    return synth.f32_to_bf16_bits(np.asarray(x, np.float32))
+
+
+def test_prune_nm_bf16_reduces_to_the_int8_rule(orc):
+    # int8 values are exact in bf16 and keep their magnitude order
+    for seed in range(6):
+        a = synth.int8_uniform(np.random.default_rng(1200 + seed), (7, 64))
+        a[0, :8] = [-128, 127, 127, -128, 0, 0, 0, 5]
+        a[1, :8] = [1, -1, 1, -1, 0, 0, 0, 0]
+        for keep, group in ((2, 4), (6, 8), (3, 16), (0, 4)):
+            got = orc.prune_nm(_bf(a.astype(np.float32)), keep, group)
+            exp = _bf(orc.prune_nm(a, keep, group).astype(np.float32))
+            np.testing.assert_array_equal(got, exp)
+
+
+def test_prune_nm_bf16_hand_cases(orc):
+    inf, nan = np.inf, np.nan
+    rows = [
+        ([1.5, -2.0, 0.25, -0.0], [1.5, -2.0, 0.0, 0.0]),
+        ([-1.0, 1.0078125, 0.5, 1.0], [-1.0, 1.0078125, 0.0, 0.0]),    # 1 and -1 tie
+        ([3.0, -3.0, 3.0, -3.0], [3.0, -3.0, 0.0, 0.0]),
+        ([inf, nan, 1.0, -inf], [inf, nan, 0.0, 0.0]),                 # NaN first, then inf
+        ([0.5, -inf, 65504.0, 1e30], [0.0, -inf, 0.0, 1e30]),
+    ]
+    a = _bf([r[0] for r in rows])
+    exp = _bf([r[1] for r in rows])
+    got = orc.prune_nm(a, 2, 4)
+    np.testing.assert_array_equal(got, exp)
+    # signed zeros tie (kept as they are), subnormals beat zero, NaNs tie
+    bits = np.array([[0x8000, 0x0000, 0x0000, 0x8000],
+                     [0x0001, 0x8002, 0x0000, 0x0001],
+                     [0x7FC0, 0x7FFF, 0xFFC1, 0x3F80],
+                     [0x0000, 0x0000, 0x0000, 0x0001]], np.uint16)
+    exp = np.array([[0x8000, 0x0000, 0, 0],
+                    [0x0001, 0x8002, 0, 0],
+                    [0x7FC0, 0x7FFF, 0, 0],
+                    [0x0000, 0, 0, 0x0001]], np.uint16)
+    np.testing.assert_array_equal(orc.prune_nm(bits, 2, 4), exp)
+    with pytest.raises(ValueError):
+        orc.prune_nm(np.zeros((1, 6), np.uint16), 2, 4)
+
+
+@pytest.mark.parametrize("keep,group", [(2, 4), (6, 8), (1, 3)])
+def test_prune_nm_bf16_brute_force(orc, keep, group):
+    # against a sort of each group by (NaN first, larger |a|, lower position)
+    r = np.random.default_rng(1300 + keep + group)
+    pool = np.array([0.0, -0.0, 1.0, -1.0, 2.5, -2.5, np.inf, -np.inf, np.nan, 1e-39, 7.0],
+                    np.float32)
+    a = _bf(r.choice(pool, size=(30, group * 6)))
+    a[:, ::5] = r.integers(0, 1 << 16, size=a[:, ::5].shape, dtype=np.uint16)  # any pattern
+    got = orc.prune_nm(a, keep, group)
+    with np.errstate(invalid="ignore"):
+        x = synth.bf16_bits_to_f32(a).astype(np.float64)
+    for i in range(a.shape[0]):
+        for g in range(a.shape[1] // group):
+            seg = x[i, g * group:(g + 1) * group]
+            order = sorted(range(group), key=lambda t: (0 if np.isnan(seg[t]) else 1,
+                                                        -abs(seg[t]) if not np.isnan(seg[t]) else 0.0,
+                                                        t))
+            mask = np.zeros(group, bool)
+            mask[order[:keep]] = True
+            o = got[i, g * group:(g + 1) * group]
+            src = a[i, g * group:(g + 1) * group]
+            np.testing.assert_array_equal(o[mask], src[mask])
+            assert (o[~mask] == 0).all()

@@ -64,3 +64,74 @@ def test_tvw_arguments(S):
         with pytest.raises(S.SpmmError) as e:
             S.spmm_pack_tvw(np.zeros(shape, np.int8), tm, tk)
         assert e.value.name == "SPMM_ERR_INVALID_ARG"
+
+
+# ---- bf16 -------------------------------------------------------------------------
+
+def _densify_tiles(tv, tmeta, tk):
+    """Expand stored tiles ([nt, tm, tk/2] kept values, [nt, tm, tk/8] nibble
+    bytes) to dense [nt, tm, tk], checking that positions ascend."""
+    nt, tm = tv.shape[:2]
+    out = np.zeros((nt, tm, tk), tv.dtype)
+    t_i, r_i = np.indices((nt, tm))
+    for g in range(tk // 4):
+        nib = (tmeta[:, :, g // 2] >> (4 * (g % 2))) & 0xF
+        i0, i1 = nib & 3, nib >> 2
+        assert (i0 < i1).all()
+        out[t_i, r_i, 4 * g + i0] = tv[:, :, 2 * g]
+        out[t_i, r_i, 4 * g + i1] = tv[:, :, 2 * g + 1]
+    return out
+
+
+def _check_tvw_bf16(S, orc, a, tm, tk):
+    M = S.spmm_pack_tvw(a, tm, tk)
+    info = S.spmm_matrix_info(M)
+    assert info["dtype"] == S.BF16
+    rp = S.spmm_matrix_array(M, S.ARRAY_ROW_PTR)
+    ci = S.spmm_matrix_array(M, S.ARRAY_COL_IDX)
+    tv = S.spmm_matrix_array(M, S.ARRAY_VALS)
+    assert tv.dtype == np.uint16
+    tv = tv.reshape(-1, tm, tk // 2)
+    tmeta = S.spmm_matrix_array(M, S.ARRAY_META).reshape(-1, tm, tk // 8)
+    m, k = a.shape
+    dense = _densify_tiles(tv, tmeta, tk)
+    pruned = orc.prune_nm(a, 2, 4)
+    nonzero = ((a & 0x7FFF) != 0).reshape(m // tm, tm, k // tk, tk).any(axis=(1, 3))
+    q = 0
+    for T in range(m // tm):
+        kept = np.nonzero(nonzero[T])[0]
+        np.testing.assert_array_equal(ci[rp[T]:rp[T + 1]], kept)
+        for s in kept:
+            np.testing.assert_array_equal(dense[q], pruned[T * tm:(T + 1) * tm, s * tk:(s + 1) * tk])
+            q += 1
+    assert q == len(ci) == info["nnzb"]
+    return M
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_tvw_bf16_tiles_are_the_pruned_nonzero_tiles(S, orc, seed):
+    r = np.random.default_rng(1400 + seed)
+    tm, tk = [(256, 128), (256, 64), (32, 16), (16, 8)][seed]
+    m, k = tm * int(r.integers(1, 4)), tk * int(r.integers(1, 5))
+    nt = int(r.integers(0, (m // tm) * (k // tk) + 1))
+    a, _ = synth.block_sparse_dense_bf16(m, k, tm, tk, nt, 1.0, 80 + seed)
+    # specials: NaN, infinities, signed zeros, subnormals, equal magnitudes;
+    # a tile holding only -0 stays unstored
+    extra = r.integers(0, [m, k], size=(int(r.integers(0, 12)), 2))
+    a[extra[:, 0], extra[:, 1]] = r.choice(
+        np.array([0x7FC0, 0x7F80, 0xFF80, 0x8000, 0x0001, 0x8001, 0x3F80, 0xBF80], np.uint16),
+        size=len(extra))
+    _check_tvw_bf16(S, orc, a, tm, tk)
+
+
+def test_tvw_bf16_negative_zero_tile_is_not_stored(S, orc):
+    a = np.zeros((256, 256), np.uint16)
+    a[:, :128] = 0x8000                               # -0 everywhere: numerically zero
+    a[5, 200] = 0x3F80
+    M = _check_tvw_bf16(S, orc, a, 256, 128)
+    np.testing.assert_array_equal(S.spmm_matrix_array(M, S.ARRAY_COL_IDX), [1])
+
+
+def test_tvw_dtype_argument(S):
+    with pytest.raises(TypeError):
+        S.spmm_pack_tvw(np.zeros((256, 128), np.float32), 256, 128)

@@ -291,13 +291,13 @@ __device__ __forceinline__ void sp24_body(
 #pragma unroll
     for (int j = 0; j < 4; ++j) bop[j] = read_b<E>(sbb, lane, wn, j);
     // The index words of a wave's 8 row tiles sit together per lane (one or
-    // two 16-byte reads); the A fragments of the first four row tiles are
+    // two 16-byte reads, consecutive lanes 16 bytes apart); the A fragments of the first four row tiles are
     // read with them, those of the last four behind the first 16 sparse MFMAs.
     const i32x4 *afr = reinterpret_cast<const i32x4 *>(sb);
     int idx[8];
     if constexpr (E::kIdx == 4) {
-      const i32x4 *mfr = reinterpret_cast<const i32x4 *>(sb + kAVBytes) + (wm * 64 + lane) * 2;
-      const i32x4 lo = mfr[0], hi = mfr[1];
+      const i32x4 *mfr = reinterpret_cast<const i32x4 *>(sb + kAVBytes) + wm * 128 + lane;
+      const i32x4 lo = mfr[0], hi = mfr[64];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         idx[i] = lo[i];
@@ -405,17 +405,20 @@ void sp24_piece(const char *v, int64_t vs, const uint8_t *mt, int64_t ms, int64_
       for (int b = 0; b < 16; ++b)
         vdst[(t16 * 64 + l) * 16 + b] = (row < rows_ok && c0 + b < vcols) ? v[row * vs + c0 + b] : 0;
     }
-  // index words: [row half wm 2][lane 64][row tile i 8][kIdx bytes]; lane l
-  // of row half wm gets, for its 8 row tiles, bytes kIdx*(l/16).. of row
-  // (8*wm + i)*16 + l%16
+  // index words: lane l of row half wm gets, for its 8 row tiles i, bytes
+  // kIdx*(l/16).. of row (8*wm + i)*16 + l%16, as 16-byte pieces that
+  // consecutive lanes read 16 bytes apart (no LDS bank conflict):
+  // int8 [wm 2][i/4 2][lane 64][i%4 4][4 bytes], bf16 [wm 2][lane 64][i 8][2 bytes]
   constexpr int kI = E::kIdx;
+  constexpr int kPer = 16 / kI;  // row tiles per 16-byte piece
   for (int wm = 0; wm < 2; ++wm)
     for (int l = 0; l < 64; ++l)
       for (int i = 0; i < 8; ++i) {
         const int64_t row = (wm * 8 + i) * 16 + (l & 15);
         const int64_t c0 = (l >> 4) * kI;
+        const int64_t piece = (wm * (8 / kPer) + i / kPer) * 64 + l;
         for (int b = 0; b < kI; ++b)
-          mdst[((wm * 64 + l) * 8 + i) * kI + b] =
+          mdst[piece * 16 + (i % kPer) * kI + b] =
               (row < rows_ok && c0 + b < mcols) ? mt[row * ms + c0 + b] : uint8_t(0);
       }
 }

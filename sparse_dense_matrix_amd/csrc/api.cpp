@@ -129,10 +129,22 @@ spmm_status_t plan_bcsr(spmm_plan_s *p) {
   if ((s = upload_vec(p, a.brow_ptr, &rp)) != SPMM_OK) return s;
   if ((s = upload_vec(p, a.bcol_idx, &ci)) != SPMM_OK) return s;
   if ((s = upload_vec(p, frag, &fv)) != SPMM_OK) return s;
+  // block rows in dispatch order: most stored blocks first (ties by index),
+  // so the longest tiles of a column tile start first and the short ones
+  // fill in behind them
+  const int32_t mb = static_cast<int32_t>(a.m / 64);
+  std::vector<int32_t> order(static_cast<size_t>(mb));
+  for (int32_t i = 0; i < mb; ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
+    return a.brow_ptr[x + 1] - a.brow_ptr[x] > a.brow_ptr[y + 1] - a.brow_ptr[y];
+  });
+  int32_t *ro = nullptr;
+  if ((s = upload_vec(p, order, &ro)) != SPMM_OK) return s;
   L.row_ptr = rp;
   L.col_idx = ci;
   L.frag = fv;
-  L.mb = static_cast<int32_t>(a.m / 64);
+  L.row_order = ro;
+  L.mb = mb;
   L.n = p->n;
   L.k_rows = a.k;
   L.col_perm = nullptr;

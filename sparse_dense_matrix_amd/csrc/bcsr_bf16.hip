@@ -24,7 +24,9 @@
 //     C writes from evicting B from L2;
 //   - tiles are dealt so that each XCD walks a contiguous range, block rows
 //     fastest: the workgroups resident on one XCD share the B column slab of
-//     one N tile in that XCD's L2.
+//     one N tile in that XCD's L2.  Within an N tile the block rows with the
+//     most stored blocks come first (longest job first), so short tiles fill
+//     the end of the launch instead of long ones.
 // The kernel is bandwidth-bound by design: a 64-row block gives at most 64
 // flop per byte of B moved into LDS.
 #include "internal.h"
@@ -110,7 +112,7 @@ struct Operands {
 template <int kTN>
 __global__ __launch_bounds__(Geo<kTN>::kThreads) void bcsr_bf16_mfma(
     const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ col_idx,
-    const uint16_t *__restrict__ frag, int32_t mb, int32_t tiles, int32_t per_xcd, int64_t n,
+    const uint16_t *__restrict__ frag, const int32_t *__restrict__ row_order, int32_t mb, int32_t tiles, int32_t per_xcd, int64_t n,
     const uint16_t *__restrict__ B, int64_t ldb, uint16_t *__restrict__ C, int64_t ldc,
     const int32_t *__restrict__ c_rows) {
   using G = Geo<kTN>;
@@ -119,10 +121,11 @@ __global__ __launch_bounds__(Geo<kTN>::kThreads) void bcsr_bf16_mfma(
   extern __shared__ __attribute__((aligned(1024))) char lds[];
 
   // XCD-aware tile order: workgroup b runs on XCD b % 8; each XCD gets a
-  // contiguous range of logical tiles, block rows fastest.
+  // contiguous range of logical tiles, block rows fastest, and within a
+  // column tile the block rows with the most stored blocks first.
   const int t = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (t >= tiles) return;
-  const int br = t % mb;
+  const int br = row_order[t % mb];
   const int64_t n0 = static_cast<int64_t>(t / mb) * kTN;
 
   const int tid = threadIdx.x;
@@ -280,7 +283,7 @@ hipError_t launch_tn(const BcsrLaunch &a, hipStream_t s) {
   if (e != hipSuccess) return e;
   const int64_t per_xcd = (tiles + 7) / 8;
   hipLaunchKernelGGL(bcsr_bf16_mfma<kTN>, dim3(static_cast<unsigned>(8 * per_xcd)), dim3(G::kThreads),
-                     G::kLdsBytes, s, a.row_ptr, a.col_idx, a.frag, a.mb, static_cast<int32_t>(tiles),
+                     G::kLdsBytes, s, a.row_ptr, a.col_idx, a.frag, a.row_order, a.mb, static_cast<int32_t>(tiles),
                      static_cast<int32_t>(per_xcd), a.n, a.B, a.ldb, a.C, a.ldc, a.c_rows);
   return hipGetLastError();
 }

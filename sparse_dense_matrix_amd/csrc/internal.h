@@ -107,6 +107,7 @@ struct BcsrLaunch {
   const int32_t *row_ptr;   // [mb + 1]
   const int32_t *col_idx;   // [nnzb]
   const uint16_t *frag;     // [nnzb][4096] in MFMA fragment order
+  const int32_t *row_order; // [mb] block rows in dispatch order within a column tile
   int32_t mb;               // block rows (64 rows each)
   int64_t n;
   int32_t cus;              // compute units of the device (persistent grid)

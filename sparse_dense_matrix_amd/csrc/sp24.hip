@@ -24,7 +24,8 @@
 //   - D: rows 4*(l/16)+0..3, column l%16.
 // A workgroup of 8 waves computes a 256 x 256 tile of C (each wave 128 x 64,
 // 8 x 4 sparse MFMA tiles).  Operands go global -> LDS with direct loads
-// into a three-stage ring (two k-steps in flight).  The plan stores the
+// into a three-stage ring (two k-steps in flight; each step's loads go out
+// at its start, before its LDS reads).  The plan stores the
 // compressed values and the index words tiled: for each 256-row tile and
 // k-step, one contiguous 16 KB piece of values already in MFMA fragment
 // order and one contiguous piece of index words (4 KB int8, 2 KB bf16), so
@@ -280,20 +281,15 @@ __device__ __forceinline__ void sp24_body(
     if (ks + 1 < ksteps) wait_vm<kLoads>();
     else wait_vm<0>();
     barrier();  // ... for every wave; and the stage of step ks-1 is free
-    // the loads of step ks+2 are issued between this step's MFMAs, so the
-    // address unit works through them while the matrix cores run
-    const bool more = ks + kStages - 1 < ksteps;
+    // The loads of step ks+2 go out first: inline asm between the LDS reads
+    // and the MFMAs would make the compiler wait for every read before it.
     const int64_t kn = ks + kStages - 1;
-    const int sn = static_cast<int>(kn % kStages);
+    if (kn < ksteps) issue(kn, static_cast<int>(kn % kStages));
     const char *sb = lds + (ks % kStages) * kStageBytes;
     const char *sbb = sb + kAVBytes + kAMBytes;
-    i32x8 bop[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) bop[j] = read_b<E>(sbb, lane, wn, j);
     // The index words of a wave's 8 row tiles sit together per lane (one or
-    // two 16-byte reads, consecutive lanes 16 bytes apart); the A fragments of the first four row tiles are
-    // read with them, those of the last four behind the first 16 sparse MFMAs.
-    const i32x4 *afr = reinterpret_cast<const i32x4 *>(sb);
+    // two 16-byte reads, consecutive lanes 16 bytes apart), then its 8 A
+    // fragments.
     int idx[8];
     if constexpr (E::kIdx == 4) {
       const i32x4 *mfr = reinterpret_cast<const i32x4 *>(sb + kAVBytes) + wm * 128 + lane;
@@ -309,17 +305,24 @@ __device__ __forceinline__ void sp24_body(
       for (int i = 0; i < 8; ++i)
         idx[i] = static_cast<int>((static_cast<uint32_t>(w[i >> 1]) >> (16 * (i & 1))) & 0xffffu);
     }
+    const i32x4 *afr = reinterpret_cast<const i32x4 *>(sb);
     i32x4 aop[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) aop[i] = afr[(wm * 8 + i) * 64 + lane];
-    __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < 8; ++i) aop[i] = afr[(wm * 8 + i) * 64 + lane];
+    // B one column tile ahead: tile j+1's 4 transpose reads are in flight
+    // while tile j's 8 MFMAs issue.  At most 18 reads are outstanding, few
+    // enough for each wait to name a count (lgkmcnt holds at most 15).
+    i32x8 bop[4];
+    bop[0] = read_b<E>(sbb, lane, wn, 0);
 #pragma unroll
-    for (int i = 4; i < 8; ++i) aop[i] = afr[(wm * 8 + i) * 64 + lane];
+    for (int j = 0; j < 4; ++j) {
+      if (j + 1 < 4) bop[j + 1] = read_b<E>(sbb, lane, wn, j + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (j + 1 < 4) __builtin_amdgcn_s_waitcnt(0xc07f | (4 << 8));  // lgkmcnt(4)
+      else __builtin_amdgcn_s_waitcnt(0xc07f);                        // lgkmcnt(0)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mma<E>(aop[i], bop[j], acc[i][j], idx[i]);
-      if (more && i < kLoads) issue_part(kn, sn, i);
+      for (int i = 0; i < 8; ++i) acc[i][j] = mma<E>(aop[i], bop[j], acc[i][j], idx[i]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 

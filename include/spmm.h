@@ -226,8 +226,9 @@ void spmm_matrix_destroy(spmm_matrix_t a);
  *   TVW, bf16 (256 x 64j tiles):   (BF16, BF16), n % 16 == 0; fp32 sums rounded to
  *                                  nearest even
  *   SLIDE:                 (I8, I32), n % 16 == 0 (plus a k_lift * n workspace)
- * A BCSR matrix packed with reordering also gets a workspace for B's rows in
- * the packed column order (k * n * 2 bytes).  Anything else is UNSUPPORTED.  n = 0 is allowed (execute does nothing). */
+ * A BCSR matrix packed with reordering reads B's rows through its column
+ * permutation (no workspace; spmm_execute then needs k * ldb * 2 < 2^32).
+ * Anything else is UNSUPPORTED.  n = 0 is allowed (execute does nothing). */
 spmm_status_t spmm_plan(spmm_matrix_t a, int64_t n, spmm_dtype_t b_dtype,
                         spmm_dtype_t c_dtype, int32_t device, spmm_plan_t *out);
 

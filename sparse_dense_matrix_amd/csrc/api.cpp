@@ -148,18 +148,11 @@ spmm_status_t plan_bcsr(spmm_plan_s *p) {
   L.n = p->n;
   L.k_rows = a.k;
   L.col_perm = nullptr;
-  L.b_perm = nullptr;
   L.c_rows = nullptr;
   if (!a.col_perm.empty()) {
     int32_t *cp = nullptr;
-    void *ws = nullptr;
-    const int64_t ws_bytes = a.k * p->n * 2;
     if ((s = upload_vec(p, a.col_perm, &cp)) != SPMM_OK) return s;
-    if ((s = upload(p, nullptr, static_cast<size_t>(ws_bytes), &ws)) != SPMM_OK) return s;
-    p->info.device_bytes -= std::max<int64_t>(ws_bytes, 16);
-    p->info.workspace_bytes = ws_bytes;
     L.col_perm = cp;
-    L.b_perm = static_cast<uint16_t *>(ws);
   }
   if (!a.row_perm.empty()) {
     int32_t *rows = nullptr;

@@ -109,12 +109,16 @@ struct Operands {
   bf16x8 b[2];
 };
 
-template <int kTN>
+// kMap: the packed k-row j of A multiplies B row b_rows[j] (A packed with
+// its columns permuted); each lane then reads its B rows through the map,
+// looked up one block ahead.  Otherwise k-row j multiplies B row j.
+template <int kTN, bool kMap>
 __global__ __launch_bounds__(Geo<kTN>::kThreads) void bcsr_bf16_mfma(
     const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ col_idx,
-    const uint16_t *__restrict__ frag, const int32_t *__restrict__ row_order, int32_t mb, int32_t tiles, int32_t per_xcd, int64_t n,
-    const uint16_t *__restrict__ B, int64_t ldb, uint16_t *__restrict__ C, int64_t ldc,
-    const int32_t *__restrict__ c_rows) {
+    const uint16_t *__restrict__ frag, const int32_t *__restrict__ row_order, int32_t mb,
+    int32_t tiles, int32_t per_xcd, int64_t n, const uint16_t *__restrict__ B, int64_t ldb,
+    uint16_t *__restrict__ C, int64_t ldc, const int32_t *__restrict__ c_rows,
+    const int32_t *__restrict__ b_rows) {
   using G = Geo<kTN>;
   constexpr int kBRow = G::kBRow, kBBytes = G::kBBytes, kStageBytes = G::kStageBytes;
   constexpr int kBLoads = G::kBLoads, kALoads = G::kALoads;
@@ -137,21 +141,42 @@ __global__ __launch_bounds__(Geo<kTN>::kThreads) void bcsr_bf16_mfma(
   // Per-lane byte offsets of this wave's B loads relative to the block's
   // first k-row; columns past n are read from column n0 of the same row
   // (they only feed C columns that are never stored).
+  // With kMap, boff holds only the column part and brow the lane's k-row in
+  // the block; the row comes from b_rows (brow_next: the B rows of the next
+  // block, loaded one block ahead).
   uint32_t boff[kBLoads];
+  int brow[kBLoads];
 #pragma unroll
   for (int i = 0; i < kBLoads; ++i) {
     const int o = (wave * kBLoads + i) * 1024 + lane * 16;  // byte offset in the slab
     const int r = o / kBRow;
     const int c = swz(r, (o % kBRow) / 16) * 8;
     const int64_t col = (n0 + c < n) ? n0 + c : n0;
-    boff[i] = static_cast<uint32_t>((r * ldb + col) * 2);
+    boff[i] = static_cast<uint32_t>(((kMap ? 0 : r * ldb) + col) * 2);
+    brow[i] = r;
   }
+  int brow_next[kBLoads];
+  // B rows (through the map) of the block at position blk of the row's list
+  auto lookup_rows = [&](int blk) {
+    if constexpr (kMap) {
+      const int64_t k0 = static_cast<int64_t>(col_idx[blk]) * kBlk;
+#pragma unroll
+      for (int i = 0; i < kBLoads; ++i) brow_next[i] = b_rows[k0 + brow[i]];
+    }
+  };
   const uint32_t lds_base = lds_addr(lds);
   auto issue = [&](int blk, int stage) {
     const uint32_t sb = lds_base + stage * kStageBytes;
-    const uint16_t *bsrc = B + static_cast<int64_t>(col_idx[blk]) * kBlk * ldb;
+    if constexpr (kMap) {
 #pragma unroll
-    for (int i = 0; i < kBLoads; ++i) load_lds16(sb + (wave * kBLoads + i) * 1024, bsrc, boff[i]);
+      for (int i = 0; i < kBLoads; ++i)
+        load_lds16(sb + (wave * kBLoads + i) * 1024, B,
+                   static_cast<uint32_t>(brow_next[i] * ldb * 2) + boff[i]);
+    } else {
+      const uint16_t *bsrc = B + static_cast<int64_t>(col_idx[blk]) * kBlk * ldb;
+#pragma unroll
+      for (int i = 0; i < kBLoads; ++i) load_lds16(sb + (wave * kBLoads + i) * 1024, bsrc, boff[i]);
+    }
     const uint16_t *asrc = frag + static_cast<int64_t>(blk) * (kABytes / 2);
 #pragma unroll
     for (int i = 0; i < kALoads; ++i) {
@@ -198,11 +223,18 @@ __global__ __launch_bounds__(Geo<kTN>::kThreads) void bcsr_bf16_mfma(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  if (nblk > 0) issue(p0, 0);
+  if (nblk > 0) {
+    lookup_rows(p0);
+    issue(p0, 0);
+    if (nblk > 1) lookup_rows(p0 + 1);
+  }
   for (int it = 0; it < nblk; ++it) {
-    wait_vm<0>();  // this block's loads have landed
+    wait_vm<0>();  // this block's loads (and the next block's row lookups) have landed
     barrier();     // ... for every wave; and the stage of block it-1 is free
-    if (it + 1 < nblk) issue(p0 + it + 1, (it + 1) & 1);
+    if (it + 1 < nblk) {
+      issue(p0 + it + 1, (it + 1) & 1);
+      if (it + 2 < nblk) lookup_rows(p0 + it + 2);
+    }
     const char *sb = lds + (it & 1) * kStageBytes;
     // every operand of the block is read before the first MFMA, so the LDS
     // latency is paid once per block instead of once per k-step
@@ -272,35 +304,32 @@ int64_t bcsr_grid(int32_t mb, int64_t n, int /*cus*/) {
 }
 
 namespace {
-template <int kTN>
+template <int kTN, bool kMap>
 hipError_t launch_tn(const BcsrLaunch &a, hipStream_t s) {
   using G = Geo<kTN>;
   const int64_t ntn = (a.n + kTN - 1) / kTN;
   const int64_t tiles = static_cast<int64_t>(a.mb) * ntn;
   if (tiles == 0) return hipSuccess;
   if (tiles > INT32_MAX / 2 || a.ldb > (1 << 24)) return hipErrorInvalidValue;
-  hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(&bcsr_bf16_mfma<kTN>), G::kLdsBytes);
+  // through the row map every B byte offset is a 32-bit offset from B
+  if (kMap && a.k_rows * a.ldb * 2 > UINT32_MAX) return hipErrorInvalidValue;
+  auto kernel = bcsr_bf16_mfma<kTN, kMap>;
+  hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(kernel), G::kLdsBytes);
   if (e != hipSuccess) return e;
   const int64_t per_xcd = (tiles + 7) / 8;
-  hipLaunchKernelGGL(bcsr_bf16_mfma<kTN>, dim3(static_cast<unsigned>(8 * per_xcd)), dim3(G::kThreads),
-                     G::kLdsBytes, s, a.row_ptr, a.col_idx, a.frag, a.row_order, a.mb, static_cast<int32_t>(tiles),
-                     static_cast<int32_t>(per_xcd), a.n, a.B, a.ldb, a.C, a.ldc, a.c_rows);
+  hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(8 * per_xcd)), dim3(G::kThreads),
+                     G::kLdsBytes, s, a.row_ptr, a.col_idx, a.frag, a.row_order, a.mb,
+                     static_cast<int32_t>(tiles), static_cast<int32_t>(per_xcd), a.n, a.B, a.ldb,
+                     a.C, a.ldc, a.c_rows, a.col_perm);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_bcsr_bf16(const BcsrLaunch &a0, hipStream_t s) {
-  BcsrLaunch a = a0;
-  if (a.col_perm) {
-    // B's rows in the packed column order, then the multiply reads that copy
-    const int64_t k = a.k_rows;
-    hipError_t e = launch_gather_rows(a.B, a.ldb * 2, a.col_perm, k, a.n * 2, a.b_perm, a.n * 2, s);
-    if (e != hipSuccess) return e;
-    a.B = a.b_perm;
-    a.ldb = a.n;
-  }
-  return bcsr_tile_n(a.n) == 512 ? launch_tn<512>(a, s) : launch_tn<256>(a, s);
+hipError_t launch_bcsr_bf16(const BcsrLaunch &a, hipStream_t s) {
+  const bool wide = bcsr_tile_n(a.n) == 512;
+  if (a.col_perm) return wide ? launch_tn<512, true>(a, s) : launch_tn<256, true>(a, s);
+  return wide ? launch_tn<512, false>(a, s) : launch_tn<256, false>(a, s);
 }
 
 }  // namespace sdm

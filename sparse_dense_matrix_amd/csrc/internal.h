@@ -115,12 +115,11 @@ struct BcsrLaunch {
   int64_t ldb;
   uint16_t *C;
   int64_t ldc;
-  // A packed with its rows and columns permuted (spmm_pack_bcsr_csr): B's
-  // rows are gathered into b_perm (k x n, ld n) in the packed column order
-  // first, and packed row i is written to C row c_rows[i]; null otherwise
+  // A packed with its rows and columns permuted (spmm_pack_bcsr_csr): packed
+  // column j multiplies B row col_perm[j] (the kernel reads B through the
+  // map), and packed row i is written to C row c_rows[i]; null otherwise
   int64_t k_rows;           // k: rows of B
   const int32_t *col_perm;  // [k] original row of B for each packed column
-  uint16_t *b_perm;         // [k][n] workspace
   const int32_t *c_rows;    // [m] original row of C for each packed row
 };
 // Fragment order of one 64 x 64 block: [rb 2][s 4][lane 64][8 elements], lane l

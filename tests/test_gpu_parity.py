@@ -581,9 +581,22 @@ def test_reordered_bcsr_small(S, orc, reorder):
     _say(f"scrambled_small reorder={reorder} nnzb={info['nnzb']} ws={P.info()['workspace_bytes']} "
          f"rel_frob={err:.3e}")
     assert err <= TOL_BF16
+    assert P.info()["workspace_bytes"] == 0      # B is read through the permutation
     if reorder:
         assert info["nnzb"] == w.nblocks          # the hidden blocks, found again
         assert len(S.spmm_matrix_array(M, S.ARRAY_ROW_PERM)) == w.m
+
+
+def test_reordered_bcsr_wide_n(S, orc):
+    # n >= 8192 takes the 512-column tiles; a ragged last tile
+    import dataclasses
+    w = dataclasses.replace(synth.SMALL["scrambled_small"], n=8192 + 72)
+    r = np.random.default_rng(25)
+    rows = np.unique(np.concatenate([np.arange(8), r.choice(w.m, 40, replace=False)])).astype(np.int64)
+    err, M, P = _reordered_case(S, orc, w, rows=rows)
+    _say(f"scrambled_small n={w.n} tile_n={P.info()['tile_n']} rel_frob={err:.3e}")
+    assert P.info()["tile_n"] == 512
+    assert err <= TOL_BF16
 
 
 def test_reordered_bcsr_4096_sampled(S, orc):

@@ -69,6 +69,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", type=int, default=0, metavar="G",
+                    help="capture G steps into one HIP graph and replay it (steps rounded "
+                         "up to a multiple of G); 0 launches every step from Python")
     ap.add_argument("--dense-baseline", action="store_true",
                     help="BCSR workloads: also time the dense product of the same shape "
                          "(torch.matmul on the zero-filled bf16 A) to show where block "
@@ -265,12 +268,30 @@ def main():
     for _ in range(args.warmup):
         step(stream)
     torch.cuda.synchronize()
+    graph = None
+    if args.graph > 0:
+        # the same launches, recorded once: replaying G steps costs one graph
+        # launch instead of G calls from Python
+        args.steps = -(-args.steps // args.graph) * args.graph
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for _ in range(args.graph):
+                step(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            graph.replay()
+        torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record(stream)
-    for _ in range(args.steps):
-        step(stream)
+    if graph is not None:
+        with torch.cuda.stream(stream):
+            for _ in range(args.steps // args.graph):
+                graph.replay()
+    else:
+        for _ in range(args.steps):
+            step(stream)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -313,6 +334,8 @@ def main():
                    "split_rows": pinfo["num_split_rows"], "grid": pinfo["grid"],
                    **({"csr_nnz": int(d["a"]["row_ptr"][-1]), "reordered": w.reorder,
                        "scramble_seed": w.scramble} if w.scramble else {}),
+                   "launch": (f"HIP graph of {args.graph} steps, replayed" if args.graph
+                              else "one spmm_execute call per step"),
                    "parallelism": "single GPU"},
         "roofline": roof,
         "roofline_other_bound": other,

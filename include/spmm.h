@@ -144,8 +144,8 @@ spmm_status_t spmm_pack_bcsr(int64_t m, int64_t k, int32_t block_m, int32_t bloc
  * ascending position, to the lowest of the N-1 windows of four (window w
  * covers positions 2w .. 2w+3) that covers them and has room; each window is
  * then one 2:4 group.  The product is that of the pruned A.  Lifted column
- * 4w + j of group g multiplies B's row 2N g + 2w + j; spmm_execute gathers
- * those rows into a plan workspace (k_lift * n bytes) first.  Requires
+ * 4w + j of group g multiplies B's row 2N g + 2w + j; the kernel reads B's
+ * rows through that map (no workspace).  Requires
  * group even in [4, 64], k % group == 0 and k_lift % 8 == 0 (else
  * INVALID_ARG); spmm_matrix_info reports group as block_k. */
 spmm_status_t spmm_pack_slide(int64_t m, int64_t k, const int8_t *a_host, int64_t lda, int32_t group,

@@ -386,19 +386,14 @@ spmm_status_t plan_24(spmm_plan_s *p) {
   L.tile_ptr = nullptr;
   L.tile_step = nullptr;
   L.b_rows = nullptr;
-  L.b_lift = nullptr;
   if (slide) {
-    std::vector<int32_t> rows(static_cast<size_t>(k));
+    // B row of every lifted k-row, padded with row 0 to whole k-steps (the
+    // padded k-rows meet zero A values)
+    std::vector<int32_t> rows(static_cast<size_t>(k_pad), 0);
     for (int64_t j = 0; j < k; ++j) rows[j] = static_cast<int32_t>(slide_source_row(j, a.slide_group));
     int32_t *dr = nullptr;
-    void *ws = nullptr;
-    const int64_t ws_bytes = k * p->n;
     if ((s = upload_vec(p, rows, &dr)) != SPMM_OK) return s;
-    if ((s = upload(p, nullptr, static_cast<size_t>(ws_bytes), &ws)) != SPMM_OK) return s;
-    p->info.device_bytes -= std::max<int64_t>(ws_bytes, 16);
-    p->info.workspace_bytes = ws_bytes;
     L.b_rows = dr;
-    L.b_lift = static_cast<int8_t *>(ws);
   }
   p->info.tile_m = sp24_tile_m();
   p->info.tile_n = sp24_tile_n();
@@ -444,7 +439,6 @@ spmm_status_t plan_tvw(spmm_plan_s *p) {
   L.tile_ptr = tp;
   L.tile_step = ts;
   L.b_rows = nullptr;
-  L.b_lift = nullptr;
   L.m = a.m;
   L.k = a.k;
   L.n = p->n;

@@ -91,11 +91,6 @@ struct WcsrChunk {
 };
 static_assert(sizeof(WcsrChunk) == 32, "WcsrChunk layout");
 
-// dst row j = src row map[j] for j < rows, row_bytes (a multiple of 16)
-// bytes each; leading dimensions in bytes, 16-byte aligned.
-hipError_t launch_gather_rows(const void *src, int64_t ld_bytes, const int32_t *map, int64_t rows,
-                              int64_t row_bytes, void *dst, int64_t dst_ld_bytes, hipStream_t s);
-
 // Raise a kernel's dynamic LDS limit to `bytes` on the current device (once
 // per kernel and device).
 hipError_t allow_dynamic_lds(const void *kernel, size_t bytes);
@@ -200,11 +195,9 @@ struct Sp24Launch {
   // tile_step[tile_ptr[T] .. tile_ptr[T+1]); null for a plain 2:4 A
   const int32_t *tile_ptr;
   const int32_t *tile_step;
-  // sliding-window A: the kernel multiplies by B's rows in window order,
-  // b_lift[j] = B[b_rows[j]] for the k (= lifted) rows, gathered first from
-  // the caller's B of k_src rows; null otherwise
+  // sliding-window A: lifted k-row j multiplies B row b_rows[j] (k_pad
+  // entries, row 0 past k); the kernel reads B through it; null otherwise
   const int32_t *b_rows;
-  void *b_lift;
   int64_t m, k, n;
   int64_t m_pad, k_pad;
   const void *B;

@@ -183,12 +183,16 @@ __device__ __forceinline__ typename E::Acc mma(i32x4 a, i32x8 b, typename E::Acc
 // tile_step[tile_ptr[T] .. tile_ptr[T+1]), their values and index words in
 // that order.  Otherwise every k-step of every row tile is stored.  ldb and
 // ldc count elements.
-template <class E, bool kTiles>
+// kMap: slab k-row j multiplies B row b_rows[j] (sliding-window A, whose
+// lifted k-rows repeat B's rows; the table is padded with row 0 to whole
+// k-steps).  Otherwise slab k-row j multiplies B row j.
+template <class E, bool kTiles, bool kMap>
 __device__ __forceinline__ void sp24_body(
     const char *__restrict__ vals, const uint8_t *__restrict__ meta,
     const int32_t *__restrict__ tile_ptr, const int32_t *__restrict__ tile_step, int64_t m,
     int64_t k, int64_t n, int64_t k_pad, int32_t mtiles, int32_t ntiles, int32_t tiles,
-    int32_t per_xcd, const char *__restrict__ B, int64_t ldb, void *__restrict__ C, int64_t ldc) {
+    int32_t per_xcd, const char *__restrict__ B, int64_t ldb, void *__restrict__ C, int64_t ldc,
+    const int32_t *__restrict__ b_rows) {
   using G = Geo<E>;
   constexpr int kTK = G::kTK, kAVBytes = G::kAVBytes, kAMBytes = G::kAMBytes;
   constexpr int kStageBytes = G::kStageBytes, kMLanes = G::kMLanes;
@@ -229,15 +233,27 @@ __device__ __forceinline__ void sp24_body(
   // (whole k-rows of the slab).
   const uint32_t lds_base = lds_addr(lds);
   const int64_t ldb_bytes = ldb * E::kElem;
-  uint32_t b_off[4];
+  uint32_t b_off[4];  // kMap: the column part only
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = (wave * 4 + i) * G::kRowsPerLoad + lane / G::kPieces;  // k-row of the slab
     const int c = swz<E>(r, lane % G::kPieces);  // logical 16-byte piece
     constexpr int per_piece = 16 / E::kElem;    // columns per piece
     const int64_t col = (n0 + c * per_piece < n) ? n0 + c * per_piece : n0;
-    b_off[i] = static_cast<uint32_t>(r * ldb_bytes + col * E::kElem);
+    b_off[i] = static_cast<uint32_t>((kMap ? 0 : r * ldb_bytes) + col * E::kElem);
   }
+  // kMap: the B rows of this wave's 16 slab k-rows of one step, one 64-byte
+  // piece of the table, read with scalar loads a step before its loads go
+  // out (lane group q of load i takes row 4 i + q)
+  static_assert(!kMap || G::kRowsPerLoad == 4, "row map for 4 k-rows per load");
+  int trow[16];
+  auto lookup = [&](int64_t ks) {
+    if constexpr (kMap) {
+      const int32_t *t = b_rows + ks * kTK + wave * 16;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) trow[q] = t[q];
+    }
+  };
   // load `part` (0..6) of k-step ks into stage `stage`: A values 0..1,
   // index words 2, B 3..6.  Every wave issues all kLoads parts per step (the
   // vmcnt waits count them).
@@ -254,10 +270,21 @@ __device__ __forceinline__ void sp24_body(
       // are read from row 0: the matching A values are zero-padded, so they
       // add nothing
       const int i = part - 3;
-      const int64_t krow0 = kstep(ks) * kTK;
-      const int r = (wave * 4 + i) * G::kRowsPerLoad + lane / G::kPieces;
-      const uint32_t off = krow0 + r < k ? static_cast<uint32_t>(krow0 * ldb_bytes) + b_off[i]
-                                         : b_off[i] - static_cast<uint32_t>(r * ldb_bytes);
+      uint32_t off;
+      if constexpr (kMap) {
+        // lane group q takes trow[4 i + q]; written as masks so the 16
+        // values stay in scalar registers (a select chain becomes an
+        // indexed private array)
+        const int q = lane / G::kPieces;
+        const int row = (trow[4 * i] & -(q == 0)) | (trow[4 * i + 1] & -(q == 1)) |
+                        (trow[4 * i + 2] & -(q == 2)) | (trow[4 * i + 3] & -(q == 3));
+        off = static_cast<uint32_t>(row * ldb_bytes) + b_off[i];
+      } else {
+        const int64_t krow0 = kstep(ks) * kTK;
+        const int r = (wave * 4 + i) * G::kRowsPerLoad + lane / G::kPieces;
+        off = krow0 + r < k ? static_cast<uint32_t>(krow0 * ldb_bytes) + b_off[i]
+                            : b_off[i] - static_cast<uint32_t>(r * ldb_bytes);
+      }
       load_lds16(sb + kAVBytes + kAMBytes + (wave * 4 + i) * 1024, B, off);
     }
   };
@@ -275,7 +302,11 @@ __device__ __forceinline__ void sp24_body(
       for (int r = 0; r < 4; ++r) acc[i][j][r] = 0;
 
   for (int s = 0; s < kStages - 1; ++s)
-    if (s < ksteps) issue(s, s);
+    if (s < ksteps) {
+      lookup(s);
+      issue(s, s);
+    }
+  if (kStages - 1 < ksteps) lookup(kStages - 1);
   for (int64_t ks = 0; ks < ksteps; ++ks) {
     // this step's loads have landed (the next step's may still be in flight)
     if (ks + 1 < ksteps) wait_vm<kLoads>();
@@ -324,6 +355,9 @@ __device__ __forceinline__ void sp24_body(
       for (int i = 0; i < 8; ++i) acc[i][j] = mma<E>(aop[i], bop[j], acc[i][j], idx[i]);
       __builtin_amdgcn_sched_barrier(0);
     }
+    // the table rows of step ks+3, after this step's last LDS wait (a scalar
+    // load in flight would force the LDS waits above down to zero)
+    if (kn + 1 < ksteps) lookup(kn + 1);
   }
 
   // D element r of lane l is row 4*(l/16) + r, column l%16 of its 16 x 16
@@ -376,17 +410,18 @@ __device__ __forceinline__ void sp24_body(
   const char *__restrict__ vals, const uint8_t *__restrict__ meta,                              \
       const int32_t *__restrict__ tile_ptr, const int32_t *__restrict__ tile_step, int64_t m,   \
       int64_t k, int64_t n, int64_t k_pad, int32_t mtiles, int32_t ntiles, int32_t tiles,       \
-      int32_t per_xcd, const char *__restrict__ B, int64_t ldb, void *__restrict__ C, int64_t ldc
-#define SP24_PASS vals, meta, tile_ptr, tile_step, m, k, n, k_pad, mtiles, ntiles, tiles, per_xcd, B, ldb, C, ldc
+      int32_t per_xcd, const char *__restrict__ B, int64_t ldb, void *__restrict__ C, int64_t ldc, \
+      const int32_t *__restrict__ b_rows
+#define SP24_PASS vals, meta, tile_ptr, tile_step, m, k, n, k_pad, mtiles, ntiles, tiles, per_xcd, B, ldb, C, ldc, b_rows
 
-template <bool kTiles>
+template <bool kTiles, bool kMap>
 __global__ __launch_bounds__(kThreads) void sp24_i8_smfmac(SP24_ARGS) {
-  sp24_body<I8, kTiles>(SP24_PASS);
+  sp24_body<I8, kTiles, kMap>(SP24_PASS);
 }
 
 template <bool kTiles>
 __global__ __launch_bounds__(kThreads) void sp24_bf16_smfmac(SP24_ARGS) {
-  sp24_body<Bf16, kTiles>(SP24_PASS);
+  sp24_body<Bf16, kTiles, false>(SP24_PASS);
 }
 
 #undef SP24_ARGS
@@ -456,7 +491,7 @@ void tvw_layout(const char *tile_vals, const uint8_t *tile_meta, int64_t ntiles,
                     meta_tiled + (t * per + s) * G::kAMBytes);
 }
 
-template <class E, bool kTiles>
+template <class E, bool kTiles, bool kMap>
 hipError_t launch(const Sp24Launch &a, hipStream_t s) {
   using G = Geo<E>;
   const int64_t mtiles = (a.m + kTM - 1) / kTM;
@@ -465,7 +500,7 @@ hipError_t launch(const Sp24Launch &a, hipStream_t s) {
   if (tiles == 0) return hipSuccess;
   if (tiles > INT32_MAX / 2 || a.k_pad * a.ldb * E::kElem > UINT32_MAX)
     return hipErrorInvalidValue;
-  auto kernel = E::kElem == 1 ? sp24_i8_smfmac<kTiles> : sp24_bf16_smfmac<kTiles>;
+  auto kernel = E::kElem == 1 ? sp24_i8_smfmac<kTiles, kMap> : sp24_bf16_smfmac<kTiles>;
   hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(kernel), G::kLdsBytes);
   if (e != hipSuccess) return e;
   const int64_t per_xcd = (tiles + 7) / 8;
@@ -474,7 +509,7 @@ hipError_t launch(const Sp24Launch &a, hipStream_t s) {
                      a.tile_step, a.m, a.k, a.n, a.k_pad, static_cast<int32_t>(mtiles),
                      static_cast<int32_t>(ntiles), static_cast<int32_t>(tiles),
                      static_cast<int32_t>(per_xcd), static_cast<const char *>(a.B), a.ldb, a.C,
-                     a.ldc);
+                     a.ldc, a.b_rows);
   return hipGetLastError();
 }
 
@@ -505,19 +540,14 @@ int64_t sp24_grid(int64_t m, int64_t n) {
   return 8 * ((tiles + 7) / 8);
 }
 
-hipError_t launch_sp24(const Sp24Launch &a0, hipStream_t s) {
-  Sp24Launch a = a0;
-  const int elem = a.bf16 ? 2 : 1;
+hipError_t launch_sp24(const Sp24Launch &a, hipStream_t s) {
   if (a.b_rows) {
-    // sliding-window A: B's rows in lifted order first (a.k lifted rows)
-    hipError_t e =
-        launch_gather_rows(a.B, a.ldb * elem, a.b_rows, a.k, a.n * elem, a.b_lift, a.n * elem, s);
-    if (e != hipSuccess) return e;
-    a.B = a.b_lift;
-    a.ldb = a.n;
+    // sliding-window A: int8, every k-step stored, B read through the row map
+    if (a.bf16 || a.tile_ptr) return hipErrorInvalidValue;
+    return launch<I8, false, true>(a, s);
   }
-  if (a.bf16) return a.tile_ptr ? launch<Bf16, true>(a, s) : launch<Bf16, false>(a, s);
-  return a.tile_ptr ? launch<I8, true>(a, s) : launch<I8, false>(a, s);
+  if (a.bf16) return a.tile_ptr ? launch<Bf16, true, false>(a, s) : launch<Bf16, false, false>(a, s);
+  return a.tile_ptr ? launch<I8, true, false>(a, s) : launch<I8, false, false>(a, s);
 }
 
 }  // namespace sdm

@@ -159,13 +159,9 @@ spmm_status_t plan_bcsr(spmm_plan_s *p) {
     if ((s = upload_vec(p, a.row_perm, &rows)) != SPMM_OK) return s;
     L.c_rows = rows;
   }
-  int cus = 0;
-  hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, p->device);
-  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
-  L.cus = cus;
   p->info.tile_m = 64;
   p->info.tile_n = bcsr_tile_n(p->n);
-  p->info.grid = bcsr_grid(L.mb, p->n, cus);
+  p->info.grid = bcsr_grid(L.mb, p->n);
   return SPMM_OK;
 }
 

@@ -297,7 +297,7 @@ void bcsr_fragment_order(const uint16_t *blk, uint16_t *frag) {
 // small n the narrower tile gives more workgroups to fill the CUs.
 int bcsr_tile_n(int64_t n) { return n >= 8192 ? 512 : 256; }
 
-int64_t bcsr_grid(int32_t mb, int64_t n, int /*cus*/) {
+int64_t bcsr_grid(int32_t mb, int64_t n) {
   const int tn = bcsr_tile_n(n);
   const int64_t tiles = static_cast<int64_t>(mb) * ((n + tn - 1) / tn);
   return 8 * ((tiles + 7) / 8);

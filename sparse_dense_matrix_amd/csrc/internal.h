@@ -105,7 +105,6 @@ struct BcsrLaunch {
   const int32_t *row_order; // [mb] block rows in dispatch order within a column tile
   int32_t mb;               // block rows (64 rows each)
   int64_t n;
-  int32_t cus;              // compute units of the device (persistent grid)
   const uint16_t *B;
   int64_t ldb;
   uint16_t *C;
@@ -121,7 +120,7 @@ struct BcsrLaunch {
 // holding row 32*rb + l%32, columns 16*s + 8*(l/32) + 0..7.
 void bcsr_fragment_order(const uint16_t *block_rowmajor, uint16_t *frag);
 int bcsr_tile_n(int64_t n);
-int64_t bcsr_grid(int32_t mb, int64_t n, int cus);
+int64_t bcsr_grid(int32_t mb, int64_t n);
 hipError_t launch_bcsr_bf16(const BcsrLaunch &a, hipStream_t s);
 
 struct WcsrLaunch {

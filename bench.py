@@ -44,7 +44,7 @@ PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "i8": 5000.0}
 
 # kernel whose launch dominates a step, per format
 DOMINANT_KERNEL = {"bcsr": "bcsr_bf16_mfma", "wcsr": "wcsr_stream", "sp24": "sp24_i8_smfmac",
-                   "sddmm": "sddmm_f32", "sddmm_bcsr": "sddmm_bcsr_mfma", "bcsr_csr": "bcsr_bf16_mfma",
+                   "sddmm": "sddmm_csr", "sddmm_bcsr": "sddmm_bcsr_mfma", "bcsr_csr": "bcsr_bf16_mfma",
                    "tvw": "sp24_i8_smfmac", "slide": "sp24_i8_smfmac"}
 TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 
@@ -122,7 +122,7 @@ def setup(w, S, args):
     t_pack = time.perf_counter() - t0
     t0 = time.perf_counter()
     if w.fmt == "sddmm":
-        P = S.spmm_plan_sddmm(M, w.n)
+        P = S.spmm_plan_sddmm(M, w.n, {"bf16": S.BF16, "i8": S.I8}.get(w.elem, S.F32))
     elif w.fmt == "sddmm_bcsr":
         P = S.spmm_plan_sddmm(M, w.n, S.BF16 if w.elem == "bf16" else S.I8)
     else:
@@ -182,9 +182,10 @@ def algorithmic(w, d):
         # row_ptr, col_idx and out once; each X row with entries and each
         # touched Y row once (n is the inner dimension kd)
         nnz = info["nnz"]
+        e, eo, dt = {"bf16": (2, 2, "bf16"), "i8": (1, 4, "i8")}.get(w.elem, (4, 4, "f32"))
         x_rows = int(np.count_nonzero(np.diff(d["a"]["row_ptr"])))
         y_rows = len(np.unique(d["a"]["col_idx"]))
-        return flops, 8 * (w.m + 1) + 8 * nnz + (x_rows + y_rows) * n * 4, "f32"
+        return flops, 8 * (w.m + 1) + (4 + eo) * nnz + (x_rows + y_rows) * n * e, dt
     if w.fmt == "slide":
         # effective work counts the kept (2N-2)/2N of A; bytes: the lifted 2:4
         # operand (values and index bytes), B and C once
@@ -244,7 +245,8 @@ def main():
         Xt = torch.from_numpy(Xh).cuda()
         Yt = torch.from_numpy(Yh).cuda()
         if w.fmt == "sddmm":
-            Ot = torch.empty(max(d["info"]["nnz"], 1), dtype=torch.float32, device="cuda")
+            odt = {"bf16": torch.int16, "i8": torch.int32}.get(w.elem, torch.float32)
+            Ot = torch.empty(max(d["info"]["nnz"], 1), dtype=odt, device="cuda")
         else:
             odt = torch.int16 if w.elem == "bf16" else torch.int32
             Ot = torch.empty((max(d["info"]["nnzb"], 1), w.block, w.block), dtype=odt, device="cuda")
@@ -563,9 +565,12 @@ def cpu_baseline(w, d, target_s):
             oracle.csr_spmm(a["row_ptr"], a["col_idx"], a["vals"], Bf, rows=rows)
     elif w.fmt == "sddmm":
         row_nnz = np.diff(a["row_ptr"])
+        # the oracle takes the operands' exact fp32 images
+        Xf, Yf = (synth_f32(B[0]), synth_f32(B[1])) if w.elem == "bf16" else (
+            (B[0].astype(np.float32), B[1].astype(np.float32)) if w.elem == "i8" else B)
 
         def run(rows):
-            oracle.sddmm(a["row_ptr"], a["col_idx"], B[0], B[1], rows=rows)
+            oracle.sddmm(a["row_ptr"], a["col_idx"], Xf, Yf, rows=rows)
     elif w.fmt == "slide":
         pruned = oracle.prune_nm(a["dense"], w.nm_group - 2, w.nm_group)
         row_nnz = np.full(w.m, w.k * (w.nm_group - 2) // w.nm_group, dtype=np.int64)

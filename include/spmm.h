@@ -265,8 +265,10 @@ spmm_status_t spmm_execute(spmm_plan_t p, const void *b_dev, int64_t ldb, void *
  * values play no part.  SDDMM is the companion of SpMM on the Magicube page
  * ("Efficient Quantized Sparse Matrix Operations on Tensor Cores",
  * abstract), which runs both on low-precision integers.  Two patterns:
- *   - WCSR with dtype SPMM_F32: X, Y and out fp32; out holds one value per
- *     stored entry in stored order (float[nnz]); work is split by a's chunks;
+ *   - WCSR with dtype SPMM_F32 (X, Y and out fp32), SPMM_BF16 (X, Y bf16;
+ *     fp32 sums; out bf16, rounded to nearest even) or SPMM_I8 (X, Y int8;
+ *     out int32, exact while |sum| < 2^31): out holds one value per stored
+ *     entry in stored order ([nnz]); work is split by a's chunks;
  *   - BCSR of 64 x 64 blocks with dtype SPMM_BF16 (X, Y bf16; fp32 sums;
  *     out bf16, rounded to nearest even) or SPMM_I8 (X, Y int8; out int32,
  *     exact while |sum| < 2^31): every element of every stored block is
@@ -283,8 +285,8 @@ spmm_status_t spmm_plan_sddmm(spmm_matrix_t a, int64_t kd, spmm_dtype_t dtype, i
  * element type on the plan's device, 16-byte aligned, with ldx, ldy >= kd
  * (elements) and ldx * elem, ldy * elem multiples of 16 bytes (with kd = 0
  * X, Y and their ld are not read); for a BCSR pattern 64 * ldx * elem and
- * 64 * ldy * elem must stay below 4 GiB (else UNSUPPORTED).  out_dev is 4-byte aligned (WCSR) or
- * 16-byte aligned (BCSR).  Allocates nothing and does not synchronise; one
+ * 64 * ldy * elem must stay below 4 GiB (else UNSUPPORTED).  out_dev is aligned to its
+ * element (WCSR: 4 bytes for fp32 and int32, 2 for bf16) or to 16 bytes (BCSR).  Allocates nothing and does not synchronise; one
  * execute in flight per plan (the workspace).  Plans of spmm_plan are
  * refused here and SDDMM plans by spmm_execute (INVALID_ARG). */
 spmm_status_t spmm_execute_sddmm(spmm_plan_t p, const void *x_dev, int64_t ldx, const void *y_dev,

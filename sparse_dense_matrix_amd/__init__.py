@@ -336,7 +336,8 @@ def spmm_execute(plan: Plan, b, c, stream=None, ldb: int | None = None,
 
 def spmm_plan_sddmm(mat: Matrix, kd: int, dtype: int = F32, device: int = 0) -> Plan:
     """Plan the sampled product out[p] = X[i] . Y[j] over the stored entries
-    (i, j) of a WCSR matrix, inner dimension kd."""
+    (i, j) of a WCSR (dtype F32, BF16 or I8) or 64 x 64 BCSR (BF16 or I8)
+    matrix, inner dimension kd."""
     h = C.c_void_p()
     _check(_lib.spmm_plan_sddmm(mat.handle, kd, dtype, device, C.byref(h)), "spmm_plan_sddmm")
     return Plan(h)
@@ -346,8 +347,9 @@ def spmm_execute_sddmm(plan: Plan, x, y, out, stream=None, ldx: int | None = Non
                        ldy: int | None = None):
     """out[p] for every stored entry on `stream` (default: torch's current
     stream).  x [m, kd] and y [k, kd] are 2-D row-major torch tensors (or raw
-    device pointers with ldx / ldy); out is a float32 tensor of nnz elements
-    (or a raw pointer)."""
+    device pointers with ldx / ldy); out (tensor or raw pointer) holds the
+    plan's output type: fp32, bf16 bits or int32, one per stored entry (WCSR)
+    or [nnzb, 64, 64] (BCSR)."""
     if isinstance(x, int) or isinstance(y, int):
         xp, yp = int(x), int(y)
         if ldx is None or ldy is None:

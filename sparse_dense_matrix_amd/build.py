@@ -12,7 +12,7 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libspmm.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.cpp", "pack.cpp", "bcsr_bf16.hip", "wcsr_f32.hip", "sp24.hip", "sddmm_f32.hip", "sddmm_bcsr.hip"]
+SOURCES = ["api.cpp", "pack.cpp", "bcsr_bf16.hip", "wcsr_f32.hip", "sp24.hip", "sddmm_csr.hip", "sddmm_bcsr.hip"]
 ARCH = "gfx950"
 
 # Every HIP object is built with packed fp32 arithmetic disabled.

@@ -273,7 +273,7 @@ spmm_status_t plan_wcsr(spmm_plan_s *p) {
 }
 
 // ---- SDDMM plan: the WCSR chunks, the pattern, no workspace ----------------
-spmm_status_t plan_sddmm(spmm_plan_s *p, int64_t kd) {
+spmm_status_t plan_sddmm(spmm_plan_s *p, int64_t kd, spmm_dtype_t dtype) {
   const Matrix &a = *p->a;
   std::vector<WcsrChunk> chunks;
   std::vector<int32_t> slot_row;  // unused: sampled entries are independent
@@ -291,6 +291,7 @@ spmm_status_t plan_sddmm(spmm_plan_s *p, int64_t kd) {
   L.row_ptr = drp;
   L.col_idx = dci;
   L.kd = kd;
+  L.dtype = dtype;
   p->info.grid = sddmm_grid(L.num_chunks);
   return SPMM_OK;
 }
@@ -787,12 +788,13 @@ spmm_status_t spmm_plan_sddmm(spmm_matrix_t a, int64_t kd, spmm_dtype_t dtype, i
   if (!out) return fail(SPMM_ERR_INVALID_ARG, "spmm_plan_sddmm: out is NULL");
   *out = nullptr;
   if (!a || kd < 0 || kd > INT32_MAX) return fail(SPMM_ERR_INVALID_ARG, "spmm_plan_sddmm: bad matrix or kd");
-  const bool wcsr = a->format == SPMM_FORMAT_WCSR && dtype == SPMM_F32;
+  const bool wcsr = a->format == SPMM_FORMAT_WCSR &&
+                    (dtype == SPMM_F32 || dtype == SPMM_BF16 || dtype == SPMM_I8);
   const bool bcsr = a->format == SPMM_FORMAT_BCSR && (dtype == SPMM_BF16 || dtype == SPMM_I8);
   if (!wcsr && !bcsr)
     return fail(SPMM_ERR_UNSUPPORTED,
-                "spmm_plan_sddmm: needs a WCSR pattern with fp32 X, Y or a BCSR pattern with "
-                "bf16 or int8 X, Y");
+                "spmm_plan_sddmm: needs a WCSR pattern (fp32, bf16 or int8 X, Y) or a BCSR pattern "
+                "(bf16 or int8 X, Y)");
   if (bcsr && (a->bm != 64 || a->bk != 64))
     return fail(SPMM_ERR_UNSUPPORTED, "spmm_plan_sddmm: BCSR patterns take 64 x 64 blocks");
   if (bcsr && (!a->row_perm.empty() || !a->col_perm.empty()))
@@ -818,7 +820,7 @@ spmm_status_t spmm_plan_sddmm(spmm_matrix_t a, int64_t kd, spmm_dtype_t dtype, i
     p->info.n = kd;
     spmm_status_t s = SPMM_ERR_INTERNAL;
     try {
-      s = wcsr ? plan_sddmm(p, kd) : plan_sddmm_bcsr(p, kd, dtype == SPMM_I8);
+      s = wcsr ? plan_sddmm(p, kd, dtype) : plan_sddmm_bcsr(p, kd, dtype == SPMM_I8);
     } catch (...) {
       free_plan(p);
       throw;
@@ -847,13 +849,14 @@ spmm_status_t spmm_execute_sddmm(spmm_plan_t p, const void *x_dev, int64_t ldx, 
   if (bcsr ? a.bcol_idx.empty() : a.nnz == 0) return SPMM_OK;
   if (!out_dev || (kd > 0 && (!x_dev || !y_dev)))
     return fail(SPMM_ERR_INVALID_ARG, "spmm_execute_sddmm: X, Y or out is NULL");
-  const uintptr_t out_align = bcsr ? 15u : 3u;
+  // out: 16-byte pieces of blocks (BCSR), else one element per entry
+  const uintptr_t out_align = bcsr ? 15u : (p->sddmm_dtype == SPMM_BF16 ? 1u : 3u);
   if ((reinterpret_cast<uintptr_t>(out_dev) & out_align) ||
       (kd > 0 && (!aligned16(x_dev) || !aligned16(y_dev) || ldx < kd || ldy < kd ||
                   (ldx * elem) % 16 != 0 || (ldy * elem) % 16 != 0)))
     return fail(SPMM_ERR_INVALID_ARG,
                 "spmm_execute_sddmm: X/Y must be 16-byte aligned with ld >= kd and ld*elem % 16 "
-                "== 0; out aligned to 16 bytes (BCSR) or 4 bytes (WCSR)");
+                "== 0; out aligned to 16 bytes (BCSR) or to its element (WCSR)");
   // a BCSR workgroup addresses its 64 rows of X and of Y with 32-bit byte offsets
   if (bcsr && kd > 0 && 64 * std::max(ldx, ldy) * elem >= (int64_t(1) << 32))
     return fail(SPMM_ERR_UNSUPPORTED, "spmm_execute_sddmm: rows of X or Y longer than 64 MiB");
@@ -870,12 +873,12 @@ spmm_status_t spmm_execute_sddmm(spmm_plan_t p, const void *x_dev, int64_t ldx, 
     e = launch_sddmm_bcsr(L, stream);
   } else {
     SddmmLaunch L = p->sdd;
-    L.X = static_cast<const float *>(x_dev);
+    L.X = x_dev;
     L.ldx = ldx;
-    L.Y = static_cast<const float *>(y_dev);
+    L.Y = y_dev;
     L.ldy = ldy;
-    L.out = static_cast<float *>(out_dev);
-    e = launch_sddmm_f32(L, stream);
+    L.out = out_dev;
+    e = launch_sddmm_csr(L, stream);
   }
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return SPMM_OK;

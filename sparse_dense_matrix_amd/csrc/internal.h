@@ -154,13 +154,14 @@ struct SddmmLaunch {
   const int64_t *row_ptr;
   const int32_t *col_idx;
   int64_t kd;         // inner dimension
-  const float *X;     // [m][ldx]
+  spmm_dtype_t dtype; // X and Y: F32 (out fp32), BF16 (out bf16) or I8 (out int32)
+  const void *X;      // [m][ldx]
   int64_t ldx;
-  const float *Y;     // [k][ldy]
+  const void *Y;      // [k][ldy]
   int64_t ldy;
-  float *out;         // [nnz]
+  void *out;          // [nnz]
 };
-hipError_t launch_sddmm_f32(const SddmmLaunch &a, hipStream_t s);
+hipError_t launch_sddmm_csr(const SddmmLaunch &a, hipStream_t s);
 int64_t sddmm_grid(int64_t num_chunks);
 
 // SDDMM with a BCSR pattern of 64 x 64 blocks: a workgroup serves a group of

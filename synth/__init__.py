@@ -221,8 +221,8 @@ class Workload:
     block: int = 64               # bcsr
     nblocks: int = 0
     sigma: float = 0.02
-    elem: str = ""                # sddmm_bcsr: "bf16" | "i8" operands X, Y; tvw: "bf16"
-                                  # A and B (default int8)
+    elem: str = ""                # sddmm, sddmm_bcsr: "bf16" | "i8" operands X, Y (sddmm
+                                  # default fp32); tvw: "bf16" A and B (default int8)
     scramble: int = 0             # > 0: a block-sparse matrix with rows and columns
                                   # shuffled (this seed), given as CSR
     reorder: bool = False         # bcsr_csr: pack after the row/column reordering
@@ -279,6 +279,11 @@ WORKLOADS: Dict[str, Workload] = {
     # the sampled dense-dense product on the power-law pattern, inner dimension 128
     "sddmm_powerlaw_1m": Workload("sddmm_powerlaw_1m", "sddmm", 1_000_000, 1_000_000, 128, 20260003,
                                   powerlaw=True),
+    # the same pattern with bf16 and int8 X, Y
+    "sddmm_bf16_powerlaw_1m": Workload("sddmm_bf16_powerlaw_1m", "sddmm", 1_000_000, 1_000_000, 128,
+                                       20260003, powerlaw=True, elem="bf16"),
+    "sddmm_i8_powerlaw_1m": Workload("sddmm_i8_powerlaw_1m", "sddmm", 1_000_000, 1_000_000, 128,
+                                     20260003, powerlaw=True, elem="i8"),
     # the same product on the block pattern of the 18944 x 3584 layer: the
     # layer's weight gradient over one GPU's share (8192) of 65536 tokens
     "sddmm_bcsr_prefill_kd8192": _bcsr("sddmm_bcsr_prefill_kd8192", 18944, 3584, 8192, 0.90,
@@ -339,14 +344,14 @@ def make_a(w: Workload) -> dict:
 
 def make_xy(w: Workload, kd: int | None = None, elem: str | None = None):
     """Draw the dense operands of the sampled product: X [m x kd] and
-    Y [k x kd], row-major; float32 N(0, 1) for the CSR pattern, bf16 bits
-    N(0, 1) or int8 uniform on {-127 ... 127} for the block pattern."""
+    Y [k x kd], row-major; float32 N(0, 1) (the CSR pattern's default), bf16
+    bits N(0, 1) or int8 uniform on {-127 ... 127}."""
     kd = w.n if kd is None else kd
     elem = w.elem if elem is None else elem
-    if w.fmt == "sddmm_bcsr" and elem == "bf16":
+    if elem == "bf16":
         return (dense_bf16_normal(w.m, kd, w.seed, S_BVAL),
                 dense_bf16_normal(w.k, kd, w.seed, S_YVAL))
-    if w.fmt == "sddmm_bcsr" and elem == "i8":
+    if elem == "i8":
         return (int8_uniform(rng(w.seed, S_BVAL), (w.m, kd)),
                 int8_uniform(rng(w.seed, S_YVAL), (w.k, kd)))
     return dense_f32_normal(w.m, kd, w.seed, S_BVAL), dense_f32_normal(w.k, kd, w.seed, S_YVAL)

@@ -18,6 +18,8 @@ from gpu_helpers import TOL_BF16, TOL_F32, bf16_to_f64, run, to_dev, empty_out, 
 
 pytestmark = pytest.mark.gpu
 
+I32_SENTINEL = 0x7ABCDEF1   # an int32 no tested sum takes
+
 
 @pytest.fixture(scope="module")
 def S():
@@ -458,11 +460,116 @@ def test_sddmm_deterministic_and_plan_kinds(S, orc):
 
 
 # ---------------------------------------------------------------------------
-# SDDMM on a BCSR block pattern: bf16 -> bf16 and int8 -> int32
+# SDDMM on the CSR pattern with bf16 (-> bf16) and int8 (-> int32) operands
 # ---------------------------------------------------------------------------
 
-I32_SENTINEL = 0x7ABCDEF1
+def sddmm_typed_case(S, orc, m, k, rp, ci, X, Y, elem, W=0, T=0, rows=None, extra=0):
+    """bf16 (uint16 bits) or int8 X, Y.  The oracle gets their exact fp32
+    images and sums in fp64 (exact for the int8 products).  Returns the
+    sampled outputs (float64) and the reference."""
+    torch = pytest.importorskip("torch")
+    M = S.spmm_pack_wcsr(m, k, rp, ci, np.ones(len(ci), np.float32), W, T)
+    kd = X.shape[1]
+    P = S.spmm_plan_sddmm(M, kd, S.BF16 if elem == "bf16" else S.I8)
+    nnz = len(ci)
+    if elem == "bf16":
+        out = torch.full((max(nnz, 1),), -1, dtype=torch.int16, device="cuda")   # NaN bits
+        pad = (-kd) % 8 + extra
+    else:
+        out = torch.full((max(nnz, 1),), I32_SENTINEL, dtype=torch.int32, device="cuda")
+        pad = (-kd) % 16 + extra
+    S.spmm_execute_sddmm(P, to_dev(X, pad), to_dev(Y, pad), out)
+    torch.cuda.synchronize()
+    raw = out.cpu().numpy()[:nnz]
+    if elem == "bf16":
+        got = bf16_to_f64(raw.view(np.uint16))
+        assert np.isfinite(got).all(), "unwritten or non-finite outputs"
+        Xf, Yf = synth.bf16_bits_to_f32(X), synth.bf16_bits_to_f32(Y)
+    else:
+        assert (raw != I32_SENTINEL).all(), "unwritten outputs"
+        got = raw.astype(np.float64)
+        Xf, Yf = X.astype(np.float32), Y.astype(np.float32)
+    ref = orc.sddmm(rp, ci, Xf, Yf, rows=rows)
+    sel = got if rows is None else (np.concatenate([got[rp[i]:rp[i + 1]] for i in rows])
+                                    if len(rows) else got[:0])
+    return sel, ref, raw, P
 
+
+@pytest.mark.parametrize("elem", ["bf16", "i8"])
+@pytest.mark.parametrize("kd", [1, 8, 16, 63, 96, 128, 200, 1000])
+def test_sddmm_csr_typed_small(S, orc, elem, kd):
+    w = synth.SMALL["sddmm_small"]          # 20000 x 20000 power-law pattern
+    a = synth.make_a(w)
+    X, Y = synth.make_xy(w, kd, elem)
+    for W, T, extra in ((0, 0, 0), (16, 64, 16), (1, 5, 0)):
+        got, ref, _, P = sddmm_typed_case(S, orc, w.m, w.k, a["row_ptr"], a["col_idx"], X, Y, elem,
+                                          W, T, extra=extra)
+        if elem == "bf16":
+            err = orc.rel_frobenius(got, ref)
+            assert err <= TOL_BF16, err
+        else:
+            np.testing.assert_array_equal(got, ref)
+    _say(f"sddmm_small {elem} kd={kd} grid={P.info()['grid']} ok")
+
+
+def test_sddmm_csr_bf16_integer_values_exact(S, orc):
+    # small integers: the fp32 sums are exact, so each output is exactly the
+    # round-to-nearest-even bf16 of the exact sum
+    w = synth.SMALL["sddmm_small"]
+    a = synth.make_a(w)
+    r = np.random.default_rng(26)
+    kd = 200
+    X = synth.f32_to_bf16_bits(r.integers(-3, 4, size=(w.m, kd)).astype(np.float32))
+    Y = synth.f32_to_bf16_bits(r.integers(-3, 4, size=(w.k, kd)).astype(np.float32))
+    _, ref, raw, _ = sddmm_typed_case(S, orc, w.m, w.k, a["row_ptr"], a["col_idx"], X, Y, "bf16")
+    exp = synth.f32_to_bf16_bits(ref.astype(np.float32))
+    nz = ref != 0
+    np.testing.assert_array_equal(raw.view(np.uint16)[nz], exp[nz])
+    assert (raw.view(np.uint16)[~nz] & 0x7FFF == 0).all()
+
+
+def test_sddmm_csr_typed_extremes_and_kd0(S, orc):
+    # int8 extremes: -128 * -128 summed over a long row stays exact
+    k, kd = 5000, 1024
+    rp = np.array([0, 3, 3, 5000], np.int64)
+    ci = np.concatenate([[0, 7, 4999], np.arange(4997)]).astype(np.int32)
+    X = np.full((3, kd), -128, np.int8)
+    Y = synth.int8_uniform(np.random.default_rng(27), (k, kd))
+    Y[0] = -128
+    got, ref, _, _ = sddmm_typed_case(S, orc, 3, k, rp, ci, X, Y, "i8", 1, 300)
+    np.testing.assert_array_equal(got, ref)
+    assert got[0] == 128 * 128 * kd
+    # kd = 0: empty sums
+    for elem in ("bf16", "i8"):
+        Xe = np.zeros((3, 0), np.uint16 if elem == "bf16" else np.int8)
+        Ye = np.zeros((k, 0), Xe.dtype)
+        got, _, _, _ = sddmm_typed_case(S, orc, 3, k, rp, ci, Xe, Ye, elem, 16, 512)
+        assert (got == 0).all()
+
+
+@pytest.mark.parametrize("name", ["sddmm_bf16_powerlaw_1m", "sddmm_i8_powerlaw_1m"])
+def test_sddmm_csr_typed_1m_sampled(S, orc, name):
+    w = synth.WORKLOADS[name]
+    a = synth.make_a(w)
+    X, Y = synth.make_xy(w)
+    lens = np.diff(a["row_ptr"])
+    r = np.random.default_rng(28)
+    rows = np.unique(np.concatenate([np.argsort(lens)[-100:], r.choice(w.m, 1000, replace=False),
+                                     np.arange(20), np.arange(w.m - 20, w.m)])).astype(np.int64)
+    got, ref, _, P = sddmm_typed_case(S, orc, w.m, w.k, a["row_ptr"], a["col_idx"], X, Y, w.elem,
+                                      rows=rows)
+    if w.elem == "bf16":
+        err = orc.rel_frobenius(got, ref)
+        _say(f"{name} rows={len(rows)} rel_frob={err:.3e}")
+        assert err <= TOL_BF16
+    else:
+        np.testing.assert_array_equal(got, ref)
+        _say(f"{name} rows={len(rows)} exact")
+
+
+# ---------------------------------------------------------------------------
+# SDDMM on a BCSR block pattern: bf16 -> bf16 and int8 -> int32
+# ---------------------------------------------------------------------------
 
 def sddmm_bcsr_case(S, orc, a_bits, X, Y, elem, blocks=None, extra=0):
     """Run the block-pattern SDDMM and return (got [nnzb, 64, 64], ref for

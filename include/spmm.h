@@ -1,7 +1,7 @@
 /*
  * spmm.h -- C ABI of the MI355X (gfx950) sparse x dense multiplication library.
  *
- * The library computes C = A * B, A sparse, B and C dense, for three sparse
+ * The library computes C = A * B, A sparse, B and C dense, for these sparse
  * encodings:
  *
  *   BCSR  block compressed sparse row, bf16 A and B, fp32 accumulation,
@@ -19,6 +19,15 @@
  *         GEMM", abstract (2:4 pattern); "Efficient Quantized Sparse Matrix
  *         Operations on Tensor Cores", abstract (SpMM on low-precision
  *         integers); the N:M entry of the "Daily Papers" search page.
+ *   TVW   tile-vector-wise: tiles of A that hold a nonzero are stored, 2:4
+ *         inside; int8 (int32 C) or bf16 (bf16 C).  "Accelerating Sparse
+ *         DNNs Based on Tiled GEMM", abstract.
+ *   SLIDE (2N-2):2N weights as N-1 overlapping 2:4 windows per group, int8;
+ *         the (2N-2):2N entry of the "Daily Papers" search page.
+ *
+ * and the sampled dense-dense product (SDDMM) on a WCSR or BCSR pattern, the
+ * companion of SpMM on the Magicube page ("Efficient Quantized Sparse Matrix
+ * Operations on Tensor Cores", abstract).
  *
  * Usage: pack A once on the host (spmm_pack_*), build a device plan for a
  * given number of columns n (spmm_plan), then multiply any number of dense B
@@ -74,9 +83,11 @@ typedef struct {
   int32_t format;        /* spmm_format_t                                      */
   int32_t dtype;         /* element type of A                                  */
   int64_t m, k;          /* logical shape of A                                 */
-  int64_t nnz;           /* stored entries: nnzb*bm*bk, CSR nnz, or m*k/2      */
-  int64_t nnzb;          /* BCSR: stored blocks; otherwise 0                   */
-  int32_t block_m, block_k;        /* BCSR block shape; otherwise 0            */
+  int64_t nnz;           /* stored entries: nnzb*bm*bk (BCSR), CSR nnz, m*k/2   */
+                         /* (2:4), nnzb*bm*bk/2 (TVW), m*k_lift/2 (SLIDE)      */
+  int64_t nnzb;          /* BCSR: stored blocks; TVW: stored tiles; else 0    */
+  int32_t block_m, block_k;        /* BCSR block / TVW tile shape; SLIDE: 0 and */
+                                   /* the group width 2N; otherwise 0          */
   int32_t window_rows;             /* WCSR: rows per window W; otherwise 0     */
   int64_t max_chunk_nnz;           /* WCSR: chunk bound T; otherwise 0         */
   int64_t num_windows, num_chunks; /* WCSR; otherwise 0                        */

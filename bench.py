@@ -50,7 +50,7 @@ TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 
 
 def dominant_kernel(w) -> str:
-    if w.fmt == "tvw" and w.elem == "bf16":
+    if w.fmt in ("tvw", "sp24") and w.elem == "bf16":
         return "sp24_bf16_smfmac"
     return DOMINANT_KERNEL[w.fmt]
 CSRC = os.path.join(ROOT, "sparse_dense_matrix_amd", "csrc")
@@ -118,7 +118,7 @@ def setup(w, S, args):
         types = (S.I8, S.I32)
     else:
         M = S.spmm_pack_24(a["dense"])
-        types = (S.I8, S.I32)
+        types = (S.BF16, S.BF16) if w.elem == "bf16" else (S.I8, S.I32)
     t_pack = time.perf_counter() - t0
     t0 = time.perf_counter()
     if w.fmt == "sddmm":
@@ -201,8 +201,9 @@ def algorithmic(w, d):
         a_bytes = info["nnz"] * e + info["nnz"] // 4 + 4 * (w.m // synth_tile_m() + 1 + info["nnzb"])
         return (flops, a_bytes + len(steps) * synth_tile_k() * n * e + w.m * n * ec,
                 "bf16" if w.elem == "bf16" else "i8")
-    a_bytes = w.m * w.k // 2 + w.m * w.k // 8
-    return flops, a_bytes + w.k * n + w.m * n * 4, "i8"
+    e, ec = (2, 2) if w.elem == "bf16" else (1, 4)
+    a_bytes = w.m * w.k // 2 * e + w.m * w.k // 8
+    return flops, a_bytes + w.k * n * e + w.m * n * ec, "bf16" if w.elem == "bf16" else "i8"
 
 
 def main():
@@ -259,7 +260,7 @@ def main():
         Bt = Bh.cuda()
         cdt = {"bcsr": torch.int16, "bcsr_csr": torch.int16, "wcsr": torch.float32,
                "sp24": torch.int32, "tvw": torch.int32, "slide": torch.int32}[w.fmt]
-        if w.fmt == "tvw" and w.elem == "bf16":
+        if w.fmt in ("tvw", "sp24") and w.elem == "bf16":
             cdt = torch.int16
         Ct = torch.empty((w.m, w.n), dtype=cdt, device="cuda")
 
@@ -310,7 +311,7 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, d, args.cpu_seconds)
     dense = None
-    if args.dense_baseline and (w.fmt == "bcsr" or (w.fmt == "tvw" and w.elem == "bf16")):
+    if args.dense_baseline and (w.fmt == "bcsr" or (w.fmt in ("tvw", "sp24") and w.elem == "bf16")):
         dense = dense_baseline(torch, w, d, Bt, stream, args, ms_step)
     elif args.dense_baseline and w.fmt in ("tvw", "sp24", "slide"):
         dense = dense_baseline_i8(torch, w, d, Bt, stream, args, ms_step)
@@ -598,7 +599,7 @@ def cpu_baseline(w, d, target_s):
                 "sample": f"{count} of {units} stored blocks (uniform without replacement, "
                           f"seed 0), full inner dimension {w.n}; "
                           + ("fp64" if w.elem == "bf16" else "int64") + " accumulation"}
-    elif w.fmt == "tvw" and w.elem == "bf16":
+    elif w.fmt in ("tvw", "sp24") and w.elem == "bf16":
         # the oracle's 2:4 pruning, then its BCSR product over tiles of
         # 256 x 128 (every element of a stored tile, pruned or not, is walked)
         pruned = oracle.prune_nm(a["dense"], 2, 4)

@@ -110,7 +110,8 @@ typedef struct {
  *    SPMM_ARRAY_CHUNK_WINDOW  int32[num_chunks]    window of each chunk
  *    SPMM_ARRAY_CHUNK_BEGIN   int64[num_chunks+1]  first stored entry; last = nnz
  *  2:4
- *    SPMM_ARRAY_VALS      int8[m * k/2]   the two kept values of group g of row i at
+ *    SPMM_ARRAY_VALS      int8 or bf16 (uint16)[m * k/2]  the two kept values of group g
+ *                                         of row i at
  *                                         [i*k/2 + 2g], [i*k/2 + 2g + 1], ascending position
  *    SPMM_ARRAY_META      uint8[m * k/8]  nibble (i0 | i1 << 2) of group g in byte
  *                                         i*k/8 + g/2, low nibble for even g
@@ -209,13 +210,15 @@ spmm_status_t spmm_pack_wcsr(int64_t m, int64_t k, spmm_dtype_t dtype,
                              const void *vals, int32_t window_rows,
                              int64_t max_chunk_nnz, spmm_matrix_t *out);
 
-/* 2:4 from a dense row-major int8 matrix a_host [m x k] (lda >= k): in every
- * group of 4 consecutive elements of a row keep the two of largest |a| (as
- * integers: |-128| = 128), ties to the lower position, and store them with
- * their 2-bit positions as described above.  Packing an already 2:4 matrix is
+/* 2:4 from a dense row-major matrix a_host [m x k] (lda >= k) of dtype SPMM_I8
+ * (int8) or SPMM_BF16 (uint16 bit patterns; else UNSUPPORTED): in every group
+ * of 4 consecutive elements of a row keep the two of largest |a| (int8 as
+ * integers: |-128| = 128; bf16 in magnitude order, every NaN above infinity
+ * and NaNs equal), ties to the lower position, and store them with their
+ * 2-bit positions as described above.  Packing an already 2:4 matrix is
  * lossless.  Requires k % 8 == 0. */
-spmm_status_t spmm_pack_24(int64_t m, int64_t k, const int8_t *a_host, int64_t lda,
-                           spmm_matrix_t *out);
+spmm_status_t spmm_pack_24(int64_t m, int64_t k, spmm_dtype_t dtype, const void *a_host,
+                           int64_t lda, spmm_matrix_t *out);
 
 spmm_status_t spmm_matrix_info(spmm_matrix_t a, spmm_matrix_info_t *info);
 /* Read-only view of a canonical array, valid while the matrix lives.
@@ -232,7 +235,8 @@ void spmm_matrix_destroy(spmm_matrix_t a);
  * for n columns, and allocate the workspace.  Supported (b_dtype, c_dtype):
  *   BCSR (64 x 64 blocks): (BF16, BF16), n % 8 == 0
  *   WCSR:                  (F32, F32), any n >= 1
- *   2:4:                   (I8, I32), n % 16 == 0
+ *   2:4, int8:             (I8, I32), n % 16 == 0
+ *   2:4, bf16:             (BF16, BF16), n % 16 == 0; fp32 sums rounded to nearest even
  *   TVW, int8 (256 x 128j tiles):  (I8, I32), n % 16 == 0
  *   TVW, bf16 (256 x 64j tiles):   (BF16, BF16), n % 16 == 0; fp32 sums rounded to
  *                                  nearest even

@@ -86,7 +86,7 @@ def _load():
         "spmm_pack_bcsr": (st, [i64, i64, i32, i32, st, P, i64, C.POINTER(P)]),
         "spmm_pack_wcsr": (st, [i64, i64, st, P, P, P, i32, i64, C.POINTER(P)]),
         "spmm_pack_bcsr_csr": (st, [i64, i64, st, P, P, P, i32, i32, i32, C.POINTER(P)]),
-        "spmm_pack_24": (st, [i64, i64, P, i64, C.POINTER(P)]),
+        "spmm_pack_24": (st, [i64, i64, i32, P, i64, C.POINTER(P)]),
         "spmm_pack_tvw": (st, [i64, i64, i32, P, i64, i32, i32, C.POINTER(P)]),
         "spmm_pack_slide": (st, [i64, i64, P, i64, i32, C.POINTER(P)]),
         "spmm_matrix_info": (st, [P, C.POINTER(MatrixInfo)]),
@@ -244,11 +244,19 @@ def spmm_pack_wcsr(m: int, k: int, row_ptr, col_idx, vals,
 
 
 def spmm_pack_24(a: np.ndarray) -> Matrix:
-    a = np.ascontiguousarray(a, dtype=np.int8)
+    """2:4 from a dense matrix: int8, or bf16 given as uint16 bit patterns."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        dtype = BF16
+    elif a.dtype == np.int8:
+        dtype = I8
+    else:
+        raise TypeError("spmm_pack_24 takes int8 or uint16 (bf16 bits) values")
+    a = np.ascontiguousarray(a)
     if a.ndim != 2:
         raise ValueError("a must be 2-D")
     h = C.c_void_p()
-    _check(_lib.spmm_pack_24(a.shape[0], a.shape[1], _ptr(a), a.shape[1], C.byref(h)),
+    _check(_lib.spmm_pack_24(a.shape[0], a.shape[1], dtype, _ptr(a), a.shape[1], C.byref(h)),
            "spmm_pack_24")
     return Matrix(h)
 
@@ -281,7 +289,7 @@ def spmm_matrix_array(mat: Matrix, which: int) -> np.ndarray:
     info = spmm_matrix_info(mat)
     fmt = info["format"]
     dt = np.dtype(_ARRAY_DTYPES[(fmt, which)])
-    if fmt == FORMAT_TVW and which == ARRAY_VALS and info["dtype"] == BF16:
+    if fmt in (FORMAT_TVW, FORMAT_24) and which == ARRAY_VALS and info["dtype"] == BF16:
         dt = np.dtype(np.uint16)
     if count.value == 0:
         return np.zeros(0, dtype=dt)

@@ -358,16 +358,19 @@ spmm_status_t plan_24(spmm_plan_s *p) {
   if (p->n % 16 != 0) return fail(SPMM_ERR_UNSUPPORTED, "spmm_plan: 2:4 needs n % 16 == 0");
   // a sliding-window matrix is the 2:4 matrix of its lifted columns
   const bool slide = a.format == SPMM_FORMAT_SLIDE;
+  const bool bf16 = a.dtype == SPMM_BF16;
+  const int64_t elem = bf16 ? 2 : 1;
   const int64_t k = slide ? a.k_lift : a.k;
-  const int64_t TM = sp24_tile_m(), TK = sp24_tile_k(false);
+  const int64_t TM = sp24_tile_m(), TK = sp24_tile_k(bf16);
   const int64_t m_pad = (a.m + TM - 1) / TM * TM;
   const int64_t k_pad = std::max<int64_t>(TK, (k + TK - 1) / TK * TK);
-  std::vector<int8_t> v(static_cast<size_t>(m_pad * (k_pad / 2)));
+  std::vector<int8_t> v(static_cast<size_t>(m_pad * (k_pad / 2) * elem));
   std::vector<uint8_t> mt(static_cast<size_t>(m_pad * (k_pad / 8)));
-  sp24_tile_layout(a.vals24.data(), a.meta24.data(), a.m, k, m_pad, k_pad, false, v.data(),
-                   mt.data());
+  const void *src = bf16 ? static_cast<const void *>(a.vals24_bf16.data())
+                         : static_cast<const void *>(a.vals24.data());
+  sp24_tile_layout(src, a.meta24.data(), a.m, k, m_pad, k_pad, bf16, v.data(), mt.data());
   Sp24Launch &L = p->sp24;
-  L.bf16 = false;
+  L.bf16 = bf16;
   spmm_status_t s;
   int8_t *dv = nullptr;
   uint8_t *dm = nullptr;
@@ -587,16 +590,18 @@ spmm_status_t spmm_pack_wcsr(int64_t m, int64_t k, spmm_dtype_t dtype,
   });
 }
 
-spmm_status_t spmm_pack_24(int64_t m, int64_t k, const int8_t *a_host, int64_t lda,
-                           spmm_matrix_t *out) {
+spmm_status_t spmm_pack_24(int64_t m, int64_t k, spmm_dtype_t dtype, const void *a_host,
+                           int64_t lda, spmm_matrix_t *out) {
   if (!out) return fail(SPMM_ERR_INVALID_ARG, "spmm_pack_24: out is NULL");
   *out = nullptr;
+  if (dtype != SPMM_I8 && dtype != SPMM_BF16)
+    return fail(SPMM_ERR_UNSUPPORTED, "spmm_pack_24: int8 or bf16 values only");
   if (m < 0 || k < 0 || m > INT32_MAX || k > INT32_MAX || k % 8 != 0 || lda < k ||
       (m * k > 0 && !a_host))
     return fail(SPMM_ERR_INVALID_ARG, "spmm_pack_24: bad shape (k % 8 == 0 needed), lda or pointer");
   return guarded([&]() -> spmm_status_t {
     auto *a = new spmm_matrix_s();
-    spmm_status_t s = pack_24_i8(m, k, a_host, lda, *a);
+    spmm_status_t s = pack_24(m, k, dtype, a_host, lda, *a);
     if (s != SPMM_OK) {
       delete a;
       return s;
@@ -655,7 +660,8 @@ spmm_status_t spmm_matrix_array(spmm_matrix_t a, int32_t which, const void **dat
       if (which == SPMM_ARRAY_CHUNK_BEGIN) return give(a->chunk_begin);
       break;
     case SPMM_FORMAT_24:
-      if (which == SPMM_ARRAY_VALS) return give(a->vals24);
+      if (which == SPMM_ARRAY_VALS)
+        return a->dtype == SPMM_BF16 ? give(a->vals24_bf16) : give(a->vals24);
       if (which == SPMM_ARRAY_META) return give(a->meta24);
       break;
     case SPMM_FORMAT_SLIDE:
@@ -686,8 +692,8 @@ spmm_status_t spmm_plan(spmm_matrix_t a, int64_t n, spmm_dtype_t b_dtype, spmm_d
       ((a->format == SPMM_FORMAT_24 || a->format == SPMM_FORMAT_TVW ||
         a->format == SPMM_FORMAT_SLIDE) &&
        a->dtype == SPMM_I8 && b_dtype == SPMM_I8 && c_dtype == SPMM_I32) ||
-      (a->format == SPMM_FORMAT_TVW && a->dtype == SPMM_BF16 && b_dtype == SPMM_BF16 &&
-       c_dtype == SPMM_BF16);
+      ((a->format == SPMM_FORMAT_TVW || a->format == SPMM_FORMAT_24) && a->dtype == SPMM_BF16 &&
+       b_dtype == SPMM_BF16 && c_dtype == SPMM_BF16);
   if (!ok_types) return fail(SPMM_ERR_UNSUPPORTED, "spmm_plan: unsupported (format, B, C) types");
   int ndev = 0;
   hipError_t e = hipGetDeviceCount(&ndev);

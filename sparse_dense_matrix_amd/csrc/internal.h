@@ -47,8 +47,8 @@ struct Matrix {
   std::vector<int32_t> chunk_window;
   std::vector<int64_t> chunk_begin;
   // 2:4 (and the stored tiles of tile-vector-wise: brow_ptr / bcol_idx over
-  // tiles of bm x bk, vals24 / meta24 tile after tile); bf16 values of a
-  // bf16 tile-vector-wise matrix go to vals24_bf16 instead of vals24
+  // tiles of bm x bk, vals24 / meta24 tile after tile); bf16 values go to
+  // vals24_bf16 instead of vals24
   std::vector<int8_t> vals24;
   std::vector<uint16_t> vals24_bf16;
   std::vector<uint8_t> meta24;
@@ -63,7 +63,9 @@ spmm_status_t pack_bcsr_bf16(int64_t m, int64_t k, int32_t bm, int32_t bk,
 spmm_status_t pack_wcsr_f32(int64_t m, int64_t k, const int64_t *row_ptr,
                             const int32_t *col_idx, const float *vals, int32_t W,
                             int64_t T, Matrix &out);
-spmm_status_t pack_24_i8(int64_t m, int64_t k, const int8_t *a, int64_t lda, Matrix &out);
+// dtype SPMM_I8 (a: int8) or SPMM_BF16 (a: bf16 bit patterns)
+spmm_status_t pack_24(int64_t m, int64_t k, spmm_dtype_t dtype, const void *a, int64_t lda,
+                      Matrix &out);
 spmm_status_t pack_slide_i8(int64_t m, int64_t k, const int8_t *a, int64_t lda, int32_t group,
                             Matrix &out);
 // lifted row j of a sliding-window matrix -> row of B it multiplies

@@ -317,16 +317,28 @@ static void prune_row(const T *row, int64_t len, T *v, uint8_t *mt) {
   }
 }
 
-spmm_status_t pack_24_i8(int64_t m, int64_t k, const int8_t *a, int64_t lda, Matrix &out) {
+template <class V>
+static void pack_24_t(int64_t m, int64_t k, const V *a, int64_t lda, std::vector<V> &vals,
+                      Matrix &out) {
+  vals.assign(static_cast<size_t>(m * (k / 2)), 0);
+  out.meta24.assign(static_cast<size_t>(m * (k / 8)), 0);
+  for (int64_t i = 0; i < m; ++i)
+    prune_row(a + i * lda, k, vals.data() + i * (k / 2), out.meta24.data() + i * (k / 8));
+}
+
+spmm_status_t pack_24(int64_t m, int64_t k, spmm_dtype_t dtype, const void *a, int64_t lda,
+                      Matrix &out) {
   out.format = SPMM_FORMAT_24;
-  out.dtype = SPMM_I8;
+  out.dtype = dtype;
   out.m = m;
   out.k = k;
   out.nnz = m * (k / 2);
-  out.vals24.assign(static_cast<size_t>(m * (k / 2)), 0);
-  out.meta24.assign(static_cast<size_t>(m * (k / 8)), 0);
-  for (int64_t i = 0; i < m; ++i)
-    prune_row(a + i * lda, k, out.vals24.data() + i * (k / 2), out.meta24.data() + i * (k / 8));
+  out.vals24.clear();
+  out.vals24_bf16.clear();
+  if (dtype == SPMM_BF16)
+    pack_24_t(m, k, static_cast<const uint16_t *>(a), lda, out.vals24_bf16, out);
+  else
+    pack_24_t(m, k, static_cast<const int8_t *>(a), lda, out.vals24, out);
   return SPMM_OK;
 }
 

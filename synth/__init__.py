@@ -222,7 +222,7 @@ class Workload:
     nblocks: int = 0
     sigma: float = 0.02
     elem: str = ""                # sddmm, sddmm_bcsr: "bf16" | "i8" operands X, Y (sddmm
-                                  # default fp32); tvw: "bf16" A and B (default int8)
+                                  # default fp32); sp24, tvw: "bf16" A and B (default int8)
     scramble: int = 0             # > 0: a block-sparse matrix with rows and columns
                                   # shuffled (this seed), given as CSR
     reorder: bool = False         # bcsr_csr: pack after the row/column reordering
@@ -249,6 +249,8 @@ WORKLOADS: Dict[str, Workload] = {
     "csr_powerlaw_1m": Workload("csr_powerlaw_1m", "wcsr", 1_000_000, 1_000_000, 128, 20260003,
                                 powerlaw=True),
     "sp24_i8_8192": Workload("sp24_i8_8192", "sp24", 8192, 8192, 2048, 20260004),
+    # the same shapes in bf16: weights N(0, 0.02), B N(0, 1)
+    "sp24_bf16_8192": Workload("sp24_bf16_8192", "sp24", 8192, 8192, 2048, 20260014, elem="bf16"),
     "bcsr_prefill_18944x3584": _bcsr("bcsr_prefill_18944x3584", 18944, 3584, 65536, 0.90, 20260005),
     # the same layer at milder block sparsity (50% and 70% of the blocks zero)
     "bcsr_prefill_18944x3584_z50": _bcsr("bcsr_prefill_18944x3584_z50", 18944, 3584, 65536, 0.50,
@@ -300,6 +302,7 @@ SMALL: Dict[str, Workload] = {
                                    powerlaw=True, cap=3000, band_half=64),
     "bcsr_small": _bcsr("bcsr_small", 640, 512, 1000, 0.7, 33),
     "sp24_small": Workload("sp24_small", "sp24", 320, 512, 400, 34),
+    "sp24_bf16_small": Workload("sp24_bf16_small", "sp24", 320, 512, 400, 41, elem="bf16"),
     "bcsr_prefill_slice": _bcsr("bcsr_prefill_slice", 18944, 3584, 4096 + 64 * 3, 0.90, 20260005),
     "sddmm_small": Workload("sddmm_small", "sddmm", 20000, 20000, 96, 32, powerlaw=True, cap=3000,
                             band_half=64),
@@ -332,6 +335,8 @@ def make_a(w: Workload) -> dict:
     if w.fmt in ("bcsr", "sddmm_bcsr"):
         a, ids = block_sparse_dense_bf16(w.m, w.k, w.block, w.block, w.nblocks, w.sigma, w.seed)
         return {"dense": a, "block_ids": ids}
+    if w.fmt == "sp24" and w.elem == "bf16":
+        return {"dense": f32_to_bf16_bits(normal_f32(rng(w.seed, S_AVAL), (w.m, w.k), w.sigma))}
     if w.fmt in ("sp24", "slide"):
         return {"dense": int8_uniform(rng(w.seed, S_AVAL), (w.m, w.k))}
     if w.fmt == "tvw" and w.elem == "bf16":
@@ -365,7 +370,7 @@ def make_b(w: Workload, n: int | None = None) -> np.ndarray:
         return bf16_bits_to_f32(bits) if w.fmt == "wcsr" else bits   # the same values
     if w.fmt == "wcsr":
         return dense_f32_normal(w.k, n, w.seed)
-    if w.fmt == "bcsr" or (w.fmt == "tvw" and w.elem == "bf16"):
+    if w.fmt == "bcsr" or (w.fmt in ("tvw", "sp24") and w.elem == "bf16"):
         return dense_bf16_normal(w.k, n, w.seed)
     if w.fmt in ("sp24", "tvw", "slide"):
         return int8_uniform(rng(w.seed, S_BVAL), (w.k, n))

@@ -121,6 +121,31 @@ def test_pack_24_matches_oracle(S, orc, seed):
     np.testing.assert_array_equal(S.spmm_matrix_array(M, S.ARRAY_META), mt.ravel())
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_pack_24_bf16_is_the_oracle_prune(S, orc, seed):
+    # densify the library's arrays and compare with the oracle's bf16 pruning
+    r = np.random.default_rng(60 + seed)
+    m, k = int(r.integers(1, 40)), 8 * int(r.integers(1, 12))
+    a = synth.f32_to_bf16_bits(r.normal(size=(m, k)).astype(np.float32))
+    a[r.random((m, k)) < 0.2] = 0
+    specials = np.array([0x7FC0, 0x7F80, 0xFF80, 0x8000, 0x0001, 0x3F80, 0xBF80], np.uint16)
+    idx = r.integers(0, [m, k], size=(min(m * k, 12), 2))
+    a[idx[:, 0], idx[:, 1]] = r.choice(specials, size=len(idx))
+    M = S.spmm_pack_24(a)
+    v = S.spmm_matrix_array(M, S.ARRAY_VALS).reshape(m, k // 2)
+    mt = S.spmm_matrix_array(M, S.ARRAY_META).reshape(m, k // 8)
+    assert v.dtype == np.uint16 and S.spmm_matrix_info(M)["dtype"] == S.BF16
+    dense = np.zeros((m, k), np.uint16)
+    rows = np.arange(m)
+    for g in range(k // 4):
+        nib = (mt[:, g // 2] >> (4 * (g % 2))) & 0xF
+        i0, i1 = nib & 3, nib >> 2
+        assert (i0 < i1).all()
+        dense[rows, 4 * g + i0] = v[:, 2 * g]
+        dense[rows, 4 * g + i1] = v[:, 2 * g + 1]
+    np.testing.assert_array_equal(dense, orc.prune_nm(a, 2, 4))
+
+
 def test_pack_24_full_config(S, orc):
     w = synth.WORKLOADS["sp24_i8_8192"]
     a = synth.make_a(w)["dense"]
@@ -178,11 +203,15 @@ def test_bcsr_and_24_shape_errors(S):
     assert _status(S, S.spmm_pack_bcsr, np.zeros((64, 64), np.uint16), 64, 64,
                    S.F32) == "SPMM_ERR_UNSUPPORTED"
     assert _status(S, S.spmm_pack_24, np.zeros((4, 12), np.int8)) == "SPMM_ERR_INVALID_ARG"
+    import ctypes
+    h, buf = ctypes.c_void_p(), np.zeros(32, np.float32)
+    assert S.lib().spmm_pack_24(4, 8, S.F32, buf.ctypes.data, 8, ctypes.byref(h)) == 2  # UNSUPPORTED
+    assert not h.value
 
 
 def test_null_out_and_handles(S):
     lib = S.lib()
-    assert lib.spmm_pack_24(4, 8, None, 8, None) == 1
+    assert lib.spmm_pack_24(4, 8, S.I8, None, 8, None) == 1
     assert lib.spmm_matrix_info(None, None) == 1
     assert lib.spmm_execute(None, None, 0, None, 0, None) == 1
     lib.spmm_matrix_destroy(None)

@@ -78,6 +78,9 @@ def test_graph_24_tvw_and_slide(S):
     w = synth.SMALL["sp24_small"]
     _spmm_case(S, S.spmm_pack_24(synth.make_a(w)["dense"]), (S.I8, S.I32), synth.make_b(w),
                w.m, w.n, torch.int32)
+    w = synth.SMALL["sp24_bf16_small"]
+    _spmm_case(S, S.spmm_pack_24(synth.make_a(w)["dense"]), (S.BF16, S.BF16), synth.make_b(w),
+               w.m, w.n, torch.int16)
     w = synth.SMALL["tvw_bf16_small"]
     _spmm_case(S, S.spmm_pack_tvw(synth.make_a(w)["dense"], 256, 128), (S.BF16, S.BF16),
                synth.make_b(w), w.m, w.n, torch.int16)

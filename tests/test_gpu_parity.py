@@ -298,6 +298,92 @@ def test_sp24_8192_config_sampled(S, orc):
 
 
 # ---------------------------------------------------------------------------
+# 2:4 bf16
+# ---------------------------------------------------------------------------
+
+def sp24_bf16_case(S, orc, a_bits, B_bits, rows=None, pad=0):
+    """GPU result (uint16 bits) and the oracle's fp64 product of the 2:4-pruned
+    A (its pruning, then its dense fp64 product: any m and k)."""
+    m, n = a_bits.shape[0], B_bits.shape[1]
+    M = S.spmm_pack_24(a_bits)
+    P = S.spmm_plan(M, n, S.BF16, S.BF16)
+    got = run(S, P, B_bits, m, n, "bf16", pad)
+    pruned = orc.prune_nm(a_bits, 2, 4)
+    ref = orc.gemm_f64(bf16_to_f64(pruned if rows is None else pruned[rows]), bf16_to_f64(B_bits))
+    g = bf16_to_f64(got if rows is None else got[rows])
+    assert np.isfinite(g).all(), "unwritten or non-finite outputs"
+    return g, ref, got
+
+
+def test_sp24_bf16_small_ragged(S, orc):
+    w = synth.SMALL["sp24_bf16_small"]   # 320 x 512, n = 400: ragged m and n tiles
+    a = synth.make_a(w)["dense"]
+    B = synth.make_b(w)
+    for pad in (0, 16):
+        g, ref, _ = sp24_bf16_case(S, orc, a, B, pad=pad)
+        err = orc.rel_frobenius(g, ref)
+        assert err <= TOL_BF16, err
+    _say(f"sp24_bf16_small rel={err:.2e}")
+
+
+@pytest.mark.parametrize("m,k,n", [(1, 8, 16), (17, 136, 48), (130, 264, 144), (64, 1024, 16)])
+def test_sp24_bf16_shapes(S, orc, m, k, n):
+    r = np.random.default_rng(m * 1000 + k + 7)
+    a = synth.f32_to_bf16_bits(synth.normal_f32(r, (m, k), 0.02))
+    B = synth.f32_to_bf16_bits(synth.normal_f32(r, (k, n), 1.0))
+    g, ref, _ = sp24_bf16_case(S, orc, a, B)
+    err = orc.rel_frobenius(g, ref)
+    assert err <= TOL_BF16, err
+
+
+def test_sp24_bf16_integer_values_are_exact(S, orc):
+    # small integers: every fp32 partial sum is exact, so C must be exactly the
+    # round-to-nearest-even bf16 of the exact sum; pins the kept positions, the
+    # k order of B and the epilogue bit for bit, over ragged m, k and n
+    r = np.random.default_rng(46)
+    m, k, n = 330, 520, 272
+    a = r.integers(-3, 4, size=(m, k)).astype(np.float32)
+    a[100:164] = 0                               # an all-zero row band
+    a_bits = synth.f32_to_bf16_bits(a)
+    B = synth.f32_to_bf16_bits(r.integers(-4, 5, size=(k, n)).astype(np.float32))
+    _, ref, got = sp24_bf16_case(S, orc, a_bits, B)
+    assert np.abs(ref).max() < 2 ** 24
+    np.testing.assert_array_equal(got & 0x7FFF, synth.f32_to_bf16_bits(ref.astype(np.float32)) & 0x7FFF)
+    nz = ref != 0
+    np.testing.assert_array_equal(got[nz], synth.f32_to_bf16_bits(ref[nz].astype(np.float32)))
+
+
+def test_sp24_bf16_identity_and_zero(S, orc):
+    m = 256
+    eye = synth.f32_to_bf16_bits(np.eye(m, dtype=np.float32))   # one nonzero per group: kept
+    B = synth.dense_bf16_normal(m, 272, 47)
+    _, _, got = sp24_bf16_case(S, orc, eye, B)
+    np.testing.assert_array_equal(got, B)
+    Z = np.zeros((128, 192), np.uint16)
+    M = S.spmm_pack_24(Z)
+    P = S.spmm_plan(M, 32, S.BF16, S.BF16)
+    got = run(S, P, synth.dense_bf16_normal(192, 32, 48), 128, 32, "bf16")
+    assert (got & 0x7FFF == 0).all()
+    for types in ((S.I8, S.I32), (S.BF16, S.F32)):
+        with pytest.raises(S.SpmmError) as ei:
+            S.spmm_plan(M, 32, *types)
+        assert ei.value.name == "SPMM_ERR_UNSUPPORTED"
+
+
+def test_sp24_bf16_8192_sampled(S, orc):
+    w = synth.WORKLOADS["sp24_bf16_8192"]
+    a = synth.make_a(w)["dense"]
+    B = synth.make_b(w)
+    r = np.random.default_rng(25)
+    rows = np.unique(np.concatenate([np.arange(16), np.arange(w.m - 16, w.m),
+                                     r.choice(w.m, 48, replace=False)])).astype(np.int64)
+    g, ref, _ = sp24_bf16_case(S, orc, a, B, rows=rows)
+    err = orc.rel_frobenius(g, ref)
+    assert err <= TOL_BF16, err
+    _say(f"sp24_bf16_8192 rows={len(rows)} rel={err:.2e}")
+
+
+# ---------------------------------------------------------------------------
 # boundary behaviour on the device
 # ---------------------------------------------------------------------------
 

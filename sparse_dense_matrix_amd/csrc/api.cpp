@@ -133,17 +133,42 @@ spmm_status_t plan_bcsr(spmm_plan_s *p) {
   // so the longest tiles of a column tile start first and the short ones
   // fill in behind them
   const int32_t mb = static_cast<int32_t>(a.m / 64);
-  std::vector<int32_t> order(static_cast<size_t>(mb));
-  for (int32_t i = 0; i < mb; ++i) order[i] = i;
-  std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
-    return a.brow_ptr[x + 1] - a.brow_ptr[x] > a.brow_ptr[y + 1] - a.brow_ptr[y];
-  });
+  std::vector<int32_t> sorted(static_cast<size_t>(mb));
+  for (int32_t i = 0; i < mb; ++i) sorted[i] = i;
+  auto blocks = [&](int32_t r) { return a.brow_ptr[r + 1] - a.brow_ptr[r]; };
+  std::stable_sort(sorted.begin(), sorted.end(),
+                   [&](int32_t x, int32_t y) { return blocks(x) > blocks(y); });
+  // row groups of about equal work (a tile costs its blocks plus one for the
+  // C write): longest first, each to the lightest group (lowest on ties);
+  // every group keeps the longest-first order.  The order array carries the
+  // groups' start offsets after its mb entries.
+  const BcsrSchedule sc = bcsr_schedule(a.brow_ptr.data(), mb, p->n);
+  const int groups = sc.row_groups;
+  std::vector<std::vector<int32_t>> members(static_cast<size_t>(groups));
+  std::vector<int64_t> load(static_cast<size_t>(groups), 0);
+  for (int32_t r : sorted) {
+    const size_t g = static_cast<size_t>(std::min_element(load.begin(), load.end()) - load.begin());
+    members[g].push_back(r);
+    load[g] += blocks(r) + 1;
+  }
+  std::vector<int32_t> order;
+  order.reserve(static_cast<size_t>(mb) + 9);
+  std::vector<int32_t> seg(1, 0);
+  for (const auto &g : members) {
+    order.insert(order.end(), g.begin(), g.end());
+    seg.push_back(static_cast<int32_t>(order.size()));
+  }
+  order.insert(order.end(), seg.begin(), seg.end());
   int32_t *ro = nullptr;
   if ((s = upload_vec(p, order, &ro)) != SPMM_OK) return s;
   L.row_ptr = rp;
   L.col_idx = ci;
   L.frag = fv;
   L.row_order = ro;
+  L.row_seg = ro + mb;
+  L.row_groups = groups;
+  L.tn = sc.tn;
+  L.grid = bcsr_grid(seg.data(), sc, p->n);
   L.mb = mb;
   L.n = p->n;
   L.k_rows = a.k;
@@ -160,8 +185,8 @@ spmm_status_t plan_bcsr(spmm_plan_s *p) {
     L.c_rows = rows;
   }
   p->info.tile_m = 64;
-  p->info.tile_n = bcsr_tile_n(p->n);
-  p->info.grid = bcsr_grid(L.mb, p->n);
+  p->info.tile_n = L.tn;
+  p->info.grid = L.grid;
   return SPMM_OK;
 }
 

@@ -24,11 +24,16 @@
 //     C writes from evicting B from L2;
 //   - tiles are dealt so that each XCD walks a contiguous range, block rows
 //     fastest: the workgroups resident on one XCD share the B column slab of
-//     one N tile in that XCD's L2.  Within an N tile the block rows with the
-//     most stored blocks come first (longest job first), so short tiles fill
-//     the end of the launch instead of long ones.
+//     one N tile in that XCD's L2.  When A is too large to stay in L2 while
+//     every N tile walks all of it, the plan splits the block rows into row
+//     groups of about equal work and gives each XCD one group's tiles, so
+//     its share of A stays resident.  Within an N tile the block rows with
+//     the most stored blocks come first (longest job first), so short tiles
+//     fill the end of the launch instead of long ones.
 // The kernel is bandwidth-bound by design: a 64-row block gives at most 64
 // flop per byte of B moved into LDS.
+#include <algorithm>
+
 #include "internal.h"
 
 // load_lds16 below names m0 as clobbered on purpose (it sets m0 for the
@@ -115,8 +120,9 @@ struct Operands {
 template <int kTN, bool kMap>
 __global__ __launch_bounds__(Geo<kTN>::kThreads) void bcsr_bf16_mfma(
     const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ col_idx,
-    const uint16_t *__restrict__ frag, const int32_t *__restrict__ row_order, int32_t mb,
-    int32_t tiles, int32_t per_xcd, int64_t n, const uint16_t *__restrict__ B, int64_t ldb,
+    const uint16_t *__restrict__ frag, const int32_t *__restrict__ row_order,
+    const int32_t *__restrict__ row_seg, int32_t row_groups, int32_t ntn, int64_t n,
+    const uint16_t *__restrict__ B, int64_t ldb,
     uint16_t *__restrict__ C, int64_t ldc, const int32_t *__restrict__ c_rows,
     const int32_t *__restrict__ b_rows) {
   using G = Geo<kTN>;
@@ -124,13 +130,19 @@ __global__ __launch_bounds__(Geo<kTN>::kThreads) void bcsr_bf16_mfma(
   constexpr int kBLoads = G::kBLoads, kALoads = G::kALoads;
   extern __shared__ __attribute__((aligned(1024))) char lds[];
 
-  // XCD-aware tile order: workgroup b runs on XCD b % 8; each XCD gets a
-  // contiguous range of logical tiles, block rows fastest, and within a
-  // column tile the block rows with the most stored blocks first.
-  const int t = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (t >= tiles) return;
-  const int br = row_order[t % mb];
-  const int64_t n0 = static_cast<int64_t>(t / mb) * kTN;
+  // XCD-aware tile order: workgroup b runs on XCD x = b % 8, which serves
+  // row group x % row_groups (block rows row_order[row_seg[g] ..
+  // row_seg[g+1]), most stored blocks first) and a contiguous range of that
+  // group's tiles, block rows fastest.
+  const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const int grp = x % row_groups, part = x / row_groups, parts = 8 / row_groups;
+  const int r0 = row_seg[grp], cnt = row_seg[grp + 1] - r0;
+  const int tg = cnt * ntn;                      // tiles of the row group
+  const int per = (tg + parts - 1) / parts;      // ... per XCD serving it
+  const int t = part * per + j;
+  if (j >= per || t >= tg) return;
+  const int br = row_order[r0 + t % cnt];
+  const int64_t n0 = static_cast<int64_t>(t / cnt) * kTN;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -293,14 +305,38 @@ void bcsr_fragment_order(const uint16_t *blk, uint16_t *frag) {
               blk[(32 * rb + (l & 31)) * kBlk + 16 * s + 8 * (l >> 5) + i];
 }
 
-// Wider tiles re-read each A block fewer times (once per kTN columns); for
-// small n the narrower tile gives more workgroups to fill the CUs.
-int bcsr_tile_n(int64_t n) { return n >= 8192 ? 512 : 256; }
+BcsrSchedule bcsr_schedule(const int32_t *row_ptr, int32_t mb, int64_t n) {
+  BcsrSchedule sc;
+  // Wider tiles re-read each A block fewer times (once per tn columns); for
+  // small n the narrower tile gives more workgroups to fill the CUs.
+  sc.tn = n >= 8192 ? 512 : 256;
+  sc.row_groups = 1;
+  // Eight row groups when A would otherwise be walked from beyond L2 again
+  // for every N tile of an XCD (A larger than half an XCD's 4 MB L2) while an
+  // eighth of it fits in that half, and every group still has enough block
+  // rows to fill an XCD's CUs.  The N tile is then 256 wide: its B slab
+  // shares L2 with the group's A, and two workgroups fit in a CU.  A larger A
+  // does not stay resident either way, and the split only costs B reuse.
+  const int64_t a_bytes = static_cast<int64_t>(row_ptr[mb]) * kABytes, half_l2 = 2 << 20;
+  if (n >= 8192 && a_bytes > half_l2 && a_bytes <= 8 * half_l2 && mb >= 8 * 32) {
+    sc.row_groups = 8;
+    sc.tn = 256;
+  }
+#ifdef SDM_BCSR_ROW_GROUPS
+  sc.row_groups = mb >= SDM_BCSR_ROW_GROUPS ? SDM_BCSR_ROW_GROUPS : 1;
+#endif
+#ifdef SDM_BCSR_TILE_N
+  sc.tn = SDM_BCSR_TILE_N;
+#endif
+  return sc;
+}
 
-int64_t bcsr_grid(int32_t mb, int64_t n) {
-  const int tn = bcsr_tile_n(n);
-  const int64_t tiles = static_cast<int64_t>(mb) * ((n + tn - 1) / tn);
-  return 8 * ((tiles + 7) / 8);
+int64_t bcsr_grid(const int32_t *row_seg, const BcsrSchedule &sc, int64_t n) {
+  const int64_t ntn = (n + sc.tn - 1) / sc.tn, parts = 8 / sc.row_groups;
+  int64_t per = 0;
+  for (int g = 0; g < sc.row_groups; ++g)
+    per = std::max(per, ((row_seg[g + 1] - row_seg[g]) * ntn + parts - 1) / parts);
+  return 8 * per;
 }
 
 namespace {
@@ -311,23 +347,25 @@ hipError_t launch_tn(const BcsrLaunch &a, hipStream_t s) {
   const int64_t tiles = static_cast<int64_t>(a.mb) * ntn;
   if (tiles == 0) return hipSuccess;
   if (tiles > INT32_MAX / 2 || a.ldb > (1 << 24)) return hipErrorInvalidValue;
+  if (a.row_groups < 1 || a.row_groups > 8 || 8 % a.row_groups != 0) return hipErrorInvalidValue;
   // through the row map every B byte offset is a 32-bit offset from B
   if (kMap && a.k_rows * a.ldb * 2 > UINT32_MAX) return hipErrorInvalidValue;
   auto kernel = bcsr_bf16_mfma<kTN, kMap>;
   hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(kernel), G::kLdsBytes);
   if (e != hipSuccess) return e;
-  const int64_t per_xcd = (tiles + 7) / 8;
-  hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(8 * per_xcd)), dim3(G::kThreads),
-                     G::kLdsBytes, s, a.row_ptr, a.col_idx, a.frag, a.row_order, a.mb,
-                     static_cast<int32_t>(tiles), static_cast<int32_t>(per_xcd), a.n, a.B, a.ldb,
-                     a.C, a.ldc, a.c_rows, a.col_perm);
+  if (a.grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(a.grid)), dim3(G::kThreads),
+                     G::kLdsBytes, s, a.row_ptr, a.col_idx, a.frag, a.row_order, a.row_seg,
+                     a.row_groups, static_cast<int32_t>(ntn), a.n, a.B, a.ldb, a.C, a.ldc, a.c_rows,
+                     a.col_perm);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_bcsr_bf16(const BcsrLaunch &a, hipStream_t s) {
-  const bool wide = bcsr_tile_n(a.n) == 512;
+  if (a.tn != 256 && a.tn != 512) return hipErrorInvalidValue;
+  const bool wide = a.tn == 512;
   if (a.col_perm) return wide ? launch_tn<512, true>(a, s) : launch_tn<256, true>(a, s);
   return wide ? launch_tn<512, false>(a, s) : launch_tn<256, false>(a, s);
 }

@@ -104,7 +104,11 @@ struct BcsrLaunch {
   const int32_t *row_ptr;   // [mb + 1]
   const int32_t *col_idx;   // [nnzb]
   const uint16_t *frag;     // [nnzb][4096] in MFMA fragment order
-  const int32_t *row_order; // [mb] block rows in dispatch order within a column tile
+  const int32_t *row_order; // [mb] block rows, row group by row group, each in dispatch order
+  const int32_t *row_seg;   // [row_groups + 1] start of each row group in row_order
+  int32_t row_groups;       // 1, 2, 4 or 8: XCD x serves row group x % row_groups
+  int32_t tn;               // columns of C per workgroup: 256 or 512
+  int64_t grid;             // workgroups (bcsr_grid)
   int32_t mb;               // block rows (64 rows each)
   int64_t n;
   const uint16_t *B;
@@ -121,8 +125,14 @@ struct BcsrLaunch {
 // Fragment order of one 64 x 64 block: [rb 2][s 4][lane 64][8 elements], lane l
 // holding row 32*rb + l%32, columns 16*s + 8*(l/32) + 0..7.
 void bcsr_fragment_order(const uint16_t *block_rowmajor, uint16_t *frag);
-int bcsr_tile_n(int64_t n);
-int64_t bcsr_grid(int32_t mb, int64_t n);
+// Tile width and row groups for the XCD mapping of a plan (see the kernel),
+// and the grid for a given split of row_order into groups.
+struct BcsrSchedule {
+  int tn;
+  int row_groups;
+};
+BcsrSchedule bcsr_schedule(const int32_t *row_ptr, int32_t mb, int64_t n);
+int64_t bcsr_grid(const int32_t *row_seg, const BcsrSchedule &sc, int64_t n);
 hipError_t launch_bcsr_bf16(const BcsrLaunch &a, hipStream_t s);
 
 struct WcsrLaunch {

@@ -137,6 +137,32 @@ def test_bcsr_prefill_config_sampled(S, orc, name):
         assert err <= TOL_BF16
 
 
+def test_bcsr_row_groups_skewed_rows(S, orc):
+    # A of ~7 MB at n >= 8192 takes the row-group schedule (each XCD serves an
+    # eighth of the block rows, 256-wide N tiles): empty block rows, one full
+    # block row, a ragged block-row count and a ragged last N tile
+    m, k, n = 16576, 2048, 8200
+    a, _ = synth.block_sparse_dense_bf16(m, k, 64, 64, 830, 0.02, 83)
+    a[: 10 * 64] = 0
+    a[100 * 64: 101 * 64] = synth.dense_bf16_normal(64, k, 84, sigma=0.02)
+    B = synth.dense_bf16_normal(k, n, 85)
+    M = S.spmm_pack_bcsr(a, 64, 64)
+    P = S.spmm_plan(M, n, S.BF16, S.BF16)
+    assert P.info()["tile_n"] == 256
+    got = run(S, P, B, m, n, "bf16")
+    assert (got != 0xFFFF).all(), "some C element was not written"
+    assert (got[: 10 * 64] & 0x7FFF == 0).all()
+    r = np.random.default_rng(86)
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(6400, 6464), np.arange(m - 64, m),
+                                     r.choice(m, 128, replace=False)])).astype(np.int64)
+    rp, ci, v = orc.pack_bcsr(a, 64, 64)
+    ref = orc.bcsr_spmm(64, 64, rp, ci, v, B, rows=rows)
+    err = orc.rel_frobenius(bf16_to_f64(got[rows]), ref)
+    _say(f"bcsr row groups m={m} n={n} blocks={S.spmm_matrix_info(M)['nnzb']} "
+         f"grid={P.info()['grid']} rel_frob={err:.3e}")
+    assert err <= TOL_BF16
+
+
 def test_bcsr_deterministic(S, orc):
     w = synth.SMALL["bcsr_small"]
     a = synth.make_a(w)["dense"]

@@ -491,7 +491,7 @@ def sddmm_case(S, orc, m, k, rp, ci, X, Y, W=0, T=0, rows=None, extra=0):
     return orc.rel_frobenius(sel, ref), got, P
 
 
-@pytest.mark.parametrize("kd", [1, 4, 63, 96, 128, 200, 300, 301, 1000])
+@pytest.mark.parametrize("kd", [1, 4, 32, 63, 64, 96, 128, 200, 300, 301, 1000])
 def test_sddmm_small(S, orc, kd):
     w = synth.SMALL["sddmm_small"]          # 20000 x 20000 power-law pattern
     a = synth.make_a(w)
@@ -608,7 +608,7 @@ def sddmm_typed_case(S, orc, m, k, rp, ci, X, Y, elem, W=0, T=0, rows=None, extr
 
 
 @pytest.mark.parametrize("elem", ["bf16", "i8"])
-@pytest.mark.parametrize("kd", [1, 8, 16, 63, 96, 128, 200, 1000])
+@pytest.mark.parametrize("kd", [1, 8, 16, 63, 64, 96, 128, 200, 256, 1000])
 def test_sddmm_csr_typed_small(S, orc, elem, kd):
     w = synth.SMALL["sddmm_small"]          # 20000 x 20000 power-law pattern
     a = synth.make_a(w)

@@ -240,7 +240,7 @@ void spmm_matrix_destroy(spmm_matrix_t a);
  *   TVW, int8 (256 x 128j tiles):  (I8, I32), n % 16 == 0
  *   TVW, bf16 (256 x 64j tiles):   (BF16, BF16), n % 16 == 0; fp32 sums rounded to
  *                                  nearest even
- *   SLIDE:                 (I8, I32), n % 16 == 0 (plus a k_lift * n workspace)
+ *   SLIDE:                 (I8, I32), n % 16 == 0 (no workspace)
  * A BCSR matrix packed with reordering reads B's rows through its column
  * permutation (no workspace; spmm_execute then needs k * ldb * 2 < 2^32).
  * Anything else is UNSUPPORTED.  n = 0 is allowed (execute does nothing). */
@@ -269,7 +269,12 @@ void spmm_plan_destroy(spmm_plan_t p);
  * ldb * elem, ldc * elem multiples of 16 bytes.  Allocates nothing and does
  * not synchronise; launch errors are returned, faults surface at the caller's
  * next synchronisation.  A plan's workspace allows one execute in flight at a
- * time: concurrent streams need separate plans.  B and C must not overlap. */
+ * time: concurrent streams need separate plans.  B and C must not overlap.
+ * The kernels address B with 32-bit byte offsets: BCSR needs ldb <= 2^24
+ * (and k * ldb * 2 < 2^32 when packed with reordering); 2:4, TVW and SLIDE
+ * need k_pad * ldb * elem < 2^32, k_pad being k (k_lift for SLIDE) rounded up
+ * to the k-step of 128 (int8) or 64 (bf16).  Larger ldb returns UNSUPPORTED
+ * before anything is launched. */
 spmm_status_t spmm_execute(spmm_plan_t p, const void *b_dev, int64_t ldb, void *c_dev,
                            int64_t ldc, hipStream_t stream);
 

@@ -785,6 +785,14 @@ spmm_status_t spmm_execute(spmm_plan_t p, const void *b_dev, int64_t ldb, void *
       (ldc * ec) % 16 != 0)
     return fail(SPMM_ERR_INVALID_ARG,
                 "spmm_execute: B/C must be 16-byte aligned with ld >= n and ld*elem % 16 == 0");
+  // the kernels address B with 32-bit byte offsets from its start (BCSR:
+  // from the first row of a block; through a row map: from row 0)
+  if (a.format == SPMM_FORMAT_BCSR) {
+    if (ldb > (int64_t(1) << 24) || (p->bcsr.col_perm && a.k * ldb * 2 > int64_t(UINT32_MAX)))
+      return fail(SPMM_ERR_UNSUPPORTED, "spmm_execute: ldb too large for this BCSR plan");
+  } else if (a.format != SPMM_FORMAT_WCSR && p->sp24.k_pad * ldb * eb > int64_t(UINT32_MAX)) {
+    return fail(SPMM_ERR_UNSUPPORTED, "spmm_execute: k_pad * ldb * elem must be below 2^32");
+  }
   DeviceScope ds(p->device);
   if (ds.err != hipSuccess) return hip_fail(ds.err, "hipSetDevice");
   hipError_t e = hipSuccess;

@@ -440,6 +440,17 @@ def test_execute_rejects_bad_layouts(S):
     with pytest.raises(S.SpmmError) as ei:          # ldb < n
         S.spmm_execute(P, B.data_ptr(), Cw.data_ptr(), ldb=32, ldc=64)
     assert ei.value.name == "SPMM_ERR_INVALID_ARG"
+    # leading dimensions past the kernels' 32-bit B offsets are refused before
+    # any launch (nothing reads B here)
+    with pytest.raises(S.SpmmError) as ei:
+        S.spmm_execute(P, B.data_ptr(), Cw.data_ptr(), ldb=(1 << 24) + 8, ldc=64)
+    assert ei.value.name == "SPMM_ERR_UNSUPPORTED"
+    M24 = S.spmm_pack_24(np.ones((16, 8192), np.int8))
+    P24 = S.spmm_plan(M24, 16, S.I8, S.I32)
+    C24 = torch.zeros((16, 16), dtype=torch.int32, device="cuda")
+    with pytest.raises(S.SpmmError) as ei:
+        S.spmm_execute(P24, B.data_ptr(), C24.data_ptr(), ldb=1 << 20, ldc=16)
+    assert ei.value.name == "SPMM_ERR_UNSUPPORTED"
 
 
 def test_two_plans_two_streams(S, orc):

@@ -215,7 +215,7 @@ def main():
         trace_summary(args.trace_summary)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU: the multiply shards by columns "
+        print(json.dumps({"error": "this library runs on one GPU: the multiply shards by columns "
                                    "of B with no communication, but only the one-GPU path is "
                                    "built and measured; run with --gpus 1"}), flush=True)
         sys.exit(2)
@@ -354,7 +354,7 @@ def main():
 
 def library_digest() -> str:
     """sha256 (first 16 hex digits) over every library source file: traffic
-    counters taken with another digest no longer describe this build."""
+    counters taken with another digest no longer describe the library as built."""
     import hashlib
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):

@@ -12,7 +12,8 @@
 //     tiles;
 //   - a stage holds one stored block: the B slab (64 k-rows x kTN columns,
 //     row-major) and the A block, pre-arranged by the plan in MFMA fragment
-//     order;
+//     order; or, for rows of few blocks at kTN = 256, half a block (32
+//     k-rows), so that a stage is 20 KB and more workgroups share a CU;
 //   - B is n-contiguous but the MFMA wants k-contiguous operands: the gfx950
 //     LDS transpose read (ds_read_b64_tr_b16) gives each lane 4 k-values of
 //     one column, two reads make an operand.  The slab's 16-byte pieces are
@@ -55,18 +56,23 @@ constexpr int kStages = 2;                // one block in flight while one is us
 constexpr int kABytes = kBlk * kBlk * 2;  // 8 KB
 constexpr int kCPitch = 144;              // bytes per row of a wave's staged C tile
 
-// Tile geometry for kTN columns of C per workgroup (one wave per 64 columns).
-template <int kTN>
+// Tile geometry for kTN columns of C per workgroup (one wave per 64 columns)
+// and kKH k-rows (a whole block, or half of one) per stage.
+template <int kTN, int kKH = kBlk>
 struct Geo {
   static constexpr int kWaves = kTN / 64;
   static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kSteps = kKH / 16;         // MFMA k-steps per stage
+  static constexpr int kPer = kBlk / kKH;         // stages per block
   static constexpr int kBRow = kTN * 2;           // bytes per k-row of the B slab
-  static constexpr int kBBytes = kBlk * kBRow;
-  static constexpr int kStageBytes = kBBytes + kABytes;
+  static constexpr int kBBytes = kKH * kBRow;
+  static constexpr int kAStage = kABytes / kPer;  // the stage's share of the A block
+  static constexpr int kStageBytes = kBBytes + kAStage;
   static constexpr int kBLoads = kBBytes / 1024 / kWaves;  // 1 KB wave loads per wave per stage
-  static constexpr int kALoads = kABytes / 1024 / kWaves;
+  static constexpr int kALoads = kAStage / 1024 / kWaves;
   static constexpr int kLdsBytes = kStages * kStageBytes;
-  static_assert(kBLoads * kWaves * 1024 == kBBytes && kALoads * kWaves * 1024 == kABytes, "split");
+  static_assert(kKH == 64 || kKH == 32, "whole or half blocks");
+  static_assert(kBLoads * kWaves * 1024 == kBBytes && kALoads * kWaves * 1024 == kAStage, "split");
   static_assert(kWaves * 64 * kCPitch <= kLdsBytes, "C staging fits in the ring");
   static_assert(kLdsBytes <= 160 * 1024, "LDS");
 };
@@ -117,7 +123,8 @@ struct Operands {
 // kMap: the packed k-row j of A multiplies B row b_rows[j] (A packed with
 // its columns permuted); each lane then reads its B rows through the map,
 // looked up one block ahead.  Otherwise k-row j multiplies B row j.
-template <int kTN, bool kMap>
+// kKH: k-rows per stage (64: one block per stage; 32: two stages per block).
+template <int kTN, bool kMap, int kKH>
 __global__ __launch_bounds__(Geo<kTN>::kThreads) void bcsr_bf16_mfma(
     const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ col_idx,
     const uint16_t *__restrict__ frag, const int32_t *__restrict__ row_order,
@@ -125,7 +132,9 @@ __global__ __launch_bounds__(Geo<kTN>::kThreads) void bcsr_bf16_mfma(
     const uint16_t *__restrict__ B, int64_t ldb,
     uint16_t *__restrict__ C, int64_t ldc, const int32_t *__restrict__ c_rows,
     const int32_t *__restrict__ b_rows) {
-  using G = Geo<kTN>;
+  using G = Geo<kTN, kKH>;
+  static_assert(!kMap || kKH == kBlk, "the row map is looked up per block");
+  constexpr int kSteps = G::kSteps, kPer = G::kPer;
   constexpr int kBRow = G::kBRow, kBBytes = G::kBBytes, kStageBytes = G::kStageBytes;
   constexpr int kBLoads = G::kBLoads, kALoads = G::kALoads;
   extern __shared__ __attribute__((aligned(1024))) char lds[];
@@ -177,7 +186,10 @@ __global__ __launch_bounds__(Geo<kTN>::kThreads) void bcsr_bf16_mfma(
     }
   };
   const uint32_t lds_base = lds_addr(lds);
-  auto issue = [&](int blk, int stage) {
+  // loads of stage unit `unit` of the row: part unit % kPer of block
+  // p0 + unit / kPer
+  auto issue = [&](int unit, int stage) {
+    const int blk = p0 + unit / kPer, part = unit % kPer;
     const uint32_t sb = lds_base + stage * kStageBytes;
     if constexpr (kMap) {
 #pragma unroll
@@ -185,15 +197,17 @@ __global__ __launch_bounds__(Geo<kTN>::kThreads) void bcsr_bf16_mfma(
         load_lds16(sb + (wave * kBLoads + i) * 1024, B,
                    static_cast<uint32_t>(brow_next[i] * ldb * 2) + boff[i]);
     } else {
-      const uint16_t *bsrc = B + static_cast<int64_t>(col_idx[blk]) * kBlk * ldb;
+      const uint16_t *bsrc = B + (static_cast<int64_t>(col_idx[blk]) * kBlk + part * kKH) * ldb;
 #pragma unroll
       for (int i = 0; i < kBLoads; ++i) load_lds16(sb + (wave * kBLoads + i) * 1024, bsrc, boff[i]);
     }
     const uint16_t *asrc = frag + static_cast<int64_t>(blk) * (kABytes / 2);
 #pragma unroll
     for (int i = 0; i < kALoads; ++i) {
-      const int o = (wave * kALoads + i) * 1024;
-      load_lds16(sb + kBBytes + o, asrc, static_cast<uint32_t>(o + lane * 16));
+      // 1 KB piece q of the stage: row half q / kSteps, k-step q % kSteps
+      const int q = wave * kALoads + i;
+      const int go = ((q / kSteps) * 4 + part * kSteps + q % kSteps) * 1024;
+      load_lds16(sb + kBBytes + q * 1024, asrc, static_cast<uint32_t>(go + lane * 16));
     }
   };
 
@@ -208,7 +222,7 @@ __global__ __launch_bounds__(Geo<kTN>::kThreads) void bcsr_bf16_mfma(
     Operands o;
     const bf16x8 *afr = reinterpret_cast<const bf16x8 *>(sb + kBBytes);
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) o.a[rb] = afr[(rb * 4 + s) * 64 + lane];
+    for (int rb = 0; rb < 2; ++rb) o.a[rb] = afr[(rb * kSteps + s) * 64 + lane];
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
       s16x4 part[2];
@@ -235,27 +249,28 @@ __global__ __launch_bounds__(Geo<kTN>::kThreads) void bcsr_bf16_mfma(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  if (nblk > 0) {
+  const int nunit = nblk * kPer;  // stages to run (with kMap, one per block)
+  if (nunit > 0) {
     lookup_rows(p0);
-    issue(p0, 0);
+    issue(0, 0);
     if (nblk > 1) lookup_rows(p0 + 1);
   }
-  for (int it = 0; it < nblk; ++it) {
-    wait_vm<0>();  // this block's loads (and the next block's row lookups) have landed
-    barrier();     // ... for every wave; and the stage of block it-1 is free
-    if (it + 1 < nblk) {
-      issue(p0 + it + 1, (it + 1) & 1);
+  for (int it = 0; it < nunit; ++it) {
+    wait_vm<0>();  // this stage's loads (and the next block's row lookups) have landed
+    barrier();     // ... for every wave; and the stage of unit it-1 is free
+    if (it + 1 < nunit) {
+      issue(it + 1, (it + 1) & 1);
       if (it + 2 < nblk) lookup_rows(p0 + it + 2);
     }
     const char *sb = lds + (it & 1) * kStageBytes;
     // every operand of the block is read before the first MFMA, so the LDS
     // latency is paid once per block instead of once per k-step
-    Operands ops[4];
+    Operands ops[kSteps];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) ops[s] = read_ops(sb, s);
+    for (int s = 0; s < kSteps; ++s) ops[s] = read_ops(sb, s);
     __builtin_amdgcn_sched_barrier(0);  // keep the compiler from interleaving them again
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int s = 0; s < kSteps; ++s)
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
@@ -305,7 +320,7 @@ void bcsr_fragment_order(const uint16_t *blk, uint16_t *frag) {
               blk[(32 * rb + (l & 31)) * kBlk + 16 * s + 8 * (l >> 5) + i];
 }
 
-BcsrSchedule bcsr_schedule(const int32_t *row_ptr, int32_t mb, int64_t n) {
+BcsrSchedule bcsr_schedule(const int32_t *row_ptr, int32_t mb, int64_t n, bool mapped) {
   BcsrSchedule sc;
   // Wider tiles re-read each A block fewer times (once per tn columns); for
   // small n the narrower tile gives more workgroups to fill the CUs.
@@ -328,6 +343,15 @@ BcsrSchedule bcsr_schedule(const int32_t *row_ptr, int32_t mb, int64_t n) {
 #ifdef SDM_BCSR_TILE_N
   sc.tn = SDM_BCSR_TILE_N;
 #endif
+  // Half-block stages at 256 columns when block rows hold few blocks (at
+  // most 16 on average): a 20 KB stage lets a third workgroup onto the CU.
+  // Rows of many blocks keep whole-block stages: there a barrier per 8
+  // MFMAs costs more than the extra workgroup gains.  Through a row map the
+  // lookups go per block, so whole blocks.
+  sc.kh = (sc.tn == 256 && !mapped && row_ptr[mb] <= 16 * static_cast<int64_t>(mb)) ? 32 : 64;
+#ifdef SDM_BCSR_KH
+  sc.kh = (sc.tn == 256 && !mapped) ? SDM_BCSR_KH : 64;
+#endif
   return sc;
 }
 
@@ -340,9 +364,9 @@ int64_t bcsr_grid(const int32_t *row_seg, const BcsrSchedule &sc, int64_t n) {
 }
 
 namespace {
-template <int kTN, bool kMap>
+template <int kTN, bool kMap, int kKH>
 hipError_t launch_tn(const BcsrLaunch &a, hipStream_t s) {
-  using G = Geo<kTN>;
+  using G = Geo<kTN, kKH>;
   const int64_t ntn = (a.n + kTN - 1) / kTN;
   const int64_t tiles = static_cast<int64_t>(a.mb) * ntn;
   if (tiles == 0) return hipSuccess;
@@ -350,7 +374,7 @@ hipError_t launch_tn(const BcsrLaunch &a, hipStream_t s) {
   if (a.row_groups < 1 || a.row_groups > 8 || 8 % a.row_groups != 0) return hipErrorInvalidValue;
   // through the row map every B byte offset is a 32-bit offset from B
   if (kMap && a.k_rows * a.ldb * 2 > UINT32_MAX) return hipErrorInvalidValue;
-  auto kernel = bcsr_bf16_mfma<kTN, kMap>;
+  auto kernel = bcsr_bf16_mfma<kTN, kMap, kKH>;
   hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(kernel), G::kLdsBytes);
   if (e != hipSuccess) return e;
   if (a.grid <= 0) return hipSuccess;
@@ -365,9 +389,11 @@ hipError_t launch_tn(const BcsrLaunch &a, hipStream_t s) {
 
 hipError_t launch_bcsr_bf16(const BcsrLaunch &a, hipStream_t s) {
   if (a.tn != 256 && a.tn != 512) return hipErrorInvalidValue;
+  if (a.kh != 64 && (a.kh != 32 || a.tn != 256 || a.col_perm)) return hipErrorInvalidValue;
   const bool wide = a.tn == 512;
-  if (a.col_perm) return wide ? launch_tn<512, true>(a, s) : launch_tn<256, true>(a, s);
-  return wide ? launch_tn<512, false>(a, s) : launch_tn<256, false>(a, s);
+  if (a.col_perm) return wide ? launch_tn<512, true, 64>(a, s) : launch_tn<256, true, 64>(a, s);
+  if (wide) return launch_tn<512, false, 64>(a, s);
+  return a.kh == 32 ? launch_tn<256, false, 32>(a, s) : launch_tn<256, false, 64>(a, s);
 }
 
 }  // namespace sdm

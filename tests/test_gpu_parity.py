@@ -137,6 +137,22 @@ def test_bcsr_prefill_config_sampled(S, orc, name):
         assert err <= TOL_BF16
 
 
+def test_bcsr_many_blocks_per_row(S, orc):
+    # more than 16 stored blocks per block row on average: whole-block LDS
+    # stages at 256 columns (few blocks per row take half-block stages, as
+    # in every other small case); an empty block row and a ragged n
+    m, k, n = 320, 2048, 520
+    a, _ = synth.block_sparse_dense_bf16(m, k, 64, 64, 144, 0.02, 87)
+    a[128:192] = 0
+    B = synth.dense_bf16_normal(k, n, 88)
+    g, ref, got = bcsr_case(S, orc, a, B)
+    assert (got[128:192] & 0x7FFF == 0).all()
+    err = orc.rel_frobenius(g, ref)
+    _say(f"bcsr many blocks per row: blocks={int(np.count_nonzero(a.reshape(5, 64, 32, 64).any(axis=(1, 3))))} "
+         f"rel_frob={err:.3e}")
+    assert err <= TOL_BF16
+
+
 def test_bcsr_row_groups_skewed_rows(S, orc):
     # A of ~7 MB at n >= 8192 takes the row-group schedule (each XCD serves an
     # eighth of the block rows, 256-wide N tiles): empty block rows, one full

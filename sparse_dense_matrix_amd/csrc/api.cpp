@@ -422,8 +422,9 @@ spmm_status_t plan_24(spmm_plan_s *p) {
     L.b_rows = dr;
   }
   p->info.tile_m = sp24_tile_m();
-  p->info.tile_n = sp24_tile_n();
-  p->info.grid = sp24_grid(a.m, p->n);
+  L.tn = sp24_tile_n(p->n, L.b_rows != nullptr);
+  p->info.tile_n = L.tn;
+  p->info.grid = sp24_grid(a.m, p->n, L.tn);
   return SPMM_OK;
 }
 
@@ -471,8 +472,9 @@ spmm_status_t plan_tvw(spmm_plan_s *p) {
   L.m_pad = a.m;
   L.k_pad = a.k;
   p->info.tile_m = sp24_tile_m();
-  p->info.tile_n = sp24_tile_n();
-  p->info.grid = sp24_grid(a.m, p->n);
+  L.tn = sp24_tile_n(p->n, L.b_rows != nullptr);
+  p->info.tile_n = L.tn;
+  p->info.grid = sp24_grid(a.m, p->n, L.tn);
   return SPMM_OK;
 }
 

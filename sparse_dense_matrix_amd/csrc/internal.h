@@ -215,6 +215,7 @@ struct Sp24Launch {
   const int32_t *b_rows;
   int64_t m, k, n;
   int64_t m_pad, k_pad;
+  int32_t tn;   // columns of C per workgroup (sp24_tile_n)
   const void *B;
   int64_t ldb;  // elements
   void *C;
@@ -233,9 +234,10 @@ void sp24_tile_layout(const void *vals, const uint8_t *meta, int64_t m, int64_t 
 void tvw_tile_layout(const void *tile_vals, const uint8_t *tile_meta, int64_t ntiles, int32_t tk,
                      bool bf16, void *vals_tiled, uint8_t *meta_tiled);
 int sp24_tile_m();
-int sp24_tile_n();
+// columns of C per workgroup for n columns; mapped: B read through a row map
+int sp24_tile_n(int64_t n, bool mapped);
 int sp24_tile_k(bool bf16);  // dense k per step: 128 int8, 64 bf16
-int64_t sp24_grid(int64_t m, int64_t n);
+int64_t sp24_grid(int64_t m, int64_t n, int tn);
 hipError_t launch_sp24(const Sp24Launch &a, hipStream_t s);
 
 }  // namespace sdm

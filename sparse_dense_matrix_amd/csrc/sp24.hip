@@ -22,18 +22,21 @@
 //     transpose read ds_read_b64_tr_b8 (8 k-values per read); bf16: rows
 //     8*(l/16)+0..7 and 32+8*(l/16)+0..7 with ds_read_b64_tr_b16 (4 per read);
 //   - D: rows 4*(l/16)+0..3, column l%16.
-// A workgroup of 8 waves computes a 256 x 256 tile of C (each wave 128 x 64,
+// A workgroup computes a 256 x 128 tile of C with 4 waves (each 128 x 64,
 // 8 x 4 sparse MFMA tiles).  Operands go global -> LDS with direct loads
-// into a three-stage ring (two k-steps in flight; each step's loads go out
-// at its start, before its LDS reads).  The plan stores the
+// into a two-stage ring (72 KB), so two workgroups share a CU and one
+// covers the other's barriers and epilogue; each step's loads go out at its
+// start, before its LDS reads.  The row-map path (below) uses 256 x 256
+// tiles of 8 waves and a three-stage ring instead (156 KB).  The plan stores the
 // compressed values and the index words tiled: for each 256-row tile and
 // k-step, one contiguous 16 KB piece of values already in MFMA fragment
 // order and one contiguous piece of index words (4 KB int8, 2 KB bf16), so
-// every direct load reads 1 KB of consecutive bytes.  The B slab (32 KB:
-// 128 k-rows of 256 bytes, or 64 of 512) has its 16-byte pieces XOR-swizzled
-// by k-row so the transpose reads are bank-conflict free.  The tile order
-// groups 4 row tiles with every column tile on one XCD, so A panels are
-// shared 8-fold and B panels 4-fold in that XCD's L2.
+// every direct load reads 1 KB of consecutive bytes.  The B slab (16 KB at
+// 128 columns: 128 k-rows of 128 bytes, or 64 of 256) has its 16-byte
+// pieces XOR-swizzled by k-row so the transpose reads are bank-conflict
+// free.  The tile order
+// groups 4 row tiles with every column tile on one XCD, so each A panel is
+// shared by all column tiles and each B panel 4-fold in that XCD's L2.
 //
 // The same kernel runs the tile-vector-wise pattern of the tiled-GEMM page
 // (abstract: tile-wise sparsity at the global-memory level combined with 2:4
@@ -60,12 +63,24 @@ typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int kTM = 256, kTN = 256;
-constexpr int kWaves = 8;                       // 2 (rows) x 4 (columns)
-constexpr int kThreads = 64 * kWaves;
+constexpr int kTM = 256;
 constexpr int kMG = 4;                          // row tiles grouped on one XCD
-constexpr int kStages = 3;                      // two k-steps in flight
-constexpr int kLoads = 7;                       // direct loads per wave per k-step
+
+// Workgroup tile: 256 rows x kN columns of C, waves of 128 x 64 (2 x kN/64).
+// kN = 256: 8 waves and a three-stage ring (156 KB, one workgroup per CU);
+// kN = 128: 4 waves and a two-stage ring (72 KB, two workgroups per CU, so
+// one covers the other's barriers and epilogue).
+template <int kN>
+struct Tile {
+  static_assert(kN == 256 || kN == 128, "tile width");
+  static constexpr int kWaves = kN / 32;
+  static constexpr int kWN = kWaves / 2;        // waves along n
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kStages = kN == 256 ? 3 : 2;
+  static constexpr int kAL = 16 / kWaves;       // 1 KB loads of A values per wave per k-step
+  static constexpr int kBL = 4;                 // ... of the B slab
+  static constexpr int kLoads = kAL + 1 + kBL;  // direct loads per wave per k-step
+};
 
 // Element types.  kTK: dense k per step (one sparse MFMA deep); kElem:
 // bytes per element; kIdx: index bytes per lane and 16-row tile.
@@ -78,31 +93,40 @@ struct Bf16 {
   using Acc = f32x4;
 };
 
-template <class E>
+template <class E, int kN>
 struct Geo {
+  using T = Tile<kN>;
   static constexpr int kTK = E::kTK;
-  static constexpr int kBRow = kTN * E::kElem;               // bytes per k-row of the B slab
+  static constexpr int kBRow = kN * E::kElem;                // bytes per k-row of the B slab
   static constexpr int kPieces = kBRow / 16;                  // 16-byte pieces per k-row
   static constexpr int kRowsPerLoad = 1024 / kBRow;           // k-rows per 1 KB wave load
   static constexpr int kAVBytes = kTM * kTK / 2 * E::kElem;   // 16 KB compressed values
   static constexpr int kAMBytes = kTM * kTK / 8;              // index bytes
-  static constexpr int kBBytes = kTK * kBRow;                 // 32 KB
+  static constexpr int kBBytes = kTK * kBRow;                 // 32 KB (kN 256), 16 KB (128)
   static constexpr int kStageBytes = kAVBytes + kAMBytes + kBBytes;
-  static constexpr int kLdsBytes = kStages * kStageBytes;     // 156 KB / 150 KB
-  static constexpr int kMLanes = kAMBytes / kWaves / 16;      // lanes of a wave that load index bytes
+  static constexpr int kLdsBytes = T::kStages * kStageBytes;  // 156 / 150 KB, 72 / 68 KB
+  static constexpr int kMLanes = kAMBytes / T::kWaves / 16;   // lanes of a wave that load index bytes
   static_assert(kLdsBytes <= 160 * 1024, "LDS");
-  static_assert(kAVBytes == 2 * kWaves * 1024 && kBBytes == 4 * kWaves * 1024, "loads per wave");
+  static_assert(kAVBytes == T::kAL * T::kWaves * 1024 && kBBytes == T::kBL * T::kWaves * 1024,
+                "loads per wave");
+  static_assert(kMLanes <= 64, "one index load per wave");
   static_assert(kAMBytes == 2 * 64 * 8 * E::kIdx, "index layout");
 };
 
 // Physical 16-byte piece of logical piece c in k-row r of the B slab.  A
-// transpose read is served 32 lanes at a time; those lanes touch 16 k-rows
-// of one piece (int8: rows 0..7 and 16..23 of a 32-row group) or 8 k-rows
-// of two neighbouring pieces (bf16: rows 0..3 and 8..11 of a 16-row group).
-// The XOR spreads them over the 16 bank groups of 16 bytes.
-template <class E>
+// transpose read is served 32 lanes at a time, 256 bytes over the 64 banks
+// (16 groups of 16 bytes); those lanes touch 16 k-rows of one piece (int8:
+// rows 0..7 and 16..23 of a 32-row group) or 8 k-rows of two neighbouring
+// pieces (bf16: rows 0..3 and 8..11 of a 16-row group).  The XOR spreads
+// them over the 16 bank groups: with 256-byte rows (int8 at kN = 256, bf16
+// at 128) a piece's bank group is its index; with 128-byte rows (int8 at
+// 128) it is the row's parity times 8 plus the index, so the 8 rows of
+// each parity take the 8 indices; with 512-byte rows (bf16 at 256) the
+// index modulo 16.
+template <class E, int kN>
 __device__ __forceinline__ int swz(int r, int c) {
-  if constexpr (E::kElem == 1) return c ^ ((r & 7) | (((r >> 4) & 1) << 3));
+  if constexpr (E::kElem == 1 && kN == 256) return c ^ ((r & 7) | (((r >> 4) & 1) << 3));
+  else if constexpr (E::kElem == 1) return c ^ (((r >> 1) & 3) | (((r >> 4) & 1) << 2));
   else return c ^ (((r & 3) | (((r >> 3) & 1) << 2)) << 1);
 }
 
@@ -145,9 +169,9 @@ __device__ __forceinline__ int quad_swap(int v) {
 // int8: in a 16-lane group, lane p supplies the 8 columns 8*(p%2).. of k-row
 // p/2, and lane i then holds k-rows 0..7 of column i; bf16: lane p supplies
 // the 4 columns 4*(p%4).. of k-row p/4, lane i then holds k-rows 0..3.
-template <class E>
+template <class E, int kN>
 __device__ __forceinline__ i32x8 read_b(const char *sbb, int lane, int wn, int j) {
-  using G = Geo<E>;
+  using G = Geo<E, kN>;
   const int g = lane >> 4, pl = lane & 15;
   i32x2 q[4];
   if constexpr (E::kElem == 1) {
@@ -156,7 +180,7 @@ __device__ __forceinline__ i32x8 read_b(const char *sbb, int lane, int wn, int j
       const int r = 16 * g + (pl >> 1) + (h & 1) * 8 + (h >> 1) * 64;
       const int c = wn * 64 + 8 * (pl & 1) + 16 * j;  // byte column
       q[h] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-          (lds_i32x2 *)(sbb + r * G::kBRow + swz<E>(r, c >> 4) * 16 + (c & 15)));
+          (lds_i32x2 *)(sbb + r * G::kBRow + swz<E, kN>(r, c >> 4) * 16 + (c & 15)));
     }
   } else {
 #pragma unroll
@@ -164,7 +188,7 @@ __device__ __forceinline__ i32x8 read_b(const char *sbb, int lane, int wn, int j
       const int r = 8 * g + (pl >> 2) + (h & 1) * 4 + (h >> 1) * 32;
       const int c = wn * 64 + 4 * (pl & 3) + 16 * j;  // element column
       q[h] = __builtin_bit_cast(i32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4 *)(sbb + r * G::kBRow + swz<E>(r, c >> 3) * 16 + (c & 7) * 2)));
+          (lds_s16x4 *)(sbb + r * G::kBRow + swz<E, kN>(r, c >> 3) * 16 + (c & 7) * 2)));
     }
   }
   return i32x8{q[0][0], q[0][1], q[1][0], q[1][1], q[2][0], q[2][1], q[3][0], q[3][1]};
@@ -186,16 +210,18 @@ __device__ __forceinline__ typename E::Acc mma(i32x4 a, i32x8 b, typename E::Acc
 // kMap: slab k-row j multiplies B row b_rows[j] (sliding-window A, whose
 // lifted k-rows repeat B's rows; the table is padded with row 0 to whole
 // k-steps).  Otherwise slab k-row j multiplies B row j.
-template <class E, bool kTiles, bool kMap>
+template <class E, int kN, bool kTiles, bool kMap>
 __device__ __forceinline__ void sp24_body(
     const char *__restrict__ vals, const uint8_t *__restrict__ meta,
     const int32_t *__restrict__ tile_ptr, const int32_t *__restrict__ tile_step, int64_t m,
     int64_t k, int64_t n, int64_t k_pad, int32_t mtiles, int32_t ntiles, int32_t tiles,
     int32_t per_xcd, const char *__restrict__ B, int64_t ldb, void *__restrict__ C, int64_t ldc,
     const int32_t *__restrict__ b_rows) {
-  using G = Geo<E>;
+  using G = Geo<E, kN>;
+  using T = Tile<kN>;
   constexpr int kTK = G::kTK, kAVBytes = G::kAVBytes, kAMBytes = G::kAMBytes;
   constexpr int kStageBytes = G::kStageBytes, kMLanes = G::kMLanes;
+  constexpr int kStages = T::kStages, kLoads = T::kLoads, kAL = T::kAL, kBL = T::kBL;
   extern __shared__ __attribute__((aligned(1024))) char lds[];
 
   // logical tile t: groups of kMG row tiles x every column tile, contiguous
@@ -205,12 +231,12 @@ __device__ __forceinline__ void sp24_body(
   const int grp = t / (kMG * ntiles), rem = t % (kMG * ntiles);
   const int gsize = min(kMG, mtiles - grp * kMG);
   const int64_t m0 = static_cast<int64_t>(grp * kMG + rem % gsize) * kTM;
-  const int64_t n0 = static_cast<int64_t>(rem / gsize) * kTN;
+  const int64_t n0 = static_cast<int64_t>(rem / gsize) * kN;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave / T::kWN, wn = wave % T::kWN;
   // this row tile's stored k-steps and their tiled values and index words
   int64_t first, ksteps;
   if constexpr (kTiles) {
@@ -228,16 +254,16 @@ __device__ __forceinline__ void sp24_body(
     else return ks;
   };
 
-  // Loads of one k-step, per wave: A values 2 x 1 KB and kMLanes x 16 bytes
-  // of index words, all consecutive bytes of the tiled copies; B 4 x 1 KB
-  // (whole k-rows of the slab).
+  // Loads of one k-step, per wave: A values kAL x 1 KB and kMLanes x 16
+  // bytes of index words, all consecutive bytes of the tiled copies; B kBL x
+  // 1 KB (whole k-rows of the slab).
   const uint32_t lds_base = lds_addr(lds);
   const int64_t ldb_bytes = ldb * E::kElem;
-  uint32_t b_off[4];  // kMap: the column part only
+  uint32_t b_off[kBL];  // kMap: the column part only
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (wave * 4 + i) * G::kRowsPerLoad + lane / G::kPieces;  // k-row of the slab
-    const int c = swz<E>(r, lane % G::kPieces);  // logical 16-byte piece
+  for (int i = 0; i < kBL; ++i) {
+    const int r = (wave * kBL + i) * G::kRowsPerLoad + lane / G::kPieces;  // k-row of the slab
+    const int c = swz<E, kN>(r, lane % G::kPieces);  // logical 16-byte piece
     constexpr int per_piece = 16 / E::kElem;    // columns per piece
     const int64_t col = (n0 + c * per_piece < n) ? n0 + c * per_piece : n0;
     b_off[i] = static_cast<uint32_t>((kMap ? 0 : r * ldb_bytes) + col * E::kElem);
@@ -245,7 +271,7 @@ __device__ __forceinline__ void sp24_body(
   // kMap: the B rows of this wave's 16 slab k-rows of one step, one 64-byte
   // piece of the table, read with scalar loads a step before its loads go
   // out (lane group q of load i takes row 4 i + q)
-  static_assert(!kMap || G::kRowsPerLoad == 4, "row map for 4 k-rows per load");
+  static_assert(!kMap || (G::kRowsPerLoad == 4 && kBL == 4), "row map for 4 x 4 k-rows per wave");
   int trow[16];
   auto lookup = [&](int64_t ks) {
     if constexpr (kMap) {
@@ -254,22 +280,22 @@ __device__ __forceinline__ void sp24_body(
       for (int q = 0; q < 16; ++q) trow[q] = t[q];
     }
   };
-  // load `part` (0..6) of k-step ks into stage `stage`: A values 0..1,
-  // index words 2, B 3..6.  Every wave issues all kLoads parts per step (the
-  // vmcnt waits count them).
+  // load `part` of k-step ks into stage `stage`: A values 0 .. kAL-1,
+  // index words kAL, B after them.  Every wave issues all kLoads parts per
+  // step (the vmcnt waits count them).
   auto issue_part = [&](int64_t ks, int stage, int part) {
     const uint32_t sb = lds_base + stage * kStageBytes;
-    if (part < 2) {
-      const uint32_t o = (wave * 2 + part) * 1024;
+    if (part < kAL) {
+      const uint32_t o = (wave * kAL + part) * 1024;
       load_lds16(sb + o, vt + ks * kAVBytes, o + lane * 16);
-    } else if (part == 2) {
+    } else if (part == kAL) {
       const uint32_t o = wave * kMLanes * 16;
       if (lane < kMLanes) load_lds16(sb + kAVBytes + o, mtl + ks * kAMBytes, o + lane * 16);
     } else {
       // k-rows past k (the last step when k is not a whole number of steps)
       // are read from row 0: the matching A values are zero-padded, so they
       // add nothing
-      const int i = part - 3;
+      const int i = part - kAL - 1;
       uint32_t off;
       if constexpr (kMap) {
         // lane group q takes trow[4 i + q]; written as masks so the 16
@@ -281,11 +307,11 @@ __device__ __forceinline__ void sp24_body(
         off = static_cast<uint32_t>(row * ldb_bytes) + b_off[i];
       } else {
         const int64_t krow0 = kstep(ks) * kTK;
-        const int r = (wave * 4 + i) * G::kRowsPerLoad + lane / G::kPieces;
+        const int r = (wave * kBL + i) * G::kRowsPerLoad + lane / G::kPieces;
         off = krow0 + r < k ? static_cast<uint32_t>(krow0 * ldb_bytes) + b_off[i]
                             : b_off[i] - static_cast<uint32_t>(r * ldb_bytes);
       }
-      load_lds16(sb + kAVBytes + kAMBytes + (wave * 4 + i) * 1024, B, off);
+      load_lds16(sb + kAVBytes + kAMBytes + (wave * kBL + i) * 1024, B, off);
     }
   };
   auto issue = [&](int64_t ks, int stage) {
@@ -308,12 +334,14 @@ __device__ __forceinline__ void sp24_body(
     }
   if (kStages - 1 < ksteps) lookup(kStages - 1);
   for (int64_t ks = 0; ks < ksteps; ++ks) {
-    // this step's loads have landed (the next step's may still be in flight)
-    if (ks + 1 < ksteps) wait_vm<kLoads>();
+    // this step's loads have landed (with three stages the next step's may
+    // still be in flight)
+    if (kStages > 2 && ks + 1 < ksteps) wait_vm<kLoads>();
     else wait_vm<0>();
     barrier();  // ... for every wave; and the stage of step ks-1 is free
-    // The loads of step ks+2 go out first: inline asm between the LDS reads
-    // and the MFMAs would make the compiler wait for every read before it.
+    // The loads of step ks+kStages-1 go out first: inline asm between the
+    // LDS reads and the MFMAs would make the compiler wait for every read
+    // before it.
     const int64_t kn = ks + kStages - 1;
     if (kn < ksteps) issue(kn, static_cast<int>(kn % kStages));
     const char *sb = lds + (ks % kStages) * kStageBytes;
@@ -344,10 +372,10 @@ __device__ __forceinline__ void sp24_body(
     // while tile j's 8 MFMAs issue.  At most 18 reads are outstanding, few
     // enough for each wait to name a count (lgkmcnt holds at most 15).
     i32x8 bop[4];
-    bop[0] = read_b<E>(sbb, lane, wn, 0);
+    bop[0] = read_b<E, kN>(sbb, lane, wn, 0);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      if (j + 1 < 4) bop[j + 1] = read_b<E>(sbb, lane, wn, j + 1);
+      if (j + 1 < 4) bop[j + 1] = read_b<E, kN>(sbb, lane, wn, j + 1);
       __builtin_amdgcn_sched_barrier(0);
       if (j + 1 < 4) __builtin_amdgcn_s_waitcnt(0xc07f | (4 << 8));  // lgkmcnt(4)
       else __builtin_amdgcn_s_waitcnt(0xc07f);                        // lgkmcnt(0)
@@ -414,14 +442,14 @@ __device__ __forceinline__ void sp24_body(
       const int32_t *__restrict__ b_rows
 #define SP24_PASS vals, meta, tile_ptr, tile_step, m, k, n, k_pad, mtiles, ntiles, tiles, per_xcd, B, ldb, C, ldc, b_rows
 
-template <bool kTiles, bool kMap>
-__global__ __launch_bounds__(kThreads) void sp24_i8_smfmac(SP24_ARGS) {
-  sp24_body<I8, kTiles, kMap>(SP24_PASS);
+template <int kN, bool kTiles, bool kMap>
+__global__ __launch_bounds__(Tile<kN>::kThreads) void sp24_i8_smfmac(SP24_ARGS) {
+  sp24_body<I8, kN, kTiles, kMap>(SP24_PASS);
 }
 
-template <bool kTiles>
-__global__ __launch_bounds__(kThreads) void sp24_bf16_smfmac(SP24_ARGS) {
-  sp24_body<Bf16, kTiles, false>(SP24_PASS);
+template <int kN, bool kTiles>
+__global__ __launch_bounds__(Tile<kN>::kThreads) void sp24_bf16_smfmac(SP24_ARGS) {
+  sp24_body<Bf16, kN, kTiles, false>(SP24_PASS);
 }
 
 #undef SP24_ARGS
@@ -465,7 +493,7 @@ void sp24_piece(const char *v, int64_t vs, const uint8_t *mt, int64_t ms, int64_
 template <class E>
 void tile_layout(const char *vals, const uint8_t *meta, int64_t m, int64_t k, int64_t m_pad,
                  int64_t k_pad, char *vals_tiled, uint8_t *meta_tiled) {
-  using G = Geo<E>;
+  using G = Geo<E, 256>;  // the A layout does not depend on the tile width
   const int64_t ksteps = k_pad / G::kTK;
   const int64_t vrow = k / 2 * E::kElem, vstep = G::kTK / 2 * E::kElem;
   for (int64_t t = 0; t < m_pad / kTM; ++t)
@@ -480,7 +508,7 @@ void tile_layout(const char *vals, const uint8_t *meta, int64_t m, int64_t k, in
 template <class E>
 void tvw_layout(const char *tile_vals, const uint8_t *tile_meta, int64_t ntiles, int32_t tk,
                 char *vals_tiled, uint8_t *meta_tiled) {
-  using G = Geo<E>;
+  using G = Geo<E, 256>;
   const int64_t per = tk / G::kTK;  // k-steps per stored tile
   const int64_t vrow = tk / 2 * E::kElem, vstep = G::kTK / 2 * E::kElem;
   for (int64_t t = 0; t < ntiles; ++t)
@@ -491,20 +519,20 @@ void tvw_layout(const char *tile_vals, const uint8_t *tile_meta, int64_t ntiles,
                     meta_tiled + (t * per + s) * G::kAMBytes);
 }
 
-template <class E, bool kTiles, bool kMap>
+template <class E, int kN, bool kTiles, bool kMap>
 hipError_t launch(const Sp24Launch &a, hipStream_t s) {
-  using G = Geo<E>;
+  using G = Geo<E, kN>;
   const int64_t mtiles = (a.m + kTM - 1) / kTM;
-  const int64_t ntiles = (a.n + kTN - 1) / kTN;
+  const int64_t ntiles = (a.n + kN - 1) / kN;
   const int64_t tiles = mtiles * ntiles;
   if (tiles == 0) return hipSuccess;
   if (tiles > INT32_MAX / 2 || a.k_pad * a.ldb * E::kElem > UINT32_MAX)
     return hipErrorInvalidValue;
-  auto kernel = E::kElem == 1 ? sp24_i8_smfmac<kTiles, kMap> : sp24_bf16_smfmac<kTiles>;
+  auto kernel = E::kElem == 1 ? sp24_i8_smfmac<kN, kTiles, kMap> : sp24_bf16_smfmac<kN, kTiles>;
   hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(kernel), G::kLdsBytes);
   if (e != hipSuccess) return e;
   const int64_t per_xcd = (tiles + 7) / 8;
-  hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(8 * per_xcd)), dim3(kThreads),
+  hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(8 * per_xcd)), dim3(Tile<kN>::kThreads),
                      G::kLdsBytes, s, static_cast<const char *>(a.vals), a.meta, a.tile_ptr,
                      a.tile_step, a.m, a.k, a.n, a.k_pad, static_cast<int32_t>(mtiles),
                      static_cast<int32_t>(ntiles), static_cast<int32_t>(tiles),
@@ -532,22 +560,35 @@ void tvw_tile_layout(const void *tile_vals, const uint8_t *tile_meta, int64_t nt
 }
 
 int sp24_tile_m() { return kTM; }
-int sp24_tile_n() { return kTN; }
+int sp24_tile_n(int64_t n, bool mapped) {
+  (void)n;
+  // 128 columns: two workgroups per CU.  The row-map path reads four B rows
+  // per 1 KB load and so keeps 256-byte slab rows (256 int8 columns).
+  return mapped ? 256 : 128;
+}
 int sp24_tile_k(bool bf16) { return bf16 ? Bf16::kTK : I8::kTK; }
 
-int64_t sp24_grid(int64_t m, int64_t n) {
-  const int64_t tiles = ((m + kTM - 1) / kTM) * ((n + kTN - 1) / kTN);
+int64_t sp24_grid(int64_t m, int64_t n, int tn) {
+  const int64_t tiles = ((m + kTM - 1) / kTM) * ((n + tn - 1) / tn);
   return 8 * ((tiles + 7) / 8);
 }
+
+namespace {
+template <int kN>
+hipError_t launch_n(const Sp24Launch &a, hipStream_t s) {
+  if (a.bf16) return a.tile_ptr ? launch<Bf16, kN, true, false>(a, s) : launch<Bf16, kN, false, false>(a, s);
+  return a.tile_ptr ? launch<I8, kN, true, false>(a, s) : launch<I8, kN, false, false>(a, s);
+}
+}  // namespace
 
 hipError_t launch_sp24(const Sp24Launch &a, hipStream_t s) {
   if (a.b_rows) {
     // sliding-window A: int8, every k-step stored, B read through the row map
-    if (a.bf16 || a.tile_ptr) return hipErrorInvalidValue;
-    return launch<I8, false, true>(a, s);
+    if (a.bf16 || a.tile_ptr || a.tn != 256) return hipErrorInvalidValue;
+    return launch<I8, 256, false, true>(a, s);
   }
-  if (a.bf16) return a.tile_ptr ? launch<Bf16, true, false>(a, s) : launch<Bf16, false, false>(a, s);
-  return a.tile_ptr ? launch<I8, true, false>(a, s) : launch<I8, false, false>(a, s);
+  if (a.tn != 128) return hipErrorInvalidValue;
+  return launch_n<128>(a, s);
 }
 
 }  // namespace sdm

@@ -26,8 +26,7 @@
 // 8 x 4 sparse MFMA tiles).  Operands go global -> LDS with direct loads
 // into a two-stage ring (72 KB), so two workgroups share a CU and one
 // covers the other's barriers and epilogue; each step's loads go out at its
-// start, before its LDS reads.  The row-map path (below) uses 256 x 256
-// tiles of 8 waves and a three-stage ring instead (156 KB).  The plan stores the
+// start, before its LDS reads.  The plan stores the
 // compressed values and the index words tiled: for each 256-row tile and
 // k-step, one contiguous 16 KB piece of values already in MFMA fragment
 // order and one contiguous piece of index words (4 KB int8, 2 KB bf16), so
@@ -67,16 +66,16 @@ constexpr int kTM = 256;
 constexpr int kMG = 4;                          // row tiles grouped on one XCD
 
 // Workgroup tile: 256 rows x kN columns of C, waves of 128 x 64 (2 x kN/64).
-// kN = 256: 8 waves and a three-stage ring (156 KB, one workgroup per CU);
-// kN = 128: 4 waves and a two-stage ring (72 KB, two workgroups per CU, so
-// one covers the other's barriers and epilogue).
+// kN = 128: 4 waves and a two-stage ring (72 KB), so two workgroups share a
+// CU and one covers the other's barriers and epilogue.  (256 x 256 tiles of
+// 8 waves with a three-stage ring, one workgroup per CU, were 11-16% slower.)
 template <int kN>
 struct Tile {
-  static_assert(kN == 256 || kN == 128, "tile width");
+  static_assert(kN == 128, "tile width");
   static constexpr int kWaves = kN / 32;
   static constexpr int kWN = kWaves / 2;        // waves along n
   static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kStages = kN == 256 ? 3 : 2;
+  static constexpr int kStages = 2;
   static constexpr int kAL = 16 / kWaves;       // 1 KB loads of A values per wave per k-step
   static constexpr int kBL = 4;                 // ... of the B slab
   static constexpr int kLoads = kAL + 1 + kBL;  // direct loads per wave per k-step
@@ -102,9 +101,9 @@ struct Geo {
   static constexpr int kRowsPerLoad = 1024 / kBRow;           // k-rows per 1 KB wave load
   static constexpr int kAVBytes = kTM * kTK / 2 * E::kElem;   // 16 KB compressed values
   static constexpr int kAMBytes = kTM * kTK / 8;              // index bytes
-  static constexpr int kBBytes = kTK * kBRow;                 // 32 KB (kN 256), 16 KB (128)
+  static constexpr int kBBytes = kTK * kBRow;                 // 16 KB
   static constexpr int kStageBytes = kAVBytes + kAMBytes + kBBytes;
-  static constexpr int kLdsBytes = T::kStages * kStageBytes;  // 156 / 150 KB, 72 / 68 KB
+  static constexpr int kLdsBytes = T::kStages * kStageBytes;  // 72 KB int8, 68 KB bf16
   static constexpr int kMLanes = kAMBytes / T::kWaves / 16;   // lanes of a wave that load index bytes
   static_assert(kLdsBytes <= 160 * 1024, "LDS");
   static_assert(kAVBytes == T::kAL * T::kWaves * 1024 && kBBytes == T::kBL * T::kWaves * 1024,
@@ -118,15 +117,14 @@ struct Geo {
 // (16 groups of 16 bytes); those lanes touch 16 k-rows of one piece (int8:
 // rows 0..7 and 16..23 of a 32-row group) or 8 k-rows of two neighbouring
 // pieces (bf16: rows 0..3 and 8..11 of a 16-row group).  The XOR spreads
-// them over the 16 bank groups: with 256-byte rows (int8 at kN = 256, bf16
-// at 128) a piece's bank group is its index; with 128-byte rows (int8 at
-// 128) it is the row's parity times 8 plus the index, so the 8 rows of
-// each parity take the 8 indices; with 512-byte rows (bf16 at 256) the
-// index modulo 16.
+// them over the 16 bank groups.  bf16 rows are 256 bytes, so a piece's bank
+// group is its index.  int8 rows are 128 bytes, so the bank group is the
+// row's parity times 8 plus the index, and the 8 rows of each parity take
+// the 8 indices.
 template <class E, int kN>
 __device__ __forceinline__ int swz(int r, int c) {
-  if constexpr (E::kElem == 1 && kN == 256) return c ^ ((r & 7) | (((r >> 4) & 1) << 3));
-  else if constexpr (E::kElem == 1) return c ^ (((r >> 1) & 3) | (((r >> 4) & 1) << 2));
+  static_assert(kN == 128, "slab rows of 128 int8 or bf16 columns");
+  if constexpr (E::kElem == 1) return c ^ (((r >> 1) & 3) | (((r >> 4) & 1) << 2));
   else return c ^ (((r & 3) | (((r >> 3) & 1) << 2)) << 1);
 }
 
@@ -268,16 +266,17 @@ __device__ __forceinline__ void sp24_body(
     const int64_t col = (n0 + c * per_piece < n) ? n0 + c * per_piece : n0;
     b_off[i] = static_cast<uint32_t>((kMap ? 0 : r * ldb_bytes) + col * E::kElem);
   }
-  // kMap: the B rows of this wave's 16 slab k-rows of one step, one 64-byte
-  // piece of the table, read with scalar loads a step before its loads go
-  // out (lane group q of load i takes row 4 i + q)
-  static_assert(!kMap || (G::kRowsPerLoad == 4 && kBL == 4), "row map for 4 x 4 k-rows per wave");
-  int trow[16];
+  // kMap: the B rows of this wave's kBL * kRowsPerLoad slab k-rows of one
+  // step, one piece of the table, read with scalar loads a step before its
+  // loads go out (lane group q of load i takes row kRowsPerLoad * i + q)
+  constexpr int kRPL = G::kRowsPerLoad, kWRows = kBL * kRPL;
+  static_assert(!kMap || kWRows <= 32, "row map: at most 32 table entries per wave and step");
+  int trow[kMap ? kWRows : 1];
   auto lookup = [&](int64_t ks) {
     if constexpr (kMap) {
-      const int32_t *t = b_rows + ks * kTK + wave * 16;
+      const int32_t *t = b_rows + ks * kTK + wave * kWRows;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) trow[q] = t[q];
+      for (int q = 0; q < kWRows; ++q) trow[q] = t[q];
     }
   };
   // load `part` of k-step ks into stage `stage`: A values 0 .. kAL-1,
@@ -298,12 +297,13 @@ __device__ __forceinline__ void sp24_body(
       const int i = part - kAL - 1;
       uint32_t off;
       if constexpr (kMap) {
-        // lane group q takes trow[4 i + q]; written as masks so the 16
+        // lane group q takes trow[kRPL i + q]; written as masks so the
         // values stay in scalar registers (a select chain becomes an
         // indexed private array)
         const int q = lane / G::kPieces;
-        const int row = (trow[4 * i] & -(q == 0)) | (trow[4 * i + 1] & -(q == 1)) |
-                        (trow[4 * i + 2] & -(q == 2)) | (trow[4 * i + 3] & -(q == 3));
+        int row = 0;
+#pragma unroll
+        for (int j = 0; j < kRPL; ++j) row |= trow[kRPL * i + j] & -(q == j);
         off = static_cast<uint32_t>(row * ldb_bytes) + b_off[i];
       } else {
         const int64_t krow0 = kstep(ks) * kTK;
@@ -334,10 +334,9 @@ __device__ __forceinline__ void sp24_body(
     }
   if (kStages - 1 < ksteps) lookup(kStages - 1);
   for (int64_t ks = 0; ks < ksteps; ++ks) {
-    // this step's loads have landed (with three stages the next step's may
-    // still be in flight)
-    if (kStages > 2 && ks + 1 < ksteps) wait_vm<kLoads>();
-    else wait_vm<0>();
+    // this step's loads have landed (nothing else is in flight: two stages)
+    static_assert(kStages == 2, "one k-step in flight");
+    wait_vm<0>();
     barrier();  // ... for every wave; and the stage of step ks-1 is free
     // The loads of step ks+kStages-1 go out first: inline asm between the
     // LDS reads and the MFMAs would make the compiler wait for every read
@@ -493,7 +492,7 @@ void sp24_piece(const char *v, int64_t vs, const uint8_t *mt, int64_t ms, int64_
 template <class E>
 void tile_layout(const char *vals, const uint8_t *meta, int64_t m, int64_t k, int64_t m_pad,
                  int64_t k_pad, char *vals_tiled, uint8_t *meta_tiled) {
-  using G = Geo<E, 256>;  // the A layout does not depend on the tile width
+  using G = Geo<E, 128>;  // the A layout does not depend on the tile width
   const int64_t ksteps = k_pad / G::kTK;
   const int64_t vrow = k / 2 * E::kElem, vstep = G::kTK / 2 * E::kElem;
   for (int64_t t = 0; t < m_pad / kTM; ++t)
@@ -508,7 +507,7 @@ void tile_layout(const char *vals, const uint8_t *meta, int64_t m, int64_t k, in
 template <class E>
 void tvw_layout(const char *tile_vals, const uint8_t *tile_meta, int64_t ntiles, int32_t tk,
                 char *vals_tiled, uint8_t *meta_tiled) {
-  using G = Geo<E, 256>;
+  using G = Geo<E, 128>;
   const int64_t per = tk / G::kTK;  // k-steps per stored tile
   const int64_t vrow = tk / 2 * E::kElem, vstep = G::kTK / 2 * E::kElem;
   for (int64_t t = 0; t < ntiles; ++t)
@@ -528,7 +527,10 @@ hipError_t launch(const Sp24Launch &a, hipStream_t s) {
   if (tiles == 0) return hipSuccess;
   if (tiles > INT32_MAX / 2 || a.k_pad * a.ldb * E::kElem > UINT32_MAX)
     return hipErrorInvalidValue;
-  auto kernel = E::kElem == 1 ? sp24_i8_smfmac<kN, kTiles, kMap> : sp24_bf16_smfmac<kN, kTiles>;
+  auto kernel = [] {
+    if constexpr (E::kElem == 1) return sp24_i8_smfmac<kN, kTiles, kMap>;
+    else return sp24_bf16_smfmac<kN, kTiles>;
+  }();
   hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(kernel), G::kLdsBytes);
   if (e != hipSuccess) return e;
   const int64_t per_xcd = (tiles + 7) / 8;
@@ -562,9 +564,8 @@ void tvw_tile_layout(const void *tile_vals, const uint8_t *tile_meta, int64_t nt
 int sp24_tile_m() { return kTM; }
 int sp24_tile_n(int64_t n, bool mapped) {
   (void)n;
-  // 128 columns: two workgroups per CU.  The row-map path reads four B rows
-  // per 1 KB load and so keeps 256-byte slab rows (256 int8 columns).
-  return mapped ? 256 : 128;
+  (void)mapped;
+  return 128;  // two workgroups per CU
 }
 int sp24_tile_k(bool bf16) { return bf16 ? Bf16::kTK : I8::kTK; }
 
@@ -584,8 +585,8 @@ hipError_t launch_n(const Sp24Launch &a, hipStream_t s) {
 hipError_t launch_sp24(const Sp24Launch &a, hipStream_t s) {
   if (a.b_rows) {
     // sliding-window A: int8, every k-step stored, B read through the row map
-    if (a.bf16 || a.tile_ptr || a.tn != 256) return hipErrorInvalidValue;
-    return launch<I8, 256, false, true>(a, s);
+    if (a.bf16 || a.tile_ptr || a.tn != 128) return hipErrorInvalidValue;
+    return launch<I8, 128, false, true>(a, s);
   }
   if (a.tn != 128) return hipErrorInvalidValue;
   return launch_n<128>(a, s);

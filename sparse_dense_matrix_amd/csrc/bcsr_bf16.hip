@@ -18,8 +18,9 @@
 //     LDS transpose read (ds_read_b64_tr_b16) gives each lane 4 k-values of
 //     one column, two reads make an operand.  The slab's 16-byte pieces are
 //     XOR-swizzled by k-row so those reads hit 64 distinct banks;
-//   - the ring has two stages (80 KB at kTN = 256, so two workgroups share a
-//     CU and one hides the other's pipeline fill and epilogue);
+//   - the ring has two stages (80 KB at kTN = 256, 40 KB with half blocks,
+//     so two or three workgroups share a CU and each hides the others'
+//     barriers, pipeline fill and epilogue; 144 KB at kTN = 512);
 //   - the finished tile is rounded to bf16, staged in the (now idle) ring and
 //     written to C with 16-byte non-temporal stores, which keep the streaming
 //     C writes from evicting B from L2;

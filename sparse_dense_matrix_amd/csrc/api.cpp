@@ -142,7 +142,7 @@ spmm_status_t plan_bcsr(spmm_plan_s *p) {
   // C write): longest first, each to the lightest group (lowest on ties);
   // every group keeps the longest-first order.  The order array carries the
   // groups' start offsets after its mb entries.
-  const BcsrSchedule sc = bcsr_schedule(a.brow_ptr.data(), mb, p->n, !a.col_perm.empty());
+  const BcsrSchedule sc = bcsr_schedule(a.brow_ptr.data(), mb, p->n);
   const int groups = sc.row_groups;
   std::vector<std::vector<int32_t>> members(static_cast<size_t>(groups));
   std::vector<int64_t> load(static_cast<size_t>(groups), 0);

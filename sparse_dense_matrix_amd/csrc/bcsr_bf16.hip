@@ -134,7 +134,6 @@ __global__ __launch_bounds__(Geo<kTN>::kThreads) void bcsr_bf16_mfma(
     uint16_t *__restrict__ C, int64_t ldc, const int32_t *__restrict__ c_rows,
     const int32_t *__restrict__ b_rows) {
   using G = Geo<kTN, kKH>;
-  static_assert(!kMap || kKH == kBlk, "the row map is looked up per block");
   constexpr int kSteps = G::kSteps, kPer = G::kPer;
   constexpr int kBRow = G::kBRow, kBBytes = G::kBBytes, kStageBytes = G::kStageBytes;
   constexpr int kBLoads = G::kBLoads, kALoads = G::kALoads;
@@ -178,10 +177,11 @@ __global__ __launch_bounds__(Geo<kTN>::kThreads) void bcsr_bf16_mfma(
     brow[i] = r;
   }
   int brow_next[kBLoads];
-  // B rows (through the map) of the block at position blk of the row's list
-  auto lookup_rows = [&](int blk) {
+  // B rows (through the map) of stage unit `unit` of the row: part
+  // unit % kPer of block p0 + unit / kPer
+  auto lookup_rows = [&](int unit) {
     if constexpr (kMap) {
-      const int64_t k0 = static_cast<int64_t>(col_idx[blk]) * kBlk;
+      const int64_t k0 = static_cast<int64_t>(col_idx[p0 + unit / kPer]) * kBlk + (unit % kPer) * kKH;
 #pragma unroll
       for (int i = 0; i < kBLoads; ++i) brow_next[i] = b_rows[k0 + brow[i]];
     }
@@ -250,18 +250,18 @@ __global__ __launch_bounds__(Geo<kTN>::kThreads) void bcsr_bf16_mfma(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int nunit = nblk * kPer;  // stages to run (with kMap, one per block)
+  const int nunit = nblk * kPer;  // stages to run
   if (nunit > 0) {
-    lookup_rows(p0);
+    lookup_rows(0);
     issue(0, 0);
-    if (nblk > 1) lookup_rows(p0 + 1);
+    if (nunit > 1) lookup_rows(1);
   }
   for (int it = 0; it < nunit; ++it) {
-    wait_vm<0>();  // this stage's loads (and the next block's row lookups) have landed
+    wait_vm<0>();  // this stage's loads (and the next unit's row lookups) have landed
     barrier();     // ... for every wave; and the stage of unit it-1 is free
     if (it + 1 < nunit) {
       issue(it + 1, (it + 1) & 1);
-      if (it + 2 < nblk) lookup_rows(p0 + it + 2);
+      if (it + 2 < nunit) lookup_rows(it + 2);
     }
     const char *sb = lds + (it & 1) * kStageBytes;
     // every operand of the block is read before the first MFMA, so the LDS
@@ -321,7 +321,7 @@ void bcsr_fragment_order(const uint16_t *blk, uint16_t *frag) {
               blk[(32 * rb + (l & 31)) * kBlk + 16 * s + 8 * (l >> 5) + i];
 }
 
-BcsrSchedule bcsr_schedule(const int32_t *row_ptr, int32_t mb, int64_t n, bool mapped) {
+BcsrSchedule bcsr_schedule(const int32_t *row_ptr, int32_t mb, int64_t n) {
   BcsrSchedule sc;
   // Wider tiles re-read each A block fewer times (once per tn columns); for
   // small n the narrower tile gives more workgroups to fill the CUs.
@@ -347,12 +347,8 @@ BcsrSchedule bcsr_schedule(const int32_t *row_ptr, int32_t mb, int64_t n, bool m
   // Half-block stages at 256 columns when block rows hold few blocks (at
   // most 16 on average): a 20 KB stage lets a third workgroup onto the CU.
   // Rows of many blocks keep whole-block stages: there a barrier per 8
-  // MFMAs costs more than the extra workgroup gains.  Through a row map the
-  // lookups go per block, so whole blocks.
-  sc.kh = (sc.tn == 256 && !mapped && row_ptr[mb] <= 16 * static_cast<int64_t>(mb)) ? 32 : 64;
-#ifdef SDM_BCSR_KH
-  sc.kh = (sc.tn == 256 && !mapped) ? SDM_BCSR_KH : 64;
-#endif
+  // MFMAs costs more than the extra workgroup gains.
+  sc.kh = (sc.tn == 256 && row_ptr[mb] <= 16 * static_cast<int64_t>(mb)) ? 32 : 64;
   return sc;
 }
 
@@ -390,9 +386,12 @@ hipError_t launch_tn(const BcsrLaunch &a, hipStream_t s) {
 
 hipError_t launch_bcsr_bf16(const BcsrLaunch &a, hipStream_t s) {
   if (a.tn != 256 && a.tn != 512) return hipErrorInvalidValue;
-  if (a.kh != 64 && (a.kh != 32 || a.tn != 256 || a.col_perm)) return hipErrorInvalidValue;
+  if (a.kh != 64 && (a.kh != 32 || a.tn != 256)) return hipErrorInvalidValue;
   const bool wide = a.tn == 512;
-  if (a.col_perm) return wide ? launch_tn<512, true, 64>(a, s) : launch_tn<256, true, 64>(a, s);
+  if (a.col_perm) {
+    if (wide) return launch_tn<512, true, 64>(a, s);
+    return a.kh == 32 ? launch_tn<256, true, 32>(a, s) : launch_tn<256, true, 64>(a, s);
+  }
   if (wide) return launch_tn<512, false, 64>(a, s);
   return a.kh == 32 ? launch_tn<256, false, 32>(a, s) : launch_tn<256, false, 64>(a, s);
 }

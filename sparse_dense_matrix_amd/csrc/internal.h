@@ -108,7 +108,7 @@ struct BcsrLaunch {
   const int32_t *row_seg;   // [row_groups + 1] start of each row group in row_order
   int32_t row_groups;       // 1, 2, 4 or 8: XCD x serves row group x % row_groups
   int32_t tn;               // columns of C per workgroup: 256 or 512
-  int32_t kh;               // k-rows per LDS stage: 64 (whole blocks) or 32 (tn 256, no map)
+  int32_t kh;               // k-rows per LDS stage: 64 (whole blocks) or 32 (tn 256 only)
   int64_t grid;             // workgroups (bcsr_grid)
   int32_t mb;               // block rows (64 rows each)
   int64_t n;
@@ -133,8 +133,7 @@ struct BcsrSchedule {
   int row_groups;
   int kh;
 };
-// mapped: A packed with its columns permuted (B read through the row map)
-BcsrSchedule bcsr_schedule(const int32_t *row_ptr, int32_t mb, int64_t n, bool mapped);
+BcsrSchedule bcsr_schedule(const int32_t *row_ptr, int32_t mb, int64_t n);
 int64_t bcsr_grid(const int32_t *row_seg, const BcsrSchedule &sc, int64_t n);
 hipError_t launch_bcsr_bf16(const BcsrLaunch &a, hipStream_t s);
 

@@ -818,6 +818,22 @@ def _reordered_case(S, orc, w, rows=None):
     return orc.rel_frobenius(bf16_to_f64(g), ref), M, P
 
 
+def test_reordered_bcsr_many_blocks_per_row(S, orc):
+    # 24 of 32 blocks per block row: the reordering still pays (the scrambled
+    # pattern touches nearly every block) and the rows stay long, so the
+    # kernel reads B through the row map with whole-block stages at 256
+    # columns
+    w = synth.Workload("scrambled_dense_rows", "bcsr_csr", 512, 2048, 264, 90, nblocks=192,
+                       scramble=91, reorder=True)
+    err, M, P = _reordered_case(S, orc, w)
+    info = S.spmm_matrix_info(M)
+    _say(f"reordered dense rows: blocks={info['nnzb']} tile_n={P.info()['tile_n']} rel_frob={err:.3e}")
+    assert S.spmm_matrix_array(M, S.ARRAY_COL_PERM).size == w.k
+    assert 192 <= info["nnzb"] < 256 and info["nnzb"] > 16 * (w.m // 64)
+    assert P.info()["tile_n"] == 256
+    assert err <= TOL_BF16
+
+
 @pytest.mark.parametrize("reorder", [True, False])
 def test_reordered_bcsr_small(S, orc, reorder):
     import dataclasses

@@ -72,6 +72,9 @@ def parse():
     ap.add_argument("--graph", type=int, default=0, metavar="G",
                     help="capture G steps into one HIP graph and replay it (steps rounded "
                          "up to a multiple of G); 0 launches every step from Python")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time each step alone after overwriting a 512 MB buffer (L2 and "
+                         "Infinity Cache evicted); reported as `cold` beside the warm line")
     ap.add_argument("--dense-baseline", action="store_true",
                     help="BCSR workloads: also time the dense product of the same shape "
                          "(torch.matmul on the zero-filled bf16 A) to show where block "
@@ -307,6 +310,30 @@ def main():
     roof, other = roofline(w, flops, nbytes, dtype, ms_step)
     pinfo = S.spmm_plan_info(d["P"])
 
+    cold = None
+    if args.cold:
+        # each step timed on its own after a 512 MB fill on the same stream,
+        # which leaves no operand in L2 or the Infinity Cache; the median
+        # over the steps is reported
+        flush = torch.empty(128 << 20, dtype=torch.float32, device="cuda")
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        with torch.cuda.stream(stream):
+            for i, (e0, e1) in enumerate(evs):
+                flush.fill_(float(i))
+                e0.record(stream)
+                step(stream)
+                e1.record(stream)
+        torch.cuda.synchronize()
+        times = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+        ms_cold = times[len(times) // 2]
+        roof_c, other_c = roofline(w, flops, nbytes, dtype, ms_cold)
+        cold = {"ms_per_step_median": round(ms_cold, 6), "ms_min": round(times[0], 6),
+                "ms_max": round(times[-1], 6),
+                "value": round(flops / (ms_cold * 1e-3) / 1e9, 1), "roofline": roof_c,
+                "roofline_other_bound": other_c}
+        del flush
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, d, args.cpu_seconds)
@@ -349,6 +376,8 @@ def main():
     }
     if dense is not None:
         out["dense_baseline"] = dense
+    if cold is not None:
+        out["cold"] = cold
     print(json.dumps(out), flush=True)
 
 

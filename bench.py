@@ -5,12 +5,15 @@ A step is one spmm_execute (every kernel the plan launches) over one dense B
 that is already resident in HBM; packing and planning are one-time costs,
 reported separately.  For the sampled dense-dense workloads (format sddmm) a
 step is one spmm_execute_sddmm over resident X and Y, and n is the inner
-dimension kd.  The default workload is the 4096 x 4096 BCSR bf16
-matrix with 90% of its 64 x 64 blocks zero and B of 4096 columns; the other
+dimension kd.  The default workload is the largest one-GPU case: the
+block-sparse prefill layer, A 18944 x 3584 bf16 in 64 x 64 blocks with 90% of
+the blocks zero, times B of 65,536 token columns (the 7B-model prefill at 90%
+block sparsity and 64K tokens of the AsyncSparse page's abstract); the other
 workloads of the catalogue run with --workload.
 
 Prints one JSON line:
-  value      effective GFLOP/s = 2 * nnz * n / (time per step)  (n = kd for sddmm)
+  value      effective GFLOP/s = 2 * nnz * n / (time per step)  (n = kd for sddmm),
+             warm: K back-to-back steps between two HIP events
   roofline   the dominant kernel against its bound: the larger of the HBM
              time (algorithmic bytes at 8 TB/s) and the MFMA time
              (algorithmic flops at the dtype's dense peak), from HIP events
@@ -18,8 +21,12 @@ Prints one JSON line:
              `traffic` is the HBM bytes per launch the hardware counters saw
              (profiles/hbm_traffic.md), or null when the library source has
              changed since they were taken
+  cold       each of --cold-steps launches timed alone right after a 512 MB
+             fill on the same stream (no operand left in L2 or the Infinity
+             Cache): median, min, max, stdev, and the roofline of the median
   cpu_baseline  the CPU oracle timed on a bounded sample of rows of the same
-             workload (a reported baseline, not a target)
+             workload (a reported baseline, not a target), with the host's
+             CPU model
 """
 from __future__ import annotations
 
@@ -36,7 +43,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "SpMM effective GFLOP/s (2*nnz*N) and % of HBM/MFMA roofline on 1 MI355X"
-HEADLINE = "bcsr_4096_b64_90"
+HEADLINE = "bcsr_prefill_18944x3584"
 
 # MI355X published peaks
 PEAK_HBM_GBS = 8000.0
@@ -72,9 +79,10 @@ def parse():
     ap.add_argument("--graph", type=int, default=0, metavar="G",
                     help="capture G steps into one HIP graph and replay it (steps rounded "
                          "up to a multiple of G); 0 launches every step from Python")
-    ap.add_argument("--cold", action="store_true",
-                    help="also time each step alone after overwriting a 512 MB buffer (L2 and "
-                         "Infinity Cache evicted); reported as `cold` beside the warm line")
+    ap.add_argument("--cold-steps", type=int, default=50,
+                    help="launches timed one by one, each after overwriting a 512 MB buffer "
+                         "(L2 and Infinity Cache evicted); their median is reported as `cold` "
+                         "beside the warm line (0 skips it)"),
     ap.add_argument("--dense-baseline", action="store_true",
                     help="BCSR workloads: also time the dense product of the same shape "
                          "(torch.matmul on the zero-filled bf16 A) to show where block "
@@ -311,13 +319,12 @@ def main():
     pinfo = S.spmm_plan_info(d["P"])
 
     cold = None
-    if args.cold:
-        # each step timed on its own after a 512 MB fill on the same stream,
-        # which leaves no operand in L2 or the Infinity Cache; the median
-        # over the steps is reported
+    if args.cold_steps > 0:
+        # each launch timed on its own after a 512 MB fill on the same stream,
+        # which leaves no operand in L2 or the Infinity Cache
         flush = torch.empty(128 << 20, dtype=torch.float32, device="cuda")
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
+               for _ in range(args.cold_steps)]
         with torch.cuda.stream(stream):
             for i, (e0, e1) in enumerate(evs):
                 flush.fill_(float(i))
@@ -325,13 +332,18 @@ def main():
                 step(stream)
                 e1.record(stream)
         torch.cuda.synchronize()
-        times = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
-        ms_cold = times[len(times) // 2]
+        times = np.array(sorted(e0.elapsed_time(e1) for e0, e1 in evs))
+        ms_cold = float(np.median(times))
         roof_c, other_c = roofline(w, flops, nbytes, dtype, ms_cold)
-        cold = {"ms_per_step_median": round(ms_cold, 6), "ms_min": round(times[0], 6),
-                "ms_max": round(times[-1], 6),
+        cold = {"launches": args.cold_steps, "ms_median": round(ms_cold, 6),
+                "ms_min": round(float(times[0]), 6), "ms_max": round(float(times[-1]), 6),
+                "ms_stdev": round(float(times.std(ddof=1)) if len(times) > 1 else 0.0, 6),
                 "value": round(flops / (ms_cold * 1e-3) / 1e9, 1), "roofline": roof_c,
-                "roofline_other_bound": other_c}
+                "roofline_other_bound": other_c,
+                "what": "each launch alone after a 512 MB fill on the same stream (L2 and "
+                        "Infinity Cache hold no operand); median over the launches"}
+        log(f"cold: median {ms_cold:.4f} ms over {args.cold_steps} launches "
+            f"(min {times[0]:.4f}, max {times[-1]:.4f})")
         del flush
 
     cpu = None
@@ -575,6 +587,18 @@ def synth_f32(B):
     return synth.bf16_bits_to_f32(B) if B.dtype == np.uint16 else B
 
 
+def cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo ("unknown" elsewhere)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, d, target_s):
     """Time the oracle on a growing sample of rows until it takes about
     target_s; report effective GFLOP/s over the sampled rows."""
@@ -624,7 +648,7 @@ def cpu_baseline(w, d, target_s):
         flops = 2.0 * count * w.block * w.block * w.n
         log(f"cpu oracle: {count} blocks in {spent:.2f}s on {oracle.num_threads()} threads")
         return {"value": round(flops / spent / 1e9, 3), "unit": "GFLOP/s",
-                "cores": oracle.num_threads(), "kind": "oracle",
+                "cores": oracle.num_threads(), "cpu_model": cpu_model(), "kind": "oracle",
                 "sample": f"{count} of {units} stored blocks (uniform without replacement, "
                           f"seed 0), full inner dimension {w.n}; "
                           + ("fp64" if w.elem == "bf16" else "int64") + " accumulation"}
@@ -665,7 +689,7 @@ def cpu_baseline(w, d, target_s):
     flops = 2.0 * float(row_nnz[rows].sum()) * w.n
     log(f"cpu oracle: {len(rows)} rows in {spent:.2f}s on {oracle.num_threads()} threads")
     return {"value": round(flops / spent / 1e9, 3), "unit": "GFLOP/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
+            "cores": oracle.num_threads(), "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"{len(rows)} of {w.m} rows (uniform without replacement, seed 0), "
                       + ("all their stored entries" if w.fmt == "sddmm" else f"all {w.n} columns")
                       + "; fp64 accumulation"}

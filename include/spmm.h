@@ -138,7 +138,11 @@ typedef enum {
 
 /* ---- packing (host only; inputs are borrowed for the call and copied) ---- */
 
-/* BCSR from a dense row-major bf16 matrix a_host [m x k] (uint16 bit patterns,
+/* Defining passage: "AsyncSparse: Accelerating Sparse Matrix-Matrix
+ * Multiplication on Asynchronous GPU Architectures", abstract (BCSR for
+ * structured sparsity) and the caption of Figure 2 (BCSR and WCSR compared
+ * on one matrix); the block size is not given there, the kernels take 64.
+ * BCSR from a dense row-major bf16 matrix a_host [m x k] (uint16 bit patterns,
  * leading dimension lda >= k).  A block_m x block_k block is stored when any
  * element is numerically nonzero (+0 and -0 are zero, NaN is not); block rows
  * ascending, block columns ascending, values row-major within the block.
@@ -196,7 +200,12 @@ spmm_status_t spmm_pack_bcsr_csr(int64_t m, int64_t k, spmm_dtype_t dtype,
                                  const void *vals, int32_t block_m, int32_t block_k,
                                  int32_t reorder, spmm_matrix_t *out);
 
-/* WCSR from a canonical CSR on the host: row_ptr int64[m+1] with row_ptr[0] = 0,
+/* Defining passage: the AsyncSparse page, abstract (WCSR for irregular
+ * sparsity, large row windows split across thread blocks for load balance)
+ * and the summary's "What carries the argument" (windowed irregular
+ * sparsity with cross-block row splitting).  The pages give neither window
+ * height nor split size; both are arguments here.
+ * WCSR from a canonical CSR on the host: row_ptr int64[m+1] with row_ptr[0] = 0,
  * non-decreasing; col_idx int32[nnz] strictly ascending within each row and in
  * [0, k); vals float[nnz] (explicit zeros are kept).  Anything else is
  * INVALID_ARG, never silently fixed.  Rows are grouped into windows of
@@ -210,7 +219,13 @@ spmm_status_t spmm_pack_wcsr(int64_t m, int64_t k, spmm_dtype_t dtype,
                              const void *vals, int32_t window_rows,
                              int64_t max_chunk_nnz, spmm_matrix_t *out);
 
-/* 2:4 from a dense row-major matrix a_host [m x k] (lda >= k) of dtype SPMM_I8
+/* Defining passage: "Accelerating Sparse DNNs Based on Tiled GEMM",
+ * abstract (the 2:4 pattern the sparse tensor core runs at the register
+ * level); "Efficient Quantized Sparse Matrix Operations on Tensor Cores",
+ * abstract (SpMM on low-precision integers); the N:M entry of the "Daily
+ * Papers" search page (definition of N:M).  The dtype argument goes beyond
+ * the int8 case: the same pattern in bf16.
+ * 2:4 from a dense row-major matrix a_host [m x k] (lda >= k) of dtype SPMM_I8
  * (int8) or SPMM_BF16 (uint16 bit patterns; else UNSUPPORTED): in every group
  * of 4 consecutive elements of a row keep the two of largest |a| (int8 as
  * integers: |-128| = 128; bf16 in magnitude order, every NaN above infinity
@@ -231,7 +246,11 @@ void spmm_matrix_destroy(spmm_matrix_t a);
 
 /* ---- plan (host -> device, synchronous) ---- */
 
-/* Copy the packed operand to device `device`, choose the kernel and tiles
+/* The pages give no planning step; the plan is where the per-format kernel
+ * choice of the AsyncSparse page (abstract: one kernel for block-structured,
+ * one for irregular sparsity) and the 2:4 kernel of "Accelerating Sparse
+ * DNNs Based on Tiled GEMM" (abstract) are made, once per (A, n).
+ * Copy the packed operand to device `device`, choose the kernel and tiles
  * for n columns, and allocate the workspace.  Supported (b_dtype, c_dtype):
  *   BCSR (64 x 64 blocks): (BF16, BF16), n % 8 == 0
  *   WCSR:                  (F32, F32), any n >= 1
@@ -263,7 +282,11 @@ void spmm_plan_destroy(spmm_plan_t p);
 
 /* ---- execute (asynchronous on the caller's stream) ---- */
 
-/* C = A * B on `stream`; every element of C[m x n] is overwritten (rows of A
+/* Defining passage: the product SpMM computes, sparse A times dense B, as
+ * stated in the AsyncSparse page's abstract (SpMM as a kernel of scientific
+ * computing and machine learning) and in the Magicube page's abstract
+ * ("Efficient Quantized Sparse Matrix Operations on Tensor Cores").
+ * C = A * B on `stream`; every element of C[m x n] is overwritten (rows of A
  * without entries give zeros).  b_dev [k x n] and c_dev [m x n] are device
  * pointers on the plan's device, 16-byte aligned, with ldb >= n, ldc >= n and
  * ldb * elem, ldc * elem multiples of 16 bytes.  Allocates nothing and does

@@ -44,13 +44,11 @@ def _compile(src: str, verbose: bool, extra=(), build_dir: str = BUILD_DIR) -> s
     return obj
 
 
-def build(verbose: bool = False, defines=(), out: str = LIB, build_dir: str = BUILD_DIR) -> str:
-    """Compile every source and link `out`.  `defines` (NAME=VALUE strings)
-    override compile-time tile parameters for experiments."""
+def build(verbose: bool = False, out: str = LIB, build_dir: str = BUILD_DIR) -> str:
+    """Compile every source and link `out`."""
     os.makedirs(build_dir, exist_ok=True)
-    extra = [f"-D{d}" for d in defines]
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose, extra, build_dir), SOURCES))
+        objs = list(ex.map(lambda s: _compile(s, verbose, build_dir=build_dir), SOURCES))
     tmp = out + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:

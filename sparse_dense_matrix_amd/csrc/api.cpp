@@ -323,9 +323,8 @@ spmm_status_t plan_sddmm(spmm_plan_s *p, int64_t kd, spmm_dtype_t dtype) {
 }
 
 // ---- SDDMM plan on a BCSR pattern: block groups and inner-dimension ranges ---
-#ifndef SDM_SDDMM_UNITS
-#define SDM_SDDMM_UNITS 2048
-#endif
+// workgroups a block-SDDMM launch aims for (about eight per CU)
+constexpr int64_t kSddmmUnits = 2048;
 spmm_status_t plan_sddmm_bcsr(spmm_plan_s *p, int64_t kd, bool int8) {
   const Matrix &a = *p->a;
   const int64_t nnzb = static_cast<int64_t>(a.bcol_idx.size());
@@ -338,12 +337,12 @@ spmm_status_t plan_sddmm_bcsr(spmm_plan_s *p, int64_t kd, bool int8) {
                     {static_cast<int32_t>(r), b, std::min<int32_t>(G, a.brow_ptr[r + 1] - b), 0});
   const int64_t ngroups = static_cast<int64_t>(groups.size() / 4);
   // ranges of the inner dimension: enough workgroups for the chip (about
-  // SDM_SDDMM_UNITS), each range at least 16 chunks long
+  // kSddmmUnits), each range at least 16 chunks long
   const int64_t chunk = sddmm_bcsr_chunk(int8);
   const int64_t chunks = (kd + chunk - 1) / chunk;
   int64_t nsplit = 1;
   if (ngroups > 0 && chunks > 0) {
-    nsplit = std::min<int64_t>((SDM_SDDMM_UNITS + ngroups - 1) / ngroups,
+    nsplit = std::min<int64_t>((kSddmmUnits + ngroups - 1) / ngroups,
                                std::max<int64_t>(1, chunks / 16));
     nsplit = std::max<int64_t>(1, nsplit);
   }
@@ -389,7 +388,8 @@ spmm_status_t plan_24(spmm_plan_s *p) {
   const int64_t k = slide ? a.k_lift : a.k;
   const int64_t TM = sp24_tile_m(), TK = sp24_tile_k(bf16);
   const int64_t m_pad = (a.m + TM - 1) / TM * TM;
-  const int64_t k_pad = std::max<int64_t>(TK, (k + TK - 1) / TK * TK);
+  // k = 0 gives no k-steps: the kernel then writes zeros and never reads B
+  const int64_t k_pad = (k + TK - 1) / TK * TK;
   std::vector<int8_t> v(static_cast<size_t>(m_pad * (k_pad / 2) * elem));
   std::vector<uint8_t> mt(static_cast<size_t>(m_pad * (k_pad / 8)));
   const void *src = bf16 ? static_cast<const void *>(a.vals24_bf16.data())

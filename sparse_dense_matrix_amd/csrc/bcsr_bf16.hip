@@ -338,12 +338,6 @@ BcsrSchedule bcsr_schedule(const int32_t *row_ptr, int32_t mb, int64_t n) {
     sc.row_groups = 8;
     sc.tn = 256;
   }
-#ifdef SDM_BCSR_ROW_GROUPS
-  sc.row_groups = mb >= SDM_BCSR_ROW_GROUPS ? SDM_BCSR_ROW_GROUPS : 1;
-#endif
-#ifdef SDM_BCSR_TILE_N
-  sc.tn = SDM_BCSR_TILE_N;
-#endif
   // Half-block stages at 256 columns when block rows hold few blocks (at
   // most 16 on average): a 20 KB stage lets a third workgroup onto the CU.
   // Rows of many blocks keep whole-block stages: there a barrier per 8

@@ -47,19 +47,13 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-#ifndef SDM_SDDMM_CHUNK
-#define SDM_SDDMM_CHUNK 128
-#endif
-#ifndef SDM_SDDMM_STAGES
-#define SDM_SDDMM_STAGES 2
-#endif
 constexpr int kBlk = 64;                        // block edge
 constexpr int kWaves = 4;                       // one stored block per wave
-constexpr int kChunkBytes = SDM_SDDMM_CHUNK;    // bytes of a row per pipeline step
+constexpr int kChunkBytes = 128;               // bytes of a row per pipeline step
 constexpr int kPieces = kChunkBytes / 16;       // 16-byte pieces per chunk row
 constexpr int kSteps = kPieces / 2;             // MFMA k-steps per chunk (a lane takes half a row)
 constexpr int kTileBytes = kBlk * kChunkBytes;  // one 64-row chunk
-constexpr int kStages = SDM_SDDMM_STAGES;       // LDS ring: kStages - 1 chunks load ahead
+constexpr int kStages = 2;                     // LDS ring: kStages - 1 chunks load ahead
 constexpr int kAhead = kStages - 1;
 constexpr int kStageBytes = (1 + kWaves) * kTileBytes;  // X_I, then Y_J of each wave
 constexpr int kLdsBytes = kStages * kStageBytes;

@@ -307,9 +307,19 @@ __device__ __forceinline__ void sp24_body(
         off = static_cast<uint32_t>(row * ldb_bytes) + b_off[i];
       } else {
         const int64_t krow0 = kstep(ks) * kTK;
-        const int r = (wave * kBL + i) * G::kRowsPerLoad + lane / G::kPieces;
-        off = krow0 + r < k ? static_cast<uint32_t>(krow0 * ldb_bytes) + b_off[i]
-                            : b_off[i] - static_cast<uint32_t>(r * ldb_bytes);
+        off = static_cast<uint32_t>(krow0 * ldb_bytes) + b_off[i];
+        if (krow0 + kTK > k) {
+          // the last step of a k that is not a whole number of steps: slab
+          // k-rows past k are filled with zeros instead of being loaded, so
+          // the zero-padded A values meet zeros (0 * Inf would be NaN)
+          const int r = (wave * kBL + i) * G::kRowsPerLoad + lane / G::kPieces;
+          const uint32_t dst = (wave * kBL + i) * 1024 + lane * 16;
+          if (krow0 + r >= k) {
+            *reinterpret_cast<i32x4 *>(lds + stage * kStageBytes + kAVBytes + kAMBytes + dst) =
+                i32x4{0, 0, 0, 0};
+            return;
+          }
+        }
       }
       load_lds16(sb + kAVBytes + kAMBytes + (wave * kBL + i) * 1024, B, off);
     }

@@ -54,3 +54,16 @@ def run(S, plan, B: np.ndarray, m: int, n: int, kind: str, pad: int = 0):
 
 def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def assert_all_written(got: np.ndarray, kind: str):
+    """Every element of C was written: none still holds empty_out's sentinel
+    (bf16 0xFFFF is a NaN, fp32 NaN, int32 -2^31; no finite product of the
+    tested inputs takes them)."""
+    if kind == "bf16":
+        bad = int(np.count_nonzero(np.asarray(got).view(np.uint16) == 0xFFFF))
+    elif kind == "f32":
+        bad = int(np.count_nonzero(~np.isfinite(got)))
+    else:
+        bad = int(np.count_nonzero(np.asarray(got) == -(2 ** 31)))
+    assert bad == 0, f"{bad} elements of C were not written"

@@ -14,7 +14,8 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_helpers import TOL_BF16, TOL_F32, bf16_to_f64, run, to_dev, empty_out, from_dev
+from gpu_helpers import (TOL_BF16, TOL_F32, assert_all_written, bf16_to_f64, empty_out, from_dev,
+                         run, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -42,10 +43,11 @@ def bcsr_case(S, orc, a_bits, B_bits, rows=None, pad=0):
     M = S.spmm_pack_bcsr(a_bits, 64, 64)
     P = S.spmm_plan(M, n, S.BF16, S.BF16)
     got = run(S, P, B_bits, m, n, "bf16", pad)
+    assert_all_written(got, "bf16")
     rp, ci, v = orc.pack_bcsr(a_bits, 64, 64)
     ref = orc.bcsr_spmm(64, 64, rp, ci, v, B_bits, rows=rows)
     g = bf16_to_f64(got if rows is None else got[rows])
-    assert np.isfinite(g).all(), "unwritten or non-finite outputs"
+    assert np.isfinite(g).all(), "non-finite outputs"
     return g, ref, got
 
 
@@ -102,39 +104,99 @@ def test_bcsr_empty_and_dense_block_rows(S, orc):
 
 
 def test_bcsr_4096_config(S, orc):
+    # every row and column of C against the oracle
     w = synth.WORKLOADS["bcsr_4096_b64_90"]
     a = synth.make_a(w)["dense"]
     B = synth.make_b(w)
-    r = np.random.default_rng(5)
-    rows = np.unique(np.concatenate([np.arange(64), np.arange(w.m - 64, w.m),
-                                     r.choice(w.m, 256, replace=False)])).astype(np.int64)
-    g, ref, _ = bcsr_case(S, orc, a, B, rows=rows)
+    g, ref, _ = bcsr_case(S, orc, a, B)
     err = orc.rel_frobenius(g, ref)
-    _say(f"bcsr_4096 rows={len(rows)} rel_frob={err:.3e}")
+    _say(f"bcsr_4096 all {w.m} rows rel_frob={err:.3e}")
     assert err <= TOL_BF16
+
+
+# column ranges of the prefill layer checked over every row: the first and
+# the last 1024 columns and two interior ranges that straddle N-tile
+# boundaries of every tile width the plan may take (256 and 512); C's columns
+# are independent, so these check the same sums as whole rows
+PREFILL_COLS = ((0, 1024), (16128, 17152), (40704, 41728), (65536 - 1024, 65536))
 
 
 @pytest.mark.parametrize("name", ["bcsr_prefill_18944x3584", "bcsr_prefill_18944x3584_z70",
                                   "bcsr_prefill_18944x3584_z50"])
-def test_bcsr_prefill_config_sampled(S, orc, name):
+def test_bcsr_prefill_config(S, orc, name):
     w = synth.WORKLOADS[name]
     a = synth.make_a(w)["dense"]
     B = synth.make_b(w)
-    r = np.random.default_rng(6)
-    rows = np.unique(np.concatenate([np.arange(64), np.arange(w.m - 64, w.m),
-                                     r.choice(w.m, 64, replace=False)])).astype(np.int64)
     M = S.spmm_pack_bcsr(a, 64, 64)
     P = S.spmm_plan(M, w.n, S.BF16, S.BF16)
+    _say(f"{name}: plan tile_n={P.info()['tile_n']} grid={P.info()['grid']}")
     got = run(S, P, B, w.m, w.n, "bf16")
-    assert (got != 0xFFFF).all(), "some C element was not written"
+    assert_all_written(got, "bf16")
     rp, ci, v = orc.pack_bcsr(a, 64, 64)
-    # the sampled rows over the first and the last 2048 columns (C's columns
-    # are independent, so slabs check the same sums as whole rows)
-    for j0, j1 in ((0, 2048), (w.n - 2048, w.n)):
-        ref = orc.bcsr_spmm(64, 64, rp, ci, v, B, rows=rows, j0=j0, j1=j1)
-        err = orc.rel_frobenius(bf16_to_f64(got[rows][:, j0:j1]), ref)
-        _say(f"{name} rows={len(rows)} cols=[{j0},{j1}) rel_frob={err:.3e}")
+    for j0, j1 in PREFILL_COLS:
+        ref = orc.bcsr_spmm(64, 64, rp, ci, v, B, j0=j0, j1=j1)
+        err = orc.rel_frobenius(bf16_to_f64(got[:, j0:j1]), ref)
+        _say(f"{name} all {w.m} rows cols=[{j0},{j1}) rel_frob={err:.3e}")
         assert err <= TOL_BF16
+
+
+def _int_bcsr(m, k, nblocks, seed, empty_rows=()):
+    """bf16 bits of an m x k matrix with `nblocks` uniformly placed 64 x 64
+    blocks of small integers (-3..3, zeros included) and the given block rows
+    emptied."""
+    r = np.random.default_rng(seed)
+    mb, kb = m // 64, k // 64
+    a = np.zeros((m, k), np.float32)
+    for b in r.choice(mb * kb, nblocks, replace=False):
+        i, j = divmod(int(b), kb)
+        a[i * 64:(i + 1) * 64, j * 64:(j + 1) * 64] = r.integers(-3, 4, size=(64, 64))
+    for i in empty_rows:
+        a[i * 64:(i + 1) * 64] = 0
+    return synth.f32_to_bf16_bits(a)
+
+
+def _assert_int_exact(got, ref):
+    """Integer-valued inputs: every fp32 partial sum is exact, so C must be
+    exactly the round-to-nearest-even bf16 of the exact sum (zeros may carry
+    either sign)."""
+    assert np.abs(ref).max() < 2 ** 24
+    exp = synth.f32_to_bf16_bits(ref.astype(np.float32))
+    np.testing.assert_array_equal(got & 0x7FFF, exp & 0x7FFF)
+    nz = ref != 0
+    np.testing.assert_array_equal(got[nz], exp[nz])
+
+
+def test_bcsr_integer_values_many_blocks_per_row_exact(S, orc):
+    # about 20 stored blocks per block row (whole-block stages), an empty
+    # block row, a ragged n; bit-exact against the oracle's exact sums
+    m, k, n = 640, 2048, 1032
+    a = _int_bcsr(m, k, 200, 91, empty_rows=(3,))
+    B = synth.f32_to_bf16_bits(np.random.default_rng(92).integers(-4, 5, size=(k, n)).astype(np.float32))
+    M = S.spmm_pack_bcsr(a, 64, 64)
+    P = S.spmm_plan(M, n, S.BF16, S.BF16)
+    got = run(S, P, B, m, n, "bf16")
+    assert_all_written(got, "bf16")
+    rp, ci, v = orc.pack_bcsr(a, 64, 64)
+    assert np.diff(rp).max() > 16 and np.diff(rp).mean() > 16
+    _say(f"bcsr integer many blocks: blocks={len(ci)} tile_n={P.info()['tile_n']}")
+    _assert_int_exact(got, orc.bcsr_spmm(64, 64, rp, ci, v, B))
+
+
+def test_bcsr_integer_values_row_groups_exact(S, orc):
+    # A of ~3.4 MB at n >= 8192 takes the row-group schedule (each XCD serves
+    # an eighth of the block rows); ragged last N tile, empty block rows;
+    # every row bit-exact over the first, an interior and the last columns
+    m, k, n = 20480, 1024, 8200
+    a = _int_bcsr(m, k, 420, 93, empty_rows=(0, 1, 2, 150))
+    B = synth.f32_to_bf16_bits(np.random.default_rng(94).integers(-4, 5, size=(k, n)).astype(np.float32))
+    M = S.spmm_pack_bcsr(a, 64, 64)
+    P = S.spmm_plan(M, n, S.BF16, S.BF16)
+    got = run(S, P, B, m, n, "bf16")
+    assert_all_written(got, "bf16")
+    rp, ci, v = orc.pack_bcsr(a, 64, 64)
+    _say(f"bcsr integer row groups: blocks={len(ci)} tile_n={P.info()['tile_n']} grid={P.info()['grid']}")
+    for j0, j1 in ((0, 512), (3968, 4480), (n - 520, n)):
+        _assert_int_exact(got[:, j0:j1], orc.bcsr_spmm(64, 64, rp, ci, v, B, j0=j0, j1=j1))
 
 
 def test_bcsr_many_blocks_per_row(S, orc):
@@ -199,9 +261,9 @@ def wcsr_case(S, orc, m, k, rp, ci, v, B, W, T, rows=None, pad=0):
     M = S.spmm_pack_wcsr(m, k, rp, ci, v, W, T)
     P = S.spmm_plan(M, n, S.F32, S.F32)
     got = run(S, P, B, m, n, "f32", pad)
+    assert_all_written(got, "f32")
     ref = orc.csr_spmm(rp, ci, v, B, rows=rows)
     g = got if rows is None else got[rows]
-    assert np.isfinite(got).all(), "unwritten or non-finite outputs"
     return orc.rel_frobenius(g, ref), got, P
 
 
@@ -258,19 +320,17 @@ def test_wcsr_empty_and_giant_rows(S, orc):
     assert (got == 0).all()
 
 
-def test_wcsr_powerlaw_1m_config_sampled(S, orc):
+def test_wcsr_powerlaw_1m_config(S, orc):
+    # every row of C against the oracle (all 10^6 rows, 128 columns)
     w = synth.WORKLOADS["csr_powerlaw_1m"]
     a = synth.make_a(w)
     B = synth.make_b(w)
-    lens = np.diff(a["row_ptr"])
-    r = np.random.default_rng(10)
-    rows = np.unique(np.concatenate([np.argsort(lens)[-300:], r.choice(w.m, 3000, replace=False),
-                                     np.arange(100), np.arange(w.m - 100, w.m)])).astype(np.int64)
-    err, got, P = wcsr_case(S, orc, w.m, w.k, a["row_ptr"], a["col_idx"], a["vals"], B, 16, 512,
-                            rows=rows)
-    _say(f"csr_powerlaw_1m rows={len(rows)} split_rows={P.info()['num_split_rows']} "
+    err, got, P = wcsr_case(S, orc, w.m, w.k, a["row_ptr"], a["col_idx"], a["vals"], B, 16, 512)
+    _say(f"csr_powerlaw_1m all {w.m} rows split_rows={P.info()['num_split_rows']} "
          f"rel_frob={err:.3e}")
     assert err <= TOL_F32
+    lens = np.diff(a["row_ptr"])
+    assert (got[lens == 0] == 0).all()
 
 
 def test_wcsr_deterministic(S, orc):
@@ -293,6 +353,7 @@ def sp24_case(S, orc, a, B, rows=None, pad=0):
     M = S.spmm_pack_24(a)
     P = S.spmm_plan(M, n, S.I8, S.I32)
     got = run(S, P, B, m, n, "i32", pad)
+    assert_all_written(got, "i32")
     v, mt = orc.pack24(a)
     ref = orc.sp24_spmm(v, mt, B, rows=rows)
     return got if rows is None else got[rows], ref
@@ -328,15 +389,30 @@ def test_sp24_identity_and_extremes(S, orc):
     np.testing.assert_array_equal(got, np.full((128, 32), (k // 2) * 16384, np.int32))
 
 
-def test_sp24_8192_config_sampled(S, orc):
+def test_sp24_8192_config(S, orc):
+    # every element of C bit for bit
     w = synth.WORKLOADS["sp24_i8_8192"]
     a = synth.make_a(w)["dense"]
     B = synth.make_b(w)
-    r = np.random.default_rng(11)
-    rows = np.unique(np.concatenate([np.arange(128), np.arange(w.m - 128, w.m),
-                                     r.choice(w.m, 256, replace=False)])).astype(np.int64)
-    got, ref = sp24_case(S, orc, a, B, rows=rows)
+    got, ref = sp24_case(S, orc, a, B)
     np.testing.assert_array_equal(got, ref)
+    _say(f"sp24_i8_8192 all {w.m} rows exact")
+
+
+def test_sp24_empty_k_writes_zeros(S, orc):
+    # k = 0 (a valid pack): the plan has no k-steps, execute takes a NULL B
+    # and must write zeros without reading B; int8, bf16 and (2N-2):2N
+    torch = __import__("torch")
+    m, n = 300, 32
+    cases = [(S.spmm_pack_24(np.zeros((m, 0), np.int8)), (S.I8, S.I32), torch.int32, "i32"),
+             (S.spmm_pack_24(np.zeros((m, 0), np.uint16)), (S.BF16, S.BF16), torch.int16, "bf16"),
+             (S.spmm_pack_slide(np.zeros((m, 0), np.int8), 8), (S.I8, S.I32), torch.int32, "i32")]
+    for M, types, cdt, kind in cases:
+        P = S.spmm_plan(M, n, *types)
+        Ct = empty_out(m, n, kind)
+        S.spmm_execute(P, 0, Ct.data_ptr(), ldb=n, ldc=n)
+        got = from_dev(Ct, kind)
+        assert (np.asarray(got).view(np.uint16 if kind == "bf16" else np.int32) & (0x7FFF if kind == "bf16" else -1) == 0).all()
 
 
 # ---------------------------------------------------------------------------
@@ -350,6 +426,7 @@ def sp24_bf16_case(S, orc, a_bits, B_bits, rows=None, pad=0):
     M = S.spmm_pack_24(a_bits)
     P = S.spmm_plan(M, n, S.BF16, S.BF16)
     got = run(S, P, B_bits, m, n, "bf16", pad)
+    assert_all_written(got, "bf16")
     pruned = orc.prune_nm(a_bits, 2, 4)
     ref = orc.gemm_f64(bf16_to_f64(pruned if rows is None else pruned[rows]), bf16_to_f64(B_bits))
     g = bf16_to_f64(got if rows is None else got[rows])
@@ -393,6 +470,32 @@ def test_sp24_bf16_integer_values_are_exact(S, orc):
     np.testing.assert_array_equal(got & 0x7FFF, synth.f32_to_bf16_bits(ref.astype(np.float32)) & 0x7FFF)
     nz = ref != 0
     np.testing.assert_array_equal(got[nz], synth.f32_to_bf16_bits(ref[nz].astype(np.float32)))
+
+
+def test_sp24_bf16_ragged_k_padding_meets_zeros(S, orc):
+    # k = 72 is not a whole number of 64-deep steps: the last step's slab
+    # k-rows past k must be zeros, not copies of a B row, or a padded zero of
+    # A times an infinite B element would turn whole columns into NaN.  B row
+    # 0 holds +Inf in every third column and every row keeps A[i, 0] = 1 (the
+    # largest of its group), so those columns must come out exactly +Inf
+    r = np.random.default_rng(49)
+    m, k, n = 130, 72, 96
+    a = synth.normal_f32(r, (m, k), 0.02)
+    a[:, 0] = 1.0
+    a_bits = synth.f32_to_bf16_bits(a)
+    B = synth.f32_to_bf16_bits(synth.normal_f32(r, (k, n), 1.0))
+    B[0, ::3] = 0x7F80
+    M = S.spmm_pack_24(a_bits)
+    P = S.spmm_plan(M, n, S.BF16, S.BF16)
+    got = run(S, P, B, m, n, "bf16")
+    assert (got[:, ::3] == 0x7F80).all(), "infinite columns"
+    fin = np.ones(n, bool)
+    fin[::3] = False
+    pruned = orc.prune_nm(a_bits, 2, 4)
+    ref = orc.gemm_f64(bf16_to_f64(pruned), bf16_to_f64(B[:, fin]))
+    g = bf16_to_f64(got[:, fin])
+    assert np.isfinite(g).all()
+    assert orc.rel_frobenius(g, ref) <= TOL_BF16
 
 
 def test_sp24_bf16_identity_and_zero(S, orc):
@@ -889,6 +992,7 @@ def tvw_case(S, orc, a, B, rows=None, pad=0):
     M = S.spmm_pack_tvw(a, 256, 128)
     P = S.spmm_plan(M, n, S.I8, S.I32)
     got = run(S, P, B, m, n, "i32", pad)
+    assert_all_written(got, "i32")
     v, mt = orc.pack24(a)
     ref = orc.sp24_spmm(v, mt, B, rows=rows)
     np.testing.assert_array_equal(got if rows is None else got[rows], ref)
@@ -961,6 +1065,7 @@ def tvw_bf16_case(S, orc, a_bits, B_bits, tk=128, rows=None, pad=0):
     M = S.spmm_pack_tvw(a_bits, 256, tk)
     P = S.spmm_plan(M, n, S.BF16, S.BF16)
     got = run(S, P, B_bits, m, n, "bf16", pad)
+    assert_all_written(got, "bf16")
     pruned = orc.prune_nm(a_bits, 2, 4)
     rp, ci, v = orc.pack_bcsr(pruned, 256, tk)
     ref = orc.bcsr_spmm(256, tk, rp, ci, v, B_bits, rows=rows)
@@ -1050,6 +1155,7 @@ def slide_case(S, orc, a, B, group, rows=None, pad=0):
     M = S.spmm_pack_slide(a, group)
     P = S.spmm_plan(M, n, S.I8, S.I32)
     got = run(S, P, B, m, n, "i32", pad)
+    assert_all_written(got, "i32")
     pruned = orc.prune_nm(a, group - 2, group)
     ref = orc.gemm_i8(pruned if rows is None else pruned[rows], B)
     g = got if rows is None else got[rows]

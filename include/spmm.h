@@ -301,6 +301,22 @@ void spmm_plan_destroy(spmm_plan_t p);
 spmm_status_t spmm_execute(spmm_plan_t p, const void *b_dev, int64_t ldb, void *c_dev,
                            int64_t ldc, hipStream_t stream);
 
+/* For callers that cannot allocate device memory while they run: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same as spmm_execute (same checks, kernels and results), except that the
+ * partial rows of a WCSR plan's split rows (num_slots * n * 4 bytes, see
+ * spmm_plan_info) are kept in a fixed scratch array of 32 MiB per GPU inside
+ * the library instead of the plan's workspace; other formats use no scratch.
+ * Allocates nothing: the array is part of the library's device image, held
+ * by every GPU the library runs on until the process ends.  A plan needing
+ * more than 32 MiB returns UNSUPPORTED before anything is launched.  Every
+ * call on one GPU shares that GPU's array, and a call leaves its partial rows
+ * there: calls that overlap on one GPU (concurrent streams, or host threads
+ * launching at once) race and give wrong results; order them on one stream
+ * or use spmm_execute with separate plans. */
+spmm_status_t spmm_execute_noalloc(spmm_plan_t p, const void *b_dev, int64_t ldb, void *c_dev,
+                                   int64_t ldc, hipStream_t stream);
+
 /* ---- sampled dense-dense product (SDDMM) ---- */
 
 /* Plan out[p] = sum over t < kd of X[i][t] * Y[j][t] for every stored entry

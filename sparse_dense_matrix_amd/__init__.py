@@ -23,7 +23,7 @@ __all__ = [
     "ARRAY_CHUNK_WINDOW", "ARRAY_CHUNK_BEGIN", "ARRAY_ROW_PERM", "ARRAY_COL_PERM",
     "spmm_pack_bcsr", "spmm_pack_bcsr_csr", "spmm_pack_wcsr", "spmm_pack_24", "spmm_pack_tvw", "spmm_pack_slide",
     "spmm_matrix_info",
-    "spmm_matrix_array", "spmm_plan", "spmm_plan_info", "spmm_execute",
+    "spmm_matrix_array", "spmm_plan", "spmm_plan_info", "spmm_execute", "spmm_execute_noalloc",
     "spmm_plan_sddmm", "spmm_execute_sddmm",
     "spmm_status_str", "spmm_last_error", "LIB_PATH", "EXPORTS",
 ]
@@ -47,7 +47,8 @@ EXPORTS = (
     "spmm_pack_bcsr", "spmm_pack_bcsr_csr", "spmm_pack_wcsr", "spmm_pack_24", "spmm_pack_tvw", "spmm_pack_slide",
     "spmm_matrix_info",
     "spmm_matrix_array", "spmm_matrix_destroy", "spmm_plan", "spmm_plan_info",
-    "spmm_plan_destroy", "spmm_execute", "spmm_plan_sddmm", "spmm_execute_sddmm",
+    "spmm_plan_destroy", "spmm_execute", "spmm_execute_noalloc", "spmm_plan_sddmm",
+    "spmm_execute_sddmm",
     "spmm_status_str", "spmm_last_error",
 )
 
@@ -96,6 +97,7 @@ def _load():
         "spmm_plan_info": (st, [P, C.POINTER(PlanInfo)]),
         "spmm_plan_destroy": (None, [P]),
         "spmm_execute": (st, [P, P, i64, P, i64, P]),
+        "spmm_execute_noalloc": (st, [P, P, i64, P, i64, P]),
         "spmm_plan_sddmm": (st, [P, i64, st, i32, C.POINTER(P)]),
         "spmm_execute_sddmm": (st, [P, P, i64, P, i64, P, P]),
         "spmm_status_str": (C.c_char_p, [st]),
@@ -319,12 +321,7 @@ def _dev_ptr_ld(t):
     return t.data_ptr(), t.stride(0)
 
 
-def spmm_execute(plan: Plan, b, c, stream=None, ldb: int | None = None,
-                 ldc: int | None = None):
-    """C = A * B on `stream` (default: torch's current stream on C's device).
-
-    b and c are torch tensors on the plan's device, or raw device pointers
-    with ldb / ldc given."""
+def _execute(fn: str, plan: Plan, b, c, stream, ldb, ldc):
     if isinstance(b, int) or isinstance(c, int):
         bp, cp = int(b), int(c)
         if ldb is None or ldc is None:
@@ -338,8 +335,25 @@ def spmm_execute(plan: Plan, b, c, stream=None, ldb: int | None = None,
         stream = torch.cuda.current_stream(dev).cuda_stream
     elif hasattr(stream, "cuda_stream"):
         stream = stream.cuda_stream
-    _check(_lib.spmm_execute(plan.handle, C.c_void_p(bp), ldb, C.c_void_p(cp), ldc,
-                             C.c_void_p(stream)), "spmm_execute")
+    _check(getattr(_lib, fn)(plan.handle, C.c_void_p(bp), ldb, C.c_void_p(cp), ldc,
+                             C.c_void_p(stream)), fn)
+
+
+def spmm_execute(plan: Plan, b, c, stream=None, ldb: int | None = None,
+                 ldc: int | None = None):
+    """C = A * B on `stream` (default: torch's current stream on C's device).
+
+    b and c are torch tensors on the plan's device, or raw device pointers
+    with ldb / ldc given."""
+    _execute("spmm_execute", plan, b, c, stream, ldb, ldc)
+
+
+def spmm_execute_noalloc(plan: Plan, b, c, stream=None, ldb: int | None = None,
+                         ldc: int | None = None):
+    """spmm_execute that allocates nothing: a WCSR plan's partial rows live in
+    the library's fixed per-GPU scratch array (calls that overlap on one GPU
+    race).  Arguments as for spmm_execute."""
+    _execute("spmm_execute_noalloc", plan, b, c, stream, ldb, ldc)
 
 
 def spmm_plan_sddmm(mat: Matrix, kd: int, dtype: int = F32, device: int = 0) -> Plan:

@@ -771,10 +771,18 @@ spmm_status_t spmm_plan_info(spmm_plan_t p, spmm_plan_info_t *info) {
 
 void spmm_plan_destroy(spmm_plan_t p) { free_plan(p); }
 
-spmm_status_t spmm_execute(spmm_plan_t p, const void *b_dev, int64_t ldb, void *c_dev,
-                           int64_t ldc, hipStream_t stream) {
-  if (!p) return fail(SPMM_ERR_INVALID_ARG, "spmm_execute: plan is NULL");
-  if (p->sddmm) return fail(SPMM_ERR_INVALID_ARG, "spmm_execute: plan is an SDDMM plan");
+}  // extern "C"
+
+namespace {
+
+// spmm_execute and spmm_execute_noalloc: the same checks and kernels; with
+// noalloc, a WCSR plan's partial rows go to the library's per-GPU scratch
+// array instead of the plan's workspace.
+spmm_status_t execute(const char *fn, spmm_plan_t p, const void *b_dev, int64_t ldb, void *c_dev,
+                      int64_t ldc, hipStream_t stream, bool noalloc) {
+  const std::string name(fn);
+  if (!p) return fail(SPMM_ERR_INVALID_ARG, name + ": plan is NULL");
+  if (p->sddmm) return fail(SPMM_ERR_INVALID_ARG, name + ": plan is an SDDMM plan");
   const Matrix &a = *p->a;
   const int64_t n = p->n;
   if (n == 0 || a.m == 0) return SPMM_OK;
@@ -783,19 +791,25 @@ spmm_status_t spmm_execute(spmm_plan_t p, const void *b_dev, int64_t ldb, void *
   const int64_t eb = bf16 ? 2 : (i8 ? 1 : 4);  // B: bf16, int8 or fp32
   const int64_t ec = bf16 ? 2 : 4;              // C: bf16, int32 or fp32
   if (!c_dev || (!b_dev && a.k > 0))
-    return fail(SPMM_ERR_INVALID_ARG, "spmm_execute: B or C is NULL");
+    return fail(SPMM_ERR_INVALID_ARG, name + ": B or C is NULL");
   if (!aligned16(b_dev) || !aligned16(c_dev) || ldb < n || ldc < n || (ldb * eb) % 16 != 0 ||
       (ldc * ec) % 16 != 0)
     return fail(SPMM_ERR_INVALID_ARG,
-                "spmm_execute: B/C must be 16-byte aligned with ld >= n and ld*elem % 16 == 0");
+                name + ": B/C must be 16-byte aligned with ld >= n and ld*elem % 16 == 0");
   // the kernels address B with 32-bit byte offsets from its start (BCSR:
   // from the first row of a block; through a row map: from row 0)
   if (a.format == SPMM_FORMAT_BCSR) {
     if (ldb > (int64_t(1) << 24) || (p->bcsr.col_perm && a.k * ldb * 2 > int64_t(UINT32_MAX)))
-      return fail(SPMM_ERR_UNSUPPORTED, "spmm_execute: ldb too large for this BCSR plan");
+      return fail(SPMM_ERR_UNSUPPORTED, name + ": ldb too large for this BCSR plan");
   } else if (a.format != SPMM_FORMAT_WCSR && p->sp24.k_pad * ldb * eb > int64_t(UINT32_MAX)) {
-    return fail(SPMM_ERR_UNSUPPORTED, "spmm_execute: k_pad * ldb * elem must be below 2^32");
+    return fail(SPMM_ERR_UNSUPPORTED, name + ": k_pad * ldb * elem must be below 2^32");
   }
+  const int64_t scratch_bytes = p->info.num_slots * n * 4;
+  if (noalloc && a.format == SPMM_FORMAT_WCSR && scratch_bytes > kNoallocScratchBytes)
+    return fail(SPMM_ERR_UNSUPPORTED,
+                name + ": the plan's partial rows need " + std::to_string(scratch_bytes) +
+                    " bytes of scratch, more than the " + std::to_string(kNoallocScratchBytes) +
+                    " the library holds per GPU; use spmm_execute");
   DeviceScope ds(p->device);
   if (ds.err != hipSuccess) return hip_fail(ds.err, "hipSetDevice");
   hipError_t e = hipSuccess;
@@ -812,6 +826,12 @@ spmm_status_t spmm_execute(spmm_plan_t p, const void *b_dev, int64_t ldb, void *
     L.ldb = ldb;
     L.C = static_cast<float *>(c_dev);
     L.ldc = ldc;
+    if (noalloc && scratch_bytes > 0) {
+      void *ptr = nullptr;
+      e = noalloc_scratch(p->device, &ptr);
+      if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress");
+      L.partial = static_cast<float *>(ptr);
+    }
     e = launch_wcsr_f32(L, stream);
   } else {
     Sp24Launch L = p->sp24;
@@ -823,6 +843,20 @@ spmm_status_t spmm_execute(spmm_plan_t p, const void *b_dev, int64_t ldb, void *
   }
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return SPMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+spmm_status_t spmm_execute(spmm_plan_t p, const void *b_dev, int64_t ldb, void *c_dev,
+                           int64_t ldc, hipStream_t stream) {
+  return execute("spmm_execute", p, b_dev, ldb, c_dev, ldc, stream, false);
+}
+
+spmm_status_t spmm_execute_noalloc(spmm_plan_t p, const void *b_dev, int64_t ldb, void *c_dev,
+                                   int64_t ldc, hipStream_t stream) {
+  return execute("spmm_execute_noalloc", p, b_dev, ldb, c_dev, ldc, stream, true);
 }
 
 spmm_status_t spmm_plan_sddmm(spmm_matrix_t a, int64_t kd, spmm_dtype_t dtype, int32_t device,

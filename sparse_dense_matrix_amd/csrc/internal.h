@@ -155,6 +155,11 @@ struct WcsrLaunch {
 };
 hipError_t launch_wcsr_f32(const WcsrLaunch &a, hipStream_t s);
 int64_t wcsr_grid(int64_t num_chunks, int64_t n);
+// Size of the per-GPU scratch array that holds a WCSR plan's partial rows in
+// spmm_execute_noalloc, and its address on `device` (which must be the
+// current device; looked up once per device, then cached).
+constexpr int64_t kNoallocScratchBytes = int64_t(32) << 20;
+hipError_t noalloc_scratch(int device, void **ptr);
 
 // Chunk descriptors of a WCSR matrix (row range of each chunk, and the
 // partial-row slots of rows split across chunks, slot_row[s] = row of slot

@@ -15,7 +15,18 @@
 //     a row cut by a chunk boundary is written as a partial row, and a second
 //     kernel adds the partial rows of each split row in chunk order.
 // No floating-point atomics: results are bitwise reproducible.
+#include <mutex>
+#include <vector>
+
 #include "internal.h"
+
+// Partial rows of split rows for spmm_execute_noalloc, which allocates
+// nothing: one fixed array per GPU, held until the process ends.  Host code
+// reaches a GPU's copy only through the address hipGetSymbolAddress returns
+// with that GPU current (the array's name on the host is not a device
+// address).  Every slot is written by wcsr_stream before wcsr_merge reads
+// it, so nothing has to be cleared between calls.
+static __device__ __align__(256) char scratch[sdm::kNoallocScratchBytes];
 
 namespace sdm {
 namespace {
@@ -197,6 +208,23 @@ hipError_t launch_v(const WcsrLaunch &a, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t noalloc_scratch(int device, void **ptr) {
+  static std::mutex mu;
+  static std::vector<void *> addr;  // per device, filled on first use
+  *ptr = nullptr;
+  if (device < 0) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr.size() <= static_cast<size_t>(device)) addr.resize(static_cast<size_t>(device) + 1, nullptr);
+  if (!addr[device]) {
+    void *a = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[device] = a;
+  }
+  *ptr = addr[device];
+  return hipSuccess;
+}
 
 int64_t wcsr_grid(int64_t num_chunks, int64_t n) {
   const int V = pick_v(n);

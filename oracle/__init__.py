@@ -17,8 +17,10 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIBRARY may point at another build of the same source (the sanitized one)
+LIB_PATH = os.environ.get("ORACLE_LIBRARY") or os.path.join(_HERE, "liboracle.so")
 _SRC = os.path.join(_HERE, "oracle.c")
+SANITIZED_LIB = os.path.join(os.path.dirname(_HERE), "_build", "sanitize", "liboracle.so")
 
 
 def build(verbose: bool = False) -> str:
@@ -31,6 +33,21 @@ def build(verbose: bool = False) -> str:
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """The same source under AddressSanitizer and UndefinedBehaviorSanitizer,
+    built with clang so that one ASan runtime serves it and the library."""
+    os.makedirs(os.path.dirname(SANITIZED_LIB), exist_ok=True)
+    tmp = SANITIZED_LIB + ".tmp"
+    cmd = ["/opt/rocm/llvm/bin/clang", "-O1", "-g", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+           "-Wall", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-fno-omit-frame-pointer", "-Wl,-rpath,/opt/rocm/llvm/lib", "-o", tmp, _SRC, "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, SANITIZED_LIB)
+    return SANITIZED_LIB
 
 
 _lib = None

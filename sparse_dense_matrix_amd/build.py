@@ -58,5 +58,51 @@ def build(verbose: bool = False, out: str = LIB, build_dir: str = BUILD_DIR) -> 
     return out
 
 
+# Host code under AddressSanitizer and UndefinedBehaviorSanitizer, for the CPU
+# tests: the packers, the ABI and the host side of every .hip file (the device
+# code is built as usual, without sanitizers).  The process that loads it must
+# preload the clang ASan runtime (asan_runtime()).
+SANITIZE = ["-O1", "-g",
+            "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+SANITIZED_LIB = os.path.join(BUILD_DIR, "sanitize", "libspmm.so")
+
+
+def asan_runtime() -> str:
+    """Path of the clang ASan runtime that matches hipcc."""
+    import glob
+    found = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not found:
+        raise RuntimeError("clang ASan runtime not found under /opt/rocm/llvm")
+    return found[-1]
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """Compile every source's host code with ASan + UBSan into SANITIZED_LIB."""
+    d = os.path.dirname(SANITIZED_LIB)
+    os.makedirs(d, exist_ok=True)
+    common = [c for c in COMMON if c != "-O3"] + SANITIZE
+
+    def comp(src):
+        obj = os.path.join(d, os.path.basename(src) + ".o")
+        lang = ["-x", "hip"] if src.endswith(".hip") else []
+        cmd = [_hipcc()] + common + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc (sanitized) failed on {src}:\n{r.stderr[-4000:]}")
+        return obj
+
+    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
+        objs = list(ex.map(comp, SOURCES))
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", SANITIZED_LIB] + objs
+    subprocess.run(cmd, check=True)
+    return SANITIZED_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--sanitize" in sys.argv:
+        print(build_sanitized(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

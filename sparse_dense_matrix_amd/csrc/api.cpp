@@ -2,6 +2,7 @@
 // upload and per-format launch dispatch.
 #include <algorithm>
 #include <cstdarg>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <new>
@@ -11,6 +12,14 @@
 namespace sdm {
 
 static thread_local std::string g_last_error;
+static thread_local int64_t g_alloc_countdown = 0;
+
+void alloc_hook_begin() {
+  const char *v = std::getenv("SPMM_TEST_FAIL_ALLOC");
+  g_alloc_countdown = v ? std::max<int64_t>(0, std::atoll(v)) : 0;
+}
+
+bool alloc_hook_fail() { return g_alloc_countdown > 0 && --g_alloc_countdown == 0; }
 
 spmm_status_t fail(spmm_status_t s, const std::string &msg) {
   g_last_error = msg;
@@ -30,7 +39,7 @@ hipError_t allow_dynamic_lds(const void *kernel, size_t bytes) {
     int device;
   };
   static std::mutex mu;
-  static std::vector<Entry> done;
+  static std::vector<Entry> done;  // not a library array: no failure hook
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -64,6 +73,12 @@ spmm_status_t guarded(F &&f) {
   }
 }
 
+// A new packed operand, owned until it is handed to the caller.
+std::unique_ptr<spmm_matrix_s> new_matrix() {
+  if (alloc_hook_fail()) throw std::bad_alloc();
+  return std::unique_ptr<spmm_matrix_s>(new spmm_matrix_s());
+}
+
 // Restores the caller's current device on scope exit.
 struct DeviceScope {
   int prev = -1;
@@ -92,10 +107,14 @@ void free_plan(spmm_plan_s *p) {
 spmm_status_t upload(spmm_plan_s *p, const void *src, size_t bytes, void **dst) {
   *dst = nullptr;
   if (bytes == 0) bytes = 16;  // keep every table pointer valid
+  p->allocations.push_back(nullptr);  // may throw; nothing is allocated yet
   void *d = nullptr;
-  hipError_t e = hipMalloc(&d, bytes);
-  if (e != hipSuccess) return hip_fail(e, "hipMalloc");
-  p->allocations.push_back(d);
+  hipError_t e = alloc_hook_fail() ? hipErrorOutOfMemory : hipMalloc(&d, bytes);
+  if (e != hipSuccess) {
+    p->allocations.pop_back();
+    return hip_fail(e, "hipMalloc");
+  }
+  p->allocations.back() = d;
   p->info.device_bytes += static_cast<int64_t>(bytes);
   if (src) {
     e = hipMemcpy(d, src, bytes, hipMemcpyHostToDevice);
@@ -106,7 +125,7 @@ spmm_status_t upload(spmm_plan_s *p, const void *src, size_t bytes, void **dst) 
 }
 
 template <class T>
-spmm_status_t upload_vec(spmm_plan_s *p, const std::vector<T> &v, T **dst) {
+spmm_status_t upload_vec(spmm_plan_s *p, const vec<T> &v, T **dst) {
   void *d = nullptr;
   spmm_status_t s = upload(p, v.empty() ? nullptr : v.data(), v.size() * sizeof(T), &d);
   *dst = static_cast<T *>(d);
@@ -120,7 +139,7 @@ spmm_status_t plan_bcsr(spmm_plan_s *p) {
     return fail(SPMM_ERR_UNSUPPORTED, "spmm_plan: BCSR kernels take 64 x 64 blocks");
   if (p->n % 8 != 0) return fail(SPMM_ERR_UNSUPPORTED, "spmm_plan: BCSR needs n % 8 == 0");
   const int64_t nnzb = static_cast<int64_t>(a.bcol_idx.size());
-  std::vector<uint16_t> frag(a.bvals.size());
+  vec<uint16_t> frag(a.bvals.size());
   for (int64_t b = 0; b < nnzb; ++b) bcsr_fragment_order(a.bvals.data() + b * 4096, frag.data() + b * 4096);
   BcsrLaunch &L = p->bcsr;
   int32_t *rp = nullptr, *ci = nullptr;
@@ -133,7 +152,7 @@ spmm_status_t plan_bcsr(spmm_plan_s *p) {
   // so the longest tiles of a column tile start first and the short ones
   // fill in behind them
   const int32_t mb = static_cast<int32_t>(a.m / 64);
-  std::vector<int32_t> sorted(static_cast<size_t>(mb));
+  vec<int32_t> sorted(static_cast<size_t>(mb));
   for (int32_t i = 0; i < mb; ++i) sorted[i] = i;
   auto blocks = [&](int32_t r) { return a.brow_ptr[r + 1] - a.brow_ptr[r]; };
   std::stable_sort(sorted.begin(), sorted.end(),
@@ -144,16 +163,16 @@ spmm_status_t plan_bcsr(spmm_plan_s *p) {
   // groups' start offsets after its mb entries.
   const BcsrSchedule sc = bcsr_schedule(a.brow_ptr.data(), mb, p->n);
   const int groups = sc.row_groups;
-  std::vector<std::vector<int32_t>> members(static_cast<size_t>(groups));
-  std::vector<int64_t> load(static_cast<size_t>(groups), 0);
+  vec<vec<int32_t>> members(static_cast<size_t>(groups));
+  vec<int64_t> load(static_cast<size_t>(groups), 0);
   for (int32_t r : sorted) {
     const size_t g = static_cast<size_t>(std::min_element(load.begin(), load.end()) - load.begin());
     members[g].push_back(r);
     load[g] += blocks(r) + 1;
   }
-  std::vector<int32_t> order;
+  vec<int32_t> order;
   order.reserve(static_cast<size_t>(mb) + 9);
-  std::vector<int32_t> seg(1, 0);
+  vec<int32_t> seg(1, 0);
   for (const auto &g : members) {
     order.insert(order.end(), g.begin(), g.end());
     seg.push_back(static_cast<int32_t>(order.size()));
@@ -194,8 +213,8 @@ spmm_status_t plan_bcsr(spmm_plan_s *p) {
 // ---- WCSR plan: chunk descriptors, split rows and their partial slots ------
 }  // namespace
 
-spmm_status_t wcsr_chunk_descriptors(const Matrix &a, std::vector<WcsrChunk> &chunks,
-                                     std::vector<int32_t> &slot_row) {
+spmm_status_t wcsr_chunk_descriptors(const Matrix &a, vec<WcsrChunk> &chunks,
+                                     vec<int32_t> &slot_row) {
   const int64_t m = a.m, W = a.window_rows;
   const int64_t C = static_cast<int64_t>(a.chunk_window.size());
   const int64_t *rp = a.row_ptr.data();
@@ -246,12 +265,12 @@ namespace {
 spmm_status_t plan_wcsr(spmm_plan_s *p) {
   const Matrix &a = *p->a;
   const int64_t C = static_cast<int64_t>(a.chunk_window.size());
-  std::vector<WcsrChunk> chunks;
-  std::vector<int32_t> slot_row;  // row of each partial slot, in slot order
+  vec<WcsrChunk> chunks;
+  vec<int32_t> slot_row;  // row of each partial slot, in slot order
   spmm_status_t st = wcsr_chunk_descriptors(a, chunks, slot_row);
   if (st != SPMM_OK) return st;
   // slots of one split row are consecutive: group them
-  std::vector<int32_t> merge_row, merge_slot;
+  vec<int32_t> merge_row, merge_slot;
   for (size_t s = 0; s < slot_row.size(); ++s) {
     if (s == 0 || slot_row[s] != slot_row[s - 1]) {
       merge_row.push_back(slot_row[s]);
@@ -301,8 +320,8 @@ spmm_status_t plan_wcsr(spmm_plan_s *p) {
 // ---- SDDMM plan: the WCSR chunks, the pattern, no workspace ----------------
 spmm_status_t plan_sddmm(spmm_plan_s *p, int64_t kd, spmm_dtype_t dtype) {
   const Matrix &a = *p->a;
-  std::vector<WcsrChunk> chunks;
-  std::vector<int32_t> slot_row;  // unused: sampled entries are independent
+  vec<WcsrChunk> chunks;
+  vec<int32_t> slot_row;  // unused: sampled entries are independent
   spmm_status_t st = wcsr_chunk_descriptors(a, chunks, slot_row);
   if (st != SPMM_OK) return st;
   SddmmLaunch &L = p->sdd;
@@ -330,7 +349,7 @@ spmm_status_t plan_sddmm_bcsr(spmm_plan_s *p, int64_t kd, bool int8) {
   const int64_t nnzb = static_cast<int64_t>(a.bcol_idx.size());
   const int G = sddmm_bcsr_group();
   // groups of up to G consecutive stored blocks of one block row
-  std::vector<int32_t> groups;
+  vec<int32_t> groups;
   for (int64_t r = 0; r + 1 < static_cast<int64_t>(a.brow_ptr.size()); ++r)
     for (int32_t b = a.brow_ptr[r]; b < a.brow_ptr[r + 1]; b += G)
       groups.insert(groups.end(),
@@ -390,8 +409,8 @@ spmm_status_t plan_24(spmm_plan_s *p) {
   const int64_t m_pad = (a.m + TM - 1) / TM * TM;
   // k = 0 gives no k-steps: the kernel then writes zeros and never reads B
   const int64_t k_pad = (k + TK - 1) / TK * TK;
-  std::vector<int8_t> v(static_cast<size_t>(m_pad * (k_pad / 2) * elem));
-  std::vector<uint8_t> mt(static_cast<size_t>(m_pad * (k_pad / 8)));
+  vec<int8_t> v(static_cast<size_t>(m_pad * (k_pad / 2) * elem));
+  vec<uint8_t> mt(static_cast<size_t>(m_pad * (k_pad / 8)));
   const void *src = bf16 ? static_cast<const void *>(a.vals24_bf16.data())
                          : static_cast<const void *>(a.vals24.data());
   sp24_tile_layout(src, a.meta24.data(), a.m, k, m_pad, k_pad, bf16, v.data(), mt.data());
@@ -415,7 +434,7 @@ spmm_status_t plan_24(spmm_plan_s *p) {
   if (slide) {
     // B row of every lifted k-row, padded with row 0 to whole k-steps (the
     // padded k-rows meet zero A values)
-    std::vector<int32_t> rows(static_cast<size_t>(k_pad), 0);
+    vec<int32_t> rows(static_cast<size_t>(k_pad), 0);
     for (int64_t j = 0; j < k; ++j) rows[j] = static_cast<int32_t>(slide_source_row(j, a.slide_group));
     int32_t *dr = nullptr;
     if ((s = upload_vec(p, rows, &dr)) != SPMM_OK) return s;
@@ -442,12 +461,12 @@ spmm_status_t plan_tvw(spmm_plan_s *p) {
                 "64 (bf16) columns");
   const int64_t ntiles = static_cast<int64_t>(a.bcol_idx.size());
   const int64_t per = a.bk / TK;
-  std::vector<int8_t> v(static_cast<size_t>(ntiles * a.bm * (a.bk / 2) * elem));
-  std::vector<uint8_t> mt(static_cast<size_t>(ntiles * a.bm * (a.bk / 8)));
+  vec<int8_t> v(static_cast<size_t>(ntiles * a.bm * (a.bk / 2) * elem));
+  vec<uint8_t> mt(static_cast<size_t>(ntiles * a.bm * (a.bk / 8)));
   const void *src = bf16 ? static_cast<const void *>(a.vals24_bf16.data())
                          : static_cast<const void *>(a.vals24.data());
   tvw_tile_layout(src, a.meta24.data(), ntiles, a.bk, bf16, v.data(), mt.data());
-  std::vector<int32_t> ptr(a.brow_ptr.size()), step(static_cast<size_t>(ntiles * per));
+  vec<int32_t> ptr(a.brow_ptr.size()), step(static_cast<size_t>(ntiles * per));
   for (size_t T = 0; T < a.brow_ptr.size(); ++T) ptr[T] = static_cast<int32_t>(a.brow_ptr[T] * per);
   for (int64_t t = 0; t < ntiles; ++t)
     for (int64_t s = 0; s < per; ++s) step[t * per + s] = static_cast<int32_t>(a.bcol_idx[t] * per + s);
@@ -504,6 +523,7 @@ const char *spmm_last_error(void) { return g_last_error.c_str(); }
 spmm_status_t spmm_pack_bcsr(int64_t m, int64_t k, int32_t block_m, int32_t block_k,
                              spmm_dtype_t dtype, const void *a_host, int64_t lda,
                              spmm_matrix_t *out) {
+  alloc_hook_begin();
   if (!out) return fail(SPMM_ERR_INVALID_ARG, "spmm_pack_bcsr: out is NULL");
   *out = nullptr;
   if (dtype != SPMM_BF16) return fail(SPMM_ERR_UNSUPPORTED, "spmm_pack_bcsr: only bf16 values");
@@ -511,20 +531,18 @@ spmm_status_t spmm_pack_bcsr(int64_t m, int64_t k, int32_t block_m, int32_t bloc
       m % block_m != 0 || k % block_k != 0 || lda < k || (m * k > 0 && !a_host))
     return fail(SPMM_ERR_INVALID_ARG, "spmm_pack_bcsr: bad shape, block, lda or pointer");
   return guarded([&]() -> spmm_status_t {
-    auto *a = new spmm_matrix_s();
+    auto a = new_matrix();
     spmm_status_t s = pack_bcsr_bf16(m, k, block_m, block_k,
                                      static_cast<const uint16_t *>(a_host), lda, *a);
-    if (s != SPMM_OK) {
-      delete a;
-      return s;
-    }
-    *out = a;
+    if (s != SPMM_OK) return s;
+    *out = a.release();
     return SPMM_OK;
   });
 }
 
 spmm_status_t spmm_pack_slide(int64_t m, int64_t k, const int8_t *a_host, int64_t lda, int32_t group,
                               spmm_matrix_t *out) {
+  alloc_hook_begin();
   if (!out) return fail(SPMM_ERR_INVALID_ARG, "spmm_pack_slide: out is NULL");
   *out = nullptr;
   // group = 2N with N >= 2; the lifted row (4(N-1) columns per group) must
@@ -534,19 +552,17 @@ spmm_status_t spmm_pack_slide(int64_t m, int64_t k, const int8_t *a_host, int64_
       (m * k > 0 && !a_host))
     return fail(SPMM_ERR_INVALID_ARG, "spmm_pack_slide: bad shape, group, lda or pointer");
   return guarded([&]() -> spmm_status_t {
-    auto *a = new spmm_matrix_s();
+    auto a = new_matrix();
     spmm_status_t s = pack_slide_i8(m, k, a_host, lda, group, *a);
-    if (s != SPMM_OK) {
-      delete a;
-      return s;
-    }
-    *out = a;
+    if (s != SPMM_OK) return s;
+    *out = a.release();
     return SPMM_OK;
   });
 }
 
 spmm_status_t spmm_pack_tvw(int64_t m, int64_t k, spmm_dtype_t dtype, const void *a_host,
                             int64_t lda, int32_t tile_m, int32_t tile_k, spmm_matrix_t *out) {
+  alloc_hook_begin();
   if (!out) return fail(SPMM_ERR_INVALID_ARG, "spmm_pack_tvw: out is NULL");
   *out = nullptr;
   if (dtype != SPMM_I8 && dtype != SPMM_BF16)
@@ -555,13 +571,10 @@ spmm_status_t spmm_pack_tvw(int64_t m, int64_t k, spmm_dtype_t dtype, const void
       tile_k % 8 != 0 || m % tile_m != 0 || k % tile_k != 0 || lda < k || (m * k > 0 && !a_host))
     return fail(SPMM_ERR_INVALID_ARG, "spmm_pack_tvw: bad shape, tile, lda or pointer");
   return guarded([&]() -> spmm_status_t {
-    auto *a = new spmm_matrix_s();
+    auto a = new_matrix();
     spmm_status_t s = pack_tvw(m, k, dtype, a_host, lda, tile_m, tile_k, *a);
-    if (s != SPMM_OK) {
-      delete a;
-      return s;
-    }
-    *out = a;
+    if (s != SPMM_OK) return s;
+    *out = a.release();
     return SPMM_OK;
   });
 }
@@ -570,6 +583,7 @@ spmm_status_t spmm_pack_bcsr_csr(int64_t m, int64_t k, spmm_dtype_t dtype,
                                  const int64_t *row_ptr, const int32_t *col_idx,
                                  const void *vals, int32_t block_m, int32_t block_k,
                                  int32_t reorder, spmm_matrix_t *out) {
+  alloc_hook_begin();
   if (!out) return fail(SPMM_ERR_INVALID_ARG, "spmm_pack_bcsr_csr: out is NULL");
   *out = nullptr;
   if (dtype != SPMM_BF16) return fail(SPMM_ERR_UNSUPPORTED, "spmm_pack_bcsr_csr: only bf16 values");
@@ -577,14 +591,11 @@ spmm_status_t spmm_pack_bcsr_csr(int64_t m, int64_t k, spmm_dtype_t dtype,
       block_k <= 0 || m % block_m != 0 || k % block_k != 0 || (reorder != 0 && reorder != 1))
     return fail(SPMM_ERR_INVALID_ARG, "spmm_pack_bcsr_csr: bad shape, block, reorder or pointer");
   return guarded([&]() -> spmm_status_t {
-    auto *a = new spmm_matrix_s();
+    auto a = new_matrix();
     spmm_status_t s = pack_bcsr_csr_bf16(m, k, row_ptr, col_idx, static_cast<const uint16_t *>(vals),
                                          block_m, block_k, reorder == 1, *a);
-    if (s != SPMM_OK) {
-      delete a;
-      return s;
-    }
-    *out = a;
+    if (s != SPMM_OK) return s;
+    *out = a.release();
     return SPMM_OK;
   });
 }
@@ -593,6 +604,7 @@ spmm_status_t spmm_pack_wcsr(int64_t m, int64_t k, spmm_dtype_t dtype,
                              const int64_t *row_ptr, const int32_t *col_idx,
                              const void *vals, int32_t window_rows,
                              int64_t max_chunk_nnz, spmm_matrix_t *out) {
+  alloc_hook_begin();
   if (!out) return fail(SPMM_ERR_INVALID_ARG, "spmm_pack_wcsr: out is NULL");
   *out = nullptr;
   if (dtype != SPMM_F32) return fail(SPMM_ERR_UNSUPPORTED, "spmm_pack_wcsr: only fp32 values");
@@ -606,20 +618,18 @@ spmm_status_t spmm_pack_wcsr(int64_t m, int64_t k, spmm_dtype_t dtype,
     window_rows = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(16, m / 16384)));
   if (max_chunk_nnz == 0) max_chunk_nnz = 512;
   return guarded([&]() -> spmm_status_t {
-    auto *a = new spmm_matrix_s();
+    auto a = new_matrix();
     spmm_status_t s = pack_wcsr_f32(m, k, row_ptr, col_idx, static_cast<const float *>(vals),
                                     window_rows, max_chunk_nnz, *a);
-    if (s != SPMM_OK) {
-      delete a;
-      return s;
-    }
-    *out = a;
+    if (s != SPMM_OK) return s;
+    *out = a.release();
     return SPMM_OK;
   });
 }
 
 spmm_status_t spmm_pack_24(int64_t m, int64_t k, spmm_dtype_t dtype, const void *a_host,
                            int64_t lda, spmm_matrix_t *out) {
+  alloc_hook_begin();
   if (!out) return fail(SPMM_ERR_INVALID_ARG, "spmm_pack_24: out is NULL");
   *out = nullptr;
   if (dtype != SPMM_I8 && dtype != SPMM_BF16)
@@ -628,13 +638,10 @@ spmm_status_t spmm_pack_24(int64_t m, int64_t k, spmm_dtype_t dtype, const void 
       (m * k > 0 && !a_host))
     return fail(SPMM_ERR_INVALID_ARG, "spmm_pack_24: bad shape (k % 8 == 0 needed), lda or pointer");
   return guarded([&]() -> spmm_status_t {
-    auto *a = new spmm_matrix_s();
+    auto a = new_matrix();
     spmm_status_t s = pack_24(m, k, dtype, a_host, lda, *a);
-    if (s != SPMM_OK) {
-      delete a;
-      return s;
-    }
-    *out = a;
+    if (s != SPMM_OK) return s;
+    *out = a.release();
     return SPMM_OK;
   });
 }
@@ -711,6 +718,7 @@ void spmm_matrix_destroy(spmm_matrix_t a) { release(a); }
 
 spmm_status_t spmm_plan(spmm_matrix_t a, int64_t n, spmm_dtype_t b_dtype, spmm_dtype_t c_dtype,
                         int32_t device, spmm_plan_t *out) {
+  alloc_hook_begin();
   if (!out) return fail(SPMM_ERR_INVALID_ARG, "spmm_plan: out is NULL");
   *out = nullptr;
   if (!a || n < 0 || n > INT32_MAX) return fail(SPMM_ERR_INVALID_ARG, "spmm_plan: bad matrix or n");
@@ -730,6 +738,7 @@ spmm_status_t spmm_plan(spmm_matrix_t a, int64_t n, spmm_dtype_t b_dtype, spmm_d
   return guarded([&]() -> spmm_status_t {
     DeviceScope ds(device);
     if (ds.err != hipSuccess) return hip_fail(ds.err, "hipSetDevice");
+    if (alloc_hook_fail()) throw std::bad_alloc();
     auto *p = new spmm_plan_s();
     retain(a);
     p->a = a;
@@ -861,6 +870,7 @@ spmm_status_t spmm_execute_noalloc(spmm_plan_t p, const void *b_dev, int64_t ldb
 
 spmm_status_t spmm_plan_sddmm(spmm_matrix_t a, int64_t kd, spmm_dtype_t dtype, int32_t device,
                               spmm_plan_t *out) {
+  alloc_hook_begin();
   if (!out) return fail(SPMM_ERR_INVALID_ARG, "spmm_plan_sddmm: out is NULL");
   *out = nullptr;
   if (!a || kd < 0 || kd > INT32_MAX) return fail(SPMM_ERR_INVALID_ARG, "spmm_plan_sddmm: bad matrix or kd");
@@ -882,6 +892,7 @@ spmm_status_t spmm_plan_sddmm(spmm_matrix_t a, int64_t kd, spmm_dtype_t dtype, i
   return guarded([&]() -> spmm_status_t {
     DeviceScope ds(device);
     if (ds.err != hipSuccess) return hip_fail(ds.err, "hipSetDevice");
+    if (alloc_hook_fail()) throw std::bad_alloc();
     auto *p = new spmm_plan_s();
     retain(a);
     p->a = a;

@@ -5,6 +5,8 @@
 
 #include <atomic>
 #include <cstdint>
+#include <memory>
+#include <new>
 #include <string>
 #include <vector>
 
@@ -20,6 +22,39 @@ spmm_status_t hip_fail(hipError_t e, const char *what);
 void clear_error();
 
 // ---------------------------------------------------------------------------
+// forced allocation failures (tests)
+// ---------------------------------------------------------------------------
+// When the environment variable SPMM_TEST_FAIL_ALLOC holds n > 0 at the start
+// of an ABI call that allocates (packing, planning), the n-th allocation of
+// that call fails as it would when memory runs out: a host allocation throws
+// std::bad_alloc, a device allocation reports hipErrorOutOfMemory.  Tests walk
+// n = 1, 2, ... to check that every failure returns SPMM_ERR_OUT_OF_MEMORY,
+// leaves *out NULL and leaks nothing.  Unset or 0: no effect.
+void alloc_hook_begin();
+bool alloc_hook_fail();  // true when this allocation is the one to fail
+
+// Allocator of every host array the library owns: std::allocator behind the
+// failure hook.
+template <class T>
+struct HostAlloc {
+  using value_type = T;
+  HostAlloc() = default;
+  template <class U>
+  HostAlloc(const HostAlloc<U> &) {}
+  T *allocate(size_t n) {
+    if (alloc_hook_fail()) throw std::bad_alloc();
+    return std::allocator<T>().allocate(n);
+  }
+  void deallocate(T *p, size_t n) { std::allocator<T>().deallocate(p, n); }
+  template <class U>
+  bool operator==(const HostAlloc<U> &) const { return true; }
+  template <class U>
+  bool operator!=(const HostAlloc<U> &) const { return false; }
+};
+template <class T>
+using vec = std::vector<T, HostAlloc<T>>;
+
+// ---------------------------------------------------------------------------
 // packed operand (host, canonical arrays)
 // ---------------------------------------------------------------------------
 struct Matrix {
@@ -29,11 +64,11 @@ struct Matrix {
   int64_t m = 0, k = 0, nnz = 0;
   // BCSR
   int32_t bm = 0, bk = 0;
-  std::vector<int32_t> brow_ptr, bcol_idx;
-  std::vector<uint16_t> bvals;
+  vec<int32_t> brow_ptr, bcol_idx;
+  vec<uint16_t> bvals;
   // BCSR of a permuted CSR matrix: original row of each row / original
   // column of each column of the packed matrix (empty: original order)
-  std::vector<int32_t> row_perm, col_perm;
+  vec<int32_t> row_perm, col_perm;
   // sliding-window 2:4 ((2N-2):2N weights): group width 2N; vals24 / meta24
   // hold the lifted 2:4 matrix of m x k_lift columns
   int32_t slide_group = 0;
@@ -41,17 +76,17 @@ struct Matrix {
   // WCSR
   int32_t window_rows = 0;
   int64_t max_chunk_nnz = 0;
-  std::vector<int64_t> row_ptr;
-  std::vector<int32_t> col_idx;
-  std::vector<float> vals;
-  std::vector<int32_t> chunk_window;
-  std::vector<int64_t> chunk_begin;
+  vec<int64_t> row_ptr;
+  vec<int32_t> col_idx;
+  vec<float> vals;
+  vec<int32_t> chunk_window;
+  vec<int64_t> chunk_begin;
   // 2:4 (and the stored tiles of tile-vector-wise: brow_ptr / bcol_idx over
   // tiles of bm x bk, vals24 / meta24 tile after tile); bf16 values go to
   // vals24_bf16 instead of vals24
-  std::vector<int8_t> vals24;
-  std::vector<uint16_t> vals24_bf16;
-  std::vector<uint8_t> meta24;
+  vec<int8_t> vals24;
+  vec<uint16_t> vals24_bf16;
+  vec<uint8_t> meta24;
 };
 
 void retain(Matrix *a);
@@ -164,8 +199,8 @@ hipError_t noalloc_scratch(int device, void **ptr);
 // Chunk descriptors of a WCSR matrix (row range of each chunk, and the
 // partial-row slots of rows split across chunks, slot_row[s] = row of slot
 // s in slot order).  Fails only on an internal inconsistency.
-spmm_status_t wcsr_chunk_descriptors(const Matrix &a, std::vector<WcsrChunk> &chunks,
-                                     std::vector<int32_t> &slot_row);
+spmm_status_t wcsr_chunk_descriptors(const Matrix &a, vec<WcsrChunk> &chunks,
+                                     vec<int32_t> &slot_row);
 
 struct SddmmLaunch {
   const WcsrChunk *chunks;
@@ -256,7 +291,7 @@ struct spmm_plan_s {
   int32_t device = 0;
   int64_t n = 0;
   spmm_plan_info_t info{};
-  std::vector<void *> allocations;
+  sdm::vec<void *> allocations;
   sdm::BcsrLaunch bcsr{};
   sdm::WcsrLaunch wcsr{};
   sdm::Sp24Launch sp24{};

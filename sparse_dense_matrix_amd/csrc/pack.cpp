@@ -28,7 +28,7 @@ spmm_status_t pack_bcsr_bf16(int64_t m, int64_t k, int32_t bm, int32_t bk,
   out.bk = bk;
   out.brow_ptr.assign(mb + 1, 0);
   out.bcol_idx.clear();
-  std::vector<uint8_t> marked(kb);
+  vec<uint8_t> marked(kb);
   for (int64_t br = 0; br < mb; ++br) {
     std::fill(marked.begin(), marked.end(), 0);
     for (int64_t i = br * bm; i < (br + 1) * bm; ++i) {
@@ -138,8 +138,8 @@ namespace {
 
 // lexicographic order of variable-length sorted lists, ties by index
 struct ListOrder {
-  const std::vector<int64_t> &ptr;
-  const std::vector<int32_t> &val;
+  const vec<int64_t> &ptr;
+  const vec<int32_t> &val;
   bool operator()(int32_t a, int32_t b) const {
     const int32_t *pa = val.data() + ptr[a], *ea = val.data() + ptr[a + 1];
     const int32_t *pb = val.data() + ptr[b], *eb = val.data() + ptr[b + 1];
@@ -152,9 +152,9 @@ struct ListOrder {
 
 // blocks a permuted CSR pattern occupies (newcol[c]: position of column c)
 int64_t count_blocks(int64_t m, const int64_t *row_ptr, const int32_t *col_idx,
-                     const std::vector<int32_t> &row_perm, const std::vector<int32_t> &newcol,
+                     const vec<int32_t> &row_perm, const vec<int32_t> &newcol,
                      int32_t bm, int32_t bk, int64_t kb) {
-  std::vector<int64_t> seen(kb, -1);
+  vec<int64_t> seen(kb, -1);
   int64_t blocks = 0;
   for (int64_t ip = 0; ip < m; ++ip) {
     const int64_t i = row_perm.empty() ? ip : row_perm[ip];
@@ -171,28 +171,28 @@ int64_t count_blocks(int64_t m, const int64_t *row_ptr, const int32_t *col_idx,
 }
 
 void cluster_order(int64_t m, int64_t k, const int64_t *row_ptr, const int32_t *col_idx,
-                   int32_t bk, std::vector<int32_t> &row_perm, std::vector<int32_t> &col_perm) {
+                   int32_t bk, vec<int32_t> &row_perm, vec<int32_t> &col_perm) {
   const int64_t nnz = row_ptr[m];
   // 1. columns by their row lists (a CSC view; rows come out ascending)
-  std::vector<int64_t> cptr(k + 1, 0);
+  vec<int64_t> cptr(k + 1, 0);
   for (int64_t p = 0; p < nnz; ++p) ++cptr[col_idx[p] + 1];
   for (int64_t c = 0; c < k; ++c) cptr[c + 1] += cptr[c];
-  std::vector<int32_t> crow(nnz);
+  vec<int32_t> crow(nnz);
   {
-    std::vector<int64_t> fill(cptr.begin(), cptr.end() - 1);
+    vec<int64_t> fill(cptr.begin(), cptr.end() - 1);
     for (int64_t i = 0; i < m; ++i)
       for (int64_t p = row_ptr[i]; p < row_ptr[i + 1]; ++p) crow[fill[col_idx[p]]++] = static_cast<int32_t>(i);
   }
   col_perm.resize(k);
   for (int64_t c = 0; c < k; ++c) col_perm[c] = static_cast<int32_t>(c);
   std::sort(col_perm.begin(), col_perm.end(), ListOrder{cptr, crow});
-  std::vector<int32_t> newcol(k);
+  vec<int32_t> newcol(k);
   for (int64_t j = 0; j < k; ++j) newcol[col_perm[j]] = static_cast<int32_t>(j);
   // 2. rows by their sorted, distinct block columns under the new order
-  std::vector<int64_t> rptr(m + 1, 0);
-  std::vector<int32_t> rblk;
+  vec<int64_t> rptr(m + 1, 0);
+  vec<int32_t> rblk;
   rblk.reserve(nnz);
-  std::vector<int32_t> tmp;
+  vec<int32_t> tmp;
   for (int64_t i = 0; i < m; ++i) {
     tmp.clear();
     for (int64_t p = row_ptr[i]; p < row_ptr[i + 1]; ++p) tmp.push_back(newcol[col_idx[p]] / bk);
@@ -214,7 +214,7 @@ spmm_status_t pack_bcsr_csr_bf16(int64_t m, int64_t k, const int64_t *row_ptr,
   spmm_status_t st = check_csr("spmm_pack_bcsr_csr", m, k, row_ptr, col_idx, vals);
   if (st != SPMM_OK) return st;
   const int64_t mb = m / bm, kb = k / bk;
-  std::vector<int32_t> row_perm, col_perm, newcol;
+  vec<int32_t> row_perm, col_perm, newcol;
   if (reorder && row_ptr[m] > 0) {
     cluster_order(m, k, row_ptr, col_idx, bk, row_perm, col_perm);
     newcol.resize(k);
@@ -239,8 +239,8 @@ spmm_status_t pack_bcsr_csr_bf16(int64_t m, int64_t k, const int64_t *row_ptr,
   out.bcol_idx.clear();
   out.bvals.clear();
   const int64_t belems = static_cast<int64_t>(bm) * bk;
-  std::vector<int32_t> slot(kb, -1);  // block column -> block index within the block row
-  std::vector<int32_t> cols;
+  vec<int32_t> slot(kb, -1);  // block column -> block index within the block row
+  vec<int32_t> cols;
   for (int64_t br = 0; br < mb; ++br) {
     cols.clear();
     for (int64_t ip = br * bm; ip < (br + 1) * bm; ++ip) {
@@ -318,7 +318,7 @@ static void prune_row(const T *row, int64_t len, T *v, uint8_t *mt) {
 }
 
 template <class V>
-static void pack_24_t(int64_t m, int64_t k, const V *a, int64_t lda, std::vector<V> &vals,
+static void pack_24_t(int64_t m, int64_t k, const V *a, int64_t lda, vec<V> &vals,
                       Matrix &out) {
   vals.assign(static_cast<size_t>(m * (k / 2)), 0);
   out.meta24.assign(static_cast<size_t>(m * (k / 8)), 0);
@@ -373,10 +373,10 @@ spmm_status_t pack_slide_i8(int64_t m, int64_t k, const int8_t *a, int64_t lda, 
   out.nnz = m * (k_lift / 2);
   out.vals24.assign(static_cast<size_t>(m * (k_lift / 2)), 0);
   out.meta24.assign(static_cast<size_t>(m * (k_lift / 8)), 0);
-  std::vector<int> rank_key(group);
-  std::vector<int8_t> lifted(static_cast<size_t>(4 * windows));
-  std::vector<int> wcount(windows);
-  std::vector<uint8_t> taken(4 * windows);
+  vec<int> rank_key(group);
+  vec<int8_t> lifted(static_cast<size_t>(4 * windows));
+  vec<int> wcount(windows);
+  vec<uint8_t> taken(4 * windows);
   for (int64_t i = 0; i < m; ++i) {
     const int8_t *row = a + i * lda;
     int8_t *v = out.vals24.data() + i * (k_lift / 2);
@@ -434,7 +434,7 @@ spmm_status_t pack_slide_i8(int64_t m, int64_t k, const int8_t *a, int64_t lda, 
 // ---------------------------------------------------------------------------
 template <class V>
 static spmm_status_t pack_tvw_t(int64_t m, int64_t k, const V *a, int64_t lda, int32_t tm,
-                                int32_t tk, std::vector<V> &vals, Matrix &out) {
+                                int32_t tk, vec<V> &vals, Matrix &out) {
   const int64_t mt = m / tm, kt = k / tk;
   out.format = SPMM_FORMAT_TVW;
   out.m = m;

@@ -156,7 +156,8 @@ def test_pack_24_full_config(S, orc):
 
 
 def test_pack_bcsr_full_configs(S, orc):
-    for name in ("bcsr_4096_b64_90",):
+    # the 4096 case and the 18944 x 3584 prefill layer, bit for bit
+    for name in ("bcsr_4096_b64_90", "bcsr_prefill_18944x3584"):
         w = synth.WORKLOADS[name]
         a = synth.make_a(w)["dense"]
         M = S.spmm_pack_bcsr(a, 64, 64)
@@ -165,6 +166,28 @@ def test_pack_bcsr_full_configs(S, orc):
         np.testing.assert_array_equal(S.spmm_matrix_array(M, S.ARRAY_ROW_PTR), rp)
         np.testing.assert_array_equal(S.spmm_matrix_array(M, S.ARRAY_COL_IDX), ci)
         np.testing.assert_array_equal(S.spmm_matrix_array(M, S.ARRAY_VALS), v.ravel())
+
+
+def test_pack_wcsr_full_config(S, orc):
+    # the 10^6-row power-law CSR at the bench's window shape (W = 16 rows, at
+    # most T = 512 entries per chunk): the CSR copy and both chunk tables, bit
+    # for bit
+    w = synth.WORKLOADS["csr_powerlaw_1m"]
+    a = synth.make_a(w)
+    M = S.spmm_pack_wcsr(w.m, w.k, a["row_ptr"], a["col_idx"], a["vals"], 16, 512)
+    info = S.spmm_matrix_info(M)
+    assert (info["window_rows"], info["max_chunk_nnz"]) == (16, 512)
+    cw, cb = orc.wcsr_chunks(w.m, a["row_ptr"], 16, 512)
+    assert info["num_chunks"] == len(cw) and len(cw) > w.m // 16
+    np.testing.assert_array_equal(S.spmm_matrix_array(M, S.ARRAY_CHUNK_WINDOW), cw)
+    np.testing.assert_array_equal(S.spmm_matrix_array(M, S.ARRAY_CHUNK_BEGIN), cb)
+    np.testing.assert_array_equal(S.spmm_matrix_array(M, S.ARRAY_ROW_PTR), a["row_ptr"])
+    np.testing.assert_array_equal(S.spmm_matrix_array(M, S.ARRAY_COL_IDX), a["col_idx"])
+    np.testing.assert_array_equal(S.spmm_matrix_array(M, S.ARRAY_VALS).view(np.uint32),
+                                  np.asarray(a["vals"], np.float32).view(np.uint32))
+    # the packer's default shape is the same for this matrix
+    D = S.spmm_pack_wcsr(w.m, w.k, a["row_ptr"], a["col_idx"], a["vals"])
+    assert S.spmm_matrix_info(D)["num_chunks"] == len(cw)
 
 
 # ---------------------------------------------------------------------------

@@ -208,7 +208,9 @@ __device__ __forceinline__ typename E::Acc mma(i32x4 a, i32x8 b, typename E::Acc
 // kMap: slab k-row j multiplies B row b_rows[j] (sliding-window A, whose
 // lifted k-rows repeat B's rows; the table is padded with row 0 to whole
 // k-steps).  Otherwise slab k-row j multiplies B row j.
-template <class E, int kN, bool kTiles, bool kMap>
+// kRagged: k is not a whole number of k-steps (plain 2:4 only); the last
+// step's slab rows past k are then zeroed in LDS before use.
+template <class E, int kN, bool kTiles, bool kMap, bool kRagged>
 __device__ __forceinline__ void sp24_body(
     const char *__restrict__ vals, const uint8_t *__restrict__ meta,
     const int32_t *__restrict__ tile_ptr, const int32_t *__restrict__ tile_step, int64_t m,
@@ -306,20 +308,13 @@ __device__ __forceinline__ void sp24_body(
         for (int j = 0; j < kRPL; ++j) row |= trow[kRPL * i + j] & -(q == j);
         off = static_cast<uint32_t>(row * ldb_bytes) + b_off[i];
       } else {
+        // k-rows past k (the last step when k is not a whole number of
+        // steps) are read from row 0 and overwritten with zeros once they
+        // have landed (see the main loop)
         const int64_t krow0 = kstep(ks) * kTK;
-        off = static_cast<uint32_t>(krow0 * ldb_bytes) + b_off[i];
-        if (krow0 + kTK > k) {
-          // the last step of a k that is not a whole number of steps: slab
-          // k-rows past k are filled with zeros instead of being loaded, so
-          // the zero-padded A values meet zeros (0 * Inf would be NaN)
-          const int r = (wave * kBL + i) * G::kRowsPerLoad + lane / G::kPieces;
-          const uint32_t dst = (wave * kBL + i) * 1024 + lane * 16;
-          if (krow0 + r >= k) {
-            *reinterpret_cast<i32x4 *>(lds + stage * kStageBytes + kAVBytes + kAMBytes + dst) =
-                i32x4{0, 0, 0, 0};
-            return;
-          }
-        }
+        const int r = (wave * kBL + i) * G::kRowsPerLoad + lane / G::kPieces;
+        off = krow0 + r < k ? static_cast<uint32_t>(krow0 * ldb_bytes) + b_off[i]
+                            : b_off[i] - static_cast<uint32_t>(r * ldb_bytes);
       }
       load_lds16(sb + kAVBytes + kAMBytes + (wave * kBL + i) * 1024, B, off);
     }
@@ -348,6 +343,18 @@ __device__ __forceinline__ void sp24_body(
     static_assert(kStages == 2, "one k-step in flight");
     wait_vm<0>();
     barrier();  // ... for every wave; and the stage of step ks-1 is free
+    if constexpr (kRagged) {
+      if (ks == ksteps - 1) {
+        // the slab rows past k hold copies of B's row 0; zero them so the
+        // zero-padded A values meet zeros (0 * Inf would give NaN in bf16)
+        char *tail = lds + (ks % kStages) * kStageBytes + kAVBytes + kAMBytes;
+        const int r0 = static_cast<int>(k - (ksteps - 1) * kTK);
+        for (int o = r0 * G::kBRow + tid * 16; o < G::kBBytes; o += T::kThreads * 16)
+          *reinterpret_cast<i32x4 *>(tail + o) = i32x4{0, 0, 0, 0};
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the zeros are written
+        barrier();
+      }
+    }
     // The loads of step ks+kStages-1 go out first: inline asm between the
     // LDS reads and the MFMAs would make the compiler wait for every read
     // before it.
@@ -451,14 +458,14 @@ __device__ __forceinline__ void sp24_body(
       const int32_t *__restrict__ b_rows
 #define SP24_PASS vals, meta, tile_ptr, tile_step, m, k, n, k_pad, mtiles, ntiles, tiles, per_xcd, B, ldb, C, ldc, b_rows
 
-template <int kN, bool kTiles, bool kMap>
+template <int kN, bool kTiles, bool kMap, bool kRagged>
 __global__ __launch_bounds__(Tile<kN>::kThreads) void sp24_i8_smfmac(SP24_ARGS) {
-  sp24_body<I8, kN, kTiles, kMap>(SP24_PASS);
+  sp24_body<I8, kN, kTiles, kMap, kRagged>(SP24_PASS);
 }
 
-template <int kN, bool kTiles>
+template <int kN, bool kTiles, bool kRagged>
 __global__ __launch_bounds__(Tile<kN>::kThreads) void sp24_bf16_smfmac(SP24_ARGS) {
-  sp24_body<Bf16, kN, kTiles, false>(SP24_PASS);
+  sp24_body<Bf16, kN, kTiles, false, kRagged>(SP24_PASS);
 }
 
 #undef SP24_ARGS
@@ -528,7 +535,7 @@ void tvw_layout(const char *tile_vals, const uint8_t *tile_meta, int64_t ntiles,
                     meta_tiled + (t * per + s) * G::kAMBytes);
 }
 
-template <class E, int kN, bool kTiles, bool kMap>
+template <class E, int kN, bool kTiles, bool kMap, bool kRagged = false>
 hipError_t launch(const Sp24Launch &a, hipStream_t s) {
   using G = Geo<E, kN>;
   const int64_t mtiles = (a.m + kTM - 1) / kTM;
@@ -538,8 +545,8 @@ hipError_t launch(const Sp24Launch &a, hipStream_t s) {
   if (tiles > INT32_MAX / 2 || a.k_pad * a.ldb * E::kElem > UINT32_MAX)
     return hipErrorInvalidValue;
   auto kernel = [] {
-    if constexpr (E::kElem == 1) return sp24_i8_smfmac<kN, kTiles, kMap>;
-    else return sp24_bf16_smfmac<kN, kTiles>;
+    if constexpr (E::kElem == 1) return sp24_i8_smfmac<kN, kTiles, kMap, kRagged>;
+    else return sp24_bf16_smfmac<kN, kTiles, kRagged>;
   }();
   hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(kernel), G::kLdsBytes);
   if (e != hipSuccess) return e;
@@ -587,8 +594,13 @@ int64_t sp24_grid(int64_t m, int64_t n, int tn) {
 namespace {
 template <int kN>
 hipError_t launch_n(const Sp24Launch &a, hipStream_t s) {
-  if (a.bf16) return a.tile_ptr ? launch<Bf16, kN, true, false>(a, s) : launch<Bf16, kN, false, false>(a, s);
-  return a.tile_ptr ? launch<I8, kN, true, false>(a, s) : launch<I8, kN, false, false>(a, s);
+  const bool ragged = a.k_pad > a.k;  // plain 2:4 only: a tile table keeps whole steps
+  if (a.bf16) {
+    if (a.tile_ptr) return launch<Bf16, kN, true, false>(a, s);
+    return ragged ? launch<Bf16, kN, false, false, true>(a, s) : launch<Bf16, kN, false, false>(a, s);
+  }
+  if (a.tile_ptr) return launch<I8, kN, true, false>(a, s);
+  return ragged ? launch<I8, kN, false, false, true>(a, s) : launch<I8, kN, false, false>(a, s);
 }
 }  // namespace
 

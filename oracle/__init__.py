@@ -83,6 +83,7 @@ def lib():
             "orc_gemm_f64": (None, [i64, i64, i64, P, P, P]),
             "orc_gemm_i8": (None, [i64, i64, i64, P, P, P]),
             "orc_num_threads": (C.c_int, []),
+            "orc_reorder_perms": (C.c_int, [i64, i64, P, P, i32, i32, P, P, P, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -277,6 +278,19 @@ def sddmm_bcsr(bm, bk, row_ptr, col_idx, X, Y, blocks=None):
     lib().orc_sddmm_bcsr_bf16(bm, bk, _p(rp), _p(ci), nbrows, _p(X), X.shape[1], _p(Y),
                               Y.shape[1], kd, len(blocks), _p(blocks), _p(out))
     return out
+
+
+# ---- row/column permutation before BCSR --------------------------------------
+def reorder_perms(m, k, row_ptr, col_idx, bm, bk):
+    """(kept, row_perm int32[m], col_perm int32[k], blocks_before, blocks_after)
+    of the permutation read in oracle.h (identity arrays when not kept)."""
+    rp, ci = _c(row_ptr, np.int64), _c(col_idx, np.int32)
+    rperm = np.zeros(max(m, 1), np.int32)
+    cperm = np.zeros(max(k, 1), np.int32)
+    before, after = C.c_int64(), C.c_int64()
+    kept = lib().orc_reorder_perms(m, k, _p(rp), _p(ci), bm, bk, _p(rperm), _p(cperm),
+                                   C.byref(before), C.byref(after))
+    return bool(kept), rperm[:m], cperm[:k], before.value, after.value
 
 
 # ---- brute force -------------------------------------------------------------

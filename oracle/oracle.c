@@ -439,3 +439,106 @@ void orc_gemm_i8(int64_t m, int64_t k, int64_t n, const int8_t *A, const int8_t 
       C[i * n + j] = s;
     }
 }
+
+/* ---- row/column permutation before BCSR (see oracle.h) ----------------- */
+
+/* lexicographic comparison of two ascending lists; a prefix comes first */
+static int orc_list_less(const int32_t *a, int64_t na, const int32_t *b, int64_t nb) {
+  for (int64_t t = 0; t < na && t < nb; ++t)
+    if (a[t] != b[t]) return a[t] < b[t];
+  return na < nb;
+}
+
+/* stable insertion sort of ids 0..n-1 by their lists (list of id i:
+ * val[ptr[i] .. ptr[i+1])); equal lists keep ascending id */
+static void orc_order_by_lists(int64_t n, const int64_t *ptr, const int32_t *val, int32_t *order) {
+  for (int64_t i = 0; i < n; ++i) {
+    int64_t j = i;
+    while (j > 0 && orc_list_less(val + ptr[i], ptr[i + 1] - ptr[i], val + ptr[order[j - 1]],
+                                  ptr[order[j - 1] + 1] - ptr[order[j - 1]])) {
+      order[j] = order[j - 1];
+      --j;
+    }
+    order[j] = (int32_t)i;
+  }
+}
+
+/* distinct (block row, block column) pairs of the pattern with row i placed
+ * at rowpos[i] and column j at colpos[j] */
+static int64_t orc_count_blocks(int64_t m, int64_t k, const int64_t *row_ptr, const int32_t *col_idx,
+                                const int32_t *rowpos, const int32_t *colpos, int32_t bm, int32_t bk) {
+  const int64_t mb = (m + bm - 1) / bm, kb = (k + bk - 1) / bk;
+  unsigned char *mask = (unsigned char *)calloc((size_t)(mb * kb > 0 ? mb * kb : 1), 1);
+  int64_t count = 0;
+  for (int64_t i = 0; i < m; ++i)
+    for (int64_t p = row_ptr[i]; p < row_ptr[i + 1]; ++p) {
+      const int64_t cell = (rowpos[i] / bm) * kb + colpos[col_idx[p]] / bk;
+      if (!mask[cell]) {
+        mask[cell] = 1;
+        ++count;
+      }
+    }
+  free(mask);
+  return count;
+}
+
+int orc_reorder_perms(int64_t m, int64_t k, const int64_t *row_ptr, const int32_t *col_idx,
+                      int32_t bm, int32_t bk, int32_t *row_perm, int32_t *col_perm,
+                      int64_t *blocks_before, int64_t *blocks_after) {
+  const int64_t nnz = row_ptr[m];
+  int32_t *ident_r = (int32_t *)calloc((size_t)(m > 0 ? m : 1), sizeof(int32_t));
+  int32_t *ident_c = (int32_t *)calloc((size_t)(k > 0 ? k : 1), sizeof(int32_t));
+  for (int64_t i = 0; i < m; ++i) ident_r[i] = (int32_t)i;
+  for (int64_t j = 0; j < k; ++j) ident_c[j] = (int32_t)j;
+  *blocks_before = orc_count_blocks(m, k, row_ptr, col_idx, ident_r, ident_c, bm, bk);
+  *blocks_after = *blocks_before;
+  int kept = 0;
+  for (int64_t i = 0; i < m; ++i) row_perm[i] = (int32_t)i;
+  for (int64_t j = 0; j < k; ++j) col_perm[j] = (int32_t)j;
+  if (nnz > 0) {
+    /* 1. each column's rows, ascending: scan the rows in order */
+    int64_t *cptr = (int64_t *)calloc((size_t)(k + 1), sizeof(int64_t));
+    int32_t *crow = (int32_t *)calloc((size_t)nnz, sizeof(int32_t));
+    for (int64_t j = 0; j < k; ++j) {
+      cptr[j + 1] = cptr[j];
+      for (int64_t i = 0; i < m; ++i)
+        for (int64_t p = row_ptr[i]; p < row_ptr[i + 1]; ++p)
+          if (col_idx[p] == j) crow[cptr[j + 1]++] = (int32_t)i;
+    }
+    int32_t *corder = (int32_t *)malloc(sizeof(int32_t) * (size_t)k);
+    orc_order_by_lists(k, cptr, crow, corder);
+    int32_t *colpos = (int32_t *)malloc(sizeof(int32_t) * (size_t)k);
+    for (int64_t jn = 0; jn < k; ++jn) colpos[corder[jn]] = (int32_t)jn;
+    /* 2. each row's distinct block columns under the new column order,
+     * ascending: walk the block columns in order and keep those the row
+     * touches */
+    const int64_t kb = (k + bk - 1) / bk;
+    int64_t *rptr = (int64_t *)calloc((size_t)(m + 1), sizeof(int64_t));
+    int32_t *rblk = (int32_t *)calloc((size_t)nnz, sizeof(int32_t));
+    for (int64_t i = 0; i < m; ++i) {
+      rptr[i + 1] = rptr[i];
+      for (int64_t c = 0; c < kb; ++c) {
+        int touches = 0;
+        for (int64_t p = row_ptr[i]; p < row_ptr[i + 1]; ++p)
+          if (colpos[col_idx[p]] / bk == c) touches = 1;
+        if (touches) rblk[rptr[i + 1]++] = (int32_t)c;
+      }
+    }
+    int32_t *rorder = (int32_t *)malloc(sizeof(int32_t) * (size_t)m);
+    orc_order_by_lists(m, rptr, rblk, rorder);
+    int32_t *rowpos = (int32_t *)malloc(sizeof(int32_t) * (size_t)m);
+    for (int64_t in = 0; in < m; ++in) rowpos[rorder[in]] = (int32_t)in;
+    const int64_t after = orc_count_blocks(m, k, row_ptr, col_idx, rowpos, colpos, bm, bk);
+    if (after < *blocks_before) {
+      kept = 1;
+      *blocks_after = after;
+      for (int64_t i = 0; i < m; ++i) row_perm[i] = rorder[i];
+      for (int64_t j = 0; j < k; ++j) col_perm[j] = corder[j];
+    }
+    free(cptr); free(crow); free(corder); free(colpos);
+    free(rptr); free(rblk); free(rorder); free(rowpos);
+  }
+  free(ident_r);
+  free(ident_c);
+  return kept;
+}

@@ -146,6 +146,23 @@ void orc_gemm_i8(int64_t m, int64_t k, int64_t n, const int8_t *A, const int8_t 
 /* Number of OpenMP threads the reference loops use. */
 int orc_num_threads(void);
 
+/* ---- row/column permutation before BCSR [DP: block-sparse SpMM on tensor
+ * cores for unstructured matrices; the goal named there is fewer nonzero
+ * blocks, the method below is this build's reading of it] ----------------
+ * For a CSR pattern (m x k): every column's list of rows, ascending; columns
+ * ordered by those lists compared lexicographically (a list that is a prefix
+ * of another comes first, so empty columns lead; equal lists by column
+ * index).  Then every row's list of distinct block columns (bk wide) under the
+ * new column order, ascending; rows ordered the same way.  The permutation is
+ * kept only when the permuted matrix occupies fewer bm x bk blocks than the
+ * original.  Outputs: row_perm[i'] = original row of row i', col_perm[j'] =
+ * original column of column j' (the identity when not kept), and the block
+ * counts before and after.  Returns 1 when kept, 0 when not (and for a
+ * matrix with no entries). */
+int orc_reorder_perms(int64_t m, int64_t k, const int64_t *row_ptr, const int32_t *col_idx,
+                      int32_t bm, int32_t bk, int32_t *row_perm, int32_t *col_perm,
+                      int64_t *blocks_before, int64_t *blocks_after);
+
 #ifdef __cplusplus
 }
 #endif

@@ -114,3 +114,150 @@ def test_reorder_arguments(S):
         S.spmm_pack_bcsr_csr(64, 64, bad, np.array([5, 5], np.int32),
                              np.array([1, 1], np.uint16), reorder=True)
     assert e.value.name == "SPMM_ERR_INVALID_ARG"
+
+
+# ---------------------------------------------------------------------------
+# the permutation itself, against the oracle's plain implementation of the
+# reading (oracle.h, orc_reorder_perms)
+# ---------------------------------------------------------------------------
+
+def _oracle_case(orc, g, name):
+    m, k, bm, bk = g[f"{name}_shape"][0]
+    rp = np.array(g[f"{name}_row_ptr"][0], np.int64)
+    ci = np.array(g[f"{name}_col_idx"][0], np.int32)
+    return m, k, bm, bk, rp, ci, orc.reorder_perms(m, k, rp, ci, bm, bk)
+
+
+def test_oracle_reorder_hand_examples(orc):
+    from conftest import read_golden
+    g = read_golden("reorder_hand.txt")
+    m, k, bm, bk, rp, ci, (kept, rperm, cperm, before, after) = _oracle_case(orc, g, "case1")
+    assert kept == bool(g["case1_kept"][0][0])
+    np.testing.assert_array_equal(rperm, g["case1_row_perm"][0])
+    np.testing.assert_array_equal(cperm, g["case1_col_perm"][0])
+    assert [before, after] == g["case1_blocks"][0]
+    m, k, bm, bk, rp, ci, (kept, rperm, cperm, before, after) = _oracle_case(orc, g, "case2")
+    assert kept == bool(g["case2_kept"][0][0])
+    np.testing.assert_array_equal(rperm, np.arange(m))
+    np.testing.assert_array_equal(cperm, np.arange(k))
+    assert [before, after] == g["case2_blocks"][0]
+
+
+def _dense_list_less(xa, xb):
+    """Lexicographic order of two ascending index lists given as 0/1 vectors,
+    a prefix first: at the first position where they differ, the list that
+    holds it is smaller unless the other one has nothing after it."""
+    d = np.nonzero(xa != xb)[0]
+    if len(d) == 0:
+        return False
+    r = d[0]
+    if xa[r]:
+        return bool(xb[r + 1:].any())
+    return not bool(xa[r + 1:].any())
+
+
+def _random_pattern(r, m, k, density, empty_rows=(), empty_cols=(), dup_cols=()):
+    nz = r.random((m, k)) < density
+    for c, src in dup_cols:
+        nz[:, c] = nz[:, src]
+    nz[list(empty_rows), :] = False
+    nz[:, list(empty_cols)] = False
+    rp = np.zeros(m + 1, np.int64)
+    np.cumsum(nz.sum(axis=1), out=rp[1:])
+    return nz, rp, np.nonzero(nz)[1].astype(np.int32)
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_oracle_reorder_invariants(orc, seed):
+    # the oracle's orders checked with a comparator written differently (on
+    # 0/1 vectors), and its block counts against a direct count
+    r = np.random.default_rng(seed)
+    m, k, bm, bk = 48, 40, 8, 8
+    nz, rp, ci = _random_pattern(r, m, k, 0.06, empty_rows=(3, 17), empty_cols=(5,),
+                                 dup_cols=((9, 2), (30, 2)))
+    kept, rperm, cperm, before, after = orc.reorder_perms(m, k, rp, ci, bm, bk)
+
+    def blocks(a):
+        return int(a.reshape(m // bm, bm, k // bk, bk).any(axis=(1, 3)).sum())
+
+    assert before == blocks(nz)
+    if not kept:
+        return
+    assert sorted(rperm) == list(range(m)) and sorted(cperm) == list(range(k))
+    for a, b in zip(cperm[:-1], cperm[1:]):
+        assert not _dense_list_less(nz[:, b], nz[:, a]), (a, b)
+        if (nz[:, a] == nz[:, b]).all():
+            assert a < b
+    pc = nz[:, cperm]
+    bcols = pc.reshape(m, k // bk, bk).any(axis=2)
+    for a, b in zip(rperm[:-1], rperm[1:]):
+        assert not _dense_list_less(bcols[b], bcols[a]), (a, b)
+        if (bcols[a] == bcols[b]).all():
+            assert a < b
+    assert after == blocks(nz[rperm][:, cperm]) and after < before
+
+
+def test_oracle_reorder_recovers_hidden_blocks(orc):
+    # full blocks hidden by shuffling rows and columns: every column of a
+    # block has the same row list, so the order must bring back exactly the
+    # original blocks (partly filled blocks need not come back whole)
+    r = np.random.default_rng(7)
+    m = k = 64
+    nz = np.zeros((m, k), bool)
+    for b in range(8):
+        nz[8 * b:8 * b + 8, 8 * ((3 * b) % 8):8 * ((3 * b) % 8) + 8] = True
+    shuf = nz[r.permutation(m)][:, r.permutation(k)]
+    rp = np.zeros(m + 1, np.int64)
+    np.cumsum(shuf.sum(axis=1), out=rp[1:])
+    kept, rperm, cperm, before, after = orc.reorder_perms(m, k, rp, np.nonzero(shuf)[1], 8, 8)
+    assert kept and after == 8 and before > 8
+
+
+@pytest.mark.parametrize("case", ["random_sparse", "ties_and_empties", "hidden_blocks", "no_gain"])
+def test_library_permutation_equals_oracle(S, orc, case):
+    r = np.random.default_rng({"random_sparse": 11, "ties_and_empties": 12, "hidden_blocks": 13,
+                               "no_gain": 14}[case])
+    m, k = 256, 320
+    if case == "random_sparse":
+        nz, rp, ci = _random_pattern(r, m, k, 0.01)
+    elif case == "ties_and_empties":
+        nz, rp, ci = _random_pattern(r, m, k, 0.02, empty_rows=range(0, 256, 9),
+                                     empty_cols=range(1, 320, 7), dup_cols=((10, 3), (200, 3), (64, 65)))
+    elif case == "hidden_blocks":
+        base = np.zeros((m, k), bool)
+        for b in r.choice(4 * 5, 6, replace=False):
+            i, j = divmod(int(b), 5)
+            base[64 * i:64 * i + 64, 64 * j:64 * j + 64] = r.random((64, 64)) < 0.5
+        nz = base[r.permutation(m)][:, r.permutation(k)]
+        rp = np.zeros(m + 1, np.int64)
+        np.cumsum(nz.sum(axis=1), out=rp[1:])
+        ci = np.nonzero(nz)[1].astype(np.int32)
+    else:
+        nz = np.zeros((m, k), bool)
+        nz[:64, :64] = True                      # one full block: nothing to gain
+        rp = np.zeros(m + 1, np.int64)
+        np.cumsum(nz.sum(axis=1), out=rp[1:])
+        ci = np.nonzero(nz)[1].astype(np.int32)
+    vals = np.full(len(ci), 0x3F80, np.uint16)
+    M = S.spmm_pack_bcsr_csr(m, k, rp, ci, vals, reorder=True)
+    kept, rperm, cperm, before, after = orc.reorder_perms(m, k, rp, ci, 64, 64)
+    got_r = S.spmm_matrix_array(M, S.ARRAY_ROW_PERM)
+    got_c = S.spmm_matrix_array(M, S.ARRAY_COL_PERM)
+    if kept:
+        np.testing.assert_array_equal(got_r, rperm)
+        np.testing.assert_array_equal(got_c, cperm)
+    else:
+        assert len(got_r) == 0 and len(got_c) == 0
+    assert S.spmm_matrix_info(M)["nnzb"] == after
+    assert kept == (case != "no_gain")
+
+
+def test_library_permutation_equals_oracle_scrambled_4096(S, orc):
+    # the scrambled 4096 workload: its 410 hidden blocks, permutations bit for bit
+    w = synth.WORKLOADS["scrambled_4096_bcsr_reordered"]
+    a = synth.make_a(w)
+    M = S.spmm_pack_bcsr_csr(w.m, w.k, a["row_ptr"], a["col_idx"], a["vals_bf16"], reorder=True)
+    kept, rperm, cperm, before, after = orc.reorder_perms(w.m, w.k, a["row_ptr"], a["col_idx"], 64, 64)
+    assert kept and after == 410
+    np.testing.assert_array_equal(S.spmm_matrix_array(M, S.ARRAY_ROW_PERM), rperm)
+    np.testing.assert_array_equal(S.spmm_matrix_array(M, S.ARRAY_COL_PERM), cperm)

@@ -148,30 +148,45 @@ spmm_status_t plan_bcsr(spmm_plan_s *p) {
   if ((s = upload_vec(p, a.brow_ptr, &rp)) != SPMM_OK) return s;
   if ((s = upload_vec(p, a.bcol_idx, &ci)) != SPMM_OK) return s;
   if ((s = upload_vec(p, frag, &fv)) != SPMM_OK) return s;
-  // block rows in dispatch order: most stored blocks first (ties by index),
-  // so the longest tiles of a column tile start first and the short ones
-  // fill in behind them
   const int32_t mb = static_cast<int32_t>(a.m / 64);
-  vec<int32_t> sorted(static_cast<size_t>(mb));
-  for (int32_t i = 0; i < mb; ++i) sorted[i] = i;
-  auto blocks = [&](int32_t r) { return a.brow_ptr[r + 1] - a.brow_ptr[r]; };
-  std::stable_sort(sorted.begin(), sorted.end(),
-                   [&](int32_t x, int32_t y) { return blocks(x) > blocks(y); });
-  // row groups of about equal work (a tile costs its blocks plus one for the
-  // C write): longest first, each to the lightest group (lowest on ties);
-  // every group keeps the longest-first order.  The order array carries the
-  // groups' start offsets after its mb entries.
   const BcsrSchedule sc = bcsr_schedule(a.brow_ptr.data(), mb, p->n);
+  // Paired block rows (two rows per tile over the union of their block
+  // columns) at 256-wide half-block stages, when the pairing saves at least
+  // a tenth of the B slab loads and the pairs still give every CU several
+  // tiles.  Not for column-permuted A (the kernel reads B rows in place).
+  vec<int32_t> pair_rows, pair_ptr, units;
+  bool paired = false;
+  if (sc.tn == kBcsrPairTN && sc.kh == kBcsrPairKH && a.col_perm.empty() && mb >= 2) {
+    const double saving = bcsr_pairing(a.brow_ptr.data(), a.bcol_idx.data(), mb,
+                                       static_cast<int32_t>((a.k + 63) / 64), pair_rows, pair_ptr, units);
+    const int64_t tiles = static_cast<int64_t>(pair_ptr.size() - 1) * ((p->n + sc.tn - 1) / sc.tn);
+    paired = saving >= kBcsrPairMinSaving && tiles >= kBcsrPairMinTiles;
+  }
+  // tiles (block rows, or pairs) in dispatch order: most work first (ties by
+  // index), so the longest tiles of a column tile start first and the short
+  // ones fill in behind them.  A tile's work is its stages (blocks, or units
+  // of a pair) plus one per C block row it writes.
+  const int32_t ntiles = paired ? static_cast<int32_t>(pair_ptr.size() - 1) : mb;
+  auto work = [&](int32_t r) -> int64_t {
+    if (!paired) return a.brow_ptr[r + 1] - a.brow_ptr[r] + 1;
+    return pair_ptr[r + 1] - pair_ptr[r] + 1 + (pair_rows[2 * r + 1] >= 0 ? 1 : 0);
+  };
+  vec<int32_t> sorted(static_cast<size_t>(ntiles));
+  for (int32_t i = 0; i < ntiles; ++i) sorted[i] = i;
+  std::stable_sort(sorted.begin(), sorted.end(), [&](int32_t x, int32_t y) { return work(x) > work(y); });
+  // row groups of about equal work: longest first, each to the lightest
+  // group (lowest on ties); every group keeps the longest-first order.  The
+  // order array carries the groups' start offsets after its entries.
   const int groups = sc.row_groups;
   vec<vec<int32_t>> members(static_cast<size_t>(groups));
   vec<int64_t> load(static_cast<size_t>(groups), 0);
   for (int32_t r : sorted) {
     const size_t g = static_cast<size_t>(std::min_element(load.begin(), load.end()) - load.begin());
     members[g].push_back(r);
-    load[g] += blocks(r) + 1;
+    load[g] += work(r);
   }
   vec<int32_t> order;
-  order.reserve(static_cast<size_t>(mb) + 9);
+  order.reserve(static_cast<size_t>(ntiles) + 9);
   vec<int32_t> seg(1, 0);
   for (const auto &g : members) {
     order.insert(order.end(), g.begin(), g.end());
@@ -184,7 +199,22 @@ spmm_status_t plan_bcsr(spmm_plan_s *p) {
   L.col_idx = ci;
   L.frag = fv;
   L.row_order = ro;
-  L.row_seg = ro + mb;
+  L.row_seg = ro + ntiles;
+  L.paired = paired;
+  L.pair_rows = nullptr;
+  L.pair_ptr = nullptr;
+  L.units = nullptr;
+  L.npairs = 0;
+  if (paired) {
+    int32_t *prw = nullptr, *pp = nullptr, *un = nullptr;
+    if ((s = upload_vec(p, pair_rows, &prw)) != SPMM_OK) return s;
+    if ((s = upload_vec(p, pair_ptr, &pp)) != SPMM_OK) return s;
+    if ((s = upload_vec(p, units, &un)) != SPMM_OK) return s;
+    L.pair_rows = prw;
+    L.pair_ptr = pp;
+    L.units = reinterpret_cast<const int4 *>(un);
+    L.npairs = ntiles;
+  }
   L.row_groups = groups;
   L.tn = sc.tn;
   L.kh = sc.kh;
@@ -204,7 +234,7 @@ spmm_status_t plan_bcsr(spmm_plan_s *p) {
     if ((s = upload_vec(p, a.row_perm, &rows)) != SPMM_OK) return s;
     L.c_rows = rows;
   }
-  p->info.tile_m = 64;
+  p->info.tile_m = paired ? 128 : 64;
   p->info.tile_n = L.tn;
   p->info.grid = L.grid;
   return SPMM_OK;

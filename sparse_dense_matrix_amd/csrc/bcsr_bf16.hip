@@ -310,6 +310,206 @@ __global__ __launch_bounds__(Geo<kTN>::kThreads) void bcsr_bf16_mfma(
   }
 }
 
+// Paired block rows: a tile is two block rows times 256 columns of C, eight
+// waves, waves 0-3 owning the first row's 64 x 256 and waves 4-7 the
+// second's.  The pair walks the union of its rows' block columns in column
+// order (units: column, block of the first row, block of the second, -1 for
+// none), half a block per stage: a stage holds the 32 x 256 B half-slab and
+// both rows' A halves, so a B slab both rows use is loaded once instead of
+// twice.  Waves whose row has no block in a unit skip its MFMAs.
+// The ring has three stages (two units in flight while one is used): the
+// C staging area is as large as three stages anyway.  A unit's descriptor
+// is loaded a stage before its loads are issued, so the scalar load's
+// latency is not paid at the issue.  Everything else (DMA loads, swizzle,
+// transpose reads, epilogue, tile dealing with pairs in place of block
+// rows) is the single-row kernel's.
+struct PairGeo {
+  static constexpr int kTN = 256, kKH = 32;
+  static constexpr int kRingStages = 3;
+  static constexpr int kWaves = 8;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kSteps = kKH / 16;
+  static constexpr int kPer = kBlk / kKH;
+  static constexpr int kBRow = kTN * 2;
+  static constexpr int kBBytes = kKH * kBRow;  // 16 KB
+  static constexpr int kAStage = kABytes / kPer;  // one row's share, 4 KB
+  static constexpr int kStageBytes = kBBytes + 2 * kAStage;
+  static constexpr int kBLoads = kBBytes / 1024 / kWaves;  // 2
+  static constexpr int kRing = kRingStages * kStageBytes;
+  static constexpr int kCBytes = kWaves * 64 * kCPitch;  // staged C of the two rows
+  static constexpr int kLdsBytes = kRing > kCBytes ? kRing : kCBytes;
+  static_assert(kBLoads * kWaves * 1024 == kBBytes, "split");
+  static_assert(kAStage == 4 * 1024, "one 1 KB A piece per wave of a row");
+  static_assert(2 * kLdsBytes <= 160 * 1024, "two workgroups per CU");
+  static_assert(kTN == kBcsrPairTN && kKH == kBcsrPairKH, "the plan's pair tile");
+};
+
+__global__ __launch_bounds__(PairGeo::kThreads, 2) void bcsr_bf16_pair(
+    const int4 *__restrict__ units, const int32_t *__restrict__ pair_ptr,
+    const int32_t *__restrict__ pair_rows, const uint16_t *__restrict__ frag,
+    const int32_t *__restrict__ pair_order, const int32_t *__restrict__ pair_seg,
+    int32_t row_groups, int32_t ntn, int64_t n, const uint16_t *__restrict__ B, int64_t ldb,
+    uint16_t *__restrict__ C, int64_t ldc, const int32_t *__restrict__ c_rows) {
+  using G = PairGeo;
+  constexpr int kSteps = G::kSteps, kPer = G::kPer, kTN = G::kTN;
+  constexpr int kBRow = G::kBRow, kBBytes = G::kBBytes, kStageBytes = G::kStageBytes;
+  constexpr int kBLoads = G::kBLoads;
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+
+  const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const int grp = x % row_groups, part = x / row_groups, parts = 8 / row_groups;
+  const int r0 = pair_seg[grp], cnt = pair_seg[grp + 1] - r0;
+  const int tg = cnt * ntn;
+  const int per = (tg + parts - 1) / parts;
+  const int t = part * per + j;
+  if (j >= per || t >= tg) return;
+  const int pr = pair_order[r0 + t % cnt];
+  const int64_t n0 = static_cast<int64_t>(t / cnt) * kTN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = wave >> 2;  // which row of the pair
+  const int cw = wave & 3;     // which 64 columns
+  const int u0 = pair_ptr[pr], nu = pair_ptr[pr + 1] - u0;
+
+  uint32_t boff[kBLoads];
+#pragma unroll
+  for (int i = 0; i < kBLoads; ++i) {
+    const int o = (wave * kBLoads + i) * 1024 + lane * 16;
+    const int r = o / kBRow;
+    const int c = swz(r, (o % kBRow) / 16) * 8;
+    const int64_t col = (n0 + c < n) ? n0 + c : n0;
+    boff[i] = static_cast<uint32_t>((r * ldb + col) * 2);
+  }
+  const uint32_t lds_base = lds_addr(lds);
+  // the block of this wave's row in unit u of the pair (-1: none)
+  auto row_block = [&](const int4 &un) { return half ? un.z : un.y; };
+  auto issue = [&](int unit, int stage, const int4 &un) {
+    const int p = unit % kPer;
+    const uint32_t sb = lds_base + stage * kStageBytes;
+    const uint16_t *bsrc = B + (static_cast<int64_t>(un.x) * kBlk + p * G::kKH) * ldb;
+#pragma unroll
+    for (int i = 0; i < kBLoads; ++i) load_lds16(sb + (wave * kBLoads + i) * 1024, bsrc, boff[i]);
+    const int blk = row_block(un);
+    if (blk >= 0) {
+      // 1 KB piece cw of the row's stage share: row half cw / kSteps, k-step cw % kSteps
+      const int go = ((cw / kSteps) * 4 + p * kSteps + cw % kSteps) * 1024;
+      load_lds16(sb + kBBytes + half * G::kAStage + cw * 1024,
+                 frag + static_cast<int64_t>(blk) * (kABytes / 2), static_cast<uint32_t>(go + lane * 16));
+    }
+  };
+
+  const int g = lane >> 5;
+  const int pl = lane & 15;
+  const int tr_row = 8 * g + (pl >> 2);
+  const int tr_col = cw * 64 + ((lane >> 4) & 1) * 16 + 4 * (pl & 3);
+  auto read_ops = [&](const char *sb, int s) {
+    Operands o;
+    const bf16x8 *afr = reinterpret_cast<const bf16x8 *>(sb + kBBytes + half * G::kAStage);
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) o.a[rb] = afr[(rb * kSteps + s) * 64 + lane];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      s16x4 part[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = 16 * s + tr_row + 4 * h;
+        const int c = tr_col + 32 * cb;
+        part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4 *)(sb + r * kBRow + swz(r, c >> 3) * 16 + (c & 7) * 2));
+      }
+      s16x8 bs;
+      bs[0] = part[0][0]; bs[1] = part[0][1]; bs[2] = part[0][2]; bs[3] = part[0][3];
+      bs[4] = part[1][0]; bs[5] = part[1][1]; bs[6] = part[1][2]; bs[7] = part[1][3];
+      o.b[cb] = __builtin_bit_cast(bf16x8, bs);
+    }
+    return o;
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.0f;
+
+  const int nunit = nu * kPer;
+  // Unit descriptors sit in registers: lane l holds unit l of the pair (the
+  // plan pairs rows only while every pair has at most 64 units), and a wave
+  // reads one out with v_readlane, so no load waits inside the loop.
+  const int4 win = lane < nu ? units[u0 + lane] : make_int4(0, -1, -1, 0);
+  // descriptor of stage unit i; past the end, the last one again (unused:
+  // nothing is issued or computed for it)
+  const int last = nunit > 0 ? nunit - 1 : 0;
+  auto desc = [&](int i) {
+    const int l = min(i, last) / kPer;
+    return make_int4(__builtin_amdgcn_readlane(win.x, l), __builtin_amdgcn_readlane(win.y, l),
+                     __builtin_amdgcn_readlane(win.z, l), 0);
+  };
+  // descriptors of stage units it, it + 1, it + 2
+  int4 d0 = desc(0), d1 = desc(1), d2 = desc(2);
+  if (nunit > 0) issue(0, 0, d0);
+  if (nunit > 1) issue(1, 1, d1);
+  int cur = 0;  // stage of unit it
+  for (int it = 0; it < nunit; ++it) {
+    // this unit's loads have landed; the next unit's may still be in flight
+    // (loads complete in issue order)
+    if (it + 1 >= nunit) wait_vm<0>();
+    else if (row_block(d1) >= 0) wait_vm<kBLoads + 1>();
+    else wait_vm<kBLoads>();
+    barrier();  // ... for every wave; and the stage of unit it-1 is free
+    if (it + 2 < nunit) issue(it + 2, cur == 0 ? 2 : cur - 1, d2);
+    const int4 d3 = desc(it + 3);  // used two stages from now
+    if (row_block(d0) >= 0) {
+      const char *sb = lds + cur * kStageBytes;
+      Operands ops[kSteps];
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s) ops[s] = read_ops(sb, s);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+            acc[rb][cb] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(ops[s].a[rb], ops[s].b[cb], acc[rb][cb], 0, 0, 0);
+    }
+    cur = cur == 2 ? 0 : cur + 1;
+    d0 = d1;
+    d1 = d2;
+    d2 = d3;
+  }
+
+  barrier();  // every wave is done reading the ring
+  char *ct = lds + wave * 64 * kCPitch;
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = rb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        const int col = cb * 32 + (lane & 31);
+        *reinterpret_cast<unsigned short *>(ct + row * kCPitch + col * 2) = to_bf16_rne(acc[rb][cb][r]);
+      }
+  __builtin_amdgcn_wave_barrier();
+  const int br = pair_rows[2 * pr + half];
+  const int64_t col = n0 + cw * 64 + (lane & 7) * 8;
+  if (br >= 0 && col < n) {
+    const int64_t row0 = static_cast<int64_t>(br) * kBlk;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int row = q * 8 + (lane >> 3);
+      const int64_t crow = c_rows ? c_rows[row0 + row] : row0 + row;
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(ct + row * kCPitch + (lane & 7) * 16);
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(C + crow * ldc + col));
+    }
+  }
+}
+
 }  // namespace
 
 void bcsr_fragment_order(const uint16_t *blk, uint16_t *frag) {
@@ -354,6 +554,69 @@ int64_t bcsr_grid(const int32_t *row_seg, const BcsrSchedule &sc, int64_t n) {
   return 8 * per;
 }
 
+double bcsr_pairing(const int32_t *row_ptr, const int32_t *col_idx, int32_t mb, int32_t kb,
+                    vec<int32_t> &pair_rows, vec<int32_t> &pair_ptr, vec<int32_t> &units) {
+  pair_rows.clear();
+  pair_ptr.assign(1, 0);
+  units.clear();
+  const int64_t nnzb = row_ptr[mb];
+  // block rows of each block column, ascending
+  vec<int32_t> cptr(static_cast<size_t>(kb) + 1, 0), crows(static_cast<size_t>(nnzb));
+  for (int64_t q = 0; q < nnzb; ++q) ++cptr[col_idx[q] + 1];
+  for (int32_t c = 0; c < kb; ++c) cptr[c + 1] += cptr[c];
+  {
+    vec<int32_t> fill(cptr.begin(), cptr.end() - 1);
+    for (int32_t r = 0; r < mb; ++r)
+      for (int32_t q = row_ptr[r]; q < row_ptr[r + 1]; ++q) crows[fill[col_idx[q]]++] = r;
+  }
+  auto blocks = [&](int32_t r) { return row_ptr[r + 1] - row_ptr[r]; };
+  vec<int32_t> order(static_cast<size_t>(mb));
+  for (int32_t i = 0; i < mb; ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int32_t x, int32_t y) { return blocks(x) > blocks(y); });
+  vec<char> used(static_cast<size_t>(mb), 0);
+  vec<int32_t> shared(static_cast<size_t>(mb), 0), touched;
+  size_t next = 0;  // first row of `order` that may still be unpaired
+  for (int32_t r : order) {
+    if (used[r]) continue;
+    used[r] = 1;
+    touched.clear();
+    for (int32_t q = row_ptr[r]; q < row_ptr[r + 1]; ++q)
+      for (int32_t i = cptr[col_idx[q]]; i < cptr[col_idx[q] + 1]; ++i)
+        if (!used[crows[i]] && shared[crows[i]]++ == 0) touched.push_back(crows[i]);
+    int32_t best = -1, best_shared = 0;
+    for (int32_t s2 : touched) {
+      if (shared[s2] > best_shared || (shared[s2] == best_shared && s2 < best)) {
+        best = s2;
+        best_shared = shared[s2];
+      }
+      shared[s2] = 0;
+    }
+    if (best < 0) {  // no unpaired row shares a column: take the longest one left
+      while (next < order.size() && used[order[next]]) ++next;
+      if (next < order.size()) best = order[next];
+    }
+    if (best >= 0) used[best] = 1;
+    pair_rows.push_back(r);
+    pair_rows.push_back(best);
+    // the union of the two rows' block columns, ascending
+    int32_t q0 = row_ptr[r], e0 = row_ptr[r + 1];
+    int32_t q1 = best >= 0 ? row_ptr[best] : 0, e1 = best >= 0 ? row_ptr[best + 1] : 0;
+    while (q0 < e0 || q1 < e1) {
+      const int32_t c0 = q0 < e0 ? col_idx[q0] : INT32_MAX, c1 = q1 < e1 ? col_idx[q1] : INT32_MAX;
+      const int32_t c = std::min(c0, c1);
+      units.push_back(c);
+      units.push_back(c0 == c ? q0++ : -1);
+      units.push_back(c1 == c ? q1++ : -1);
+      units.push_back(0);
+    }
+    pair_ptr.push_back(static_cast<int32_t>(units.size() / 4));
+    if (pair_ptr.back() - pair_ptr[pair_ptr.size() - 2] > kBcsrPairMaxUnits) return 0.0;
+  }
+  const double stored = static_cast<double>(units.size() / 4);
+  return nnzb > 0 ? 1.0 - stored / static_cast<double>(nnzb) : 0.0;
+}
+
 namespace {
 template <int kTN, bool kMap, int kKH>
 hipError_t launch_tn(const BcsrLaunch &a, hipStream_t s) {
@@ -376,9 +639,29 @@ hipError_t launch_tn(const BcsrLaunch &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+hipError_t launch_pair(const BcsrLaunch &a, hipStream_t s) {
+  using G = PairGeo;
+  if (a.tn != G::kTN || a.kh != G::kKH || a.col_perm) return hipErrorInvalidValue;
+  const int64_t ntn = (a.n + G::kTN - 1) / G::kTN;
+  const int64_t tiles = static_cast<int64_t>(a.npairs) * ntn;
+  if (tiles == 0) return hipSuccess;
+  if (tiles > INT32_MAX / 2 || a.ldb > (1 << 24)) return hipErrorInvalidValue;
+  if (a.row_groups < 1 || a.row_groups > 8 || 8 % a.row_groups != 0) return hipErrorInvalidValue;
+  auto kernel = bcsr_bf16_pair;
+  hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(kernel), G::kLdsBytes);
+  if (e != hipSuccess) return e;
+  if (a.grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(a.grid)), dim3(G::kThreads),
+                     G::kLdsBytes, s, a.units, a.pair_ptr, a.pair_rows, a.frag, a.row_order,
+                     a.row_seg, a.row_groups, static_cast<int32_t>(ntn), a.n, a.B, a.ldb, a.C,
+                     a.ldc, a.c_rows);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_bcsr_bf16(const BcsrLaunch &a, hipStream_t s) {
+  if (a.paired) return launch_pair(a, s);
   if (a.tn != 256 && a.tn != 512) return hipErrorInvalidValue;
   if (a.kh != 64 && (a.kh != 32 || a.tn != 256)) return hipErrorInvalidValue;
   const bool wide = a.tn == 512;

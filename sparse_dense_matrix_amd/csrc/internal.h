@@ -157,7 +157,29 @@ struct BcsrLaunch {
   int64_t k_rows;           // k: rows of B
   const int32_t *col_perm;  // [k] original row of B for each packed column
   const int32_t *c_rows;    // [m] original row of C for each packed row
+  // Paired block rows (bcsr_bf16_pair): a tile is two block rows that walk
+  // the union of their block columns, so a B slab both use is loaded once.
+  // row_order / row_seg then hold pairs instead of block rows.
+  bool paired;
+  const int32_t *pair_rows;  // [2 * npairs] block rows of each pair (second -1 when alone)
+  const int32_t *pair_ptr;   // [npairs + 1] units of pair p: [pair_ptr[p], pair_ptr[p+1])
+  const int4 *units;         // per unit: block column, block of the first row, of the second (-1: none)
+  int32_t npairs;
 };
+// The paired kernel's tile (256 columns, half-block stages) and when the plan
+// takes it: the pairing saves at least this fraction of B slab loads and
+// leaves at least this many tiles.
+constexpr int kBcsrPairTN = 256, kBcsrPairKH = 32;
+constexpr double kBcsrPairMinSaving = 0.10;
+constexpr int64_t kBcsrPairMinTiles = 8 * 256;
+// a pair's units sit one per lane of a wave
+constexpr int32_t kBcsrPairMaxUnits = 64;
+// Pairs of block rows for the paired kernel: greedy, largest rows first, each
+// with the unpaired row sharing most block columns (ties: lowest index).
+// Returns the fraction of B slab loads the pairing saves; 0 when a pair would
+// exceed kBcsrPairMaxUnits (the pairing is then not to be used).
+double bcsr_pairing(const int32_t *row_ptr, const int32_t *col_idx, int32_t mb, int32_t kb,
+                    vec<int32_t> &pair_rows, vec<int32_t> &pair_ptr, vec<int32_t> &units);
 // Fragment order of one 64 x 64 block: [rb 2][s 4][lane 64][8 elements], lane l
 // holding row 32*rb + l%32, columns 16*s + 8*(l/32) + 0..7.
 void bcsr_fragment_order(const uint16_t *block_rowmajor, uint16_t *frag);

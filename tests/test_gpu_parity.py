@@ -199,6 +199,70 @@ def test_bcsr_integer_values_row_groups_exact(S, orc):
         _assert_int_exact(got[:, j0:j1], orc.bcsr_spmm(64, 64, rp, ci, v, B, j0=j0, j1=j1))
 
 
+def test_bcsr_paired_block_rows_exact(S, orc):
+    # enough 64-row block rows at n < 8192 for the plan to pair them (tile_m
+    # 128: two block rows walk the union of their block columns): rows that
+    # share every column, rows that share none, empty rows next to full
+    # ones, an odd block-row count and a ragged last N tile; integer values,
+    # bit-exact over every row
+    m, k, n = 64 * 131, 1024, 8120
+    mb, kb = m // 64, k // 64
+    r = np.random.default_rng(95)
+    mask = np.zeros((mb, kb), bool)
+    mask[0:10, [0, 3, 5]] = True                  # identical columns
+    for i in range(10, 26):
+        mask[i, i - 10] = True                    # one column each, all different
+    # rows 26..31 stay empty
+    mask[32, :] = True                            # a full block row
+    for i in range(33, mb):
+        mask[i, r.choice(kb, 3, replace=False)] = True
+    a = np.zeros((m, k), np.float32)
+    for i, j in zip(*np.nonzero(mask)):
+        a[i * 64:(i + 1) * 64, j * 64:(j + 1) * 64] = r.integers(-3, 4, size=(64, 64))
+    a = synth.f32_to_bf16_bits(a)
+    B = synth.f32_to_bf16_bits(r.integers(-4, 5, size=(k, n)).astype(np.float32))
+    M = S.spmm_pack_bcsr(a, 64, 64)
+    P = S.spmm_plan(M, n, S.BF16, S.BF16)
+    info = P.info()
+    _say(f"bcsr paired rows: tile_m={info['tile_m']} tile_n={info['tile_n']} grid={info['grid']}")
+    assert info["tile_m"] == 128 and info["tile_n"] == 256
+    got = run(S, P, B, m, n, "bf16")
+    assert_all_written(got, "bf16")
+    assert (got[26 * 64:32 * 64] & 0x7FFF == 0).all()
+    rp, ci, v = orc.pack_bcsr(a, 64, 64)
+    for j0, j1 in ((0, 520), (3840, 4352), (n - 440, n)):
+        _assert_int_exact(got[:, j0:j1], orc.bcsr_spmm(64, 64, rp, ci, v, B, j0=j0, j1=j1))
+
+
+def test_bcsr_pair_over_64_units_keeps_single_rows(S, orc):
+    # a block row with 80 stored blocks: its pair would walk more than 64
+    # block columns, more than a wave holds descriptors for, so the plan keeps
+    # single-row tiles (tile_m 64); the result is still exact
+    m, k, n = 64 * 131, 64 * 80, 8120
+    mb, kb = m // 64, k // 64
+    r = np.random.default_rng(96)
+    mask = np.zeros((mb, kb), bool)
+    mask[5, :] = True
+    for i in range(mb):
+        if i != 5:
+            mask[i, r.choice(kb, 3, replace=False)] = True
+    a = np.zeros((m, k), np.float32)
+    for i, j in zip(*np.nonzero(mask)):
+        a[i * 64:(i + 1) * 64, j * 64:(j + 1) * 64] = r.integers(-3, 4, size=(64, 64))
+    a = synth.f32_to_bf16_bits(a)
+    B = synth.f32_to_bf16_bits(r.integers(-4, 5, size=(k, n)).astype(np.float32))
+    M = S.spmm_pack_bcsr(a, 64, 64)
+    P = S.spmm_plan(M, n, S.BF16, S.BF16)
+    info = P.info()
+    _say(f"bcsr long row: tile_m={info['tile_m']} tile_n={info['tile_n']} grid={info['grid']}")
+    assert info["tile_m"] == 64
+    got = run(S, P, B, m, n, "bf16")
+    assert_all_written(got, "bf16")
+    rp, ci, v = orc.pack_bcsr(a, 64, 64)
+    for j0, j1 in ((0, 264), (n - 264, n)):
+        _assert_int_exact(got[:, j0:j1], orc.bcsr_spmm(64, 64, rp, ci, v, B, j0=j0, j1=j1))
+
+
 def test_bcsr_many_blocks_per_row(S, orc):
     # more than 16 stored blocks per block row on average: whole-block LDS
     # stages at 256 columns (few blocks per row take half-block stages, as

@@ -323,35 +323,45 @@ __global__ __launch_bounds__(Geo<kTN>::kThreads) void bcsr_bf16_mfma(
 // latency is not paid at the issue.  Everything else (DMA loads, swizzle,
 // transpose reads, epilogue, tile dealing with pairs in place of block
 // rows) is the single-row kernel's.
+constexpr int kPairWaveCols = 128;  // C columns per wave in the paired kernel
+
+template <int kWC>
 struct PairGeo {
   static constexpr int kTN = 256, kKH = 32;
   static constexpr int kRingStages = 3;
-  static constexpr int kWaves = 8;
+  static constexpr int kColWaves = kTN / kWC;   // waves per block row
+  static constexpr int kWaves = 2 * kColWaves;
   static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kCb = kWC / 32;          // MFMA column tiles per wave
+  static constexpr int kPitch = kWC * 2 + 16;   // bytes per row of a wave's staged C tile
   static constexpr int kSteps = kKH / 16;
   static constexpr int kPer = kBlk / kKH;
   static constexpr int kBRow = kTN * 2;
   static constexpr int kBBytes = kKH * kBRow;  // 16 KB
   static constexpr int kAStage = kABytes / kPer;  // one row's share, 4 KB
   static constexpr int kStageBytes = kBBytes + 2 * kAStage;
-  static constexpr int kBLoads = kBBytes / 1024 / kWaves;  // 2
+  static constexpr int kBLoads = kBBytes / 1024 / kWaves;
+  static constexpr int kALoads = kAStage / 1024 / kColWaves;  // per wave of a row
   static constexpr int kRing = kRingStages * kStageBytes;
-  static constexpr int kCBytes = kWaves * 64 * kCPitch;  // staged C of the two rows
+  static constexpr int kCBytes = kWaves * 64 * kPitch;  // staged C of the two rows
   static constexpr int kLdsBytes = kRing > kCBytes ? kRing : kCBytes;
   static_assert(kBLoads * kWaves * 1024 == kBBytes, "split");
-  static_assert(kAStage == 4 * 1024, "one 1 KB A piece per wave of a row");
+  static_assert(kALoads * kColWaves * 1024 == kAStage, "A split");
+  static_assert(kWC == 64 || kWC == 128, "64 or 128 columns per wave");
   static_assert(2 * kLdsBytes <= 160 * 1024, "two workgroups per CU");
   static_assert(kTN == kBcsrPairTN && kKH == kBcsrPairKH, "the plan's pair tile");
 };
 
-__global__ __launch_bounds__(PairGeo::kThreads, 2) void bcsr_bf16_pair(
+template <int kWC>
+__global__ __launch_bounds__(PairGeo<kWC>::kThreads, 2) void bcsr_bf16_pair(
     const int4 *__restrict__ units, const int32_t *__restrict__ pair_ptr,
     const int32_t *__restrict__ pair_rows, const uint16_t *__restrict__ frag,
     const int32_t *__restrict__ pair_order, const int32_t *__restrict__ pair_seg,
     int32_t row_groups, int32_t ntn, int64_t n, const uint16_t *__restrict__ B, int64_t ldb,
     uint16_t *__restrict__ C, int64_t ldc, const int32_t *__restrict__ c_rows) {
-  using G = PairGeo;
-  constexpr int kSteps = G::kSteps, kPer = G::kPer, kTN = G::kTN;
+  using G = PairGeo<kWC>;
+  constexpr int kSteps = G::kSteps, kPer = G::kPer, kTN = G::kTN, kCb = G::kCb;
+  constexpr int kALoads = G::kALoads, kPitch = G::kPitch;
   constexpr int kBRow = G::kBRow, kBBytes = G::kBBytes, kStageBytes = G::kStageBytes;
   constexpr int kBLoads = G::kBLoads;
   extern __shared__ __attribute__((aligned(1024))) char lds[];
@@ -369,8 +379,8 @@ __global__ __launch_bounds__(PairGeo::kThreads, 2) void bcsr_bf16_pair(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int half = wave >> 2;  // which row of the pair
-  const int cw = wave & 3;     // which 64 columns
+  const int half = wave / G::kColWaves;  // which row of the pair
+  const int cw = wave % G::kColWaves;    // which kWC columns
   const int u0 = pair_ptr[pr], nu = pair_ptr[pr + 1] - u0;
 
   uint32_t boff[kBLoads];
@@ -393,24 +403,32 @@ __global__ __launch_bounds__(PairGeo::kThreads, 2) void bcsr_bf16_pair(
     for (int i = 0; i < kBLoads; ++i) load_lds16(sb + (wave * kBLoads + i) * 1024, bsrc, boff[i]);
     const int blk = row_block(un);
     if (blk >= 0) {
-      // 1 KB piece cw of the row's stage share: row half cw / kSteps, k-step cw % kSteps
-      const int go = ((cw / kSteps) * 4 + p * kSteps + cw % kSteps) * 1024;
-      load_lds16(sb + kBBytes + half * G::kAStage + cw * 1024,
-                 frag + static_cast<int64_t>(blk) * (kABytes / 2), static_cast<uint32_t>(go + lane * 16));
+#pragma unroll
+      for (int i = 0; i < kALoads; ++i) {
+        // 1 KB piece q of the row's stage share: row half q / kSteps, k-step q % kSteps
+        const int q = cw * kALoads + i;
+        const int go = ((q / kSteps) * 4 + p * kSteps + q % kSteps) * 1024;
+        load_lds16(sb + kBBytes + half * G::kAStage + q * 1024,
+                   frag + static_cast<int64_t>(blk) * (kABytes / 2), static_cast<uint32_t>(go + lane * 16));
+      }
     }
   };
 
   const int g = lane >> 5;
   const int pl = lane & 15;
   const int tr_row = 8 * g + (pl >> 2);
-  const int tr_col = cw * 64 + ((lane >> 4) & 1) * 16 + 4 * (pl & 3);
+  const int tr_col = cw * kWC + ((lane >> 4) & 1) * 16 + 4 * (pl & 3);
+  struct Ops {
+    bf16x8 a[2];
+    bf16x8 b[kCb];
+  };
   auto read_ops = [&](const char *sb, int s) {
-    Operands o;
+    Ops o;
     const bf16x8 *afr = reinterpret_cast<const bf16x8 *>(sb + kBBytes + half * G::kAStage);
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) o.a[rb] = afr[(rb * kSteps + s) * 64 + lane];
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
+    for (int cb = 0; cb < kCb; ++cb) {
       s16x4 part[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -427,11 +445,11 @@ __global__ __launch_bounds__(PairGeo::kThreads, 2) void bcsr_bf16_pair(
     return o;
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[2][kCb];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
+    for (int jj = 0; jj < kCb; ++jj)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.0f;
 
@@ -457,21 +475,21 @@ __global__ __launch_bounds__(PairGeo::kThreads, 2) void bcsr_bf16_pair(
     // this unit's loads have landed; the next unit's may still be in flight
     // (loads complete in issue order)
     if (it + 1 >= nunit) wait_vm<0>();
-    else if (row_block(d1) >= 0) wait_vm<kBLoads + 1>();
+    else if (row_block(d1) >= 0) wait_vm<kBLoads + kALoads>();
     else wait_vm<kBLoads>();
     barrier();  // ... for every wave; and the stage of unit it-1 is free
     if (it + 2 < nunit) issue(it + 2, cur == 0 ? 2 : cur - 1, d2);
     const int4 d3 = desc(it + 3);  // used two stages from now
     if (row_block(d0) >= 0) {
       const char *sb = lds + cur * kStageBytes;
-      Operands ops[kSteps];
+      Ops ops[kSteps];
 #pragma unroll
       for (int s = 0; s < kSteps; ++s) ops[s] = read_ops(sb, s);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int s = 0; s < kSteps; ++s)
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
+        for (int cb = 0; cb < kCb; ++cb)
 #pragma unroll
           for (int rb = 0; rb < 2; ++rb)
             acc[rb][cb] =
@@ -484,27 +502,29 @@ __global__ __launch_bounds__(PairGeo::kThreads, 2) void bcsr_bf16_pair(
   }
 
   barrier();  // every wave is done reading the ring
-  char *ct = lds + wave * 64 * kCPitch;
+  char *ct = lds + wave * 64 * kPitch;
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int cb = 0; cb < kCb; ++cb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = rb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
         const int col = cb * 32 + (lane & 31);
-        *reinterpret_cast<unsigned short *>(ct + row * kCPitch + col * 2) = to_bf16_rne(acc[rb][cb][r]);
+        *reinterpret_cast<unsigned short *>(ct + row * kPitch + col * 2) = to_bf16_rne(acc[rb][cb][r]);
       }
   __builtin_amdgcn_wave_barrier();
+  // 16-byte pieces: kWC / 8 per row, 64 lanes cover kRowsPer rows at a time
+  constexpr int kPieces = kWC / 8, kRowsPer = 64 / kPieces;
   const int br = pair_rows[2 * pr + half];
-  const int64_t col = n0 + cw * 64 + (lane & 7) * 8;
+  const int64_t col = n0 + cw * kWC + (lane % kPieces) * 8;
   if (br >= 0 && col < n) {
     const int64_t row0 = static_cast<int64_t>(br) * kBlk;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int row = q * 8 + (lane >> 3);
+    for (int q = 0; q < 64 / kRowsPer; ++q) {
+      const int row = q * kRowsPer + lane / kPieces;
       const int64_t crow = c_rows ? c_rows[row0 + row] : row0 + row;
-      const u32x4 v = *reinterpret_cast<const u32x4 *>(ct + row * kCPitch + (lane & 7) * 16);
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(ct + row * kPitch + (lane % kPieces) * 16);
       __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(C + crow * ldc + col));
     }
   }
@@ -639,15 +659,16 @@ hipError_t launch_tn(const BcsrLaunch &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int kWC>
 hipError_t launch_pair(const BcsrLaunch &a, hipStream_t s) {
-  using G = PairGeo;
+  using G = PairGeo<kWC>;
   if (a.tn != G::kTN || a.kh != G::kKH || a.col_perm) return hipErrorInvalidValue;
   const int64_t ntn = (a.n + G::kTN - 1) / G::kTN;
   const int64_t tiles = static_cast<int64_t>(a.npairs) * ntn;
   if (tiles == 0) return hipSuccess;
   if (tiles > INT32_MAX / 2 || a.ldb > (1 << 24)) return hipErrorInvalidValue;
   if (a.row_groups < 1 || a.row_groups > 8 || 8 % a.row_groups != 0) return hipErrorInvalidValue;
-  auto kernel = bcsr_bf16_pair;
+  auto kernel = bcsr_bf16_pair<kWC>;
   hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(kernel), G::kLdsBytes);
   if (e != hipSuccess) return e;
   if (a.grid <= 0) return hipSuccess;
@@ -661,7 +682,7 @@ hipError_t launch_pair(const BcsrLaunch &a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_bcsr_bf16(const BcsrLaunch &a, hipStream_t s) {
-  if (a.paired) return launch_pair(a, s);
+  if (a.paired) return launch_pair<kPairWaveCols>(a, s);
   if (a.tn != 256 && a.tn != 512) return hipErrorInvalidValue;
   if (a.kh != 64 && (a.kh != 32 || a.tn != 256)) return hipErrorInvalidValue;
   const bool wide = a.tn == 512;

@@ -56,9 +56,13 @@ DOMINANT_KERNEL = {"bcsr": "bcsr_bf16_mfma", "wcsr": "wcsr_stream", "sp24": "sp2
 TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 
 
-def dominant_kernel(w) -> str:
+def dominant_kernel(w, pinfo=None) -> str:
+    """Kernel whose launch dominates a step; a BCSR plan with 128-row tiles
+    (paired block rows) runs the paired kernel."""
     if w.fmt in ("tvw", "sp24") and w.elem == "bf16":
         return "sp24_bf16_smfmac"
+    if w.fmt in ("bcsr", "bcsr_csr") and pinfo is not None and pinfo["tile_m"] == 128:
+        return "bcsr_bf16_pair"
     return DOMINANT_KERNEL[w.fmt]
 CSRC = os.path.join(ROOT, "sparse_dense_matrix_amd", "csrc")
 
@@ -315,8 +319,9 @@ def main():
 
     flops, nbytes, dtype = algorithmic(w, d)
     gflops = flops / (ms_step * 1e-3) / 1e9
-    roof, other = roofline(w, flops, nbytes, dtype, ms_step)
     pinfo = S.spmm_plan_info(d["P"])
+    kernel = dominant_kernel(w, pinfo)
+    roof, other = roofline(w, kernel, flops, nbytes, dtype, ms_step)
 
     cold = None
     if args.cold_steps > 0:
@@ -334,7 +339,7 @@ def main():
         torch.cuda.synchronize()
         times = np.array(sorted(e0.elapsed_time(e1) for e0, e1 in evs))
         ms_cold = float(np.median(times))
-        roof_c, other_c = roofline(w, flops, nbytes, dtype, ms_cold)
+        roof_c, other_c = roofline(w, kernel, flops, nbytes, dtype, ms_cold)
         cold = {"launches": args.cold_steps, "ms_median": round(ms_cold, 6),
                 "ms_min": round(float(times[0]), 6), "ms_max": round(float(times[-1]), 6),
                 "ms_stdev": round(float(times.std(ddof=1)) if len(times) > 1 else 0.0, 6),
@@ -374,6 +379,7 @@ def main():
                    "window_rows": d["info"]["window_rows"],
                    "max_chunk_nnz": d["info"]["max_chunk_nnz"],
                    "split_rows": pinfo["num_split_rows"], "grid": pinfo["grid"],
+                   "tile_m": pinfo["tile_m"], "tile_n": pinfo["tile_n"], "kernel": kernel,
                    **({"csr_nnz": int(d["a"]["row_ptr"][-1]), "reordered": w.reorder,
                        "scramble_seed": w.scramble} if w.scramble else {}),
                    "launch": (f"HIP graph of {args.graph} steps, replayed" if args.graph
@@ -484,11 +490,12 @@ def dense_baseline_i8(torch, w, d, Bt, stream, args, ms_sparse):
             "what": "torch._int_mm on the unpruned int8 A, same B, int32 C"}
 
 
-def roofline(w, flops, nbytes, dtype, ms_step):
+def roofline(w, kernel, flops, nbytes, dtype, ms_step):
     """(roofline of the binding bound, the other bound).  The binding bound is
-    the one whose time at peak is longer."""
+    the one whose time at peak is longer; `kernel` is the step's dominant
+    kernel, whose counters give `traffic`."""
     t = ms_step * 1e-3
-    traffic = measured_traffic(w.name, dominant_kernel(w))
+    traffic = measured_traffic(w.name, kernel)
     hbm = {"bound": "hbm", "achieved": round(nbytes / t / 1e9, 1), "peak": PEAK_HBM_GBS,
            "unit": "GB/s", "frac": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4),
            "traffic": traffic}

@@ -149,18 +149,27 @@ spmm_status_t plan_bcsr(spmm_plan_s *p) {
   if ((s = upload_vec(p, a.bcol_idx, &ci)) != SPMM_OK) return s;
   if ((s = upload_vec(p, frag, &fv)) != SPMM_OK) return s;
   const int32_t mb = static_cast<int32_t>(a.m / 64);
-  const BcsrSchedule sc = bcsr_schedule(a.brow_ptr.data(), mb, p->n);
+  BcsrSchedule sc = bcsr_schedule(a.brow_ptr.data(), mb, p->n);
   // Paired block rows (two rows per tile over the union of their block
-  // columns) at 256-wide half-block stages, when the pairing saves at least
-  // a tenth of the B slab loads and the pairs still give every CU several
-  // tiles.  Not for column-permuted A (the kernel reads B rows in place).
+  // columns, 256-wide half-block stages) when the pairing saves at least a
+  // tenth of the B slab loads and the pairs still give every CU several
+  // tiles; in place of the single-row schedules of 256-wide half-block
+  // stages and of 512-wide whole-block stages (not of 256-wide whole-block
+  // stages, which only rows of many blocks at small n take).  Not for
+  // column-permuted A (the kernel reads B rows in place).
   vec<int32_t> pair_rows, pair_ptr, units;
   bool paired = false;
-  if (sc.tn == kBcsrPairTN && sc.kh == kBcsrPairKH && a.col_perm.empty() && mb >= 2) {
+  const bool half_sched = sc.tn == kBcsrPairTN && sc.kh == kBcsrPairKH;
+  if ((half_sched || sc.tn == 512) && a.col_perm.empty() && mb >= 2) {
     const double saving = bcsr_pairing(a.brow_ptr.data(), a.bcol_idx.data(), mb,
                                        static_cast<int32_t>((a.k + 63) / 64), pair_rows, pair_ptr, units);
-    const int64_t tiles = static_cast<int64_t>(pair_ptr.size() - 1) * ((p->n + sc.tn - 1) / sc.tn);
+    const int64_t tiles =
+        static_cast<int64_t>(pair_ptr.size() - 1) * ((p->n + kBcsrPairTN - 1) / kBcsrPairTN);
     paired = saving >= kBcsrPairMinSaving && tiles >= kBcsrPairMinTiles;
+    if (paired) {
+      sc.tn = kBcsrPairTN;
+      sc.kh = kBcsrPairKH;
+    }
   }
   // tiles (block rows, or pairs) in dispatch order: most work first (ties by
   // index), so the longest tiles of a column tile start first and the short

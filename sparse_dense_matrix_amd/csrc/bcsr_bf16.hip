@@ -32,8 +32,10 @@
 //     its share of A stays resident.  Within an N tile the block rows with
 //     the most stored blocks come first (longest job first), so short tiles
 //     fill the end of the launch instead of long ones.
-// The kernel is bandwidth-bound by design: a 64-row block gives at most 64
-// flop per byte of B moved into LDS.
+// A 64-row block gives at most 64 flop per byte of B moved into LDS.  When
+// block rows share block columns, bcsr_bf16_pair (below) computes two block
+// rows per tile over the union of their block columns, so a B slab both
+// rows use is moved into LDS once.
 #include <algorithm>
 
 #include "internal.h"

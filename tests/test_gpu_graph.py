@@ -65,6 +65,15 @@ def test_graph_bcsr_and_reordered(S):
     _spmm_case(S, M, (S.BF16, S.BF16), synth.make_b(w), w.m, w.n, torch.int16)
 
 
+def test_graph_bcsr_paired_rows(S):
+    # the prefill layer's block pattern at n = 4288: two block rows per tile
+    import torch
+    w = synth.SMALL["bcsr_prefill_slice"]
+    M = S.spmm_pack_bcsr(synth.make_a(w)["dense"])
+    assert S.spmm_plan(M, w.n, S.BF16, S.BF16).info()["tile_m"] == 128
+    _spmm_case(S, M, (S.BF16, S.BF16), synth.make_b(w), w.m, w.n, torch.int16)
+
+
 def test_graph_wcsr_with_split_rows(S):
     import torch
     w = synth.SMALL["csr_powerlaw_small"]

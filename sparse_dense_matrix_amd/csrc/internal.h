@@ -274,6 +274,9 @@ struct Sp24Launch {
   // sliding-window A: lifted k-row j multiplies B row b_rows[j] (k_pad
   // entries, row 0 past k); the kernel reads B through it; null otherwise
   const int32_t *b_rows;
+  // tile-vector-wise A: the row tiles in dispatch order, groups of four per
+  // XCD (mtiles entries); null otherwise
+  const int32_t *row_order;
   int64_t m, k, n;
   int64_t m_pad, k_pad;
   int32_t tn;   // columns of C per workgroup (sp24_tile_n)

@@ -216,7 +216,7 @@ __device__ __forceinline__ void sp24_body(
     const int32_t *__restrict__ tile_ptr, const int32_t *__restrict__ tile_step, int64_t m,
     int64_t k, int64_t n, int64_t k_pad, int32_t mtiles, int32_t ntiles, int32_t tiles,
     int32_t per_xcd, const char *__restrict__ B, int64_t ldb, void *__restrict__ C, int64_t ldc,
-    const int32_t *__restrict__ b_rows) {
+    const int32_t *__restrict__ b_rows, const int32_t *__restrict__ row_order) {
   using G = Geo<E, kN>;
   using T = Tile<kN>;
   constexpr int kTK = G::kTK, kAVBytes = G::kAVBytes, kAMBytes = G::kAMBytes;
@@ -230,8 +230,19 @@ __device__ __forceinline__ void sp24_body(
   if (t >= tiles) return;
   const int grp = t / (kMG * ntiles), rem = t % (kMG * ntiles);
   const int gsize = min(kMG, mtiles - grp * kMG);
-  const int64_t m0 = static_cast<int64_t>(grp * kMG + rem % gsize) * kTM;
-  const int64_t n0 = static_cast<int64_t>(rem / gsize) * kN;
+  int64_t m0, n0;
+  if constexpr (kTiles) {
+    // row tiles of unequal work, in the plan's order (row_order), row slot
+    // slowest: with 16 column tiles the two workgroups a CU holds
+    // (workgroups j and j + 32 of an XCD) are slots 0 and 2, or 1 and 3, of
+    // the group, in the same column tile, and the plan puts a heavy and a
+    // light row tile in those slots
+    m0 = static_cast<int64_t>(row_order[grp * kMG + rem / ntiles]) * kTM;
+    n0 = static_cast<int64_t>(rem % ntiles) * kN;
+  } else {
+    m0 = static_cast<int64_t>(grp * kMG + rem % gsize) * kTM;
+    n0 = static_cast<int64_t>(rem / gsize) * kN;
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -455,8 +466,8 @@ __device__ __forceinline__ void sp24_body(
       const int32_t *__restrict__ tile_ptr, const int32_t *__restrict__ tile_step, int64_t m,   \
       int64_t k, int64_t n, int64_t k_pad, int32_t mtiles, int32_t ntiles, int32_t tiles,       \
       int32_t per_xcd, const char *__restrict__ B, int64_t ldb, void *__restrict__ C, int64_t ldc, \
-      const int32_t *__restrict__ b_rows
-#define SP24_PASS vals, meta, tile_ptr, tile_step, m, k, n, k_pad, mtiles, ntiles, tiles, per_xcd, B, ldb, C, ldc, b_rows
+      const int32_t *__restrict__ b_rows, const int32_t *__restrict__ row_order
+#define SP24_PASS vals, meta, tile_ptr, tile_step, m, k, n, k_pad, mtiles, ntiles, tiles, per_xcd, B, ldb, C, ldc, b_rows, row_order
 
 template <int kN, bool kTiles, bool kMap, bool kRagged>
 __global__ __launch_bounds__(Tile<kN>::kThreads) void sp24_i8_smfmac(SP24_ARGS) {
@@ -544,6 +555,7 @@ hipError_t launch(const Sp24Launch &a, hipStream_t s) {
   if (tiles == 0) return hipSuccess;
   if (tiles > INT32_MAX / 2 || a.k_pad * a.ldb * E::kElem > UINT32_MAX)
     return hipErrorInvalidValue;
+  if (kTiles && !a.row_order) return hipErrorInvalidValue;
   auto kernel = [] {
     if constexpr (E::kElem == 1) return sp24_i8_smfmac<kN, kTiles, kMap, kRagged>;
     else return sp24_bf16_smfmac<kN, kTiles, kRagged>;
@@ -556,7 +568,7 @@ hipError_t launch(const Sp24Launch &a, hipStream_t s) {
                      a.tile_step, a.m, a.k, a.n, a.k_pad, static_cast<int32_t>(mtiles),
                      static_cast<int32_t>(ntiles), static_cast<int32_t>(tiles),
                      static_cast<int32_t>(per_xcd), static_cast<const char *>(a.B), a.ldb, a.C,
-                     a.ldc, a.b_rows);
+                     a.ldc, a.b_rows, a.row_order);
   return hipGetLastError();
 }
 

@@ -312,19 +312,20 @@ __global__ __launch_bounds__(Geo<kTN>::kThreads) void bcsr_bf16_mfma(
   }
 }
 
-// Paired block rows: a tile is two block rows times 256 columns of C, eight
-// waves, waves 0-3 owning the first row's 64 x 256 and waves 4-7 the
-// second's.  The pair walks the union of its rows' block columns in column
-// order (units: column, block of the first row, block of the second, -1 for
+// Paired block rows: a tile is two block rows times 256 columns of C.  Each
+// wave owns 64 rows x kWC columns of one of the two rows (kWC = 128: 2 x 4
+// MFMA tiles, so each A fragment read from LDS feeds 4 MFMAs; four waves).
+// The pair walks the union of its rows' block columns in column order
+// (units: column, block of the first row, block of the second, -1 for
 // none), half a block per stage: a stage holds the 32 x 256 B half-slab and
 // both rows' A halves, so a B slab both rows use is loaded once instead of
 // twice.  Waves whose row has no block in a unit skip its MFMAs.
-// The ring has three stages (two units in flight while one is used): the
-// C staging area is as large as three stages anyway.  A unit's descriptor
-// is loaded a stage before its loads are issued, so the scalar load's
-// latency is not paid at the issue.  Everything else (DMA loads, swizzle,
-// transpose reads, epilogue, tile dealing with pairs in place of block
-// rows) is the single-row kernel's.
+// The ring has three stages (two units in flight while one is used), no
+// more LDS than the C staging takes anyway.  The unit descriptors sit in
+// registers, one per lane, and are read with v_readlane, so the loop never
+// waits on a scalar load.  Everything else (DMA loads, swizzle, transpose
+// reads, epilogue, tile dealing with pairs in place of block rows) is the
+// single-row kernel's.
 constexpr int kPairWaveCols = 128;  // C columns per wave in the paired kernel
 
 template <int kWC>

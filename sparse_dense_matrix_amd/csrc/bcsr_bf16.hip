@@ -586,6 +586,12 @@ double bcsr_pairing(const int32_t *row_ptr, const int32_t *col_idx, int32_t mb, 
   // block rows of each block column, ascending
   vec<int32_t> cptr(static_cast<size_t>(kb) + 1, 0), crows(static_cast<size_t>(nnzb));
   for (int64_t q = 0; q < nnzb; ++q) ++cptr[col_idx[q] + 1];
+  // the search below visits, for every block, the rows of its block column:
+  // the sum of the squared column counts; past kBcsrPairMaxWork the plan
+  // would take too long, and the rows are not paired
+  double visits = 0.0;
+  for (int32_t c = 0; c < kb; ++c) visits += static_cast<double>(cptr[c + 1]) * cptr[c + 1];
+  if (visits > kBcsrPairMaxWork) return 0.0;
   for (int32_t c = 0; c < kb; ++c) cptr[c + 1] += cptr[c];
   {
     vec<int32_t> fill(cptr.begin(), cptr.end() - 1);

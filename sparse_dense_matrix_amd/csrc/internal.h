@@ -174,10 +174,14 @@ constexpr double kBcsrPairMinSaving = 0.10;
 constexpr int64_t kBcsrPairMinTiles = 8 * 256;
 // a pair's units sit one per lane of a wave
 constexpr int32_t kBcsrPairMaxUnits = 64;
+// bound on the pairing search (row visits), which keeps plan time under a
+// second or so; larger patterns are not paired
+constexpr double kBcsrPairMaxWork = 1 << 28;
 // Pairs of block rows for the paired kernel: greedy, largest rows first, each
 // with the unpaired row sharing most block columns (ties: lowest index).
 // Returns the fraction of B slab loads the pairing saves; 0 when a pair would
-// exceed kBcsrPairMaxUnits (the pairing is then not to be used).
+// exceed kBcsrPairMaxUnits or the search kBcsrPairMaxWork (the pairing is
+// then not to be used).
 double bcsr_pairing(const int32_t *row_ptr, const int32_t *col_idx, int32_t mb, int32_t kb,
                     vec<int32_t> &pair_rows, vec<int32_t> &pair_ptr, vec<int32_t> &units);
 // Fragment order of one 64 x 64 block: [rb 2][s 4][lane 64][8 elements], lane l

@@ -131,6 +131,20 @@ def test_more_than_64_units_refuses(driver):
     assert saving == 0.0
 
 
+def test_search_beyond_its_bound_refuses(driver):
+    # 8,000 block rows at 30% of 56 block columns: the search would visit
+    # 56 * 2,400^2 = 3.2e8 rows, past the bound (2^28); no pairing.  At 7,000
+    # rows (2.5e8 visits) the rows are still paired.
+    r = np.random.default_rng(6)
+    for mb, paired in ((8000, False), (7000, True)):
+        mask = r.random((mb, 56)) < 0.3
+        rows = [np.nonzero(m)[0].tolist() for m in mask]
+        saving, pairs, units, rp = run_pairing(driver, rows, 56)
+        assert (saving > 0.1) == paired
+        if paired:
+            check_units(rows, rp, pairs, units)
+
+
 @pytest.mark.parametrize("name", ["bcsr_prefill_18944x3584", "bcsr_prefill_18944x3584_z70",
                                   "bcsr_4096_b64_90"])
 def test_benchmark_patterns_follow_the_rule(driver, name):

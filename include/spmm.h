@@ -262,6 +262,10 @@ void spmm_matrix_destroy(spmm_matrix_t a);
  *   SLIDE:                 (I8, I32), n % 16 == 0 (no workspace)
  * A BCSR matrix packed with reordering reads B's rows through its column
  * permutation (no workspace; spmm_execute then needs k * ldb * 2 < 2^32).
+ * Otherwise a BCSR plan may pair block rows that share block columns, so
+ * that a workgroup computes two block rows and loads a slab of B they both
+ * use once (spmm_plan_info then reports tile_m = 128); the result is the
+ * same product.
  * Anything else is UNSUPPORTED.  n = 0 is allowed (execute does nothing). */
 spmm_status_t spmm_plan(spmm_matrix_t a, int64_t n, spmm_dtype_t b_dtype,
                         spmm_dtype_t c_dtype, int32_t device, spmm_plan_t *out);

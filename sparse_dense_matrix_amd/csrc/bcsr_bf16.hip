@@ -550,15 +550,18 @@ BcsrSchedule bcsr_schedule(const int32_t *row_ptr, int32_t mb, int64_t n) {
   // small n the narrower tile gives more workgroups to fill the CUs.
   sc.tn = n >= 8192 ? 512 : 256;
   sc.row_groups = 1;
-  // Eight row groups when A would otherwise be walked from beyond L2 again
-  // for every N tile of an XCD (A larger than half an XCD's 4 MB L2) while an
+  // Row groups when A would otherwise be walked from beyond L2 again for
+  // every N tile of an XCD (A larger than half an XCD's 4 MB L2) while an
   // eighth of it fits in that half, and every group still has enough block
   // rows to fill an XCD's CUs.  The N tile is then 256 wide: its B slab
-  // shares L2 with the group's A, and two workgroups fit in a CU.  A larger A
-  // does not stay resident either way, and the split only costs B reuse.
+  // shares L2 with the group's A, and two workgroups fit in a CU.  Four
+  // groups, each served by two XCDs over half of the N tiles each, measured
+  // slightly faster than eight (a quarter of A per XCD, but half as many N
+  // tiles in flight per group).  A larger A does not stay resident either
+  // way, and the split only costs B reuse.
   const int64_t a_bytes = static_cast<int64_t>(row_ptr[mb]) * kABytes, half_l2 = 2 << 20;
   if (n >= 8192 && a_bytes > half_l2 && a_bytes <= 8 * half_l2 && mb >= 8 * 32) {
-    sc.row_groups = 8;
+    sc.row_groups = 4;
     sc.tn = 256;
   }
   // Half-block stages at 256 columns when block rows hold few blocks (at

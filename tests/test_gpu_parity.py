@@ -184,7 +184,8 @@ def test_bcsr_integer_values_many_blocks_per_row_exact(S, orc):
 
 def test_bcsr_integer_values_row_groups_exact(S, orc):
     # A of ~3.4 MB at n >= 8192 takes the row-group schedule (each XCD serves
-    # an eighth of the block rows); ragged last N tile, empty block rows;
+    # a quarter of the block rows over half the N tiles); ragged last N tile,
+    # empty block rows;
     # every row bit-exact over the first, an interior and the last columns
     m, k, n = 20480, 1024, 8200
     a = _int_bcsr(m, k, 420, 93, empty_rows=(0, 1, 2, 150))
@@ -280,8 +281,9 @@ def test_bcsr_many_blocks_per_row(S, orc):
 
 
 def test_bcsr_row_groups_skewed_rows(S, orc):
-    # A of ~7 MB at n >= 8192 takes the row-group schedule (each XCD serves an
-    # eighth of the block rows, 256-wide N tiles): empty block rows, one full
+    # A of ~7 MB at n >= 8192 takes the row-group schedule (each XCD serves a
+    # quarter of the block rows over half the N tiles, 256-wide N tiles): empty
+    # block rows, one full
     # block row, a ragged block-row count and a ragged last N tile
     m, k, n = 16576, 2048, 8200
     a, _ = synth.block_sparse_dense_bf16(m, k, 64, 64, 830, 0.02, 83)

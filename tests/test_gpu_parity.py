@@ -227,12 +227,15 @@ def test_bcsr_paired_block_rows_exact(S, orc):
     info = P.info()
     _say(f"bcsr paired rows: tile_m={info['tile_m']} tile_n={info['tile_n']} grid={info['grid']}")
     assert info["tile_m"] == 128 and info["tile_n"] == 256
-    got = run(S, P, B, m, n, "bf16")
-    assert_all_written(got, "bf16")
-    assert (got[26 * 64:32 * 64] & 0x7FFF == 0).all()
     rp, ci, v = orc.pack_bcsr(a, 64, 64)
-    for j0, j1 in ((0, 520), (3840, 4352), (n - 440, n)):
-        _assert_int_exact(got[:, j0:j1], orc.bcsr_spmm(64, 64, rp, ci, v, B, j0=j0, j1=j1))
+    refs = [(j0, j1, orc.bcsr_spmm(64, 64, rp, ci, v, B, j0=j0, j1=j1))
+            for j0, j1 in ((0, 520), (3840, 4352), (n - 440, n))]
+    for pad in (0, 24):                 # B and C with ld = n and ld = n + 24
+        got = run(S, P, B, m, n, "bf16", pad)
+        assert_all_written(got, "bf16")
+        assert (got[26 * 64:32 * 64] & 0x7FFF == 0).all()
+        for j0, j1, ref in refs:
+            _assert_int_exact(got[:, j0:j1], ref)
 
 
 def test_bcsr_pair_over_64_units_keeps_single_rows(S, orc):

@@ -28,8 +28,9 @@
 //     fastest: the workgroups resident on one XCD share the B column slab of
 //     one N tile in that XCD's L2.  When A is too large to stay in L2 while
 //     every N tile walks all of it, the plan splits the block rows into row
-//     groups of about equal work and gives each XCD one group's tiles, so
-//     its share of A stays resident.  Within an N tile the block rows with
+//     groups of about equal work and deals each group's tiles to its own
+//     XCDs (one, or two with half the N tiles each), so that share of A
+//     stays resident.  Within an N tile the block rows with
 //     the most stored blocks come first (longest job first), so short tiles
 //     fill the end of the launch instead of long ones.
 // A 64-row block gives at most 64 flop per byte of B moved into LDS.  When

@@ -510,41 +510,7 @@ spmm_status_t plan_tvw(spmm_plan_s *p) {
   for (size_t T = 0; T < a.brow_ptr.size(); ++T) ptr[T] = static_cast<int32_t>(a.brow_ptr[T] * per);
   for (int64_t t = 0; t < ntiles; ++t)
     for (int64_t s = 0; s < per; ++s) step[t * per + s] = static_cast<int32_t>(a.bcol_idx[t] * per + s);
-  // Row tiles hold different numbers of stored tiles.  The kernel deals
-  // groups of four row tiles to an XCD, row slot slowest, so that with 16
-  // column tiles (one round of workgroups) each CU holds slots 0 and 2, or
-  // 1 and 3, of a group.  Groups are filled heaviest first in snake order,
-  // which evens out their totals, and each group is ordered heaviest,
-  // second, lightest, third, which puts a heavy and a light row tile on
-  // each CU.
-  const int64_t mtiles = static_cast<int64_t>(a.brow_ptr.size()) - 1;
-  vec<int32_t> by_work(static_cast<size_t>(mtiles));
-  for (int64_t T = 0; T < mtiles; ++T) by_work[T] = static_cast<int32_t>(T);
-  std::stable_sort(by_work.begin(), by_work.end(), [&](int32_t x, int32_t y) {
-    return a.brow_ptr[x + 1] - a.brow_ptr[x] > a.brow_ptr[y + 1] - a.brow_ptr[y];
-  });
-  const int64_t groups = (mtiles + 3) / 4;
-  vec<vec<int32_t>> members(static_cast<size_t>(groups));
-  // only the last group may hold fewer than four (when mtiles % 4 != 0)
-  auto room = [&](int64_t g) {
-    return static_cast<int64_t>(members[static_cast<size_t>(g)].size()) < std::min<int64_t>(4, mtiles - 4 * g);
-  };
-  int64_t g = 0, dir = 1;
-  auto next_group = [&]() {  // snake order: 0 .. G-1, G-1 .. 0, 0 ..
-    if (g + dir < 0 || g + dir >= groups) dir = -dir;
-    else g += dir;
-  };
-  for (int64_t i = 0; i < mtiles; ++i) {
-    while (!room(g)) next_group();
-    members[static_cast<size_t>(g)].push_back(by_work[i]);
-    next_group();
-  }
-  vec<int32_t> order;
-  order.reserve(static_cast<size_t>(mtiles));
-  for (auto &mem : members) {
-    if (mem.size() == 4) std::swap(mem[2], mem[3]);  // heaviest, second, lightest, third
-    order.insert(order.end(), mem.begin(), mem.end());
-  }
+  const vec<int32_t> order = tvw_row_order(a.brow_ptr.data(), static_cast<int64_t>(a.brow_ptr.size()) - 1);
   Sp24Launch &L = p->sp24;
   spmm_status_t s;
   int8_t *dv = nullptr;

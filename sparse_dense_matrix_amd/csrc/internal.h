@@ -289,6 +289,16 @@ struct Sp24Launch {
   void *C;
   int64_t ldc;  // elements
 };
+// Dispatch order of the row tiles of a tile-vector-wise A (tile_ptr[T] ..
+// tile_ptr[T+1] are row tile T's stored tiles; mtiles row tiles).  The
+// kernel deals groups of four row tiles to an XCD, row slot slowest, so
+// that with 16 column tiles (one round of workgroups) each CU holds slots 0
+// and 2, or 1 and 3, of a group.  Groups are filled heaviest first in snake
+// order (0 .. G-1, G-1 .. 0, ...), which evens out their totals, and each
+// group of four is ordered heaviest, second, lightest, third, which puts a
+// heavy and a light row tile on each CU.  Only the last group may hold
+// fewer than four.
+vec<int32_t> tvw_row_order(const int32_t *tile_ptr, int64_t mtiles);
 // Plan-private copies of the canonical 2:4 arrays (values int8 or bf16),
 // zero-padded to m_pad x k_pad and laid out per 256-row tile and k-step
 // (sp24_tile_k) in the order the kernel's shared-memory stages hold them

@@ -43,6 +43,8 @@
 // the k-step, only the tiles holding a nonzero are stored (2:4 inside), and
 // a per-row-tile table lists their k-steps; the kernel walks that list
 // instead of every k-step, so a zero tile is never loaded.
+#include <algorithm>
+
 #include "internal.h"
 
 // load_lds16 below names m0 as clobbered on purpose (it sets m0 for the
@@ -573,6 +575,37 @@ hipError_t launch(const Sp24Launch &a, hipStream_t s) {
 }
 
 }  // namespace
+
+vec<int32_t> tvw_row_order(const int32_t *tile_ptr, int64_t mtiles) {
+  vec<int32_t> by_work(static_cast<size_t>(mtiles));
+  for (int64_t T = 0; T < mtiles; ++T) by_work[T] = static_cast<int32_t>(T);
+  std::stable_sort(by_work.begin(), by_work.end(), [&](int32_t x, int32_t y) {
+    return tile_ptr[x + 1] - tile_ptr[x] > tile_ptr[y + 1] - tile_ptr[y];
+  });
+  const int64_t groups = (mtiles + 3) / 4;
+  vec<vec<int32_t>> members(static_cast<size_t>(groups));
+  // only the last group may hold fewer than four (when mtiles % 4 != 0)
+  auto room = [&](int64_t g) {
+    return static_cast<int64_t>(members[static_cast<size_t>(g)].size()) < std::min<int64_t>(4, mtiles - 4 * g);
+  };
+  int64_t g = 0, dir = 1;
+  auto next_group = [&]() {  // snake order: 0 .. G-1, G-1 .. 0, 0 ..
+    if (g + dir < 0 || g + dir >= groups) dir = -dir;
+    else g += dir;
+  };
+  for (int64_t i = 0; i < mtiles; ++i) {
+    while (!room(g)) next_group();
+    members[static_cast<size_t>(g)].push_back(by_work[i]);
+    next_group();
+  }
+  vec<int32_t> order;
+  order.reserve(static_cast<size_t>(mtiles));
+  for (auto &mem : members) {
+    if (mem.size() == 4) std::swap(mem[2], mem[3]);  // heaviest, second, lightest, third
+    order.insert(order.end(), mem.begin(), mem.end());
+  }
+  return order;
+}
 
 void sp24_tile_layout(const void *vals, const uint8_t *meta, int64_t m, int64_t k, int64_t m_pad,
                       int64_t k_pad, bool bf16, void *vals_tiled, uint8_t *meta_tiled) {

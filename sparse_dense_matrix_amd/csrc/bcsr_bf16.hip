@@ -53,6 +53,9 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kBlk = 64;                  // block edge
@@ -114,9 +117,55 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
       reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char *)(p)));
 }
 
-__device__ __forceinline__ unsigned short to_bf16_rne(float f) {
-  // float -> bf16 conversion rounds to nearest even (v_cvt_pk_bf16_f32)
-  return __builtin_bit_cast(unsigned short, static_cast<__bf16>(f));
+// With B as the left MFMA operand the accumulators hold a tile transposed:
+// lane l has row 32 rb + (l & 31) of the wave's 64-row tile, and registers
+// 4q..4q+3 of acc[rb][cb] are its four consecutive columns
+// 32 cb + 8q + 4 (l >> 5) ...  Round them to bf16 two at a time and stage
+// the tile as rows of kPitch bytes, 8 bytes per write.
+template <int kCb, int kPitch>
+__device__ __forceinline__ void stage_c(char *ct, const f32x16 (&acc)[2][kCb], int lane) {
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < kCb; ++cb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int row = rb * 32 + (lane & 31);
+        const int col = cb * 32 + 8 * q + 4 * (lane >> 5);
+        const f32x16 &v = acc[rb][cb];
+        const bf16x2 lo = __builtin_convertvector((f32x2){v[4 * q], v[4 * q + 1]}, bf16x2);
+        const bf16x2 hi = __builtin_convertvector((f32x2){v[4 * q + 2], v[4 * q + 3]}, bf16x2);
+        *reinterpret_cast<u32x2 *>(ct + row * kPitch + col * 2) =
+            (u32x2){__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
+      }
+}
+
+// Write a staged 64 x (32 kCb) tile to C rows row0 .. row0 + 63 (through
+// c_rows when A was packed with its rows permuted), columns c0 ..: 16-byte
+// pieces, every piece read from LDS before the first store.
+template <int kCb, int kPitch>
+__device__ __forceinline__ void store_c(const char *ct, int lane, int64_t row0, int64_t c0, int64_t n,
+                                        const int32_t *__restrict__ c_rows, uint16_t *__restrict__ C,
+                                        int64_t ldc) {
+  constexpr int kPieces = kCb * 4, kRowsPer = 64 / kPieces, kQ = 64 / kRowsPer;
+  const int64_t col = c0 + (lane % kPieces) * 8;
+  if (col >= n) return;
+  u32x4 v[kQ];
+#pragma unroll
+  for (int q = 0; q < kQ; ++q)
+    v[q] = *reinterpret_cast<const u32x4 *>(ct + (q * kRowsPer + lane / kPieces) * kPitch +
+                                            (lane % kPieces) * 16);
+  const int64_t r = row0 + lane / kPieces;
+  if (c_rows) {
+#pragma unroll
+    for (int q = 0; q < kQ; ++q)
+      __builtin_nontemporal_store(
+          v[q], reinterpret_cast<u32x4 *>(C + static_cast<int64_t>(c_rows[r + q * kRowsPer]) * ldc + col));
+  } else {
+#pragma unroll
+    for (int q = 0; q < kQ; ++q)
+      __builtin_nontemporal_store(v[q], reinterpret_cast<u32x4 *>(C + (r + q * kRowsPer) * ldc + col));
+  }
 }
 
 struct Operands {
@@ -280,37 +329,17 @@ __global__ __launch_bounds__(Geo<kTN>::kThreads) void bcsr_bf16_mfma(
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
           acc[rb][cb] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(ops[s].a[rb], ops[s].b[cb], acc[rb][cb], 0, 0, 0);
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(ops[s].b[cb], ops[s].a[rb], acc[rb][cb], 0, 0, 0);
   }
 
-  // epilogue: accumulator element r of lane l is row 8*(r/4) + 4*(l/32) +
-  // r%4, column l%32 of its 32 x 32 tile.  Round to bf16, stage the wave's
-  // 64 x 64 tile in the idle ring, then write 16-byte pieces of C rows.
+  // epilogue: round to bf16, stage the wave's 64 x 64 tile in the idle ring
+  // (B was the left MFMA operand, so the accumulators hold it transposed),
+  // then write 16-byte pieces of C rows.
   barrier();  // every wave is done reading the ring
   char *ct = lds + wave * 64 * kCPitch;
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = rb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        const int col = cb * 32 + (lane & 31);
-        *reinterpret_cast<unsigned short *>(ct + row * kCPitch + col * 2) = to_bf16_rne(acc[rb][cb][r]);
-      }
+  stage_c<2, kCPitch>(ct, acc, lane);
   __builtin_amdgcn_wave_barrier();
-  const int64_t row0 = static_cast<int64_t>(br) * kBlk;
-  const int64_t col = n0 + wave * 64 + (lane & 7) * 8;
-  if (col < n) {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int row = q * 8 + (lane >> 3);
-      // packed row -> row of C (the identity unless A was packed permuted)
-      const int64_t crow = c_rows ? c_rows[row0 + row] : row0 + row;
-      const u32x4 v = *reinterpret_cast<const u32x4 *>(ct + row * kCPitch + (lane & 7) * 16);
-      __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(C + crow * ldc + col));
-    }
-  }
+  store_c<2, kCPitch>(ct, lane, static_cast<int64_t>(br) * kBlk, n0 + wave * 64, n, c_rows, C, ldc);
 }
 
 // Paired block rows: a tile is two block rows times 256 columns of C.  Each
@@ -386,6 +415,7 @@ __global__ __launch_bounds__(PairGeo<kWC>::kThreads, 2) void bcsr_bf16_pair(
   const int half = wave / G::kColWaves;  // which row of the pair
   const int cw = wave % G::kColWaves;    // which kWC columns
   const int u0 = pair_ptr[pr], nu = pair_ptr[pr + 1] - u0;
+  const int br = pair_rows[2 * pr + half];  // block row of C this wave writes (-1: none)
 
   uint32_t boff[kBLoads];
 #pragma unroll
@@ -496,8 +526,9 @@ __global__ __launch_bounds__(PairGeo<kWC>::kThreads, 2) void bcsr_bf16_pair(
         for (int cb = 0; cb < kCb; ++cb)
 #pragma unroll
           for (int rb = 0; rb < 2; ++rb)
+            // B is the left operand: the accumulators hold the tile transposed
             acc[rb][cb] =
-                __builtin_amdgcn_mfma_f32_32x32x16_bf16(ops[s].a[rb], ops[s].b[cb], acc[rb][cb], 0, 0, 0);
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(ops[s].b[cb], ops[s].a[rb], acc[rb][cb], 0, 0, 0);
     }
     cur = cur == 2 ? 0 : cur + 1;
     d0 = d1;
@@ -507,31 +538,9 @@ __global__ __launch_bounds__(PairGeo<kWC>::kThreads, 2) void bcsr_bf16_pair(
 
   barrier();  // every wave is done reading the ring
   char *ct = lds + wave * 64 * kPitch;
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int cb = 0; cb < kCb; ++cb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = rb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        const int col = cb * 32 + (lane & 31);
-        *reinterpret_cast<unsigned short *>(ct + row * kPitch + col * 2) = to_bf16_rne(acc[rb][cb][r]);
-      }
+  stage_c<kCb, kPitch>(ct, acc, lane);
   __builtin_amdgcn_wave_barrier();
-  // 16-byte pieces: kWC / 8 per row, 64 lanes cover kRowsPer rows at a time
-  constexpr int kPieces = kWC / 8, kRowsPer = 64 / kPieces;
-  const int br = pair_rows[2 * pr + half];
-  const int64_t col = n0 + cw * kWC + (lane % kPieces) * 8;
-  if (br >= 0 && col < n) {
-    const int64_t row0 = static_cast<int64_t>(br) * kBlk;
-#pragma unroll
-    for (int q = 0; q < 64 / kRowsPer; ++q) {
-      const int row = q * kRowsPer + lane / kPieces;
-      const int64_t crow = c_rows ? c_rows[row0 + row] : row0 + row;
-      const u32x4 v = *reinterpret_cast<const u32x4 *>(ct + row * kPitch + (lane % kPieces) * 16);
-      __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(C + crow * ldc + col));
-    }
-  }
+  if (br >= 0) store_c<kCb, kPitch>(ct, lane, static_cast<int64_t>(br) * kBlk, n0 + cw * kWC, n, c_rows, C, ldc);
 }
 
 }  // namespace

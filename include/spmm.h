@@ -266,7 +266,11 @@ void spmm_matrix_destroy(spmm_matrix_t a);
  * that a workgroup computes two block rows and loads a slab of B they both
  * use once (spmm_plan_info then reports tile_m = 128); the result is the
  * same product.
- * Anything else is UNSUPPORTED.  n = 0 is allowed (execute does nothing). */
+ * Anything else is UNSUPPORTED.  n = 0 is allowed (execute does nothing).
+ * With the environment variable SPMM_LOG set to anything but "" or "0"
+ * (read at each call), a plan that succeeds (this call or spmm_plan_sddmm)
+ * prints one line of its decisions on stderr: format, kernel(s), tile,
+ * grid, schedule, device and workspace bytes. */
 spmm_status_t spmm_plan(spmm_matrix_t a, int64_t n, spmm_dtype_t b_dtype,
                         spmm_dtype_t c_dtype, int32_t device, spmm_plan_t *out);
 

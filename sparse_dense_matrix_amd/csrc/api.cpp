@@ -542,6 +542,49 @@ spmm_status_t plan_tvw(spmm_plan_s *p) {
 
 bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
+// SPMM_LOG set to anything but "" or "0": every plan that succeeds prints
+// its decisions (kernel, tile, grid, schedule, device and workspace bytes)
+// as one line on stderr.  Read at each call.
+bool plan_log_on() {
+  const char *v = std::getenv("SPMM_LOG");
+  return v && v[0] && std::strcmp(v, "0") != 0;
+}
+
+void plan_log(const char *fn, const spmm_plan_s *p) {
+  static const char *const kFormat[] = {"bcsr", "wcsr", "24", "tvw", "slide"};
+  const Matrix &a = *p->a;
+  const spmm_plan_info_t &i = p->info;
+  const char *fmt = a.format >= 0 && a.format <= 4 ? kFormat[a.format] : "?";
+  std::string what;
+  if (p->sddmm && a.format == SPMM_FORMAT_WCSR) {
+    what = "kernel=sddmm_csr chunks=" + std::to_string(p->sdd.num_chunks);
+  } else if (p->sddmm) {
+    what = std::string("kernel=sddmm_bcsr_mfma") + (p->sddb.nsplit > 1 ? "+sddmm_bcsr_merge" : "") +
+           " groups=" + std::to_string(p->sddb.ngroups) + " ranges=" + std::to_string(p->sddb.nsplit);
+  } else if (a.format == SPMM_FORMAT_BCSR) {
+    const BcsrLaunch &L = p->bcsr;
+    what = std::string("kernel=") + (L.paired ? "bcsr_bf16_pair" : "bcsr_bf16_mfma") +
+           " row_groups=" + std::to_string(L.row_groups) + " stage_k=" + std::to_string(L.kh) +
+           (L.paired ? " pairs=" + std::to_string(L.npairs) : "") + (L.col_perm ? " reordered" : "");
+  } else if (a.format == SPMM_FORMAT_WCSR) {
+    what = std::string("kernel=wcsr_stream") + (p->wcsr.num_split_rows > 0 ? "+wcsr_merge" : "") +
+           " window_rows=" + std::to_string(a.window_rows) + " max_chunk_nnz=" +
+           std::to_string(a.max_chunk_nnz) + " chunks=" + std::to_string(p->wcsr.num_chunks) +
+           " split_rows=" + std::to_string(i.num_split_rows) + " slots=" + std::to_string(i.num_slots);
+  } else {
+    what = std::string("kernel=") + (p->sp24.bf16 ? "sp24_bf16_smfmac" : "sp24_i8_smfmac") +
+           " k_pad=" + std::to_string(p->sp24.k_pad);
+  }
+  std::fprintf(stderr,
+               "[spmm] %s: format=%s device=%d m=%lld k=%lld n=%lld %s tile=%dx%d grid=%lld "
+               "device_bytes=%lld workspace_bytes=%lld\n",
+               fn, fmt, static_cast<int>(i.device), static_cast<long long>(i.m),
+               static_cast<long long>(i.k), static_cast<long long>(i.n), what.c_str(),
+               static_cast<int>(i.tile_m), static_cast<int>(i.tile_n), static_cast<long long>(i.grid),
+               static_cast<long long>(i.device_bytes), static_cast<long long>(i.workspace_bytes));
+  std::fflush(stderr);
+}
+
 }  // namespace
 }  // namespace sdm
 
@@ -811,6 +854,7 @@ spmm_status_t spmm_plan(spmm_matrix_t a, int64_t n, spmm_dtype_t b_dtype, spmm_d
       return s;
     }
     *out = p;
+    if (plan_log_on()) plan_log("spmm_plan", p);
     return SPMM_OK;
   });
 }
@@ -964,6 +1008,7 @@ spmm_status_t spmm_plan_sddmm(spmm_matrix_t a, int64_t kd, spmm_dtype_t dtype, i
       return s;
     }
     *out = p;
+    if (plan_log_on()) plan_log("spmm_plan_sddmm", p);
     return SPMM_OK;
   });
 }

@@ -321,6 +321,35 @@ def test_bcsr_deterministic(S, orc):
     np.testing.assert_array_equal(x, y)
 
 
+def test_bcsr_schedules_agree_bitwise(S, orc):
+    # The prefill layer's block pattern at three widths of B: n = 1024 takes
+    # single-row tiles (too few pair tiles), n = 4288 paired block rows, n =
+    # 8192 paired rows in four row groups.  Every C element sees the same
+    # MFMAs in the same order under each schedule (stored blocks ascending,
+    # k-steps ascending), so the columns they share are equal bit for bit.
+    w = synth.SMALL["bcsr_prefill_slice"]
+    a = synth.make_a(w)["dense"]
+    B = synth.dense_bf16_normal(w.k, 8192, 86)
+    M = S.spmm_pack_bcsr(a)
+    outs, seen = {}, set()
+    for n in (1024, 4288, 8192):
+        P = S.spmm_plan(M, n, S.BF16, S.BF16)
+        info = P.info()
+        seen.add((info["tile_m"], info["tile_n"], info["grid"]))
+        _say(f"bcsr schedules: n={n} tile_m={info['tile_m']} tile_n={info['tile_n']} grid={info['grid']}")
+        outs[n] = run(S, P, np.ascontiguousarray(B[:, :n]), w.m, n, "bf16")
+        assert_all_written(outs[n], "bf16")
+    assert len(seen) == 3 and {t[0] for t in seen} == {64, 128}
+    np.testing.assert_array_equal(outs[1024], outs[4288][:, :1024])
+    np.testing.assert_array_equal(outs[1024], outs[8192][:, :1024])
+    np.testing.assert_array_equal(outs[4288], outs[8192][:, :4288])
+    # and against the oracle on a few rows, so that agreement is not shared error
+    rows = np.array([0, 1, 4095, 9000, w.m - 1], np.int64)
+    rp, ci, v = orc.pack_bcsr(a, 64, 64)
+    ref = orc.bcsr_spmm(64, 64, rp, ci, v, np.ascontiguousarray(B[:, :1024]), rows=rows)
+    assert orc.rel_frobenius(bf16_to_f64(outs[1024][rows]), ref) <= TOL_BF16
+
+
 # ---------------------------------------------------------------------------
 # WCSR fp32
 # ---------------------------------------------------------------------------

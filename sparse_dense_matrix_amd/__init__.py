@@ -33,6 +33,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("SPMM_LIBRARY") or os.path.join(HERE, "libspmm.so")
 
 F32, BF16, I8, I32 = 0, 1, 2, 3
+_ELEM = {F32: 4, BF16: 2, I8: 1, I32: 4}  # bytes per element of each type
 FORMAT_BCSR, FORMAT_WCSR, FORMAT_24, FORMAT_TVW, FORMAT_SLIDE = 0, 1, 2, 3, 4
 (ARRAY_ROW_PTR, ARRAY_COL_IDX, ARRAY_VALS, ARRAY_META, ARRAY_CHUNK_WINDOW,
  ARRAY_CHUNK_BEGIN, ARRAY_ROW_PERM, ARRAY_COL_PERM) = range(8)
@@ -158,10 +159,16 @@ class Matrix:
 
 
 class Plan:
-    """Owns a device plan (and through it a reference to its matrix)."""
+    """Owns a device plan (and through it a reference to its matrix).
 
-    def __init__(self, handle):
+    `expect` maps each dense operand of an execute call to (rows, cols,
+    bytes per element), or ("count", n, bytes) for the SDDMM output, plus
+    "device"; torch tensors handed to execute are checked against it so that
+    a kernel never reads or writes past them."""
+
+    def __init__(self, handle, expect=None):
         self.handle = handle
+        self.expect = expect or {}
 
     def __del__(self):
         h, self.handle = getattr(self, "handle", None), None
@@ -302,7 +309,9 @@ def spmm_matrix_array(mat: Matrix, which: int) -> np.ndarray:
 def spmm_plan(mat: Matrix, n: int, b_dtype: int, c_dtype: int, device: int = 0) -> Plan:
     h = C.c_void_p()
     _check(_lib.spmm_plan(mat.handle, n, b_dtype, c_dtype, device, C.byref(h)), "spmm_plan")
-    return Plan(h)
+    mi = spmm_matrix_info(mat)
+    return Plan(h, {"b": (mi["k"], n, _ELEM[b_dtype]), "c": (mi["m"], n, _ELEM[c_dtype]),
+                    "device": device})
 
 
 def spmm_plan_info(plan: Plan) -> dict:
@@ -321,12 +330,32 @@ def _dev_ptr_ld(t):
     return t.data_ptr(), t.stride(0)
 
 
+def _check_tensor(plan: Plan, name: str, t):
+    """Shape, element size and device of a torch tensor against the plan."""
+    want = plan.expect.get(name)
+    if want is None:
+        return
+    dev = plan.expect["device"]
+    if not t.is_cuda or (t.device.index if t.device.index is not None else 0) != dev:
+        raise ValueError(f"{name} must be on cuda:{dev}")
+    rows, cols, elem = want
+    if t.element_size() != elem:
+        raise ValueError(f"{name} has {t.element_size()}-byte elements; the plan takes {elem}")
+    if rows == "count":
+        if t.numel() < cols or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous with at least {cols} elements")
+    elif tuple(t.shape) != (rows, cols):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}; the plan takes ({rows}, {cols})")
+
+
 def _execute(fn: str, plan: Plan, b, c, stream, ldb, ldc):
     if isinstance(b, int) or isinstance(c, int):
         bp, cp = int(b), int(c)
         if ldb is None or ldc is None:
             raise ValueError("raw pointers need ldb and ldc")
     else:
+        _check_tensor(plan, "b", b)
+        _check_tensor(plan, "c", c)
         bp, ldb = _dev_ptr_ld(b)
         cp, ldc = _dev_ptr_ld(c)
     if stream is None:
@@ -362,7 +391,11 @@ def spmm_plan_sddmm(mat: Matrix, kd: int, dtype: int = F32, device: int = 0) -> 
     matrix, inner dimension kd."""
     h = C.c_void_p()
     _check(_lib.spmm_plan_sddmm(mat.handle, kd, dtype, device, C.byref(h)), "spmm_plan_sddmm")
-    return Plan(h)
+    mi = spmm_matrix_info(mat)
+    count = mi["nnzb"] * 64 * 64 if mi["format"] == 0 else mi["nnz"]
+    out_elem = {F32: 4, BF16: 2, I8: 4}[dtype]
+    return Plan(h, {"x": (mi["m"], kd, _ELEM[dtype]), "y": (mi["k"], kd, _ELEM[dtype]),
+                    "out": ("count", count, out_elem), "device": device})
 
 
 def spmm_execute_sddmm(plan: Plan, x, y, out, stream=None, ldx: int | None = None,
@@ -377,8 +410,12 @@ def spmm_execute_sddmm(plan: Plan, x, y, out, stream=None, ldx: int | None = Non
         if ldx is None or ldy is None:
             raise ValueError("raw pointers need ldx and ldy")
     else:
+        _check_tensor(plan, "x", x)
+        _check_tensor(plan, "y", y)
         xp, ldx = _dev_ptr_ld(x)
         yp, ldy = _dev_ptr_ld(y)
+    if not isinstance(out, int):
+        _check_tensor(plan, "out", out)
     op = int(out) if isinstance(out, int) else out.data_ptr()
     if stream is None:
         import torch

@@ -670,6 +670,34 @@ def test_execute_rejects_bad_layouts(S):
     assert ei.value.name == "SPMM_ERR_UNSUPPORTED"
 
 
+def test_binding_checks_tensors_against_the_plan(S):
+    # torch tensors handed to execute must have the plan's shapes, element
+    # sizes and device; a mismatch is refused before anything is launched
+    torch = pytest.importorskip("torch")
+    M = S.spmm_pack_bcsr(np.zeros((128, 64), np.uint16))
+    P = S.spmm_plan(M, 64, S.BF16, S.BF16)
+    B = torch.zeros((64, 64), dtype=torch.int16, device="cuda")
+    Cm = torch.zeros((128, 64), dtype=torch.int16, device="cuda")
+    S.spmm_execute(P, B, Cm)
+    for b, c, what in ((B[:32], Cm, "shape"), (B, Cm[:, :32], "shape"),
+                       (B.float(), Cm, "element"), (B, Cm.cpu(), "cuda"),
+                       (torch.zeros((64, 128), dtype=torch.int16, device="cuda"), Cm, "shape")):
+        with pytest.raises(ValueError, match=what):
+            S.spmm_execute(P, b, c)
+    Mw = S.spmm_pack_wcsr(4, 8, np.array([0, 1, 1, 2, 3], np.int64), np.array([0, 7, 3], np.int32),
+                          np.ones(3, np.float32))
+    Q = S.spmm_plan_sddmm(Mw, 16)
+    X = torch.zeros((4, 16), device="cuda")
+    Y = torch.zeros((8, 16), device="cuda")
+    out = torch.zeros(3, device="cuda")
+    S.spmm_execute_sddmm(Q, X, Y, out)
+    torch.cuda.synchronize()
+    for x, y, o, what in ((X[:, :8], Y, out, "shape"), (X, Y[:4], out, "shape"),
+                          (X, Y, out[:2], "at least 3"), (X, Y, out.double(), "element")):
+        with pytest.raises(ValueError, match=what):
+            S.spmm_execute_sddmm(Q, x, y, o)
+
+
 def test_two_plans_two_streams(S, orc):
     torch = pytest.importorskip("torch")
     w1, w2 = synth.SMALL["csr_powerlaw_small"], synth.SMALL["bcsr_small"]
